@@ -1,0 +1,211 @@
+"""Python binding of libmoedecode: same names as the C ABI, marshalling only.
+
+Device buffers are torch tensors (their ``data_ptr()`` is passed), host
+buffers are numpy arrays or pinned torch tensors, streams are
+``torch.cuda.Stream`` objects (or raw hipStream_t ints; None means torch's
+current stream). Every step of the layer runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib as L
+
+MOE_F_RMSNORM_IN = 1
+MOE_F_RESIDUAL = 2
+STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EALIGN", -4: "MOE_EHIP",
+          -5: "MOE_ENOMEM", -6: "MOE_ESTATE"}
+
+moe_decode_stats = L.moe_decode_stats
+moe_cache_event = L.moe_cache_event
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, text: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+def lib():
+    return L.load()
+
+
+def _check(st: int, fn: str) -> None:
+    if st != 0:
+        raise MoeError(st, fn, lib().moe_last_error().decode())
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def make_shape(sh) -> L.moe_shape:
+    return L.moe_shape(sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter,
+                       getattr(sh, "group", 32))
+
+
+# ------------------------------------------------------------------ misc
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_expert_bytes(hidden: int, inter: int) -> int:
+    return lib().moe_expert_bytes(hidden, inter)
+
+
+def moe_blob_layout_of(hidden: int, inter: int) -> dict:
+    out = L.moe_blob_layout()
+    _check(lib().moe_blob_layout_of(hidden, inter, C.byref(out)), "moe_blob_layout_of")
+    return {n: getattr(out, n) for n, _ in L.moe_blob_layout._fields_}
+
+
+# ------------------------------------------------------------------ routing
+def moe_route_workspace_bytes(sh, B: int) -> int:
+    s = make_shape(sh)
+    return lib().moe_route_workspace_bytes(C.byref(s), B)
+
+
+def moe_route(sh, x, wr, bias, logits_in, B, ids, w, workspace=None, stream=None):
+    s = make_shape(sh)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_route(C.byref(s), _p(x), _p(wr), _p(bias), _p(logits_in), B, _p(ids), _p(w),
+                           _p(workspace), ws_bytes, _stream(stream)), "moe_route")
+
+
+# ------------------------------------------------------------------ LFU cache
+def moe_cache_create(n_slots: int, n_experts: int) -> int:
+    h = C.c_void_p()
+    _check(lib().moe_cache_create(n_slots, n_experts, C.byref(h)), "moe_cache_create")
+    return h.value
+
+
+def moe_cache_destroy(h) -> None:
+    lib().moe_cache_destroy(h)
+
+
+def moe_cache_step(h, ids):
+    """Returns (events int32 [k][4] = expert, slot, hit, evicted; n_miss)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    k = ids.size
+    ev = (L.moe_cache_event * max(k, 1))()
+    n = C.c_int32(0)
+    _check(lib().moe_cache_step(h, ids.ctypes.data_as(C.POINTER(C.c_int32)), k, ev, C.byref(n)),
+           "moe_cache_step")
+    return events_to_array(ev, k), n.value
+
+
+def events_to_array(ev, k: int) -> np.ndarray:
+    return np.array([[e.expert, e.slot, e.hit, e.evicted] for e in ev[:k]], dtype=np.int32).reshape(k, 4)
+
+
+def moe_cache_reset(h) -> None:
+    _check(lib().moe_cache_reset(h), "moe_cache_reset")
+
+
+def moe_cache_slots(h, n_slots: int):
+    ex = np.zeros(n_slots, np.int32)
+    fr = np.zeros(n_slots, np.int32)
+    la = np.zeros(n_slots, np.int64)
+    _check(lib().moe_cache_slots(h, ex.ctypes.data_as(C.POINTER(C.c_int32)),
+                                 fr.ctypes.data_as(C.POINTER(C.c_int32)),
+                                 la.ctypes.data_as(C.POINTER(C.c_int64)), n_slots), "moe_cache_slots")
+    return ex, fr, la
+
+
+def moe_cache_counters(h):
+    a, b, c = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(lib().moe_cache_counters(h, C.byref(a), C.byref(b), C.byref(c)), "moe_cache_counters")
+    return a.value, b.value, c.value
+
+
+# ------------------------------------------------------------------ GEMV
+def moe_expert_gemv_q4(q, s, N, K, x, M, y, stream=None):
+    W = L.moe_q4(_p(q), _p(s))
+    _check(lib().moe_expert_gemv_q4(C.byref(W), N, K, _p(x), M, _p(y), _stream(stream)),
+           "moe_expert_gemv_q4")
+
+
+def moe_debug_unpack_q4(q, N, K, out, stream=None):
+    W = L.moe_q4(_p(q), None)
+    _check(lib().moe_debug_unpack_q4(C.byref(W), N, K, _p(out), _stream(stream)), "moe_debug_unpack_q4")
+
+
+# ------------------------------------------------------------------ layer
+def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
+    s = make_shape(sh)
+    out = C.c_size_t(0)
+    _check(lib().moe_layer_workspace_bytes(C.byref(s), max_B, max_T, C.byref(out)),
+           "moe_layer_workspace_bytes")
+    return out.value
+
+
+def moe_layer_create(sh, *, router, shared_blob, workspace, bias=None, experts_dev=None,
+                     experts_host=None, slot_pool=None, n_slots=0, copy_stream=None, max_B=1,
+                     max_T=0) -> int:
+    s = make_shape(sh)
+    d = L.moe_layer_desc(_p(router), _p(bias), _p(shared_blob), _p(experts_dev), _p(experts_host),
+                         _p(slot_pool), n_slots,
+                         None if copy_stream is None else _stream(copy_stream),
+                         _p(workspace), workspace.numel() * workspace.element_size())
+    h = C.c_void_p()
+    _check(lib().moe_layer_create(C.byref(s), C.byref(d), max_B, max_T, C.byref(h)), "moe_layer_create")
+    return h.value
+
+
+def moe_layer_destroy(h) -> None:
+    lib().moe_layer_destroy(h)
+
+
+def moe_layer_set_experts(h, experts_dev) -> None:
+    _check(lib().moe_layer_set_experts(h, _p(experts_dev)), "moe_layer_set_experts")
+
+
+def moe_layer_cache(h):
+    return lib().moe_layer_cache(h)
+
+
+def moe_layer_decode(h, x, add_in, B, flags, y, ids_out=None, w_out=None, u_out=None,
+                     trace_k: int = 0, stats=None, stream=None):
+    """Returns the cache events as int32 [B*k][4] when trace_k > 0 (cache mode), else None."""
+    ev = (L.moe_cache_event * (B * trace_k))() if trace_k else None
+    st = lib().moe_layer_decode(h, _p(x), _p(add_in), B, flags, _p(y), _p(ids_out), _p(w_out),
+                                _p(u_out), ev, None if stats is None else C.byref(stats),
+                                _stream(stream))
+    _check(st, "moe_layer_decode")
+    return events_to_array(ev, B * trace_k) if trace_k else None
+
+
+def moe_layer_prefill(h, x_bf16, logits_in, T, y, ids_out=None, w_out=None, stream=None):
+    _check(lib().moe_layer_prefill(h, _p(x_bf16), _p(logits_in), T, _p(y), _p(ids_out), _p(w_out),
+                                   _stream(stream)), "moe_layer_prefill")
+
+
+def moe_layer_profile(h, enable: bool) -> None:
+    _check(lib().moe_layer_profile(h, 1 if enable else 0), "moe_layer_profile")
+
+
+def moe_layer_profile_read(h, kind: int):
+    out = L.moe_kernel_time()
+    _check(lib().moe_layer_profile_read(h, kind, C.byref(out)), "moe_layer_profile_read")
+    return out.launches, out.ms_total

@@ -1,0 +1,119 @@
+// C-ABI entry points that need no layer handle: blob layout, routing, the
+// standalone int4 GEMV and the nibble unpack. Every argument is checked
+// before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include "host_common.h"
+#include "launch.h"
+
+using moe::fail;
+
+namespace moe {
+
+moe_status check_shape(const moe_shape* sh, const char* fn) {
+  if (!sh) return fail(MOE_EINVAL, "%s: shape is NULL", fn);
+  if (sh->group != kGroup) return fail(MOE_ESHAPE, "%s: group must be 32 (got %d)", fn, sh->group);
+  if (sh->hidden < kGroup || sh->hidden > MOE_MAX_DIM || sh->hidden % kGroup)
+    return fail(MOE_ESHAPE, "%s: hidden %d must be a multiple of 32 in [32, %d]", fn, sh->hidden, MOE_MAX_DIM);
+  if (sh->n_experts < 1 || sh->n_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ESHAPE, "%s: n_experts %d outside [1, %d]", fn, sh->n_experts, MOE_MAX_EXPERTS);
+  if (sh->top_k < 1 || sh->top_k > sh->n_experts || sh->top_k > MOE_MAX_TOPK)
+    return fail(MOE_ESHAPE, "%s: top_k %d outside [1, min(n_experts, %d)]", fn, sh->top_k, MOE_MAX_TOPK);
+  if (sh->inter < kGroup || sh->inter > MOE_MAX_DIM || sh->inter % kGroup)
+    return fail(MOE_ESHAPE, "%s: inter %d must be a multiple of 32 in [32, %d]", fn, sh->inter, MOE_MAX_DIM);
+  if (sh->shared_inter < kGroup || sh->shared_inter > MOE_MAX_DIM || sh->shared_inter % kGroup)
+    return fail(MOE_ESHAPE, "%s: shared_inter %d must be a multiple of 32 in [32, %d]", fn,
+                sh->shared_inter, MOE_MAX_DIM);
+  return MOE_OK;
+}
+
+size_t route_ws_bytes(const moe_shape* sh, int32_t B) {
+  return (static_cast<size_t>(B) * sh->n_experts * sizeof(double) + 255) & ~static_cast<size_t>(255);
+}
+
+}  // namespace moe
+
+#define HIP_OR_FAIL(expr, fn)                                                        \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" {
+
+size_t moe_expert_bytes(int32_t hidden, int32_t inter) {
+  if (hidden <= 0 || inter <= 0 || hidden % moe::kGroup || inter % moe::kGroup) return 0;
+  return moe::blob_offsets(hidden, inter).total;
+}
+
+moe_status moe_blob_layout_of(int32_t hidden, int32_t inter, moe_blob_layout* out) {
+  moe::clear_error();
+  if (!out) return fail(MOE_EINVAL, "moe_blob_layout_of: out is NULL");
+  if (moe_expert_bytes(hidden, inter) == 0)
+    return fail(MOE_ESHAPE, "moe_blob_layout_of: hidden %d / inter %d not positive multiples of 32", hidden, inter);
+  const moe::BlobOffsets o = moe::blob_offsets(hidden, inter);
+  *out = moe_blob_layout{o.gate_q, o.up_q, o.down_q, o.gate_s, o.up_s, o.down_s, o.total};
+  return MOE_OK;
+}
+
+size_t moe_route_workspace_bytes(const moe_shape* sh, int32_t B) {
+  if (!sh || B < 0 || sh->n_experts < 1) return 0;
+  return moe::route_ws_bytes(sh, B);
+}
+
+moe_status moe_route(const moe_shape* sh, const float* x, const uint16_t* wr, const float* bias,
+                     const float* logits_in, int32_t B, int32_t* ids, float* w, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_route";
+  moe_status st = moe::check_shape(sh, fn);
+  if (st) return st;
+  if (B < 0) return fail(MOE_ESHAPE, "%s: B=%d is negative", fn, B);
+  if (B == 0) return MOE_OK;
+  if (!ids || !w) return fail(MOE_EINVAL, "%s: ids and w must not be NULL", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (logits_in) {
+    HIP_OR_FAIL(moe::launch_route_topk(nullptr, logits_in, B, sh->n_experts, sh->top_k, ids, w,
+                                       nullptr, nullptr, s), fn);
+    return MOE_OK;
+  }
+  if (!x || !wr) return fail(MOE_EINVAL, "%s: x and wr must not be NULL without logits_in", fn);
+  if (!workspace) return fail(MOE_EINVAL, "%s: workspace is NULL", fn);
+  if (!moe::aligned16(x) || !moe::aligned16(wr) || !moe::aligned16(workspace))
+    return fail(MOE_EALIGN, "%s: x, wr and workspace must be 16-byte aligned", fn);
+  if (workspace_bytes < moe::route_ws_bytes(sh, B))
+    return fail(MOE_ENOMEM, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
+                moe::route_ws_bytes(sh, B));
+  double* z = static_cast<double*>(workspace);
+  HIP_OR_FAIL(moe::launch_route_logits(x, B, sh->hidden, wr, bias, sh->n_experts, z, s), fn);
+  HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, sh->n_experts, sh->top_k, ids, w, nullptr,
+                                     nullptr, s), fn);
+  return MOE_OK;
+}
+
+moe_status moe_expert_gemv_q4(const moe_q4* W, int32_t N, int32_t K, const float* x, int32_t M,
+                              float* y, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_expert_gemv_q4";
+  if (!W || !W->q || !W->s || !x || !y) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (K < moe::kGroup || K % moe::kGroup || K > MOE_MAX_DIM)
+    return fail(MOE_ESHAPE, "%s: K=%d must be a multiple of 32 in [32, %d]", fn, K, MOE_MAX_DIM);
+  if (N < 0 || M < 0 || M > 64) return fail(MOE_ESHAPE, "%s: N=%d, M=%d (need N >= 0, 0 <= M <= 64)", fn, N, M);
+  if (!moe::aligned16(W->q) || !moe::aligned16(x))
+    return fail(MOE_EALIGN, "%s: W.q and x must be 16-byte aligned", fn);
+  if (N == 0 || M == 0) return MOE_OK;
+  HIP_OR_FAIL(moe::launch_gemv_q4(W->q, W->s, N, K, x, M, y, static_cast<hipStream_t>(stream)), fn);
+  return MOE_OK;
+}
+
+moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* out, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_debug_unpack_q4";
+  if (!W || !W->q || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (K < 2 || K % 2 || N < 0) return fail(MOE_ESHAPE, "%s: N=%d, K=%d", fn, N, K);
+  if (N == 0) return MOE_OK;
+  HIP_OR_FAIL(moe::launch_unpack_q4(W->q, N, K, out, static_cast<hipStream_t>(stream)), fn);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device helpers shared by the libmoedecode kernels (gfx950, wave64).
+//
+// Activation vectors are carried into the int4 GEMVs as "digit planes": each
+// group of 32 consecutive fp32 values gets one scale sc = max|x| / kQmax and
+// a signed integer q = rint(x / sc) with |q| <= kQmax, written in balanced
+// base 16 as q = d0 + 16 d1 + 256 d2 + 4096 d3 with every digit in -8..7.
+// Digit d of elements [8p, 8p+8) of the group is packed into one 32-bit word
+// (element 8p+i in bits 4i..4i+3), the same order in which the weight bytes
+// hold their nibbles. One v_dot8_i32_i4 then multiplies 8 signed weight
+// nibbles by 8 signed digits and accumulates in int32, so a 16-byte weight
+// chunk (32 nibbles, exactly one quantisation group) costs 16 dot8 and a
+// handful of scalar ops, with no nibble unpacking at all. The weight side is
+// exact; the activation side is rounded to 16 bits relative to its group's
+// largest magnitude (error <= max|x_g| / (2 kQmax) per element).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 32;
+// Largest |q| whose balanced base-16 expansion has d3 in -8..7 on both signs.
+constexpr int kQmax = 30583;
+constexpr int kWave = 64;
+
+// Digit planes of one group: 4 positions x uint4 (digit words 0..3).
+struct DigitGroup {
+  uint4 p[4];
+};
+
+__device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot8(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// Sum over L consecutive lanes (L a power of two <= 64); every lane of the
+// L-lane segment receives the total.
+template <int L>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int L>
+__device__ __forceinline__ double seg_sum_f64(double v) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// GELU, tanh form: z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  return 0.5f * z * (1.0f + tanhf(k0 * (z + k1 * z * z * z)));
+}
+
+// Quantise two groups of 32 values to digit planes; called by a whole wave.
+// Lanes 0-31 take group g0, lanes 32-63 group g0+1 (skipped when >= ng).
+// v is the lane's value (already loaded); writes dig[g] and sc[g].
+__device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, DigitGroup* dig,
+                                                     float* sc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = g0 + (lane >> 5);
+  const int i = lane & 31;
+  float m = fabsf(v);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
+  int q = static_cast<int>(rintf(v * inv));
+  q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
+  const int d0 = ((q + 8) & 15) - 8;
+  q = (q - d0) / 16;
+  const int d1 = ((q + 8) & 15) - 8;
+  q = (q - d1) / 16;
+  const int d2 = ((q + 8) & 15) - 8;
+  const int d3 = (q - d2) / 16;
+  const int sh = 4 * (i & 7);
+  uint32_t w0 = static_cast<uint32_t>(d0 & 15) << sh;
+  uint32_t w1 = static_cast<uint32_t>(d1 & 15) << sh;
+  uint32_t w2 = static_cast<uint32_t>(d2 & 15) << sh;
+  uint32_t w3 = static_cast<uint32_t>(d3 & 15) << sh;
+#pragma unroll
+  for (int o = 4; o > 0; o >>= 1) {
+    w0 |= __shfl_xor(w0, o, kWave);
+    w1 |= __shfl_xor(w1, o, kWave);
+    w2 |= __shfl_xor(w2, o, kWave);
+    w3 |= __shfl_xor(w3, o, kWave);
+  }
+  if (g < ng) {
+    if ((i & 7) == 0) dig[g].p[i >> 3] = make_uint4(w0, w1, w2, w3);
+    if (i == 0) sc[g] = m / static_cast<float>(kQmax);
+  }
+}
+
+// Integer dot of one 16-byte weight chunk (32 nibbles) with one digit group:
+// returns sum_i nibble_i * q_i exactly (|result| < 2^24).
+__device__ __forceinline__ int chunk_dot(const uint4 w, const DigitGroup& x) {
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  a0 = sdot8(w.x, x.p[0].x, a0);
+  a1 = sdot8(w.x, x.p[0].y, a1);
+  a2 = sdot8(w.x, x.p[0].z, a2);
+  a3 = sdot8(w.x, x.p[0].w, a3);
+  a0 = sdot8(w.y, x.p[1].x, a0);
+  a1 = sdot8(w.y, x.p[1].y, a1);
+  a2 = sdot8(w.y, x.p[1].z, a2);
+  a3 = sdot8(w.y, x.p[1].w, a3);
+  a0 = sdot8(w.z, x.p[2].x, a0);
+  a1 = sdot8(w.z, x.p[2].y, a1);
+  a2 = sdot8(w.z, x.p[2].z, a2);
+  a3 = sdot8(w.z, x.p[2].w, a3);
+  a0 = sdot8(w.w, x.p[3].x, a0);
+  a1 = sdot8(w.w, x.p[3].y, a1);
+  a2 = sdot8(w.w, x.p[3].z, a2);
+  a3 = sdot8(w.w, x.p[3].w, a3);
+  return a0 + 16 * a1 + 256 * a2 + 4096 * a3;
+}
+
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+
+// Streaming 16-byte load of weight bytes (read once per call).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_w16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+}  // namespace moe

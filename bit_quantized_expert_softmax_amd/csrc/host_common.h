@@ -1,0 +1,34 @@
+// Host-side helpers shared by the C-ABI entry points: thread-local error
+// text, status returns and argument checks. No HIP dependency.
+#pragma once
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/moedecode.h"
+
+namespace moe {
+
+std::string& last_error_text();
+
+inline moe_status fail(moe_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  last_error_text() = buf;
+  return code;
+}
+
+// Copies the whole state of one cache into another of the same size.
+void cache_assign(moe_cache* dst, const moe_cache* src);
+
+inline void clear_error() { last_error_text().clear(); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace moe

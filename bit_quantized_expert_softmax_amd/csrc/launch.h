@@ -1,0 +1,74 @@
+// Kernel launchers used by the C-ABI layer. Each returns the HIP status of
+// its launch; argument checking happens before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace moe {
+
+constexpr int kMaxTopK = 16;
+
+// Byte offsets inside one expert blob (gate.q | up.q | down.q | gate.s | up.s | down.s).
+struct BlobOffsets {
+  size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+};
+__host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
+  BlobOffsets o;
+  o.gate_q = 0;
+  o.up_q = I * H / 2;
+  o.down_q = I * H;
+  o.gate_s = 3 * I * H / 2;
+  o.up_s = o.gate_s + I * (H / kGroup) * 2;
+  o.down_s = o.up_s + I * (H / kGroup) * 2;
+  o.total = o.down_s + H * (I / kGroup) * 2;
+  return o;
+}
+
+// ---------------------------------------------------------------- routing
+// x' = x (+ add_in); u = x' or rmsnorm(x'); writes u [B][H] and its digit planes.
+hipError_t launch_route_prep(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
+                             float* u, DigitGroup* udig, float* usc, hipStream_t s);
+// z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
+hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
+                               int E, double* z, hipStream_t s);
+// top-k (ties to the lower id) and softmax over the selected; logits from z64
+// (fp64) or z32 (fp32). ids2/w2 are optional second copies.
+hipError_t launch_route_topk(const double* z64, const float* z32, int B, int E, int k, int32_t* ids,
+                             float* w, int32_t* ids2, float* w2, hipStream_t s);
+
+// ---------------------------------------------------------------- decode FFN
+struct SlotList {
+  int32_t v[kMaxTopK];
+};
+
+struct SourceSet {
+  const uint8_t* experts;  // resident expert array or slot pool
+  const int32_t* ids;      // resident: device ids [k] of this token; nullptr in cache mode
+  SlotList slot;           // cache mode: slot of each rank
+  const uint8_t* shared;   // shared expert blob
+  size_t blob_e, blob_s;
+  int H, I, Is, k;
+};
+
+// Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k) (do_routed)
+// and/or the shared expert (do_shared). Writes a [k*I + Is] fp32 and, group by
+// group, its digit planes (the last wave to finish a group quantises it).
+hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
+                             const DigitGroup* udig, const float* usc, float* a, DigitGroup* adig,
+                             float* asc, int32_t* cnt, hipStream_t s);
+// Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
+// optional residual x' = x + add_in, y [H].
+hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,
+                           const float* asc, const float* x, const uint16_t* add_in, bool residual,
+                           float* y, hipStream_t s);
+
+// ---------------------------------------------------------------- standalone GEMV
+hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,
+                          float* y, hipStream_t s);
+hipError_t launch_unpack_q4(const uint8_t* q, int N, int K, int8_t* out, hipStream_t s);
+
+}  // namespace moe

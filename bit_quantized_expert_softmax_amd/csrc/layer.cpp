@@ -1,0 +1,403 @@
+// Layer handle: one MoE layer's weights, workspace, streams and LFU cache.
+//
+// Decode of one token ("Como executar um modelo de 26 bilhões de parâmetros
+// em dois gigabytes de memória em um Mac comum", section "Qual é o principal
+// truque da arquitetura"): the router picks 8 experts; the expert cache
+// (16 slots, LFU) is checked; missing experts are loaded into GPU-visible
+// buffers while the GPU computes the shared-expert branch; then the experts
+// run and are combined.
+//
+// Cache mode on one GPU: the slot pool lives in HBM, the backing store is
+// pinned host memory, and each miss is one host->HBM copy on a side stream.
+// The ids must reach the host before any copy can be issued (the routing of
+// a layer depends on the previous layer's output), so a cache-mode call
+// synchronises once, on an event recorded right after the 32-byte ids copy;
+// the shared-expert gate/up kernel is enqueued before that wait so the GPU is
+// busy meanwhile. A slot overwritten for token t was last read by the
+// previous call's kernels, which precede this call's routing kernels on the
+// same stream and so have finished when the ids event fires.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "host_common.h"
+#include "launch.h"
+
+using moe::fail;
+
+namespace moe {
+moe_status check_shape(const moe_shape* sh, const char* fn);
+
+namespace {
+
+struct WsLayout {
+  size_t u, udig, usc, z, ids, w, a, adig, asc, cnt, pre, total;
+};
+
+WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += (n + 255) & ~static_cast<size_t>(255);
+    return o;
+  };
+  const size_t H = sh.hidden, E = sh.n_experts, k = sh.top_k, I = sh.inter, Is = sh.shared_inter;
+  const size_t ngu = H / kGroup, nga = (k * I + Is) / kGroup;
+  const size_t B = maxB;
+  WsLayout L;
+  L.u = take(B * H * 4);
+  L.udig = take(B * ngu * sizeof(DigitGroup));
+  L.usc = take(B * ngu * 4);
+  L.z = take(B * E * 8);
+  L.ids = take(B * k * 4);
+  L.w = take(B * k * 4);
+  L.a = take(B * (k * I + Is) * 4);
+  L.adig = take(B * nga * sizeof(DigitGroup));
+  L.asc = take(B * nga * 4);
+  L.cnt = take(B * nga * 4);
+  L.pre = take(static_cast<size_t>(maxT) > 0 ? 256 : 0);  // prefill scratch reserved
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+}  // namespace moe
+
+struct moe_layer {
+  moe_shape sh{};
+  moe_layer_desc d{};
+  bool cache_mode = false;
+  int max_B = 0, max_T = 0;
+  moe_cache* cache = nullptr;
+  moe_cache* cache_backup = nullptr;
+  size_t blob_e = 0, blob_s = 0;
+  moe::WsLayout ws{};
+  uint8_t* wsb = nullptr;
+  int32_t* ids_host = nullptr;  // pinned, [top_k]
+  hipEvent_t ev_ids = nullptr, ev_fill = nullptr;
+  // profiling
+  bool prof = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[4];
+  std::vector<hipEvent_t> pool;
+  int64_t prof_launches[4] = {0, 0, 0, 0};
+  double prof_ms[4] = {0, 0, 0, 0};
+
+  template <class T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(wsb + off); }
+};
+
+namespace {
+
+hipEvent_t pool_get(moe_layer* L) {
+  if (!L->pool.empty()) {
+    hipEvent_t e = L->pool.back();
+    L->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records an event before a launch when profiling; returns it (or nullptr).
+hipEvent_t prof_begin(moe_layer* L, hipStream_t s) {
+  if (!L->prof) return nullptr;
+  hipEvent_t e = pool_get(L);
+  if (e && hipEventRecord(e, s) != hipSuccess) {
+    L->pool.push_back(e);
+    return nullptr;
+  }
+  return e;
+}
+
+void prof_end(moe_layer* L, int kind, hipEvent_t b, hipStream_t s) {
+  if (!b) return;
+  hipEvent_t e = pool_get(L);
+  if (!e || hipEventRecord(e, s) != hipSuccess) {
+    L->pool.push_back(b);
+    if (e) L->pool.push_back(e);
+    return;
+  }
+  L->rec[kind].emplace_back(b, e);
+}
+
+moe::SourceSet make_sources(const moe_layer* L) {
+  moe::SourceSet S{};
+  S.shared = L->d.shared_blob;
+  S.blob_e = L->blob_e;
+  S.blob_s = L->blob_s;
+  S.H = L->sh.hidden;
+  S.I = L->sh.inter;
+  S.Is = L->sh.shared_inter;
+  S.k = L->sh.top_k;
+  return S;
+}
+
+}  // namespace
+
+#define HIP_OR_FAIL(expr, fn)                                                        \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" {
+
+moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T, size_t* out) {
+  moe::clear_error();
+  moe_status st = moe::check_shape(sh, "moe_layer_workspace_bytes");
+  if (st) return st;
+  if (!out) return fail(MOE_EINVAL, "moe_layer_workspace_bytes: out is NULL");
+  if (max_B < 1 || max_B > 4096 || max_T < 0 || max_T > 65536)
+    return fail(MOE_ESHAPE, "moe_layer_workspace_bytes: max_B %d / max_T %d out of range", max_B, max_T);
+  *out = moe::ws_layout(*sh, max_B, max_T).total;
+  return MOE_OK;
+}
+
+moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_t max_B,
+                            int32_t max_T, moe_layer** out) {
+  moe::clear_error();
+  const char* fn = "moe_layer_create";
+  moe_status st = moe::check_shape(sh, fn);
+  if (st) return st;
+  if (!d || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (max_B < 1 || max_B > 4096 || max_T < 0 || max_T > 65536)
+    return fail(MOE_ESHAPE, "%s: max_B %d / max_T %d out of range", fn, max_B, max_T);
+  const int nga = (sh->top_k * sh->inter + sh->shared_inter) / moe::kGroup;
+  if (nga > 512)
+    return fail(MOE_ESHAPE, "%s: (top_k*inter + shared_inter)/32 = %d exceeds 512", fn, nga);
+  if (!d->router || !d->shared_blob || !d->workspace)
+    return fail(MOE_EINVAL, "%s: router, shared_blob and workspace are required", fn);
+  const bool cache_mode = d->experts_dev == nullptr;
+  if (cache_mode) {
+    if (!d->experts_host || !d->slot_pool)
+      return fail(MOE_EINVAL, "%s: cache mode needs experts_host and slot_pool", fn);
+    if (d->n_slots < sh->top_k || d->n_slots > sh->n_experts)
+      return fail(MOE_ESHAPE, "%s: n_slots %d outside [top_k=%d, n_experts=%d]", fn, d->n_slots,
+                  sh->top_k, sh->n_experts);
+    if (!moe::aligned16(d->slot_pool)) return fail(MOE_EALIGN, "%s: slot_pool not 16-byte aligned", fn);
+  } else if (!moe::aligned16(d->experts_dev)) {
+    return fail(MOE_EALIGN, "%s: experts_dev not 16-byte aligned", fn);
+  }
+  if (!moe::aligned16(d->router) || !moe::aligned16(d->shared_blob) || !moe::aligned16(d->workspace))
+    return fail(MOE_EALIGN, "%s: router, shared_blob and workspace must be 16-byte aligned", fn);
+  const moe::WsLayout ws = moe::ws_layout(*sh, max_B, max_T);
+  if (d->workspace_bytes < ws.total)
+    return fail(MOE_ENOMEM, "%s: workspace %zu bytes < %zu needed", fn, d->workspace_bytes, ws.total);
+
+  moe_layer* L = new (std::nothrow) moe_layer;
+  if (!L) return fail(MOE_ENOMEM, "%s: out of host memory", fn);
+  L->sh = *sh;
+  L->d = *d;
+  L->cache_mode = cache_mode;
+  L->max_B = max_B;
+  L->max_T = max_T;
+  L->blob_e = moe_expert_bytes(sh->hidden, sh->inter);
+  L->blob_s = moe_expert_bytes(sh->hidden, sh->shared_inter);
+  L->ws = ws;
+  L->wsb = static_cast<uint8_t*>(d->workspace);
+  auto cleanup = [&](moe_status code, const char* what, hipError_t e) {
+    moe_layer_destroy(L);
+    return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
+  };
+  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, static_cast<size_t>(max_B) * nga * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
+  if (cache_mode) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&L->ids_host), sizeof(int32_t) * moe::kMaxTopK,
+                      hipHostMallocDefault);
+    if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned ids buffer", e);
+    e = hipEventCreateWithFlags(&L->ev_ids, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
+    if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
+    moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
+    if (!cs) cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache_backup);
+    if (cs) {
+      moe_layer_destroy(L);
+      return cs;
+    }
+  }
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer* L) {
+  if (!L) return;
+  if (L->ids_host) (void)hipHostFree(L->ids_host);
+  if (L->ev_ids) (void)hipEventDestroy(L->ev_ids);
+  if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
+  for (auto& v : L->rec)
+    for (auto& p : v) {
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    }
+  for (hipEvent_t e : L->pool) (void)hipEventDestroy(e);
+  moe_cache_destroy(L->cache);
+  moe_cache_destroy(L->cache_backup);
+  delete L;
+}
+
+moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev) {
+  moe::clear_error();
+  if (!L || !experts_dev) return fail(MOE_EINVAL, "moe_layer_set_experts: NULL argument");
+  if (L->cache_mode) return fail(MOE_ESTATE, "moe_layer_set_experts: handle is in cache mode");
+  if (!moe::aligned16(experts_dev)) return fail(MOE_EALIGN, "moe_layer_set_experts: not 16-byte aligned");
+  L->d.experts_dev = experts_dev;
+  return MOE_OK;
+}
+
+moe_cache* moe_layer_cache(moe_layer* L) { return L ? L->cache : nullptr; }
+
+moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in, int32_t B,
+                            uint32_t flags, float* y, int32_t* ids_out, float* w_out, float* u_out,
+                            moe_cache_event* trace, moe_decode_stats* stats, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_layer_decode";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL)) return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  if (B < 0 || B > L->max_B) return fail(MOE_ESHAPE, "%s: B=%d outside [0, max_B=%d]", fn, B, L->max_B);
+  if (B == 0) return MOE_OK;
+  if (!x || !y) return fail(MOE_EINVAL, "%s: x and y are required", fn);
+  if (x == y) return fail(MOE_EINVAL, "%s: y must not alias x", fn);
+  if (L->cache_mode && B != 1) return fail(MOE_ESHAPE, "%s: cache mode decodes one token per call", fn);
+  const moe_shape& sh = L->sh;
+  const int H = sh.hidden, E = sh.n_experts, k = sh.top_k;
+  const int ngu = H / moe::kGroup;
+  const int nga = (k * sh.inter + sh.shared_inter) / moe::kGroup;
+  const int arow = k * sh.inter + sh.shared_inter;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float* u = L->at<float>(L->ws.u);
+  auto* udig = L->at<moe::DigitGroup>(L->ws.udig);
+  float* usc = L->at<float>(L->ws.usc);
+  double* z = L->at<double>(L->ws.z);
+  int32_t* ids = L->at<int32_t>(L->ws.ids);
+  float* w = L->at<float>(L->ws.w);
+  float* a = L->at<float>(L->ws.a);
+  auto* adig = L->at<moe::DigitGroup>(L->ws.adig);
+  float* asc = L->at<float>(L->ws.asc);
+  int32_t* cnt = L->at<int32_t>(L->ws.cnt);
+  const bool rms = flags & MOE_F_RMSNORM_IN;
+  const bool res = flags & MOE_F_RESIDUAL;
+
+  hipEvent_t pb = prof_begin(L, s);
+  HIP_OR_FAIL(moe::launch_route_prep(x, add_in, B, H, rms, u, udig, usc, s), fn);
+  HIP_OR_FAIL(moe::launch_route_logits(u, B, H, L->d.router, L->d.bias, E, z, s), fn);
+  HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, E, k, ids, w, ids_out, w_out, s), fn);
+  prof_end(L, 0, pb, s);
+  if (u_out) HIP_OR_FAIL(hipMemcpyAsync(u_out, u, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s), fn);
+
+  moe::SourceSet S = make_sources(L);
+  if (!L->cache_mode) {
+    S.experts = L->d.experts_dev;
+    for (int b = 0; b < B; ++b) {
+      S.ids = ids + static_cast<size_t>(b) * k;
+      hipEvent_t p1 = prof_begin(L, s);
+      HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, true, udig + static_cast<size_t>(b) * ngu,
+                                         usc + static_cast<size_t>(b) * ngu, a + static_cast<size_t>(b) * arow,
+                                         adig + static_cast<size_t>(b) * nga, asc + static_cast<size_t>(b) * nga,
+                                         cnt + static_cast<size_t>(b) * nga, s), fn);
+      prof_end(L, 1, p1, s);
+      hipEvent_t p2 = prof_begin(L, s);
+      HIP_OR_FAIL(moe::launch_ffn_down(S, w + static_cast<size_t>(b) * k, adig + static_cast<size_t>(b) * nga,
+                                       asc + static_cast<size_t>(b) * nga, x + static_cast<size_t>(b) * H,
+                                       add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
+                                       y + static_cast<size_t>(b) * H, s), fn);
+      prof_end(L, 2, p2, s);
+    }
+    if (stats) stats->calls += 1;
+    return MOE_OK;
+  }
+
+  // ---- cache mode, one token
+  HIP_OR_FAIL(hipMemcpyAsync(L->ids_host, ids, sizeof(int32_t) * k, hipMemcpyDeviceToHost, s), fn);
+  HIP_OR_FAIL(hipEventRecord(L->ev_ids, s), fn);
+  S.experts = L->d.slot_pool;
+  S.ids = nullptr;
+  hipEvent_t p1 = prof_begin(L, s);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, a, adig, asc, cnt, s), fn);
+  prof_end(L, 1, p1, s);
+  HIP_OR_FAIL(hipEventSynchronize(L->ev_ids), fn);
+
+  // LFU step; the pre-step state is kept so that a failed copy enqueue leaves
+  // the cache unchanged (no slot is marked resident with stale bytes)
+  moe_cache_event ev[moe::kMaxTopK];
+  int32_t n_miss = 0;
+  moe::cache_assign(L->cache_backup, L->cache);
+  moe_status cs = moe_cache_step(L->cache, L->ids_host, k, ev, &n_miss);
+  if (cs) return cs;
+  hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
+  hipError_t ce = hipSuccess;
+  for (int j = 0; j < k && ce == hipSuccess; ++j) {
+    if (ev[j].hit) continue;
+    ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e,
+                        L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e, L->blob_e,
+                        hipMemcpyHostToDevice, cp);
+  }
+  if (ce == hipSuccess && n_miss > 0) {
+    ce = hipEventRecord(L->ev_fill, cp);
+    if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+  }
+  if (ce != hipSuccess) {
+    moe::cache_assign(L->cache, L->cache_backup);
+    return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
+  }
+  for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
+  hipEvent_t p2 = prof_begin(L, s);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, a, adig, asc, cnt, s), fn);
+  prof_end(L, 1, p2, s);
+  hipEvent_t p3 = prof_begin(L, s);
+  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adig, asc, x, add_in, res, y, s), fn);
+  prof_end(L, 2, p3, s);
+  if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
+  if (stats) {
+    stats->hits += k - n_miss;
+    stats->misses += n_miss;
+    stats->h2d_bytes += static_cast<int64_t>(n_miss) * static_cast<int64_t>(L->blob_e);
+    stats->calls += 1;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in, int32_t T,
+                             float* y, int32_t* ids_out, float* w_out, void* stream) {
+  moe::clear_error();
+  (void)x_bf16; (void)logits_in; (void)T; (void)y; (void)ids_out; (void)w_out; (void)stream;
+  if (!L) return fail(MOE_EINVAL, "moe_layer_prefill: NULL handle");
+  return fail(MOE_ESTATE, "moe_layer_prefill: not available in this build");
+}
+
+moe_status moe_layer_profile(moe_layer* L, int32_t enable) {
+  moe::clear_error();
+  if (!L) return fail(MOE_EINVAL, "moe_layer_profile: NULL handle");
+  L->prof = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* out) {
+  moe::clear_error();
+  const char* fn = "moe_layer_profile_read";
+  if (!L || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (kind < 0 || kind > 3) return fail(MOE_EINVAL, "%s: kind %d outside [0, 3]", fn, kind);
+  for (auto& v : L->rec) {
+    for (auto& p : v) HIP_OR_FAIL(hipEventSynchronize(p.second), fn);
+  }
+  for (int kd = 0; kd < 4; ++kd) {
+    for (auto& p : L->rec[kd]) {
+      float ms = 0.f;
+      HIP_OR_FAIL(hipEventElapsedTime(&ms, p.first, p.second), fn);
+      L->prof_ms[kd] += ms;
+      L->prof_launches[kd] += 1;
+      L->pool.push_back(p.first);
+      L->pool.push_back(p.second);
+    }
+    L->rec[kd].clear();
+  }
+  out->launches = L->prof_launches[kind];
+  out->ms_total = L->prof_ms[kind];
+  return MOE_OK;
+}
+
+}  // extern "C"

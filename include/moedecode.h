@@ -1,0 +1,245 @@
+/*
+ * libmoedecode -- decode-time Mixture-of-Experts FFN layer with 4-bit
+ * group-quantised experts and an LFU expert-slot cache, for AMD MI355X
+ * (gfx950).
+ *
+ * The operations follow the engine described on "Como executar um modelo de
+ * 26 bilhões de parâmetros em dois gigabytes de memória em um Mac comum",
+ * section "Qual é o principal truque da arquitetura" (German twin: "So führen
+ * Sie ein 26-Milliarden-Parameter-Modell ...", section "Was ist der
+ * Haupt-Architekturtrick?"):
+ *   - the router of each layer picks the 8 experts of the current token
+ *     (moe_route);
+ *   - a local expert cache of 16 slots with an LFU policy is checked
+ *     (moe_cache_step);
+ *   - missing experts are loaded into GPU-visible buffers while the GPU runs
+ *     the shared-expert branch (moe_layer_decode, cache mode);
+ *   - 4-bit expert GEMVs (moe_expert_gemv_q4) and the MoE combine
+ *     (moe_layer_decode);
+ * and, from the same page's section "Desempenho no mundo real", prefill that
+ * lets one loaded expert serve a group of token rows (moe_layer_prefill).
+ *
+ * ---------------------------------------------------------------- formats
+ * int4 g32 matrix for y = W x, W with N outputs and K inputs (K % 32 == 0):
+ *   q : uint8 [N][K/2]   byte j of row n holds input 2j in bits 0-3 and 2j+1
+ *                        in bits 4-7; each nibble is 4-bit two's complement
+ *                        (-8..7)
+ *   s : fp16  [N][K/32]  scale of inputs [32g, 32g+32) of row n
+ *   W[n][k] = nibble(n,k) * s[n][k/32]
+ * Expert blob (one contiguous run per expert, moe_expert_bytes bytes):
+ *   gate.q [I][H/2] | up.q [I][H/2] | down.q [H][I/2] |
+ *   gate.s [I][H/32] | up.s [I][H/32] | down.s [H][I/32]
+ * Expert FFN (GeGLU): o = Wd (gelu_tanh(Wg u) * (Wu u)),
+ *   gelu_tanh(z) = z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ * Layer: z = Wr u (+ bias); ids = top-k of z (ties to the lower id, rank
+ * order); w = softmax of z over ids; y = o_shared + sum_j w_j o_{ids_j}
+ * (+ the layer input with MOE_F_RESIDUAL).
+ *
+ * ---------------------------------------------------------------- conventions
+ *  - Every call returns a moe_status; nothing throws or aborts. On an error
+ *    return nothing was enqueued and no state changed; the text is in
+ *    moe_last_error() (thread-local, valid until the next call on the thread).
+ *  - "dev" pointers are device (HBM) pointers, "host" pointers are host memory;
+ *    "pinned" means host memory allocated pinned (hipHostMalloc or torch
+ *    pin_memory). The library never takes ownership of caller memory.
+ *  - Device buffers must be 16-byte aligned (MOE_EALIGN otherwise).
+ *  - stream is a hipStream_t (NULL = the null stream). Calls documented as
+ *    asynchronous only enqueue work.
+ *  - Floating-point results are deterministic: the same inputs give the same
+ *    bits (no floating-point atomics).
+ */
+#ifndef MOEDECODE_H
+#define MOEDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_EINVAL -1 /* null pointer, id out of range, duplicate id, bad flag  */
+#define MOE_ESHAPE -2 /* K % 32 != 0, k > E, k > n_slots, size above a limit    */
+#define MOE_EALIGN -3 /* device pointer not 16-byte aligned                      */
+#define MOE_EHIP -4   /* HIP runtime error; text in moe_last_error()             */
+#define MOE_ENOMEM -5 /* workspace too small                                     */
+#define MOE_ESTATE -6 /* call not valid for this handle's mode                  */
+
+/* Limits checked by every entry point. */
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_DIM 16384
+
+const char* moe_last_error(void);
+int32_t moe_abi_version(void);
+
+typedef struct moe_shape {
+  int32_t hidden;       /* H                                   */
+  int32_t n_experts;    /* E                                   */
+  int32_t top_k;        /* k                                   */
+  int32_t inter;        /* I, routed expert intermediate width */
+  int32_t shared_inter; /* I_s, shared expert intermediate     */
+  int32_t group;        /* quantisation group; must be 32      */
+} moe_shape;
+
+typedef struct moe_q4 {
+  const uint8_t* q;  /* dev [N][K/2] */
+  const uint16_t* s; /* dev [N][K/32] fp16 bits */
+} moe_q4;
+
+/* Byte offsets of the six arrays inside one expert blob, and its size. */
+typedef struct moe_blob_layout {
+  size_t gate_q, up_q, down_q, gate_s, up_s, down_s, total;
+} moe_blob_layout;
+
+/* Blob size 27*H*I/16 (0 when H or I is not a positive multiple of 32). */
+size_t moe_expert_bytes(int32_t hidden, int32_t inter);
+moe_status moe_blob_layout_of(int32_t hidden, int32_t inter, moe_blob_layout* out);
+
+/* ---------------------------------------------------------------- 1. routing
+ * Router of one layer for B tokens: z[b][e] = sum_h x[b][h] * wr[e][h]
+ * (+ bias[e]) accumulated in fp64 (every fp32 x fp16 product is exact in
+ * fp64), or z = logits_in when logits_in != NULL (x and wr are then unused
+ * and may be NULL). ids[b][0..k) are the k largest z in rank order, ties to
+ * the lower expert id; w[b][j] = exp(z_j - z_0) / sum over the k selected.
+ *   x         dev fp32 [B][H]           wr   dev fp16 [E][H]
+ *   bias      dev fp32 [E] or NULL      logits_in dev fp32 [B][E] or NULL
+ *   ids       dev int32 [B][k] (out)    w    dev fp32 [B][k] (out)
+ *   workspace dev, at least moe_route_workspace_bytes(sh, B) bytes (holds the
+ *             fp64 logits); may be NULL when logits_in != NULL.
+ * Asynchronous on stream. */
+size_t moe_route_workspace_bytes(const moe_shape* sh, int32_t B);
+moe_status moe_route(const moe_shape* sh, const float* x, const uint16_t* wr, const float* bias,
+                     const float* logits_in, int32_t B, int32_t* ids, float* w, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- 2. LFU cache
+ * Host-only, synchronous, deterministic. One cache per layer, n_slots slots.
+ * moe_cache_step looks up one token's k ids (host, rank order, distinct):
+ *   - a resident id is a hit: its frequency grows by one, its last-use tick
+ *     becomes the current step;
+ *   - a missing id takes the lowest-index empty slot, else the slot with the
+ *     smallest (frequency, last use, slot index) among slots holding none of
+ *     this token's ids; it starts at frequency 1;
+ *   - ev[j] (host, k entries, out) describes ids[j]: expert, slot, hit (1/0),
+ *     evicted expert or -1; *n_miss (out, may be NULL) counts misses.
+ * The step counter advances by one per successful call. Errors (k > n_slots,
+ * id out of range, duplicate id) leave the cache unchanged. */
+typedef struct moe_cache moe_cache;
+typedef struct moe_cache_event {
+  int32_t expert, slot, hit, evicted;
+} moe_cache_event;
+moe_status moe_cache_create(int32_t n_slots, int32_t n_experts, moe_cache** out);
+void moe_cache_destroy(moe_cache* c);
+moe_status moe_cache_step(moe_cache* c, const int32_t* ids, int32_t k, moe_cache_event* ev,
+                          int32_t* n_miss);
+moe_status moe_cache_reset(moe_cache* c);
+/* Copies the slot table (host arrays of n entries each, any may be NULL):
+ * expert (-1 = empty), frequency, last-use step. n must equal n_slots. */
+moe_status moe_cache_slots(const moe_cache* c, int32_t* expert, int32_t* freq, int64_t* last,
+                           int32_t n);
+moe_status moe_cache_counters(const moe_cache* c, int64_t* hits, int64_t* misses, int64_t* steps);
+
+/* ---------------------------------------------------------------- 3. GEMV
+ * y[m][n] = sum_k x[m][k] * W[n][k] for M token rows sharing one int4 g32
+ * matrix W (N outputs, K inputs, K % 32 == 0). fp32 accumulation; each
+ * activation group of 32 is carried as a 16-bit fixed-point value with its
+ * own scale (relative error below 2e-5 of the group's largest magnitude).
+ *   W dev (q, s as above)    x dev fp32 [M][K]    y dev fp32 [M][N] (out)
+ *   1 <= M <= 64. x must be finite.
+ * Asynchronous on stream. */
+moe_status moe_expert_gemv_q4(const moe_q4* W, int32_t N, int32_t K, const float* x, int32_t M,
+                              float* y, void* stream);
+
+/* ---------------------------------------------------------------- 4./5. layer
+ * A layer handle binds one layer's weights and a workspace.
+ * Resident mode: experts_dev != NULL, every expert blob in HBM.
+ * Cache mode:    experts_dev == NULL, experts_host (pinned [E][blob]) holds
+ *                the experts, slot_pool (dev [n_slots][blob]) is the expert
+ *                slot cache, copy_stream carries the host->HBM miss copies.
+ * All pointers are borrowed and must stay valid and unmodified until
+ * moe_layer_destroy. */
+typedef struct moe_layer moe_layer;
+typedef struct moe_layer_desc {
+  const uint16_t* router;       /* dev fp16 [E][H]                               */
+  const float* bias;            /* dev fp32 [E] added to the logits, or NULL     */
+  const uint8_t* shared_blob;   /* dev, moe_expert_bytes(H, I_s) bytes           */
+  const uint8_t* experts_dev;   /* resident mode: dev [E][blob]; else NULL       */
+  const uint8_t* experts_host;  /* cache mode: pinned host [E][blob]; else NULL  */
+  uint8_t* slot_pool;           /* cache mode: dev [n_slots][blob]; else NULL    */
+  int32_t n_slots;              /* cache mode: k <= n_slots <= E                 */
+  void* copy_stream;            /* cache mode: hipStream_t for the miss copies   */
+  void* workspace;              /* dev, moe_layer_workspace_bytes bytes          */
+  size_t workspace_bytes;
+} moe_layer_desc;
+
+typedef struct moe_decode_stats {
+  int64_t hits, misses, h2d_bytes; /* cache mode; accumulated over calls       */
+  int64_t calls;
+} moe_decode_stats;
+
+#define MOE_F_RMSNORM_IN 1u /* u = x' / sqrt(mean(x'^2) + 1e-6) feeds router and FFN */
+#define MOE_F_RESIDUAL 2u   /* y = x' + MoE(u) instead of y = MoE(u)                 */
+
+/* Workspace for up to max_B decode tokens per call and max_T prefill tokens. */
+moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
+                                     size_t* out);
+/* Validates, clears the workspace counters (synchronously) and returns a handle. */
+moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_t max_B,
+                            int32_t max_T, moe_layer** out);
+void moe_layer_destroy(moe_layer* L);
+/* Resident mode only: point the handle at another resident expert array of the
+ * same shape (e.g. a replica). Takes effect for calls enqueued afterwards. */
+moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev);
+/* The handle's LFU cache (cache mode), or NULL. Owned by the handle. */
+moe_cache* moe_layer_cache(moe_layer* L);
+
+/* Decode B tokens through the layer.
+ *   x       dev fp32 [B][H] layer input
+ *   add_in  dev fp16 [B][H] added first, x' = x + add_in, or NULL (x' = x)
+ *   flags   MOE_F_RMSNORM_IN | MOE_F_RESIDUAL (u = x' without RMSNORM_IN)
+ *   y       dev fp32 [B][H] output; must not alias x
+ *   ids_out dev int32 [B][k], w_out dev fp32 [B][k], u_out dev fp32 [B][H]:
+ *           optional copies of the routing and of u (NULL to skip)
+ *   trace   host [B][k] cache events (cache mode) or NULL
+ *   stats   host, accumulated (cache mode counters) or NULL
+ * Resident mode is asynchronous on stream. Cache mode requires B == 1 and
+ * blocks the calling thread once, until the token's ids are on the host; it
+ * returns with the miss copies and the expert kernels enqueued (the copies on
+ * copy_stream, ordered before the expert kernels by an event). */
+moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in, int32_t B,
+                            uint32_t flags, float* y, int32_t* ids_out, float* w_out, float* u_out,
+                            moe_cache_event* trace, moe_decode_stats* stats, void* stream);
+
+/* Prefill T tokens (resident mode). x is bf16 [T][H]; routing uses
+ * logits_in (dev fp32 [T][E]) when given, else x . router. Tokens are grouped
+ * by expert; expert weights are converted to bf16 tile by tile and multiplied
+ * on the matrix cores with fp32 accumulation; the GeGLU activation is rounded
+ * to bf16 before the down projection. y dev fp32 [T][H]. ids_out / w_out
+ * optional as in decode. Asynchronous on stream. */
+moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in,
+                             int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
+
+/* Per-kernel GPU time of the handle's calls, measured with HIP events placed
+ * around each launch on the launch stream while profiling is enabled.
+ * kind: 0 = routing, 1 = routed+shared gate/up, 2 = down+combine,
+ * 3 = prefill. Reading synchronises with the recorded events. */
+typedef struct moe_kernel_time {
+  int64_t launches;
+  double ms_total;
+} moe_kernel_time;
+moe_status moe_layer_profile(moe_layer* L, int32_t enable);
+moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* out);
+
+/* ---------------------------------------------------------------- test support
+ * Unpacks the nibbles of W to int8 [N][K] (dev) for bit-exact comparison. */
+moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEDECODE_H */

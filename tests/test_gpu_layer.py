@@ -1,0 +1,145 @@
+"""GPU parity of moe_layer_decode (resident and LFU cache mode) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_expert_softmax_amd import api
+from oracle import lfu, moe
+from synth import gen
+from synth.configs import GEMMA_LAYER, SMALL_LAYER
+from tests.gpu_util import DEV, Layer, assert_close, dev, dev_u16, poisoned
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def layer_data(shape, cid):
+    key = (shape, cid)
+    if key not in _CACHE:
+        _CACHE[key] = gen.layer_inputs(shape, cid)
+    return _CACHE[key]
+
+
+def run_decode(L, x, flags=0, add_in=None, trace_k=0, stats=None):
+    B = x.shape[0]
+    sh = L.shape
+    y = poisoned((B, sh.hidden))
+    ids = poisoned((B, sh.top_k), torch.int32)
+    w = poisoned((B, sh.top_k))
+    u = poisoned((B, sh.hidden))
+    tr = api.moe_layer_decode(L.h, x, add_in, B, flags, y, ids, w, u, trace_k=trace_k, stats=stats)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(), u.cpu().numpy(), tr
+
+
+@pytest.mark.parametrize("shape,cid,tokens", [(SMALL_LAYER, 0, 8), (GEMMA_LAYER, 1, 4)])
+def test_resident_decode_b1(shape, cid, tokens):
+    d = layer_data(shape, cid)
+    L = Layer(shape, d)
+    xs = gen.x_fp32(tokens, shape.hidden, cid)
+    for t in range(tokens):
+        y, ids, w, u, _ = run_decode(L, dev(xs[t:t + 1]))
+        r = moe.layer_decode(xs[t].astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+        assert np.array_equal(ids, r["ids"]), t
+        assert_close(w, r["w"], f"w t={t}")
+        assert_close(y, r["y"], f"y t={t}")
+        assert np.array_equal(u, xs[t:t + 1])
+    L.close()
+
+
+def test_resident_decode_batched_call():
+    shape = GEMMA_LAYER
+    d = layer_data(shape, 1)
+    L = Layer(shape, d, max_B=3)
+    x = gen.x_fp32(3, shape.hidden, 1, sub=7)
+    y, ids, w, _, _ = run_decode(L, dev(x))
+    r = moe.layer_decode(x.astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+    assert np.array_equal(ids, r["ids"])
+    assert_close(y, r["y"], "y B=3")
+    L.close()
+
+
+def test_zero_input_and_determinism():
+    shape = SMALL_LAYER
+    d = layer_data(shape, 0)
+    L = Layer(shape, d)
+    y, ids, w, _, _ = run_decode(L, torch.zeros((1, shape.hidden), device=DEV))
+    assert np.all(y == 0.0) and ids[0].tolist() == list(range(8)) and np.all(w == 0.125)
+    x = dev(gen.x_fp32(1, shape.hidden, 0, sub=3))
+    y1 = run_decode(L, x)[0]
+    y2 = run_decode(L, x)[0]
+    assert np.array_equal(y1, y2)
+    L.close()
+
+
+@pytest.mark.parametrize("shape,cid", [(SMALL_LAYER, 0), (GEMMA_LAYER, 2)])
+def test_norm_residual_perturbation(shape, cid):
+    d = layer_data(shape, cid)
+    bias = gen.zipf_bias(shape.n_experts, cid, 0)
+    L = Layer(shape, d, bias=bias)
+    xs = gen.x_fp32(3, shape.hidden, cid)
+    eps = gen.eps_fp16(1, 3, shape.hidden, cid)[0]
+    lay = dict(d, bias=bias)
+    for t in range(3):
+        y, ids, w, u, _ = run_decode(L, dev(xs[t:t + 1]), api.MOE_F_RMSNORM_IN | api.MOE_F_RESIDUAL,
+                                     add_in=dev_u16(eps[t:t + 1]))
+        h2, rec = moe.stack_layer_step(xs[t], eps[t], shape, lay)
+        assert_close(u, rec["u"], "u")
+        # routing decided on the GPU's own u (both sides select in fp64 from it)
+        r_ids, r_w, _ = moe.route(u.astype(np.float64), d["router"], shape.top_k, bias)
+        assert np.array_equal(ids, r_ids)
+        assert np.array_equal(ids, rec["ids"])
+        assert_close(w, r_w, "w")
+        assert_close(y, h2, "y")
+    L.close()
+
+
+@pytest.mark.parametrize("shape,cid,slots,tokens", [(SMALL_LAYER, 0, 10, 60), (GEMMA_LAYER, 2, 16, 10)])
+def test_cache_mode_trace_and_output(shape, cid, slots, tokens):
+    d = layer_data(shape, cid)
+    bias = gen.zipf_bias(shape.n_experts, cid, 0)
+    L = Layer(shape, d, bias=bias, cache_slots=slots)
+    xs = gen.x_fp32(tokens, shape.hidden, cid, sub=11)
+    sim = lfu.LFUCache(slots, shape.n_experts)
+    stats = api.moe_decode_stats()
+    check = set(range(0, tokens, max(1, tokens // 6))) | {tokens - 1}
+    for t in range(tokens):
+        y, ids, w, u, tr = run_decode(L, dev(xs[t:t + 1]), trace_k=shape.top_k, stats=stats)
+        r_ids, r_w, _ = moe.route(xs[t:t + 1].astype(np.float64), d["router"], shape.top_k, bias)
+        assert np.array_equal(ids, r_ids), t
+        want = sim.step(ids[0])
+        assert [tuple(e) for e in tr.tolist()] == [tuple(e) for e in want], t
+        if t in check:
+            r = moe.layer_decode(xs[t].astype(np.float64), shape, d["router"], d["shared"], d["experts"],
+                                 bias=bias)
+            assert_close(y, r["y"], f"y t={t}")
+    assert stats.hits == sim.hits and stats.misses == sim.misses and stats.calls == tokens
+    assert stats.h2d_bytes == sim.misses * d["experts"].shape[1]
+    assert 0 < sim.hits
+    # every slot holds a bit-exact copy of the expert the cache says it holds
+    pool = L.pool.cpu().numpy()
+    for s_, e in enumerate(sim.expert):
+        if e >= 0:
+            assert np.array_equal(pool[s_], d["experts"][e]), (s_, e)
+    ex, fr, la = api.moe_cache_slots(api.moe_layer_cache(L.h), slots)
+    assert ex.tolist() == sim.expert and fr.tolist() == sim.freq
+    L.close()
+
+
+def test_empty_call_and_errors():
+    shape = SMALL_LAYER
+    d = layer_data(shape, 0)
+    L = Layer(shape, d)
+    x = dev(gen.x_fp32(1, shape.hidden, 0))
+    y = poisoned((1, shape.hidden))
+    api.moe_layer_decode(L.h, x, None, 0, 0, y)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(y))
+    with pytest.raises(api.MoeError):
+        api.moe_layer_decode(L.h, x, None, 2, 0, y)     # B above max_B
+    with pytest.raises(api.MoeError):
+        api.moe_layer_decode(L.h, x, None, 1, 8, y)     # unknown flag
+    with pytest.raises(api.MoeError):
+        api.moe_layer_decode(L.h, x, None, 1, 0, x)     # y aliases x
+    L.close()
