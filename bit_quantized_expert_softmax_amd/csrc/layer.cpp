@@ -65,6 +65,11 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
 }  // namespace
 }  // namespace moe
 
+// profiling kinds: 0 routing, 1 shared-expert gate/up (cache mode), 2 gate/up of
+// the routed experts (plus the shared expert in resident mode), 3 down + combine,
+// 4 prefill
+constexpr int kProfKinds = 5;
+
 struct moe_layer {
   moe_shape sh{};
   moe_layer_desc d{};
@@ -79,10 +84,10 @@ struct moe_layer {
   hipEvent_t ev_ids = nullptr, ev_fill = nullptr;
   // profiling
   bool prof = false;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[4];
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kProfKinds];
   std::vector<hipEvent_t> pool;
-  int64_t prof_launches[4] = {0, 0, 0, 0};
-  double prof_ms[4] = {0, 0, 0, 0};
+  int64_t prof_launches[kProfKinds] = {};
+  double prof_ms[kProfKinds] = {};
 
   template <class T>
   T* at(size_t off) const { return reinterpret_cast<T*>(wsb + off); }
@@ -299,13 +304,13 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                                          usc + static_cast<size_t>(b) * ngu, a + static_cast<size_t>(b) * arow,
                                          adig + static_cast<size_t>(b) * nga, asc + static_cast<size_t>(b) * nga,
                                          cnt + static_cast<size_t>(b) * nga, s), fn);
-      prof_end(L, 1, p1, s);
+      prof_end(L, 2, p1, s);
       hipEvent_t p2 = prof_begin(L, s);
       HIP_OR_FAIL(moe::launch_ffn_down(S, w + static_cast<size_t>(b) * k, adig + static_cast<size_t>(b) * nga,
                                        asc + static_cast<size_t>(b) * nga, x + static_cast<size_t>(b) * H,
                                        add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
                                        y + static_cast<size_t>(b) * H, s), fn);
-      prof_end(L, 2, p2, s);
+      prof_end(L, 3, p2, s);
     }
     if (stats) stats->calls += 1;
     return MOE_OK;
@@ -347,10 +352,10 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
   hipEvent_t p2 = prof_begin(L, s);
   HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, a, adig, asc, cnt, s), fn);
-  prof_end(L, 1, p2, s);
+  prof_end(L, 2, p2, s);
   hipEvent_t p3 = prof_begin(L, s);
   HIP_OR_FAIL(moe::launch_ffn_down(S, w, adig, asc, x, add_in, res, y, s), fn);
-  prof_end(L, 2, p3, s);
+  prof_end(L, 3, p3, s);
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
   if (stats) {
     stats->hits += k - n_miss;
@@ -380,11 +385,11 @@ moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* o
   moe::clear_error();
   const char* fn = "moe_layer_profile_read";
   if (!L || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
-  if (kind < 0 || kind > 3) return fail(MOE_EINVAL, "%s: kind %d outside [0, 3]", fn, kind);
+  if (kind < 0 || kind >= kProfKinds) return fail(MOE_EINVAL, "%s: kind %d outside [0, %d]", fn, kind, kProfKinds - 1);
   for (auto& v : L->rec) {
     for (auto& p : v) HIP_OR_FAIL(hipEventSynchronize(p.second), fn);
   }
-  for (int kd = 0; kd < 4; ++kd) {
+  for (int kd = 0; kd < kProfKinds; ++kd) {
     for (auto& p : L->rec[kd]) {
       float ms = 0.f;
       HIP_OR_FAIL(hipEventElapsedTime(&ms, p.first, p.second), fn);

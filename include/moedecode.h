@@ -226,8 +226,11 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
 
 /* Per-kernel GPU time of the handle's calls, measured with HIP events placed
  * around each launch on the launch stream while profiling is enabled.
- * kind: 0 = routing, 1 = routed+shared gate/up, 2 = down+combine,
- * 3 = prefill. Reading synchronises with the recorded events. */
+ * kind: 0 = routing (input prep, logits, top-k), 1 = shared-expert gate/up
+ * launched ahead of the miss copies (cache mode), 2 = gate/up of the routed
+ * experts (resident mode: together with the shared expert), 3 = down
+ * projections + combine, 4 = prefill. Launch counts and times accumulate
+ * over calls; reading synchronises with the recorded events. */
 typedef struct moe_kernel_time {
   int64_t launches;
   double ms_total;
