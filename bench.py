@@ -163,7 +163,7 @@ def main():
             "routed_gateup": us_gu,
             "down_combine": us_dn,
         },
-        "down_combine_GBps": down_bytes / (us_dn * 1e-6) / 1e9,
+        "down_combine_GBps": down_bytes / (us_dn * 1e-6) / 1e9 if us_dn > 0 else None,
     }
 
     # ---------------------------------------------------------------- all experts resident

@@ -17,6 +17,7 @@ constexpr int kRowsPerWave = kWave / kLanesPerRow;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kMaxTile = 8;  // token rows per pass
 
+template <int NT>
 __global__ __launch_bounds__(kThreads) void k_gemv_q4(const uint8_t* __restrict__ q,
                                                       const uint16_t* __restrict__ sc, int N, int K,
                                                       const float* __restrict__ x, int M, int tile,
@@ -27,34 +28,50 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q4(const uint8_t* __restrict_
   float* xs = reinterpret_cast<float*>(xd + static_cast<size_t>(tile) * ng);  // [tile][ng]
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int n = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave + lane / kLanesPerRow;
+  const int n_raw = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave + lane / kLanesPerRow;
+  const int n = n_raw < N ? n_raw : N - 1;  // rows past the end re-read the last row
   const int ln = lane & (kLanesPerRow - 1);
-  const uint8_t* qrow = q + static_cast<size_t>(n < N ? n : 0) * (K / 2);
-  const uint16_t* srow = sc + static_cast<size_t>(n < N ? n : 0) * ng;
+  const uint8_t* qrow = q + static_cast<size_t>(n) * (K / 2);
+  const uint16_t* srow = sc + static_cast<size_t>(n) * ng;
 
   for (int m0 = 0; m0 < M; m0 += tile) {
     const int mt = (M - m0) < tile ? (M - m0) : tile;
     __syncthreads();  // previous tile's digits are no longer read
-    for (int p = wave; p < mt * ((ng + 1) / 2); p += kWaves) {
-      const int m = p / ((ng + 1) / 2);
-      const int g0 = 2 * (p % ((ng + 1) / 2));
+    const int half = (ng + 1) / 2;
+    for (int p = wave; p < mt * half; p += kWaves) {
+      const int m = p / half;
+      const int g0 = 2 * (p % half);
       const int g = g0 + (lane >> 5);
-      const float v = g < ng ? x[static_cast<size_t>(m0 + m) * K + g * kGroup + (lane & 31)] : 0.f;
-      quant_pair_of_groups(v, g0, ng, xd + static_cast<size_t>(m) * ng, xs + static_cast<size_t>(m) * ng);
+      const float v = x[static_cast<size_t>(m0 + m) * K + (g < ng ? g : ng - 1) * kGroup + (lane & 31)];
+      quant_pair_of_groups(g < ng ? v : 0.f, g0, ng, xd + static_cast<size_t>(m) * ng,
+                           xs + static_cast<size_t>(m) * ng);
     }
     __syncthreads();
     float acc[kMaxTile];
 #pragma unroll
     for (int m = 0; m < kMaxTile; ++m) acc[m] = 0.f;
-    if (n < N) {
-      for (int c = ln; c < ng; c += kLanesPerRow) {
-        const uint4 wv = load_w16(qrow + 16 * static_cast<size_t>(c));
-        const float sw = h2f(srow[c]);
+    for (int c0 = 0; c0 < ng; c0 += kLanesPerRow * NT) {
+      uint4 wv[NT];
+      uint16_t sw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        int c = c0 + ln + kLanesPerRow * t;
+        c = c < ng ? c : ng - 1;
+        wv[t] = load_w16(qrow + 16 * static_cast<size_t>(c));
+        sw[t] = srow[c];
+      }
+      // keep every load of the batch ahead of the first use
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int c = c0 + ln + kLanesPerRow * t;
+        const int cc = c < ng ? c : ng - 1;
+        const float f = h2f(sw[t]) * static_cast<float>(c < ng);
 #pragma unroll
         for (int m = 0; m < kMaxTile; ++m) {
           if (m < mt) {
-            const int t = chunk_dot(wv, xd[static_cast<size_t>(m) * ng + c]);
-            acc[m] = fmaf(static_cast<float>(t), sw * xs[static_cast<size_t>(m) * ng + c], acc[m]);
+            const int d = chunk_dot(wv[t], xd[static_cast<size_t>(m) * ng + cc]);
+            acc[m] = fmaf(static_cast<float>(d), f * xs[static_cast<size_t>(m) * ng + cc], acc[m]);
           }
         }
       }
@@ -62,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q4(const uint8_t* __restrict_
 #pragma unroll
     for (int m = 0; m < kMaxTile; ++m) {
       const float v = seg_sum<kLanesPerRow>(acc[m]);
-      if (m < mt && n < N && ln == 0) y[static_cast<size_t>(m0 + m) * N + n] = v;
+      if (m < mt && n_raw < N && ln == 0) y[static_cast<size_t>(m0 + m) * N + n] = v;
     }
   }
 }
@@ -87,8 +104,14 @@ hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, co
   tile = tile < 1 ? 1 : (tile > kMaxTile ? kMaxTile : tile);
   if (tile > M) tile = M;
   const int blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(k_gemv_q4, dim3(blocks), dim3(kThreads), per_token * tile, s, q, sc, N, K, x,
-                     M, tile, y);
+  const int need = (ng + kLanesPerRow - 1) / kLanesPerRow;
+#define MOE_GEMV(NT) hipLaunchKernelGGL(k_gemv_q4<NT>, dim3(blocks), dim3(kThreads), per_token * tile, s, q, sc, N, K, x, M, tile, y)
+  if (need <= 2) MOE_GEMV(2);
+  else if (need <= 4) MOE_GEMV(4);
+  else if (need <= 8) MOE_GEMV(8);
+  else if (need <= 12) MOE_GEMV(12);
+  else MOE_GEMV(16);
+#undef MOE_GEMV
   return hipGetLastError();
 }
 

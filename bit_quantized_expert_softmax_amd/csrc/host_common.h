@@ -8,7 +8,7 @@
 
 #include <string>
 
-#include "../../include/moedecode.h"
+#include "moedecode.h"
 
 namespace moe {
 

@@ -29,10 +29,14 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 }
 
 // ---------------------------------------------------------------- routing
-// x' = x (+ add_in); u = x' or rmsnorm(x'); writes u [B][H] and its digit planes.
-hipError_t launch_route_prep(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
-                             float* u, DigitGroup* udig, float* usc, hipStream_t s);
-// z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
+// Layer router, one launch: x' = x (+ add_in); u = x' or rmsnorm(x'); u's
+// digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
+// finish. cnt must be zero before the launch and is zero after it.
+hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
+                              const uint16_t* wr, const float* bias, int E, int k, float* u_out,
+                              DigitGroup* udig, float* usc, double* z, int32_t* cnt, int32_t* ids,
+                              float* w, int32_t* ids2, float* w2, hipStream_t s);
+// Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
 // top-k (ties to the lower id) and softmax over the selected; logits from z64
@@ -47,24 +51,33 @@ struct SlotList {
 
 struct SourceSet {
   const uint8_t* experts;  // resident expert array or slot pool
-  const int32_t* ids;      // resident: device ids [k] of this token; nullptr in cache mode
+  const int32_t* ids;      // device ids [k] of this token, or nullptr (slots / in-kernel top-k)
   SlotList slot;           // cache mode: slot of each rank
   const uint8_t* shared;   // shared expert blob
   size_t blob_e, blob_s;
   int H, I, Is, k;
+  // in-kernel routing (gate/up kernel, resident mode): top-k of the fp64
+  // logits z [E]; the first block writes ids_g / w_g (and the optional copies)
+  const double* z;
+  int E;
+  int32_t* ids_g;
+  float* w_g;
+  int32_t* ids2;
+  float* w2;
 };
 
 // Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k) (do_routed)
-// and/or the shared expert (do_shared). Writes a [k*I + Is] fp32 and, group by
-// group, its digit planes (the last wave to finish a group quantises it).
+// and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
+// as digit planes: adig[p] holds the 4 digit words of activations
+// [8p, 8p+8) and asc[p] their scale.
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
-                             const DigitGroup* udig, const float* usc, float* a, DigitGroup* adig,
-                             float* asc, int32_t* cnt, hipStream_t s);
+                             const DigitGroup* udig, const float* usc, uint4* adig, float* asc,
+                             hipStream_t s);
 // Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
 // optional residual x' = x + add_in, y [H].
-hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,
-                           const float* asc, const float* x, const uint16_t* add_in, bool residual,
-                           float* y, hipStream_t s);
+hipError_t launch_ffn_down(const SourceSet& src, const float* w, const uint4* adig, const float* asc,
+                           const float* x, const uint16_t* add_in, bool residual, float* y,
+                           hipStream_t s);
 
 // ---------------------------------------------------------------- standalone GEMV
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,

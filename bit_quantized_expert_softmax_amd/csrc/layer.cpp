@@ -33,7 +33,7 @@ moe_status check_shape(const moe_shape* sh, const char* fn);
 namespace {
 
 struct WsLayout {
-  size_t u, udig, usc, z, ids, w, a, adig, asc, cnt, pre, total;
+  size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre, total;
 };
 
 WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
@@ -44,7 +44,7 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
     return o;
   };
   const size_t H = sh.hidden, E = sh.n_experts, k = sh.top_k, I = sh.inter, Is = sh.shared_inter;
-  const size_t ngu = H / kGroup, nga = (k * I + Is) / kGroup;
+  const size_t ngu = H / kGroup, npos = (k * I + Is) / 8;
   const size_t B = maxB;
   WsLayout L;
   L.u = take(B * H * 4);
@@ -53,10 +53,9 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.z = take(B * E * 8);
   L.ids = take(B * k * 4);
   L.w = take(B * k * 4);
-  L.a = take(B * (k * I + Is) * 4);
-  L.adig = take(B * nga * sizeof(DigitGroup));
-  L.asc = take(B * nga * 4);
-  L.cnt = take(B * nga * 4);
+  L.adig = take(B * npos * 16);
+  L.asc = take(B * npos * 4);
+  L.cnt = take(256);  // router arrival counter
   L.pre = take(static_cast<size_t>(maxT) > 0 ? 256 : 0);  // prefill scratch reserved
   L.total = off;
   return L;
@@ -207,7 +206,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     moe_layer_destroy(L);
     return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
   };
-  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, static_cast<size_t>(max_B) * nga * 4);
+  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, 256);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
@@ -266,48 +265,59 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   if (B == 0) return MOE_OK;
   if (!x || !y) return fail(MOE_EINVAL, "%s: x and y are required", fn);
   if (x == y) return fail(MOE_EINVAL, "%s: y must not alias x", fn);
+  if (!moe::aligned16(x) || (add_in && !moe::aligned16(add_in)))
+    return fail(MOE_EALIGN, "%s: x and add_in must be 16-byte aligned", fn);
   if (L->cache_mode && B != 1) return fail(MOE_ESHAPE, "%s: cache mode decodes one token per call", fn);
   const moe_shape& sh = L->sh;
   const int H = sh.hidden, E = sh.n_experts, k = sh.top_k;
   const int ngu = H / moe::kGroup;
-  const int nga = (k * sh.inter + sh.shared_inter) / moe::kGroup;
-  const int arow = k * sh.inter + sh.shared_inter;
+  const int npos = (k * sh.inter + sh.shared_inter) / 8;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  float* u = L->at<float>(L->ws.u);
   auto* udig = L->at<moe::DigitGroup>(L->ws.udig);
   float* usc = L->at<float>(L->ws.usc);
   double* z = L->at<double>(L->ws.z);
   int32_t* ids = L->at<int32_t>(L->ws.ids);
   float* w = L->at<float>(L->ws.w);
-  float* a = L->at<float>(L->ws.a);
-  auto* adig = L->at<moe::DigitGroup>(L->ws.adig);
+  uint4* adig = L->at<uint4>(L->ws.adig);
   float* asc = L->at<float>(L->ws.asc);
   int32_t* cnt = L->at<int32_t>(L->ws.cnt);
   const bool rms = flags & MOE_F_RMSNORM_IN;
   const bool res = flags & MOE_F_RESIDUAL;
 
   hipEvent_t pb = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_route_prep(x, add_in, B, H, rms, u, udig, usc, s), fn);
-  HIP_OR_FAIL(moe::launch_route_logits(u, B, H, L->d.router, L->d.bias, E, z, s), fn);
-  HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, E, k, ids, w, ids_out, w_out, s), fn);
+  // resident mode: the router only produces logits; each gate/up block takes
+  // the top-k itself (no cross-block handshake on the critical path)
+  const bool in_kernel_topk = !L->cache_mode;
+  HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out, udig,
+                                      usc, z, cnt, in_kernel_topk ? nullptr : ids,
+                                      in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
+                                      in_kernel_topk ? nullptr : w_out, s), fn);
   prof_end(L, 0, pb, s);
-  if (u_out) HIP_OR_FAIL(hipMemcpyAsync(u_out, u, sizeof(float) * B * H, hipMemcpyDeviceToDevice, s), fn);
 
   moe::SourceSet S = make_sources(L);
   if (!L->cache_mode) {
     S.experts = L->d.experts_dev;
+    S.E = E;
     for (int b = 0; b < B; ++b) {
-      S.ids = ids + static_cast<size_t>(b) * k;
+      const size_t ko = static_cast<size_t>(b) * k;
+      moe::SourceSet G = S;
+      G.ids = nullptr;
+      G.z = z + static_cast<size_t>(b) * E;
+      G.ids_g = ids + ko;
+      G.w_g = w + ko;
+      G.ids2 = ids_out ? ids_out + ko : nullptr;
+      G.w2 = w_out ? w_out + ko : nullptr;
       hipEvent_t p1 = prof_begin(L, s);
-      HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, true, udig + static_cast<size_t>(b) * ngu,
-                                         usc + static_cast<size_t>(b) * ngu, a + static_cast<size_t>(b) * arow,
-                                         adig + static_cast<size_t>(b) * nga, asc + static_cast<size_t>(b) * nga,
-                                         cnt + static_cast<size_t>(b) * nga, s), fn);
+      HIP_OR_FAIL(moe::launch_ffn_gateup(G, true, true, udig + static_cast<size_t>(b) * ngu,
+                                         usc + static_cast<size_t>(b) * ngu,
+                                         adig + static_cast<size_t>(b) * npos,
+                                         asc + static_cast<size_t>(b) * npos, s), fn);
       prof_end(L, 2, p1, s);
+      S.ids = ids + ko;
       hipEvent_t p2 = prof_begin(L, s);
-      HIP_OR_FAIL(moe::launch_ffn_down(S, w + static_cast<size_t>(b) * k, adig + static_cast<size_t>(b) * nga,
-                                       asc + static_cast<size_t>(b) * nga, x + static_cast<size_t>(b) * H,
+      HIP_OR_FAIL(moe::launch_ffn_down(S, w + ko, adig + static_cast<size_t>(b) * npos,
+                                       asc + static_cast<size_t>(b) * npos, x + static_cast<size_t>(b) * H,
                                        add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
                                        y + static_cast<size_t>(b) * H, s), fn);
       prof_end(L, 3, p2, s);
@@ -322,7 +332,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
   hipEvent_t p1 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, a, adig, asc, cnt, s), fn);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adig, asc, s), fn);
   prof_end(L, 1, p1, s);
   HIP_OR_FAIL(hipEventSynchronize(L->ev_ids), fn);
 
@@ -351,7 +361,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   }
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
   hipEvent_t p2 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, a, adig, asc, cnt, s), fn);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adig, asc, s), fn);
   prof_end(L, 2, p2, s);
   hipEvent_t p3 = prof_begin(L, s);
   HIP_OR_FAIL(moe::launch_ffn_down(S, w, adig, asc, x, add_in, res, y, s), fn);

@@ -5,69 +5,216 @@
 // arquitetura": the router of every layer picks the 8 experts the current
 // token needs. Selection is on the logits (softmax is monotone), ties go to
 // the lower expert id, the weights are a softmax over the selected logits.
+//
+// Layer path (k_route_fused): one launch per call. Every block recomputes the
+// (cheap) RMSNorm of the token, quantises its share of the input groups to
+// digit planes for the expert GEMVs, and computes the logits of 4 experts in
+// fp64. The logits are written with agent-scope (L2-bypassing) stores; after
+// its stores have completed each block bumps a counter, and the block that
+// arrives last runs top-k for every token. No block waits for another and no
+// cache writeback is needed, so the launch costs little more than its loads.
 #include <float.h>
 #include <math.h>
 
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
 
-constexpr int kPrepThreads = 256;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 
-// One block per token. x' = x + add_in (fp32 add of the fp16 perturbation);
-// u = x' * 1/sqrt(mean(x'^2) + 1e-6) when rmsnorm, else u = x'.
-__global__ __launch_bounds__(kPrepThreads) void k_route_prep(const float* __restrict__ x,
-                                                             const uint16_t* __restrict__ add_in,
-                                                             int H, int rmsnorm,
-                                                             float* __restrict__ u,
-                                                             DigitGroup* __restrict__ udig,
-                                                             float* __restrict__ usc) {
-  const int b = blockIdx.x;
-  const float* xb = x + static_cast<size_t>(b) * H;
-  const uint16_t* ab = add_in ? add_in + static_cast<size_t>(b) * H : nullptr;
-  __shared__ float red[kPrepThreads / kWave];
-  __shared__ float s_scale;
-  float r = 1.0f;
-  if (rmsnorm) {
-    float ss = 0.f;
-    for (int h = threadIdx.x; h < H; h += kPrepThreads) {
-      float v = xb[h] + (ab ? h2f(ab[h]) : 0.f);
-      ss = fmaf(v, v, ss);
-    }
-    ss = seg_sum<kWave>(ss);
-    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ss;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float t = 0.f;
-      for (int i = 0; i < kPrepThreads / kWave; ++i) t += red[i];
-      s_scale = 1.0f / sqrtf(t / static_cast<float>(H) + 1e-6f);
-    }
-    __syncthreads();
-    r = s_scale;
-  }
-  const int ng = H / kGroup;
+struct RouteArgs {
+  const float* x;
+  const uint16_t* add_in;
+  int B, H, rmsnorm;
+  const uint16_t* wr;
+  const float* bias;
+  int E, k;
+  float* u_out;       // optional [B][H]
+  DigitGroup* udig;   // [B][H/32]
+  float* usc;         // [B][H/32]
+  double* z;          // [B][E]
+  int32_t* cnt;       // arrival counter, zero between calls
+  int32_t *ids, *ids2;
+  float *w, *w2;
+};
+
+// Per wave: one expert's router row and the whole token input x' are loaded
+// in a single batch (8 consecutive inputs per lane and step); the wave
+// derives the RMSNorm factor from the same registers, so no block reduction
+// and no second pass over x' is needed. A lane's 8 inputs are exactly one
+// "position" of a quantisation group, so a wave that owns a group writes its
+// digit planes straight from registers.
+constexpr int kMaxSteps = 8;  // H <= 8 * 64 * 8 = 4096 in one batch
+
+template <bool HAS_ADD, bool RMS, bool TOPK>
+__global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
+  extern __shared__ double zs[];  // [E] for the top-k of the last block
+  __shared__ double sel_z[kMaxTopK];
+  __shared__ int sel_e[kMaxTopK];
+  __shared__ int is_last;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  float* ub = u + static_cast<size_t>(b) * H;
-  DigitGroup* db = udig + static_cast<size_t>(b) * ng;
-  float* sb = usc + static_cast<size_t>(b) * ng;
-  for (int g0 = 2 * wave; g0 < ng; g0 += 2 * (kPrepThreads / kWave)) {
-    const int g = g0 + (lane >> 5);
-    float v = 0.f;
-    if (g < ng) {
-      const int h = g * kGroup + (lane & 31);
-      v = xb[h] + (ab ? h2f(ab[h]) : 0.f);
-      if (rmsnorm) v *= r;
-      ub[h] = v;
+  const int H = A.H, ngu = H / kGroup, n8 = H / 8;
+  const int nb = gridDim.x;
+  const int gw = blockIdx.x * kWaves + wave;        // global wave index
+  const int e = gw < A.E ? gw : A.E - 1;            // expert row of this wave
+  const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
+
+  for (int b = 0; b < A.B; ++b) {
+    const float* xb = A.x + static_cast<size_t>(b) * H;
+    const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
+    // inputs wider than one batch: the RMSNorm factor needs a pass of its own
+    float r_all = 1.0f;
+    const bool multi = n8 > kWave * kMaxSteps;
+    if (RMS && multi) {
+      float ss = 0.f;
+      for (int c = lane; c < n8; c += kWave) {
+        const float4 x0 = *reinterpret_cast<const float4*>(xb + 8 * c);
+        const float4 x1 = *reinterpret_cast<const float4*>(xb + 8 * c + 4);
+        const uint4 av = HAS_ADD ? *reinterpret_cast<const uint4*>(ab + 8 * c) : make_uint4(0, 0, 0, 0);
+        const uint32_t ap[4] = {av.x, av.y, av.z, av.w};
+        const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v0 = xv[2 * i] + h2f(static_cast<uint16_t>(ap[i] & 0xFFFFu));
+          const float v1 = xv[2 * i + 1] + h2f(static_cast<uint16_t>(ap[i] >> 16));
+          ss = fmaf(v0, v0, ss);
+          ss = fmaf(v1, v1, ss);
+        }
+      }
+      ss = seg_sum<kWave>(ss);
+      r_all = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
     }
-    quant_pair_of_groups(v, g0, ng, db, sb);
+    double acc = 0.0;
+    for (int c0 = 0; c0 < n8; c0 += kWave * kMaxSteps) {
+      uint4 wv[kMaxSteps], av[kMaxSteps];
+      float4 x0[kMaxSteps], x1[kMaxSteps];
+#pragma unroll
+      for (int t = 0; t < kMaxSteps; ++t) {
+        int c = c0 + lane + kWave * t;
+        c = c < n8 ? c : n8 - 1;
+        wv[t] = *reinterpret_cast<const uint4*>(row + 8 * c);
+        x0[t] = *reinterpret_cast<const float4*>(xb + 8 * c);
+        x1[t] = *reinterpret_cast<const float4*>(xb + 8 * c + 4);
+        av[t] = HAS_ADD ? *reinterpret_cast<const uint4*>(ab + 8 * c) : make_uint4(0, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      float u[kMaxSteps][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < kMaxSteps; ++t) {
+        const int c = c0 + lane + kWave * t;
+        const uint32_t ap[4] = {av[t].x, av[t].y, av[t].z, av[t].w};
+        const float xv[8] = {x0[t].x, x0[t].y, x0[t].z, x0[t].w, x1[t].x, x1[t].y, x1[t].z, x1[t].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u[t][2 * i] = xv[2 * i] + h2f(static_cast<uint16_t>(ap[i] & 0xFFFFu));
+          u[t][2 * i + 1] = xv[2 * i + 1] + h2f(static_cast<uint16_t>(ap[i] >> 16));
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf(u[t][i], u[t][i], part);
+        ss += c < n8 ? part : 0.f;
+      }
+      float r = r_all;
+      if (RMS && !multi) {
+        ss = seg_sum<kWave>(ss);
+        r = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
+      }
+#pragma unroll
+      for (int t = 0; t < kMaxSteps; ++t) {
+        const int c = c0 + lane + kWave * t;
+        const uint32_t wp[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
+        double part = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (RMS) {
+            u[t][2 * i] *= r;
+            u[t][2 * i + 1] *= r;
+          }
+          part = fma(static_cast<double>(u[t][2 * i]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu))), part);
+          part = fma(static_cast<double>(u[t][2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), part);
+        }
+        acc += c < n8 ? part : 0.0;
+        // quantise group g = c / 4 if this wave owns it: 4 lanes hold its
+        // 4 positions of 8 values. A wave owns groups gw, gw + nb*4, ...; the
+        // test below is uniform across the wave, so the shuffles run only on
+        // the steps that hold an owned group.
+        const int g = c / 4;
+        const int g_lo = (c0 + kWave * t) / 4;  // first group of this step
+        const int period = nb * kWaves;
+        const int first_owned = g_lo + ((gw - g_lo) % period + period) % period;
+        if (first_owned >= g_lo + kWave / 4 || first_owned >= ngu) continue;
+        const bool own = c < n8 && (g % period) == gw;
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(u[t][i]));
+        m = fmaxf(m, __shfl_xor(m, 1, kWave));
+        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        if (own) {
+          const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
+          uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            int q = static_cast<int>(rintf(u[t][i] * inv));
+            q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const int dg = d < 3 ? ((q + 8) & 15) - 8 : q;
+              wd[d] |= static_cast<uint32_t>(dg & 15) << (4 * i);
+              q = (q - dg) / 16;
+            }
+          }
+          DigitGroup* dg = A.udig + static_cast<size_t>(b) * ngu + g;
+          dg->p[c & 3] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          if ((c & 3) == 0) A.usc[static_cast<size_t>(b) * ngu + g] = m / static_cast<float>(kQmax);
+          if (A.u_out) {
+            float* uo = A.u_out + static_cast<size_t>(b) * H + 8 * c;
+            *reinterpret_cast<float4*>(uo) = make_float4(u[t][0], u[t][1], u[t][2], u[t][3]);
+            *reinterpret_cast<float4*>(uo + 4) = make_float4(u[t][4], u[t][5], u[t][6], u[t][7]);
+          }
+        }
+      }
+    }
+    acc = seg_sum_f64<kWave>(acc);
+    if (lane == 0 && gw < A.E) {
+      const double zv = acc + (A.bias ? static_cast<double>(A.bias[e]) : 0.0);
+      if (TOPK)
+        __hip_atomic_store(A.z + static_cast<size_t>(b) * A.E + e, zv, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        A.z[static_cast<size_t>(b) * A.E + e] = zv;  // read after the kernel boundary
+    }
+  }
+  if (!TOPK) return;
+  // every logit store of this block has completed before the block arrives
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(A.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == nb - 1;
+    if (is_last) __hip_atomic_store(A.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  for (int b = 0; b < A.B; ++b) {
+    for (int f = threadIdx.x; f < A.E; f += kThreads)
+      zs[f] = __hip_atomic_load(A.z + static_cast<size_t>(b) * A.E + f, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const size_t o = static_cast<size_t>(b) * A.k;
+    topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids + o, A.w + o, A.ids2 ? A.ids2 + o : nullptr,
+               A.w2 ? A.w2 + o : nullptr);
   }
 }
 
 constexpr int kLogitWaves = 4;
 
-// One wave per expert row; fp64 accumulation of exact fp32 x fp16 products.
+// Standalone router: one wave per expert row, fp64 accumulation of exact
+// fp32 x fp16 products.
 __global__ __launch_bounds__(kLogitWaves* kWave) void k_route_logits(
     const float* __restrict__ u, int B, int H, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int E, double* __restrict__ z) {
@@ -76,11 +223,10 @@ __global__ __launch_bounds__(kLogitWaves* kWave) void k_route_logits(
   const int e = blockIdx.x * kLogitWaves + wave;
   if (e >= E) return;
   const uint16_t* row = wr + static_cast<size_t>(e) * H;
-  const int nc = H / 8;  // 16-byte chunks of 8 fp16
   for (int b = 0; b < B; ++b) {
     const float* ub = u + static_cast<size_t>(b) * H;
     double acc = 0.0;
-    for (int c = lane; c < nc; c += kWave) {
+    for (int c = lane; c < H / 8; c += kWave) {
       const uint4 wv = *reinterpret_cast<const uint4*>(row + 8 * c);
       const float4 u0 = *reinterpret_cast<const float4*>(ub + 8 * c);
       const float4 u1 = *reinterpret_cast<const float4*>(ub + 8 * c + 4);
@@ -88,10 +234,8 @@ __global__ __launch_bounds__(kLogitWaves* kWave) void k_route_logits(
       const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const double w_lo = static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu)));
-        const double w_hi = static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16)));
-        acc = fma(static_cast<double>(uv[2 * i]), w_lo, acc);
-        acc = fma(static_cast<double>(uv[2 * i + 1]), w_hi, acc);
+        acc = fma(static_cast<double>(uv[2 * i]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu))), acc);
+        acc = fma(static_cast<double>(uv[2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), acc);
       }
     }
     acc = seg_sum_f64<kWave>(acc);
@@ -99,80 +243,48 @@ __global__ __launch_bounds__(kLogitWaves* kWave) void k_route_logits(
   }
 }
 
-constexpr int kMaxPerLane = 1024 / kWave;  // E <= 1024
-
-__device__ __forceinline__ bool key_better(double v1, int e1, double v2, int e2) {
-  return v1 > v2 || (v1 == v2 && e1 < e2);
-}
-
-// One wave per token: k rounds of a wave-wide argmax on (z, -id).
-__global__ __launch_bounds__(kWave) void k_route_topk(const double* __restrict__ z64,
-                                                      const float* __restrict__ z32, int E, int k,
-                                                      int32_t* __restrict__ ids,
-                                                      float* __restrict__ w,
-                                                      int32_t* __restrict__ ids2,
-                                                      float* __restrict__ w2) {
+// Standalone top-k: one block per token, logits from fp64 z64 or fp32 z32.
+__global__ __launch_bounds__(kThreads) void k_route_topk(const double* __restrict__ z64,
+                                                         const float* __restrict__ z32, int E, int k,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ w,
+                                                         int32_t* __restrict__ ids2,
+                                                         float* __restrict__ w2) {
+  extern __shared__ double zs[];
+  __shared__ double sel_z[kMaxTopK];
+  __shared__ int sel_e[kMaxTopK];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  double v[kMaxPerLane];
-  const int per = (E + kWave - 1) / kWave;
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const int e = lane + kWave * j;
-    double t = -DBL_MAX;
-    if (j < per && e < E)
-      t = z64 ? z64[static_cast<size_t>(b) * E + e]
-              : static_cast<double>(z32[static_cast<size_t>(b) * E + e]);
-    v[j] = t;
-  }
-  uint32_t taken = 0;  // bit j: candidate j of this lane already selected
-  double sel_v = 0.0, v0 = 0.0;
-  int sel_e = 0;
-  for (int r = 0; r < k; ++r) {
-    double bv = -DBL_MAX;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      const int e = lane + kWave * j;
-      if (j < per && e < E && !((taken >> j) & 1u) && key_better(v[j], e, bv, be)) {
-        bv = v[j];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      const double ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (key_better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & (kWave - 1)) == lane) taken |= 1u << (be / kWave);
-    if (r == 0) v0 = bv;
-    if (lane == r) {
-      sel_v = bv;
-      sel_e = be;
-    }
-  }
-  // softmax over the k selected logits, max-subtracted (v0 is the largest)
-  double ex = lane < k ? exp(sel_v - v0) : 0.0;
-  double tot = seg_sum_f64<kWave>(ex);
-  if (lane < k) {
-    const float wv = static_cast<float>(ex / tot);
-    ids[static_cast<size_t>(b) * k + lane] = sel_e;
-    w[static_cast<size_t>(b) * k + lane] = wv;
-    if (ids2) ids2[static_cast<size_t>(b) * k + lane] = sel_e;
-    if (w2) w2[static_cast<size_t>(b) * k + lane] = wv;
-  }
+  for (int e = threadIdx.x; e < E; e += kThreads)
+    zs[e] = z64 ? z64[static_cast<size_t>(b) * E + e] : static_cast<double>(z32[static_cast<size_t>(b) * E + e]);
+  __syncthreads();
+  const size_t o = static_cast<size_t>(b) * k;
+  topk_block(zs, E, k, sel_z, sel_e, ids + o, w + o, ids2 ? ids2 + o : nullptr, w2 ? w2 + o : nullptr);
 }
 
 }  // namespace
 
-hipError_t launch_route_prep(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
-                             float* u, DigitGroup* udig, float* usc, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_prep, dim3(B), dim3(kPrepThreads), 0, s, x, add_in, H,
-                     rmsnorm ? 1 : 0, u, udig, usc);
+hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
+                              const uint16_t* wr, const float* bias, int E, int k, float* u_out,
+                              DigitGroup* udig, float* usc, double* z, int32_t* cnt, int32_t* ids,
+                              float* w, int32_t* ids2, float* w2, hipStream_t s) {
+  RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, z, cnt,
+              ids, ids2, w, w2};
+  const int blocks = (E + kWaves - 1) / kWaves;
+  const size_t lds = sizeof(double) * E;
+  const bool topk = ids != nullptr;
+#define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks), dim3(kThreads), lds, s, A)
+  if (topk) {
+    if (add_in && rmsnorm) MOE_ROUTE(true, true, true);
+    else if (add_in) MOE_ROUTE(true, false, true);
+    else if (rmsnorm) MOE_ROUTE(false, true, true);
+    else MOE_ROUTE(false, false, true);
+  } else {
+    if (add_in && rmsnorm) MOE_ROUTE(true, true, false);
+    else if (add_in) MOE_ROUTE(true, false, false);
+    else if (rmsnorm) MOE_ROUTE(false, true, false);
+    else MOE_ROUTE(false, false, false);
+  }
+#undef MOE_ROUTE
   return hipGetLastError();
 }
 
@@ -186,7 +298,8 @@ hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr,
 
 hipError_t launch_route_topk(const double* z64, const float* z32, int B, int E, int k, int32_t* ids,
                              float* w, int32_t* ids2, float* w2, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_topk, dim3(B), dim3(kWave), 0, s, z64, z32, E, k, ids, w, ids2, w2);
+  hipLaunchKernelGGL(k_route_topk, dim3(B), dim3(kThreads), sizeof(double) * E, s, z64, z32, E, k,
+                     ids, w, ids2, w2);
   return hipGetLastError();
 }
 
