@@ -79,6 +79,23 @@ hipError_t launch_ffn_down(const SourceSet& src, const float* w, const uint4* ad
                            const float* x, const uint16_t* add_in, bool residual, float* y,
                            hipStream_t s);
 
+// ---------------------------------------------------------------- prefill
+// Workspace layout of a prefill of up to T tokens (byte offsets).
+struct PrefillLayout {
+  size_t ids, w, hist, base, local_rank, seg, tiles, n_tiles, perm, pos_of, act_r, act_s, out_r, xf, z,
+      total;
+  int chunks, max_tiles;
+};
+PrefillLayout prefill_layout(int T, int E, int k, int H, int I, int Is);
+// Routing (given logits, or x . router), stable sort of the T*k assignments
+// by expert, bf16 MFMA grouped GEMMs (gate/up + GeGLU, down weighted by the
+// routing weight), shared expert, and the combine into y [T][H] fp32.
+hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
+                          const float* logits_in, const uint16_t* router, const float* bias, int T,
+                          int E, int k, int H, int I, int Is, const uint8_t* experts, size_t blob_e,
+                          const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
+                          hipStream_t s);
+
 // ---------------------------------------------------------------- standalone GEMV
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,
                           float* y, hipStream_t s);

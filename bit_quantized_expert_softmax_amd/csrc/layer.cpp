@@ -56,7 +56,9 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.adig = take(B * npos * 16);
   L.asc = take(B * npos * 4);
   L.cnt = take(256);  // router arrival counter
-  L.pre = take(static_cast<size_t>(maxT) > 0 ? 256 : 0);  // prefill scratch reserved
+  L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
+                                         sh.shared_inter).total
+                        : 0);
   L.total = off;
   return L;
 }
@@ -379,9 +381,26 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in, int32_t T,
                              float* y, int32_t* ids_out, float* w_out, void* stream) {
   moe::clear_error();
-  (void)x_bf16; (void)logits_in; (void)T; (void)y; (void)ids_out; (void)w_out; (void)stream;
-  if (!L) return fail(MOE_EINVAL, "moe_layer_prefill: NULL handle");
-  return fail(MOE_ESTATE, "moe_layer_prefill: not available in this build");
+  const char* fn = "moe_layer_prefill";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (L->cache_mode) return fail(MOE_ESTATE, "%s: prefill needs a resident-mode handle", fn);
+  if (T < 0 || T > L->max_T) return fail(MOE_ESHAPE, "%s: T=%d outside [0, max_T=%d]", fn, T, L->max_T);
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !y) return fail(MOE_EINVAL, "%s: x_bf16 and y are required", fn);
+  if (!moe::aligned16(x_bf16)) return fail(MOE_EALIGN, "%s: x_bf16 must be 16-byte aligned", fn);
+  const moe_shape& sh = L->sh;
+  if (sh.inter % 64 || sh.shared_inter % 64 || sh.hidden % 128)
+    return fail(MOE_ESHAPE, "%s: needs inter and shared_inter multiples of 64 and hidden a multiple of 128", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::PrefillLayout P = moe::prefill_layout(L->max_T, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
+                                                   sh.shared_inter);
+  hipEvent_t pb = prof_begin(L, s);
+  HIP_OR_FAIL(moe::launch_prefill(P, L->wsb + L->ws.pre, x_bf16, logits_in, L->d.router, L->d.bias, T,
+                                  sh.n_experts, sh.top_k, sh.hidden, sh.inter, sh.shared_inter,
+                                  L->d.experts_dev, L->blob_e, L->d.shared_blob, y, ids_out, w_out, s),
+              fn);
+  prof_end(L, 4, pb, s);
+  return MOE_OK;
 }
 
 moe_status moe_layer_profile(moe_layer* L, int32_t enable) {
