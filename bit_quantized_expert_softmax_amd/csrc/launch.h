@@ -32,6 +32,7 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 // Layer router, one launch: x' = x (+ add_in); u = x' or rmsnorm(x'); u's
 // digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
 // finish. cnt must be zero before the launch and is zero after it.
+// Grid: (E/4 blocks) x B tokens; the top-k variant (ids != nullptr) needs B == 1.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, double* z, int32_t* cnt, int32_t* ids,
@@ -95,6 +96,32 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
                           int E, int k, int H, int I, int Is, const uint8_t* experts, size_t blob_e,
                           const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
                           hipStream_t s);
+
+// ---------------------------------------------------------------- batched decode
+// Stable sort of A assignments (token*k + rank, expert ids[a]) by expert:
+// seg [E+1] segment starts, perm [A] sorted position -> assignment, pos_of [A]
+// assignment -> sorted position, tiles/n_tiles the 64-row tile table.
+hipError_t launch_permute(const int32_t* ids, int A, int E, int chunks, int32_t* hist, int32_t* lrank,
+                          int32_t* base, int32_t* seg, int2* tiles, int32_t* n_tiles, int32_t* perm,
+                          int32_t* pos_of, hipStream_t s);
+int permute_chunks(int A);
+
+struct BatchedBuffers {
+  const int32_t* seg;
+  const int32_t* perm;
+  const int32_t* pos_of;
+  uint4* adig_r;
+  float* asc_r;
+  uint4* adig_s;
+  float* asc_s;
+  float* out_r;
+  float* out_s;
+};
+// Grouped gate/up and down GEMVs over the expert segments, then the combine.
+hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
+                          size_t blob_e, int H, int I, int Is, int E, int k, int B,
+                          const DigitGroup* udig, const float* usc, const float* w, const float* x,
+                          const uint16_t* add_in, bool residual, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------- standalone GEMV
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,

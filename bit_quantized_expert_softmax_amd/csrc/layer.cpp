@@ -33,7 +33,11 @@ moe_status check_shape(const moe_shape* sh, const char* fn);
 namespace {
 
 struct WsLayout {
-  size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre, total;
+  size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre;
+  // batched decode (max_B > 1): expert sort and per-assignment outputs
+  size_t hist, base, lrank, seg, tiles, n_tiles, perm, pos_of, out_r, out_s;
+  int chunks;
+  size_t total;
 };
 
 WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
@@ -59,6 +63,18 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
+  const size_t A = B > 1 ? B * k : 0;
+  L.chunks = permute_chunks(static_cast<int>(A));
+  L.hist = take(static_cast<size_t>(L.chunks) * E * 4);
+  L.base = take(static_cast<size_t>(L.chunks) * E * 4);
+  L.lrank = take(A * 4);
+  L.seg = take((E + 1) * 4);
+  L.tiles = take((A / 64 + E + 1) * 8);
+  L.n_tiles = take(4);
+  L.perm = take(A * 4);
+  L.pos_of = take(A * 4);
+  L.out_r = take(A * H * 4);
+  L.out_s = take(B > 1 ? B * H * 4 : 0);
   L.total = off;
   return L;
 }
@@ -298,7 +314,37 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   prof_end(L, 0, pb, s);
 
   moe::SourceSet S = make_sources(L);
+  // grouped path: every touched expert read once per call; its LDS tiles hold
+  // 8 tokens' activation digits (fits for hidden <= 3840, intermediates <= 3272)
+  const int inter_max = sh.inter > sh.shared_inter ? sh.inter : sh.shared_inter;
+  const bool grouped = !L->cache_mode && B > 1 && 8 * ngu * 68 <= 65536 && 8 * (inter_max / 8) * 20 <= 65536;
+  if (grouped) {
+    // batched: per-token top-k, stable sort of the B*k assignments by expert,
+    // grouped GEMVs that read each touched expert once, ordered combine
+    hipEvent_t pt = prof_begin(L, s);
+    HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, E, k, ids, w, ids_out, w_out, s), fn);
+    const int A = B * k;
+    int32_t* seg = L->at<int32_t>(L->ws.seg);
+    int32_t* perm = L->at<int32_t>(L->ws.perm);
+    int32_t* pos_of = L->at<int32_t>(L->ws.pos_of);
+    HIP_OR_FAIL(moe::launch_permute(ids, A, E, L->ws.chunks, L->at<int32_t>(L->ws.hist),
+                                    L->at<int32_t>(L->ws.lrank), L->at<int32_t>(L->ws.base), seg,
+                                    L->at<int2>(L->ws.tiles), L->at<int32_t>(L->ws.n_tiles), perm, pos_of,
+                                    s), fn);
+    prof_end(L, 0, pt, s);
+    moe::BatchedBuffers bb{seg, perm, pos_of, adig, asc,
+                           adig + static_cast<size_t>(A) * (sh.inter / 8),
+                           asc + static_cast<size_t>(A) * (sh.inter / 8),
+                           L->at<float>(L->ws.out_r), L->at<float>(L->ws.out_s)};
+    hipEvent_t p1 = prof_begin(L, s);
+    HIP_OR_FAIL(moe::launch_batched(bb, L->d.experts_dev, L->d.shared_blob, L->blob_e, H, sh.inter,
+                                    sh.shared_inter, E, k, B, udig, usc, w, x, add_in, res, y, s), fn);
+    prof_end(L, 2, p1, s);
+    if (stats) stats->calls += 1;
+    return MOE_OK;
+  }
   if (!L->cache_mode) {
+    // token by token: routed + shared gate/up (with the in-kernel top-k), then down
     S.experts = L->d.experts_dev;
     S.E = E;
     for (int b = 0; b < B; ++b) {
@@ -310,16 +356,15 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       G.w_g = w + ko;
       G.ids2 = ids_out ? ids_out + ko : nullptr;
       G.w2 = w_out ? w_out + ko : nullptr;
+      uint4* adb = adig + static_cast<size_t>(b) * npos;
+      float* asb = asc + static_cast<size_t>(b) * npos;
       hipEvent_t p1 = prof_begin(L, s);
       HIP_OR_FAIL(moe::launch_ffn_gateup(G, true, true, udig + static_cast<size_t>(b) * ngu,
-                                         usc + static_cast<size_t>(b) * ngu,
-                                         adig + static_cast<size_t>(b) * npos,
-                                         asc + static_cast<size_t>(b) * npos, s), fn);
+                                         usc + static_cast<size_t>(b) * ngu, adb, asb, s), fn);
       prof_end(L, 2, p1, s);
       S.ids = ids + ko;
       hipEvent_t p2 = prof_begin(L, s);
-      HIP_OR_FAIL(moe::launch_ffn_down(S, w + ko, adig + static_cast<size_t>(b) * npos,
-                                       asc + static_cast<size_t>(b) * npos, x + static_cast<size_t>(b) * H,
+      HIP_OR_FAIL(moe::launch_ffn_down(S, w + ko, adb, asb, x + static_cast<size_t>(b) * H,
                                        add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
                                        y + static_cast<size_t>(b) * H, s), fn);
       prof_end(L, 3, p2, s);

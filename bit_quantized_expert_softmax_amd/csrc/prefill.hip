@@ -274,6 +274,17 @@ __global__ void k_bf16_to_f32(const uint16_t* __restrict__ x, size_t n, float* _
 
 }  // namespace
 
+int permute_chunks(int A) { return (A + kChunk - 1) / kChunk; }
+
+hipError_t launch_permute(const int32_t* ids, int A, int E, int chunks, int32_t* hist, int32_t* lrank,
+                          int32_t* base, int32_t* seg, int2* tiles, int32_t* n_tiles, int32_t* perm,
+                          int32_t* pos_of, hipStream_t s) {
+  hipLaunchKernelGGL(k_perm_count, dim3(chunks), dim3(kChunk), 0, s, ids, A, E, hist, lrank);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, hist, chunks, E, base, seg, tiles, n_tiles);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(chunks), dim3(kChunk), 0, s, ids, A, E, base, lrank, perm, pos_of);
+  return hipGetLastError();
+}
+
 PrefillLayout prefill_layout(int T, int E, int k, int H, int I, int Is) {
   PrefillLayout L{};
   size_t off = 0;
@@ -336,10 +347,9 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
   int32_t* n_tiles = reinterpret_cast<int32_t*>(at(L.n_tiles));
   int32_t* perm = reinterpret_cast<int32_t*>(at(L.perm));
   int32_t* pos_of = reinterpret_cast<int32_t*>(at(L.pos_of));
-  hipLaunchKernelGGL(k_perm_count, dim3(L.chunks), dim3(kChunk), 0, s, ids, A, E, hist, lrank);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, hist, L.chunks, E, base, seg, tiles, n_tiles);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(L.chunks), dim3(kChunk), 0, s, ids, A, E, base, lrank, perm, pos_of);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_permute(ids, A, E, L.chunks, hist, lrank, base, seg, tiles, n_tiles, perm, pos_of, s)) !=
+      hipSuccess)
+    return e;
 
   const __bf16* x = reinterpret_cast<const __bf16*>(x_bf16);
   __bf16* act_r = reinterpret_cast<__bf16*>(at(L.act_r));

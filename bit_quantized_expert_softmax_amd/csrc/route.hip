@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
   const int e = gw < A.E ? gw : A.E - 1;            // expert row of this wave
   const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
 
-  for (int b = 0; b < A.B; ++b) {
+  {
+    const int b = blockIdx.y;  // one token per grid row
     const float* xb = A.x + static_cast<size_t>(b) * H;
     const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
     // inputs wider than one batch: the RMSNorm factor needs a pass of its own
@@ -272,7 +273,7 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
   const int blocks = (E + kWaves - 1) / kWaves;
   const size_t lds = sizeof(double) * E;
   const bool topk = ids != nullptr;
-#define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks), dim3(kThreads), lds, s, A)
+#define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks, B), dim3(kThreads), lds, s, A)
   if (topk) {
     if (add_in && rmsnorm) MOE_ROUTE(true, true, true);
     else if (add_in) MOE_ROUTE(true, false, true);
