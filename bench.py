@@ -232,6 +232,64 @@ def main():
         detail["resident_gateup_GBps"] = gu_res / (us_r * 1e-6) / 1e9
         for h in res:
             api.moe_layer_destroy(h)
+
+        # batched decode (B tokens per step, grouped by expert) and 2048-token
+        # prefill on one layer of the same shape, unbiased routing
+        d0 = layers[0]
+        for B in (16, 64):
+            wsb = torch.zeros(api.moe_layer_workspace_bytes(sh, B, 0), dtype=torch.uint8, device=devn)
+            hb = api.moe_layer_create(sh, router=d0["router"], shared_blob=d0["shared"], workspace=wsb,
+                                      experts_dev=d0["experts_dev"], max_B=B)
+            xb = torch.from_numpy(gen.x_fp32(B * 8, H, 3, sub=B)).to(devn)
+            yb = torch.empty((B, H), device=devn)
+            idsb = torch.empty((B, k), dtype=torch.int32, device=devn)
+
+            def bstep(i):
+                api.moe_layer_decode(hb, xb[(i % 8) * B:(i % 8 + 1) * B], None, B, 0, yb, idsb)
+            for i in range(5):
+                bstep(i)
+            torch.cuda.synchronize()
+            n_it = 40
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            touched = 0
+            for i in range(n_it):
+                bstep(i)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / n_it
+            for i in range(8):
+                bstep(i)
+                touched += len(np.unique(idsb.cpu().numpy()))
+            step_bytes = touched / 8 * blob + gen.blob_bytes(H, Is) + E * H * 2
+            detail[f"batched_B{B}"] = {"tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms,
+                                       "distinct_experts": touched / 8,
+                                       "GBps": step_bytes / (ms * 1e-3) / 1e9}
+            api.moe_layer_destroy(hb)
+            del wsb
+        Tp = 2048
+        wsp = torch.zeros(api.moe_layer_workspace_bytes(sh, 1, Tp), dtype=torch.uint8, device=devn)
+        hp_ = api.moe_layer_create(sh, router=d0["router"], shared_blob=d0["shared"], workspace=wsp,
+                                   experts_dev=d0["experts_dev"], max_T=Tp)
+        xp = torch.from_numpy(gen.x_bf16(Tp, H, 4).view(np.int16)).to(devn)
+        lp = torch.from_numpy(gen.logits_uniform(Tp, E, 4)).to(devn)
+        yp = torch.empty((Tp, H), device=devn)
+        for i in range(3):
+            api.moe_layer_prefill(hp_, xp, lp, Tp, yp)
+        torch.cuda.synchronize()
+        n_it = 10
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n_it):
+            api.moe_layer_prefill(hp_, xp, lp, Tp, yp)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / n_it
+        flops = 2.0 * Tp * (k * 3 * H * I + 3 * H * Is)
+        detail["prefill_2048"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+                                  "mfma_bf16_frac": flops / (ms * 1e-3) / 2.5e15, "GFLOP": flops / 1e9}
+        api.moe_layer_destroy(hp_)
+        del wsp
         for d in layers:
             del d["experts_dev"]
 
