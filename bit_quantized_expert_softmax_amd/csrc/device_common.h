@@ -50,6 +50,35 @@ __device__ __forceinline__ double seg_sum_f64(double v) {
   return v;
 }
 
+// Cross-lane moves through DPP (no LDS traffic). CTRL is the DPP control:
+// quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2),
+// row_half_mirror = 0x141 (mirror within 8 lanes), row_mirror = 0x140
+// (mirror within 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffffll), CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, true);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Sum over aligned segments of L lanes (L = 4, 8, 16, 32 or 64); every lane of
+// a segment receives the segment total. Within 16 lanes the steps are DPP.
+template <int L, class T>
+__device__ __forceinline__ T dpp_sum(T v) {
+  v += dpp<0xB1>(v);
+  if (L >= 4) v += dpp<0x4E>(v);
+  if (L >= 8) v += dpp<0x141>(v);
+  if (L >= 16) v += dpp<0x140>(v);
+  if (L >= 32) v += __shfl_xor(v, 16, kWave);
+  if (L >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
 // GELU, tanh form: z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

@@ -69,16 +69,17 @@ struct SourceSet {
 
 // Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k) (do_routed)
 // and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
-// as digit planes: adig[p] holds the 4 digit words of activations
-// [8p, 8p+8) and asc[p] their scale.
+// as digit planes, one DigitGroup and one scale per 32 activations.
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
-                             const DigitGroup* udig, const float* usc, uint4* adig, float* asc,
+                             const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
                              hipStream_t s);
 // Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
 // optional residual x' = x + add_in, y [H].
-hipError_t launch_ffn_down(const SourceSet& src, const float* w, const uint4* adig, const float* asc,
-                           const float* x, const uint16_t* add_in, bool residual, float* y,
-                           hipStream_t s);
+hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,
+                           const float* asc, const float* x, const uint16_t* add_in, bool residual,
+                           float* y, hipStream_t s);
+// Largest LDS footprint of the one-token kernels for a shape (bytes).
+size_t decode_lds_bytes(int H, int E, int k, int I, int Is);
 
 // ---------------------------------------------------------------- prefill
 // Workspace layout of a prefill of up to T tokens (byte offsets).

@@ -190,6 +190,9 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
   const int nga = (sh->top_k * sh->inter + sh->shared_inter) / moe::kGroup;
   if (nga > 512)
     return fail(MOE_ESHAPE, "%s: (top_k*inter + shared_inter)/32 = %d exceeds 512", fn, nga);
+  const size_t lds = moe::decode_lds_bytes(sh->hidden, sh->n_experts, sh->top_k, sh->inter, sh->shared_inter);
+  if (lds > 65536)
+    return fail(MOE_ESHAPE, "%s: shape needs %zu bytes of LDS per decode block (limit 65536)", fn, lds);
   if (!d->router || !d->shared_blob || !d->workspace)
     return fail(MOE_EINVAL, "%s: router, shared_blob and workspace are required", fn);
   const bool cache_mode = d->experts_dev == nullptr;
@@ -356,7 +359,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       G.w_g = w + ko;
       G.ids2 = ids_out ? ids_out + ko : nullptr;
       G.w2 = w_out ? w_out + ko : nullptr;
-      uint4* adb = adig + static_cast<size_t>(b) * npos;
+      auto* adb = reinterpret_cast<moe::DigitGroup*>(adig + static_cast<size_t>(b) * npos);
       float* asb = asc + static_cast<size_t>(b) * npos;
       hipEvent_t p1 = prof_begin(L, s);
       HIP_OR_FAIL(moe::launch_ffn_gateup(G, true, true, udig + static_cast<size_t>(b) * ngu,
@@ -379,7 +382,8 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
   hipEvent_t p1 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adig, asc, s), fn);
+  auto* adg = reinterpret_cast<moe::DigitGroup*>(adig);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s), fn);
   prof_end(L, 1, p1, s);
   HIP_OR_FAIL(hipEventSynchronize(L->ev_ids), fn);
 
@@ -408,10 +412,10 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   }
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
   hipEvent_t p2 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adig, asc, s), fn);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s), fn);
   prof_end(L, 2, p2, s);
   hipEvent_t p3 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adig, asc, x, add_in, res, y, s), fn);
+  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s), fn);
   prof_end(L, 3, p3, s);
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
   if (stats) {

@@ -44,12 +44,15 @@ def test_batched_decode_matches_per_token_oracle(shape, cid, B):
     assert_close(w, r["w"], "w")
     assert_close(y, r["y"], f"y B={B}")
     assert np.array_equal(u, x)
-    # every token's row equals a B=1 call of the same token (grouping changes no math)
+    # every token's row matches a B=1 call of the same token: the routing is
+    # identical and the outputs differ only by activation rounding (the batched
+    # kernels quantise GeGLU activations per 8, the one-token kernels per 32;
+    # either rounds to within 0.5/30583 of its group's largest magnitude)
     L1 = Layer(shape, d)
     for t in (0, B - 1):
         y1, ids1, _, _ = decode(L1, x[t:t + 1])
         assert np.array_equal(ids1[0], ids[t])
-        assert_close(y[t], y1[0], "batched vs single", rel=2e-5)
+        assert_close(y[t], y1[0], "batched vs single", rel=1e-4)
     # same inputs, same bits
     y2, _, _, _ = decode(L, x)
     assert np.array_equal(y, y2)
