@@ -1,5 +1,6 @@
-// Batched decode (B tokens per call) of one MoE layer: tokens are grouped by
-// expert so that every touched expert's int4 rows are read once per call.
+// Batched decode (B tokens per call) of one MoE layer on the matrix cores:
+// tokens are grouped by expert so that every touched expert's int4 rows are
+// read once per call.
 //
 // The layer is the one of "Como executar um modelo de 26 bilhões de
 // parâmetros em dois gigabytes de memória em um Mac comum", section "Qual é
@@ -8,261 +9,304 @@
 // "Desempenho no mundo real".
 //
 // After routing, the B*k assignments are sorted by expert (stable: expert,
-// token, rank) and each expert becomes a segment of rows. A segment's
-// gate/up rows are streamed once into registers and multiplied with the
-// digit planes of every token of the segment (8 tokens per LDS tile); the
-// GeGLU activations are quantised per 8 values in the wave, as in B=1 decode.
-// The down kernel does the same per output row and writes one fp32 row per
+// token, rank) and each expert becomes a segment of rows; the shared expert is
+// one more segment holding every token. Per segment the projection is a small
+// dense product W [rows x K] * X [K x m], so it runs on 16x16x32 fp16 MFMA:
+//
+//   * a wave streams 16 weight rows per tile, 4 quant groups (64 contiguous
+//     bytes of each row) per K step, prefetched DEPTH steps ahead in
+//     registers: the lane of 16-lane row q loads group 4*st + q of its row
+//     (16 bytes) and that group's scale. MFMA j of the step takes dword j of
+//     every lane's group, so one MFMA's K = 32 spans the step's 4 groups (8
+//     values of each); as each lane dequantises with its own group's scale,
+//     the sum is unchanged and no lane exchange is needed;
+//   * nibbles become fp16 by the exponent trick (0x6400 | n is 1024 + n),
+//     which yields k in the order (0,4,1,5,2,6,3,7) within each 8; the
+//     activations are stored in that same order, so the dot products are
+//     unchanged. A weight is rounded once, to fp16(n * scale);
+//   * the segment's activation slice of a K step (m tokens x 128 values) is
+//     loaded with the step's weights, staged in LDS (double buffered) one
+//     step ahead, and shared by the block's 4 waves;
+//   * activations are fp16 copies pre-scaled by a per-token power of two
+//     (tsc, set by the router) so that they stay far inside the fp16 range;
+//     the epilogues undo the scale exactly.
+//
+// gate/up: a wave owns 16 (gate row, up row) pairs; the epilogue applies
+// GeGLU and stores the activations for down (fp16, same order, scaled by
+// 1/tsc^2). down: a wave owns 32 output rows and writes one fp32 row per
 // assignment; the combine adds, per token and in rank order, w_j times its
-// routed rows to the shared expert's output (and the residual).
+// routed rows to the shared expert's row (and the residual).
+#include <type_traits>
+
 #include "launch.h"
 
 namespace moe {
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kLanes = 8;                  // lanes per row (pair)
-constexpr int kRowsPerWave = kWave / kLanes;  // 8
-constexpr int kTT = 8;                     // tokens per LDS tile
+constexpr int kTile = 16;               // MFMA tile edge: rows and tokens
+constexpr int kStepK = 4 * kGroup;      // K per step: one group per 16-lane row
+constexpr int kBRow = kStepK * 2 + 16;  // LDS bytes per token of a step slice (padded)
+constexpr int kMR = 2;                  // 16-row weight tiles per wave
 
-// Segment s < E: routed expert s, rows = its assignments; s == E: shared
-// expert, rows = all B tokens.
-struct BatchArgs {
+struct MArgs {
   const uint8_t* experts;
   const uint8_t* shared;
   size_t blob_e;
   int H, I, Is, E, k, B;
   const int32_t* seg;    // [E+1] segment starts in the sorted assignment list
   const int32_t* perm;   // sorted position -> assignment (token*k + rank)
-  const DigitGroup* udig;  // [B][H/32]
-  const float* usc;
-  uint4* adig_r;  // [B*k][I/8]   routed activations by sorted position
-  float* asc_r;
-  uint4* adig_s;  // [B][Is/8]    shared activations by token
-  float* asc_s;
-  float* out_r;   // [B*k][H]
-  float* out_s;   // [B][H]
+  const uint16_t* u16;   // [B][H] fp16 inputs / tsc
+  const float* tsc;      // [B]
+  uint16_t* act_r;       // [B*k][I]  routed GeGLU activations by sorted position
+  uint16_t* act_s;       // [B][Is]   shared activations by token
+  float* out_r;          // [B*k][H]
+  float* out_s;          // [B][H]
+  int tiles_r, tiles_s;  // blocks per routed / shared segment
 };
 
-__device__ __forceinline__ void segment_rows(const BatchArgs& A, int s, int& r0, int& nrows,
-                                             const uint8_t*& blob, int& inter) {
-  if (s < A.E) {
-    r0 = A.seg[s];
-    nrows = A.seg[s + 1] - r0;
-    blob = A.experts + static_cast<size_t>(s) * A.blob_e;
-    inter = A.I;
-  } else {
-    r0 = 0;
-    nrows = A.B;
-    blob = A.shared;
-    inter = A.Is;
+// 8 signed nibbles (k = 0..7 in bits 4k..4k+3) times scale s, as fp16 in the
+// order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
+  const uint32_t x = w ^ 0x88888888u;  // nibble n -> n + 8 (unsigned)
+  const f16x2 bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
+  const f16x2 sc = {s, s};
+  const f16x2 h0 = (__builtin_bit_cast(f16x2, (x & 0x000F000Fu) | 0x64006400u) - bias) * sc;
+  const f16x2 h1 = (__builtin_bit_cast(f16x2, ((x >> 4) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
+  const f16x2 h2 = (__builtin_bit_cast(f16x2, ((x >> 8) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
+  const f16x2 h3 = (__builtin_bit_cast(f16x2, ((x >> 12) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
+  return f16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(lo))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(hi))) << 16);
+}
+
+struct WStep {
+  uint4 q[kMR];       // group 4*st + q (16-lane row q of the wave) of the lane's row
+  uint32_t s[kMR];    // its fp16 scale
+};
+
+// Weights of K step st: group 4*st + q of the lane's row in each tile (16
+// bytes; a 16-lane row of the wave reads 64 contiguous bytes of each of its 16
+// weight rows) and that group's scale. Groups past K are clamped to the last
+// one (their scale is zeroed when used). No loaded value is used here, so the
+// loads stay in flight.
+__device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow,
+                                          const uint16_t* const* srow, int ngk, int st, int q) {
+  int g = 4 * st + q;
+  g = g < ngk ? g : ngk - 1;
+#pragma unroll
+  for (int m = 0; m < kMR; ++m) {
+    // cached load: the other half of each 128-byte line is read one step later
+    b.q[m] = *reinterpret_cast<const uint4*>(qrow[m] + 16 * static_cast<size_t>(g));
+    b.s[m] = srow[m][g];
   }
 }
 
-__device__ __forceinline__ int token_of(const BatchArgs& A, int s, int row) {
-  return s < A.E ? A.perm[row] / A.k : row;
-}
-
-// Quantises the activation of segment-head lanes (0, 8, ..., 56) as one
-// position of 8 values (same encoding as the B=1 kernels).
-__device__ __forceinline__ void quant_pos8(float a, uint4* dst, float* dsc) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int p = lane >> 3;
-  float m = (lane & 7) == 0 ? fabsf(a) : 0.f;
-  m = fmaxf(m, __shfl_xor(m, 8, kWave));
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
-  int q = static_cast<int>(rintf(a * inv));
-  q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
-  uint32_t wd[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int dg = d < 3 ? ((q + 8) & 15) - 8 : q;
-    wd[d] = (lane & 7) == 0 ? static_cast<uint32_t>(dg & 15) << (4 * p) : 0u;
-    q = (q - dg) / 16;
+// One launch covers all segments: tiles_r blocks per routed expert (blocks of
+// untouched experts exit at once), then tiles_s blocks of the shared expert.
+// GATEUP: a wave's weight tiles are 16 gate rows and the 16 matching up rows;
+// else 32 consecutive down rows. NTT 16-token tiles share one pass over K.
+template <bool GATEUP, int NTT, int DEPTH>
+__global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
+  static_assert(DEPTH == 3 || DEPTH == 4, "the step sequence below is written out for 3 or 4 slots");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][NTT * kTile * kBRow];
+  int s, tile;
+  {
+    const int nr = A.E * A.tiles_r;
+    const int bx = blockIdx.x;
+    s = bx < nr ? bx / A.tiles_r : A.E;
+    tile = bx < nr ? bx % A.tiles_r : bx - nr;
   }
-#pragma unroll
-  for (int o = 8; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) wd[d] |= __shfl_xor(wd[d], o, kWave);
-  }
-  if (lane == 0) {
-    *dst = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-    *dsc = m / static_cast<float>(kQmax);
-  }
-}
-
-// Gate/up of one segment's 32-row-pair tile (4 waves x 8 pairs).
-template <int NT>
-__global__ __launch_bounds__(kThreads) void k_bgateup(BatchArgs A, int tiles_per_seg_max) {
-  extern __shared__ uint4 lds_raw[];
-  const int s = blockIdx.x / tiles_per_seg_max;
-  const int tile = blockIdx.x % tiles_per_seg_max;
-  int r0, nrows, inter;
-  const uint8_t* blob;
-  segment_rows(A, s, r0, nrows, blob, inter);
-  if (nrows == 0 || tile * kWaves * kRowsPerWave >= inter) return;
-  const int ngu = A.H / kGroup;
-  DigitGroup* xd = reinterpret_cast<DigitGroup*>(lds_raw);            // [kTT][ngu]
-  float* xs = reinterpret_cast<float*>(xd + static_cast<size_t>(kTT) * ngu);  // [kTT][ngu]
+  const bool routed = s < A.E;
+  const int r0 = routed ? A.seg[s] : 0;
+  const int m = routed ? A.seg[s + 1] - r0 : A.B;
+  if (m == 0) return;  // uniform over the block
+  const uint8_t* blob = routed ? A.experts + static_cast<size_t>(s) * A.blob_e : A.shared;
+  const int inter = routed ? A.I : A.Is;
+  const int K = GATEUP ? A.H : inter;
+  const int nrows = GATEUP ? inter : A.H;
+  const int ngk = K / kGroup;
+  const int nsteps = (ngk + 3) / 4;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int pair = lane / kLanes;
-  const int ln = lane & (kLanes - 1);
-  const int i0 = (tile * kWaves + wave) * kRowsPerWave;
-  const bool live = i0 < inter;
-  const int i = live ? i0 + pair : 0;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
   const BlobOffsets o = blob_offsets(A.H, inter);
-  const size_t hq = static_cast<size_t>(A.H) / 2;
-  const uint8_t* qg = blob + o.gate_q + static_cast<size_t>(i) * hq;
-  const uint8_t* qu = blob + o.up_q + static_cast<size_t>(i) * hq;
-  const uint16_t* sg = reinterpret_cast<const uint16_t*>(blob + o.gate_s) + static_cast<size_t>(i) * ngu;
-  const uint16_t* su = reinterpret_cast<const uint16_t*>(blob + o.up_s) + static_cast<size_t>(i) * ngu;
-  // the rows stay in registers for every token tile
-  uint4 wg[NT], wu[NT];
-  float fg[NT], fu[NT];
+  const int rbase = (tile * kWaves + wave) * (GATEUP ? kTile : kMR * kTile);
+  const bool live = rbase < nrows;
+  const uint8_t* qrow[kMR];
+  const uint16_t* srow[kMR];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int c = ln + kLanes * t;
-    c = c < ngu ? c : ngu - 1;
-    wg[t] = load_w16(qg + 16 * static_cast<size_t>(c));
-    wu[t] = load_w16(qu + 16 * static_cast<size_t>(c));
-    fg[t] = h2f(sg[c]);
-    fu[t] = h2f(su[c]);
+  for (int mr = 0; mr < kMR; ++mr) {
+    int row = (GATEUP ? rbase : rbase + kTile * mr) + l16;
+    row = live && row < nrows ? row : l16;
+    const size_t qo = GATEUP ? (mr == 0 ? o.gate_q : o.up_q) : o.down_q;
+    const size_t so = GATEUP ? (mr == 0 ? o.gate_s : o.up_s) : o.down_s;
+    qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
+    srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
   }
-  for (int m0 = 0; m0 < nrows; m0 += kTT) {
-    const int mt = nrows - m0 < kTT ? nrows - m0 : kTT;
-    __syncthreads();
-    // stage the digit planes of this tile's tokens
-    for (int idx = threadIdx.x; idx < mt * ngu * 4; idx += kThreads) {
-      const int m = idx / (ngu * 4);
-      const int r = idx % (ngu * 4);
-      const int tok = token_of(A, s, r0 + m0 + m);
-      reinterpret_cast<uint4*>(xd + static_cast<size_t>(m) * ngu)[r] =
-          reinterpret_cast<const uint4*>(A.udig + static_cast<size_t>(tok) * ngu)[r];
-    }
-    for (int idx = threadIdx.x; idx < mt * ngu; idx += kThreads) {
-      const int m = idx / ngu;
-      const int tok = token_of(A, s, r0 + m0 + m);
-      xs[idx] = A.usc[static_cast<size_t>(tok) * ngu + idx % ngu];
-    }
-    __syncthreads();
-    float ag[kTT], au[kTT];
-#pragma unroll
-    for (int m = 0; m < kTT; ++m) ag[m] = au[m] = 0.f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = ln + kLanes * t;
-      const int cc = c < ngu ? c : ngu - 1;
-      const float mask = static_cast<float>(c < ngu);
-#pragma unroll
-      for (int m = 0; m < kTT; ++m) {
-        if (m < mt) {
-          const DigitGroup& xv = xd[static_cast<size_t>(m) * ngu + cc];
-          const float f = xs[static_cast<size_t>(m) * ngu + cc] * mask;
-          ag[m] = fmaf(static_cast<float>(chunk_dot(wg[t], xv)), fg[t] * f, ag[m]);
-          au[m] = fmaf(static_cast<float>(chunk_dot(wu[t], xv)), fu[t] * f, au[m]);
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < kTT; ++m) {
-      const float g = seg_sum<kLanes>(ag[m]);
-      const float v = seg_sum<kLanes>(au[m]);
-      if (m < mt) {
-        const float a = gelu_tanh(g) * v;
-        const int row = r0 + m0 + m;  // sorted position (routed) or token (shared)
-        uint4* dst;
-        float* dsc;
-        if (s < A.E) {
-          dst = A.adig_r + static_cast<size_t>(row) * (A.I / 8) + i0 / 8;
-          dsc = A.asc_r + static_cast<size_t>(row) * (A.I / 8) + i0 / 8;
-        } else {
-          dst = A.adig_s + static_cast<size_t>(row) * (A.Is / 8) + i0 / 8;
-          dsc = A.asc_s + static_cast<size_t>(row) * (A.Is / 8) + i0 / 8;
-        }
-        quant_pos8(a, live ? dst : nullptr, live ? dsc : nullptr);
-      }
-    }
-  }
-}
 
-// Down projection of one segment's 32-output-row tile.
-template <int NT>
-__global__ __launch_bounds__(kThreads) void k_bdown(BatchArgs A, int tiles_per_seg) {
-  extern __shared__ uint4 lds_raw[];
-  const int s = blockIdx.x / tiles_per_seg;
-  const int tile = blockIdx.x % tiles_per_seg;
-  int r0, nrows, inter;
-  const uint8_t* blob;
-  segment_rows(A, s, r0, nrows, blob, inter);
-  if (nrows == 0) return;
-  const int npos = inter / 8;
-  const int ngk = inter / kGroup;
-  uint4* xd = lds_raw;                                              // [kTT][npos]
-  float* xs = reinterpret_cast<float*>(xd + static_cast<size_t>(kTT) * npos);  // [kTT][npos]
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int ln = lane & (kLanes - 1);
-  const int n = (tile * kWaves + wave) * kRowsPerWave + lane / kLanes;  // output row
-  const bool live = n < A.H;
-  const int nn = live ? n : A.H - 1;
-  const BlobOffsets o = blob_offsets(A.H, inter);
-  const uint8_t* q = blob + o.down_q + static_cast<size_t>(nn) * (inter / 2);
-  const uint16_t* sq = reinterpret_cast<const uint16_t*>(blob + o.down_s) + static_cast<size_t>(nn) * ngk;
-  uint4 wv[NT];
-  float fw[NT];
+  for (int p0 = 0; p0 < m; p0 += NTT * kTile) {
+    const int mt = m - p0 < NTT * kTile ? m - p0 : NTT * kTile;
+    // this thread's 16-byte chunks of a step slice (token = c / 16)
+    const uint16_t* brow[NTT];
+    int boff[NTT], loff[NTT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int c = ln + kLanes * t;
-    c = c < ngk ? c : ngk - 1;
-    wv[t] = load_w16(q + 16 * static_cast<size_t>(c));
-    fw[t] = h2f(sq[c]);
-  }
-  const uint4* src_d = s < A.E ? A.adig_r : A.adig_s;
-  const float* src_s = s < A.E ? A.asc_r : A.asc_s;
-  for (int m0 = 0; m0 < nrows; m0 += kTT) {
-    const int mt = nrows - m0 < kTT ? nrows - m0 : kTT;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < mt * npos; idx += kThreads) {
-      const size_t g = static_cast<size_t>(r0 + m0 + idx / npos) * npos + idx % npos;
-      xd[idx] = src_d[g];
-      xs[idx] = src_s[g];
+    for (int r = 0; r < NTT; ++r) {
+      int c = threadIdx.x + kThreads * r;
+      c = c < mt * 16 ? c : mt * 16 - 1;
+      const int row = p0 + (c >> 4);  // row of the segment
+      boff[r] = 8 * (c & 15);
+      loff[r] = (c >> 4) * kBRow + 16 * (c & 15);
+      if (GATEUP) {
+        const int t = routed ? A.perm[r0 + row] / A.k : row;
+        brow[r] = A.u16 + static_cast<size_t>(t) * A.H;
+      } else {
+        brow[r] = routed ? A.act_r + static_cast<size_t>(r0 + row) * A.I
+                         : A.act_s + static_cast<size_t>(row) * A.Is;
+      }
     }
-    __syncthreads();
-    float acc[kTT];
+
+    f32x4 acc[kMR][NTT];
 #pragma unroll
-    for (int m = 0; m < kTT; ++m) acc[m] = 0.f;
+    for (int mr = 0; mr < kMR; ++mr)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int c = ln + kLanes * t;
-      const int cc = c < ngk ? c : ngk - 1;
-      const float mask = static_cast<float>(c < ngk);
-      const uint32_t wq[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
+      for (int tt = 0; tt < NTT; ++tt) acc[mr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Load unit y = (activation slice of step y, weights of step y), issued in
+    // that order DEPTH steps ahead into ring slot y % DEPTH. Loads retire in
+    // issue order, so waiting for the slice of step x+1 (stored to LDS during
+    // step x) only waits for units issued at least DEPTH-1 steps earlier.
+    // Every ring index below is a compile-time constant, so the ring lives
+    // in registers.
+    WStep w[DEPTH];
+    u32x4 bs[DEPTH][NTT];
+    // st past the last step re-reads the last step: every step issues the
+    // same loads, so the wait counts are the same on every path
+    auto issue = [&](int st, WStep& wd, u32x4* bd) __attribute__((always_inline)) {
+      st = st < nsteps ? st : nsteps - 1;
 #pragma unroll
-      for (int m = 0; m < kTT; ++m) {
-        if (m < mt) {
-          float part = 0.f;
+      for (int r = 0; r < NTT; ++r) {
+        int kk = st * kStepK + boff[r];
+        kk = kk < K ? kk : K - 8;  // past the end: any finite values (their weights are 0)
+        bd[r] = *reinterpret_cast<const u32x4*>(brow[r] + kk);
+      }
+      load_step(wd, qrow, srow, ngk, st, q);
+    };
+    auto stage_store = [&](int bi, const u32x4* bd) __attribute__((always_inline)) {
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint4 xv = xd[static_cast<size_t>(m) * npos + 4 * cc + p];
-            const int tq = sdot8(wq[p], xv.x, 0) + 16 * sdot8(wq[p], xv.y, 0) +
-                           256 * sdot8(wq[p], xv.z, 0) + 4096 * sdot8(wq[p], xv.w, 0);
-            part = fmaf(static_cast<float>(tq), xs[static_cast<size_t>(m) * npos + 4 * cc + p], part);
+      for (int r = 0; r < NTT; ++r) *reinterpret_cast<u32x4*>(lds_b[bi] + loff[r]) = bd[r];
+    };
+    auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
+      constexpr int D = decltype(slot)::value;
+      const int st = s0 + D;
+      if (tail && st >= nsteps) return;  // uniform over the block
+      stage_store((st + 1) & 1, bs[(D + 1) % DEPTH]);  // past the end: unused
+      const uint8_t* lb = lds_b[st & 1];
+      // MFMA j takes dword j (8 nibbles) of every lane's group: the 4
+      // 16-lane rows contribute groups 4*st .. 4*st+3, each dequantised with
+      // its own scale, and the activations at the same positions
+      const bool gv = 4 * st + q < ngk;  // groups past K weigh 0
+      f16x8 a[kMR][4];
+#pragma unroll
+      for (int mr = 0; mr < kMR; ++mr) {
+        const _Float16 sc = gv ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[D].s[mr]))
+                               : static_cast<_Float16>(0.0f);
+        a[mr][0] = dequant8(w[D].q[mr].x, sc);
+        a[mr][1] = dequant8(w[D].q[mr].y, sc);
+        a[mr][2] = dequant8(w[D].q[mr].z, sc);
+        a[mr][3] = dequant8(w[D].q[mr].w, sc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+          if (tt * kTile < mt) {
+            const f16x8 bv = *reinterpret_cast<const f16x8*>(lb + (tt * kTile + l16) * kBRow + 64 * q + 16 * j);
+#pragma unroll
+            for (int mr = 0; mr < kMR; ++mr)
+              acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mr][j], bv, acc[mr][tt], 0, 0, 0);
           }
-          acc[m] = fmaf(part, fw[t] * mask, acc[m]);
         }
       }
+      // the slot's next loads go after its last use (no overlapping live
+      // ranges, so the ring keeps its registers across the loop)
+      __builtin_amdgcn_sched_barrier(0);
+      issue(st + DEPTH, w[D], bs[D]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+    issue(0, w[0], bs[0]);
+    issue(1, w[1], bs[1]);
+    issue(2, w[2], bs[2]);
+    if constexpr (DEPTH > 3) issue(3, w[DEPTH > 3 ? 3 : 0], bs[DEPTH > 3 ? 3 : 0]);
+    stage_store(0, bs[0]);
+    __syncthreads();
+    // whole groups of DEPTH steps: straight-line code with the same loads on
+    // every path, so each wait is only for the unit it needs
+    int s0 = 0;
+    for (; s0 + DEPTH <= nsteps; s0 += DEPTH) {
+      step(std::integral_constant<int, 0>{}, s0, false);
+      step(std::integral_constant<int, 1>{}, s0, false);
+      step(std::integral_constant<int, 2>{}, s0, false);
+      if constexpr (DEPTH > 3) step(std::integral_constant<int, (DEPTH > 3 ? 3 : 0)>{}, s0, false);
     }
+    if (s0 < nsteps) {  // the last 1..DEPTH-1 steps
+      step(std::integral_constant<int, 0>{}, s0, true);
+      step(std::integral_constant<int, 1>{}, s0, true);
+      step(std::integral_constant<int, 2>{}, s0, true);
+    }
+
+    // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token
+    // column l16 of each token tile (columns past mt hold garbage, unused)
 #pragma unroll
-    for (int m = 0; m < kTT; ++m) {
-      const float v = seg_sum<kLanes>(acc[m]);
-      if (m < mt && ln == 0 && live) {
-        const int row = r0 + m0 + m;
-        if (s < A.E) A.out_r[static_cast<size_t>(row) * A.H + n] = v;
-        else A.out_s[static_cast<size_t>(row) * A.H + n] = v;
+    for (int tt = 0; tt < NTT; ++tt) {
+      if (tt * kTile >= mt) continue;  // uniform
+      const int col = tt * kTile + l16;
+      const bool valid = live && col < mt;
+      const int row = p0 + (col < mt ? col : mt - 1);  // row of the segment
+      const int tok = routed ? A.perm[r0 + row] / A.k : row;
+      const float ts = A.tsc[tok];
+      if (GATEUP) {
+        float av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = gelu_tanh(acc[0][tt][i] * ts) * acc[1][tt][i] / ts;
+        const uint32_t lo = pack_f16(av[0], av[1]);
+        const uint32_t hi = pack_f16(av[2], av[3]);
+        // 16-lane rows 2b and 2b+1 hold values 0..3 and 4..7 of one 8-block
+        // of the activation row; each writes one half of the interleaved block
+        const bool odd = q & 1;
+        const uint32_t recv = static_cast<uint32_t>(__shfl_xor(static_cast<int>(odd ? lo : hi), 16, kWave));
+        uint2 out;
+        if (!odd) {
+          out.x = (lo & 0xFFFFu) | (recv << 16);
+          out.y = (lo >> 16) | (recv & 0xFFFF0000u);
+        } else {
+          out.x = (recv & 0xFFFFu) | (hi << 16);
+          out.y = (recv >> 16) | (hi & 0xFFFF0000u);
+        }
+        if (valid) {
+          uint16_t* dst = routed ? A.act_r + static_cast<size_t>(r0 + row) * A.I
+                                 : A.act_s + static_cast<size_t>(row) * A.Is;
+          *reinterpret_cast<uint2*>(dst + rbase + 8 * (q >> 1) + 4 * (q & 1)) = out;
+        }
+      } else if (valid) {
+        const float f = ts * ts;
+        float* dst = routed ? A.out_r + static_cast<size_t>(r0 + row) * A.H
+                            : A.out_s + static_cast<size_t>(row) * A.H;
+#pragma unroll
+        for (int mr = 0; mr < kMR; ++mr)
+          *reinterpret_cast<float4*>(dst + rbase + kTile * mr + 4 * q) =
+              make_float4(acc[mr][tt][0] * f, acc[mr][tt][1] * f, acc[mr][tt][2] * f, acc[mr][tt][3] * f);
       }
     }
   }
@@ -284,44 +328,34 @@ __global__ void k_bcombine(const float* __restrict__ out_s, const float* __restr
   }
 }
 
+template <bool GATEUP>
+hipError_t launch_mfma(const MArgs& A, int ntt, hipStream_t s) {
+  const dim3 grid(A.E * A.tiles_r + A.tiles_s);
+  if (ntt <= 1) hipLaunchKernelGGL((k_mfma<GATEUP, 1, 4>), grid, dim3(kThreads), 0, s, A);
+  else if (ntt == 2) hipLaunchKernelGGL((k_mfma<GATEUP, 2, 4>), grid, dim3(kThreads), 0, s, A);
+  else hipLaunchKernelGGL((k_mfma<GATEUP, 4, 3>), grid, dim3(kThreads), 0, s, A);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
-                          const DigitGroup* udig, const float* usc, const float* w, const float* x,
+                          const uint16_t* u16, const float* tsc, const float* w, const float* x,
                           const uint16_t* add_in, bool residual, float* y, hipStream_t s) {
-  BatchArgs A{experts, shared, blob_e, H, I, Is, E, k, B, bb.seg, bb.perm, udig, usc,
-              bb.adig_r, bb.asc_r, bb.adig_s, bb.asc_s, bb.out_r, bb.out_s};
-  const int ngu = H / kGroup;
-  // gate/up: (E + 1) segments x row tiles of 32 pairs (the longest segment sets the grid)
-  const int inter_max = I > Is ? I : Is;
-  const int tiles_gu = (inter_max + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave);
-  const size_t lds_gu = static_cast<size_t>(kTT) * ngu * (sizeof(DigitGroup) + sizeof(float));
-  const int need_gu = (ngu + kLanes - 1) / kLanes;
-#define MOE_BGU(NT) hipLaunchKernelGGL(k_bgateup<NT>, dim3((E + 1) * tiles_gu), dim3(kThreads), lds_gu, s, A, tiles_gu)
-  if (need_gu <= 2) MOE_BGU(2);
-  else if (need_gu <= 4) MOE_BGU(4);
-  else if (need_gu <= 8) MOE_BGU(8);
-  else if (need_gu <= 11) MOE_BGU(11);
-  else if (need_gu <= 16) MOE_BGU(16);
-  else MOE_BGU(32);
-#undef MOE_BGU
-  hipError_t e = hipGetLastError();
+  MArgs A{experts, shared, blob_e, H, I, Is, E, k, B, bb.seg, bb.perm, u16, tsc,
+          bb.act_r, bb.act_s, bb.out_r, bb.out_s, 0, 0};
+  // tokens per pass over a segment's weights: up to 64; a larger shared or
+  // expert segment takes several passes
+  const int ntt = B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4);
+  // gate/up: 64 row pairs per block
+  A.tiles_r = (I + kWaves * kTile - 1) / (kWaves * kTile);
+  A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile);
+  hipError_t e = launch_mfma<true>(A, ntt, s);
   if (e != hipSuccess) return e;
-  // down: (E + 1) segments x 32-row output tiles; the K loop covers the longer segment
-  const int tiles_dn = (H + kWaves * kRowsPerWave - 1) / (kWaves * kRowsPerWave);
-  const int npos_max = inter_max / 8;
-  const size_t lds_dn = static_cast<size_t>(kTT) * npos_max * (sizeof(uint4) + sizeof(float));
-  const int need_dn = (inter_max / kGroup + kLanes - 1) / kLanes;
-#define MOE_BDN(NT) hipLaunchKernelGGL(k_bdown<NT>, dim3((E + 1) * tiles_dn), dim3(kThreads), lds_dn, s, A, tiles_dn)
-  if (need_dn <= 2) MOE_BDN(2);
-  else if (need_dn <= 3) MOE_BDN(3);
-  else if (need_dn <= 4) MOE_BDN(4);
-  else if (need_dn <= 9) MOE_BDN(9);
-  else if (need_dn <= 16) MOE_BDN(16);
-  else MOE_BDN(32);
-#undef MOE_BDN
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // down: 128 output rows per block
+  A.tiles_r = A.tiles_s = (H + kWaves * kMR * kTile - 1) / (kWaves * kMR * kTile);
+  if ((e = launch_mfma<false>(A, ntt, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bcombine, dim3((H + 255) / 256, B), dim3(256), 0, s, bb.out_s, bb.out_r, bb.pos_of, w,
                      x, add_in, residual ? 1 : 0, H, k, y);
   return hipGetLastError();

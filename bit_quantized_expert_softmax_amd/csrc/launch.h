@@ -35,8 +35,9 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 // Grid: (E/4 blocks) x B tokens; the top-k variant (ids != nullptr) needs B == 1.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
-                              DigitGroup* udig, float* usc, double* z, int32_t* cnt, int32_t* ids,
-                              float* w, int32_t* ids2, float* w2, hipStream_t s);
+                              DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
+                              int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
+                              hipStream_t s);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
@@ -111,17 +112,16 @@ struct BatchedBuffers {
   const int32_t* seg;
   const int32_t* perm;
   const int32_t* pos_of;
-  uint4* adig_r;
-  float* asc_r;
-  uint4* adig_s;
-  float* asc_s;
-  float* out_r;
-  float* out_s;
+  uint16_t* act_r;  // [B*k][I] fp16 GeGLU activations by sorted position
+  uint16_t* act_s;  // [B][Is]
+  float* out_r;     // [B*k][H]
+  float* out_s;     // [B][H]
 };
-// Grouped gate/up and down GEMVs over the expert segments, then the combine.
+// Grouped gate/up and down products over the expert segments on the matrix
+// cores (inputs: u16/tsc of launch_route_layer), then the combine.
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
-                          const DigitGroup* udig, const float* usc, const float* w, const float* x,
+                          const uint16_t* u16, const float* tsc, const float* w, const float* x,
                           const uint16_t* add_in, bool residual, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------- standalone GEMV

@@ -35,7 +35,7 @@ namespace {
 struct WsLayout {
   size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre;
   // batched decode (max_B > 1): expert sort and per-assignment outputs
-  size_t hist, base, lrank, seg, tiles, n_tiles, perm, pos_of, out_r, out_s;
+  size_t hist, base, lrank, seg, tiles, n_tiles, perm, pos_of, out_r, out_s, u16, tsc, act;
   int chunks;
   size_t total;
 };
@@ -75,6 +75,9 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.pos_of = take(A * 4);
   L.out_r = take(A * H * 4);
   L.out_s = take(B > 1 ? B * H * 4 : 0);
+  L.u16 = take(B > 1 ? B * H * 2 : 0);
+  L.tsc = take(B > 1 ? B * 4 : 0);
+  L.act = take(B > 1 ? (A * I + B * Is) * 2 : 0);
   L.total = off;
   return L;
 }
@@ -310,17 +313,19 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   // resident mode: the router only produces logits; each gate/up block takes
   // the top-k itself (no cross-block handshake on the critical path)
   const bool in_kernel_topk = !L->cache_mode;
-  HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out, udig,
-                                      usc, z, cnt, in_kernel_topk ? nullptr : ids,
+  // grouped path (B > 1, all experts resident): every touched expert is read
+  // once per call by the matrix-core kernels, which take fp16 inputs
+  const bool grouped = !L->cache_mode && B > 1;
+  uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
+  float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
+  HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
+                                      grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
+                                      in_kernel_topk ? nullptr : ids,
                                       in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
                                       in_kernel_topk ? nullptr : w_out, s), fn);
   prof_end(L, 0, pb, s);
 
   moe::SourceSet S = make_sources(L);
-  // grouped path: every touched expert read once per call; its LDS tiles hold
-  // 8 tokens' activation digits (fits for hidden <= 3840, intermediates <= 3272)
-  const int inter_max = sh.inter > sh.shared_inter ? sh.inter : sh.shared_inter;
-  const bool grouped = !L->cache_mode && B > 1 && 8 * ngu * 68 <= 65536 && 8 * (inter_max / 8) * 20 <= 65536;
   if (grouped) {
     // batched: per-token top-k, stable sort of the B*k assignments by expert,
     // grouped GEMVs that read each touched expert once, ordered combine
@@ -335,13 +340,12 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                                     L->at<int2>(L->ws.tiles), L->at<int32_t>(L->ws.n_tiles), perm, pos_of,
                                     s), fn);
     prof_end(L, 0, pt, s);
-    moe::BatchedBuffers bb{seg, perm, pos_of, adig, asc,
-                           adig + static_cast<size_t>(A) * (sh.inter / 8),
-                           asc + static_cast<size_t>(A) * (sh.inter / 8),
+    uint16_t* act = L->at<uint16_t>(L->ws.act);
+    moe::BatchedBuffers bb{seg, perm, pos_of, act, act + static_cast<size_t>(A) * sh.inter,
                            L->at<float>(L->ws.out_r), L->at<float>(L->ws.out_s)};
     hipEvent_t p1 = prof_begin(L, s);
     HIP_OR_FAIL(moe::launch_batched(bb, L->d.experts_dev, L->d.shared_blob, L->blob_e, H, sh.inter,
-                                    sh.shared_inter, E, k, B, udig, usc, w, x, add_in, res, y, s), fn);
+                                    sh.shared_inter, E, k, B, u16, tsc, w, x, add_in, res, y, s), fn);
     prof_end(L, 2, p1, s);
     if (stats) stats->calls += 1;
     return MOE_OK;

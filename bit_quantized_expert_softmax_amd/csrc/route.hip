@@ -33,8 +33,11 @@ struct RouteArgs {
   const float* bias;
   int E, k;
   float* u_out;       // optional [B][H]
-  DigitGroup* udig;   // [B][H/32]
+  DigitGroup* udig;   // optional [B][H/32] digit planes of u
   float* usc;         // [B][H/32]
+  uint16_t* u16;      // optional [B][H] fp16 of u / tsc, each 8-block in the
+                      // order (0,4,1,5,2,6,3,7) of the matrix-core kernels
+  float* tsc;         // [B] power of two with ||u||_2 / tsc < 16
   double* z;          // [B][E]
   int32_t* cnt;       // arrival counter, zero between calls
   int32_t *ids, *ids2;
@@ -68,9 +71,9 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
     const float* xb = A.x + static_cast<size_t>(b) * H;
     const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
     // inputs wider than one batch: the RMSNorm factor needs a pass of its own
-    float r_all = 1.0f;
+    float r_all = 1.0f, ss_all = 0.f;
     const bool multi = n8 > kWave * kMaxSteps;
-    if (RMS && multi) {
+    if ((RMS || A.u16) && multi) {
       float ss = 0.f;
       for (int c = lane; c < n8; c += kWave) {
         const float4 x0 = *reinterpret_cast<const float4*>(xb + 8 * c);
@@ -86,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
           ss = fmaf(v1, v1, ss);
         }
       }
-      ss = seg_sum<kWave>(ss);
-      r_all = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
+      ss_all = seg_sum<kWave>(ss);
+      if (RMS) r_all = 1.0f / sqrtf(ss_all / static_cast<float>(H) + 1e-6f);
     }
     double acc = 0.0;
     for (int c0 = 0; c0 < n8; c0 += kWave * kMaxSteps) {
@@ -121,9 +124,22 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
         ss += c < n8 ? part : 0.f;
       }
       float r = r_all;
-      if (RMS && !multi) {
+      if ((RMS || A.u16) && !multi) {
         ss = seg_sum<kWave>(ss);
-        r = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
+        if (RMS) r = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
+      } else {
+        ss = ss_all;
+      }
+      // token scale of the fp16 copy: a power of two, so scaling is exact
+      float tsc = 1.0f;
+      if (A.u16) {
+        const float nrm = sqrtf(ss) * r;
+        if (nrm > 0.f && nrm <= FLT_MAX) {
+          int ex;
+          frexpf(nrm, &ex);
+          tsc = ldexpf(1.0f, ex - 4);
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0 && c0 == 0) A.tsc[b] = tsc;
       }
 #pragma unroll
       for (int t = 0; t < kMaxSteps; ++t) {
@@ -169,9 +185,24 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
               q = (q - dg) / 16;
             }
           }
-          DigitGroup* dg = A.udig + static_cast<size_t>(b) * ngu + g;
-          dg->p[c & 3] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-          if ((c & 3) == 0) A.usc[static_cast<size_t>(b) * ngu + g] = m / static_cast<float>(kQmax);
+          if (A.udig) {
+            DigitGroup* dg = A.udig + static_cast<size_t>(b) * ngu + g;
+            dg->p[c & 3] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            if ((c & 3) == 0) A.usc[static_cast<size_t>(b) * ngu + g] = m / static_cast<float>(kQmax);
+          }
+          if (A.u16) {
+            const float inv_t = 1.0f / tsc;
+            uint32_t hw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const _Float16 lo = static_cast<_Float16>(u[t][i] * inv_t);
+              const _Float16 hi = static_cast<_Float16>(u[t][i + 4] * inv_t);
+              hw[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+            }
+            *reinterpret_cast<uint4*>(A.u16 + static_cast<size_t>(b) * H + 8 * c) =
+                make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          }
           if (A.u_out) {
             float* uo = A.u_out + static_cast<size_t>(b) * H + 8 * c;
             *reinterpret_cast<float4*>(uo) = make_float4(u[t][0], u[t][1], u[t][2], u[t][3]);
@@ -266,9 +297,10 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const double* __restric
 
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
-                              DigitGroup* udig, float* usc, double* z, int32_t* cnt, int32_t* ids,
-                              float* w, int32_t* ids2, float* w2, hipStream_t s) {
-  RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, z, cnt,
+                              DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
+                              int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
+                              hipStream_t s) {
+  RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, u16, tsc, z, cnt,
               ids, ids2, w, w2};
   const int blocks = (E + kWaves - 1) / kWaves;
   const size_t lds = sizeof(double) * E;
