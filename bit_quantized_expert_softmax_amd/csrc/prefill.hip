@@ -5,14 +5,18 @@
 // rows so that one loaded expert serves a group of token rows at once. Here
 // the T*k (token, rank) assignments are sorted by expert (stable: expert,
 // token, rank), each expert's rows form one GEMM against its int4 weights,
-// which are dequantised tile by tile into bf16 in LDS; bf16 MFMA with fp32
-// accumulation computes gate/up, the GeGLU activation is rounded to bf16,
+// which stream through registers and are dequantised there to bf16 (one
+// rounding of the exact product); bf16 MFMA with fp32 accumulation computes
+// gate/up against activation tiles staged in LDS, the GeGLU activation is
+// rounded to bf16,
 // the down GEMM weights each row by its routing weight, and the shared
 // expert's down GEMM adds the k routed rows of every token in rank order.
 //
 // Stages (one launch each): count per 256-assignment chunk, scan (expert
 // offsets and the GEMM tile table), stable scatter, routed gate/up, shared
 // gate/up, routed down, shared down + combine.
+#include <type_traits>
+
 #include "launch.h"
 #include "moedecode.h"
 
@@ -23,10 +27,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 256;   // assignments per counting chunk
-constexpr int kTM = 64;       // GEMM tile rows
-constexpr int kTK = 32;       // K step = one quantisation group
-constexpr int kThreadsG = 256;
-constexpr int kLdsRow = 40;   // bf16 per LDS tile row (32 + pad against bank conflicts)
+constexpr int kTM = 128;      // GEMM tile rows (tokens)
 
 // ---------------------------------------------------------------- permutation
 __global__ __launch_bounds__(kChunk) void k_perm_count(const int32_t* __restrict__ ids, int n_asg, int E,
@@ -102,32 +103,79 @@ __global__ __launch_bounds__(kChunk) void k_perm_scatter(const int32_t* __restri
 }
 
 // ---------------------------------------------------------------- grouped GEMM
-__device__ __forceinline__ bf16x8 lds_frag(const __bf16* tile, int row, int lane) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * kLdsRow + 8 * (lane >> 4));
+// Weight rows stream from HBM into registers and are dequantised there; the
+// block's 128 activation rows are staged in LDS per K step (double buffered)
+// and shared by its 8 waves. A wave owns two 16-row weight tiles (GATEUP: 16
+// gate rows and the matching 16 up rows; else 32 consecutive down rows) and
+// all 8 16-row token tiles, so each dequantised weight feeds 8 MFMAs.
+//
+// K step = 4 quant groups (128 values). The lane of 16-lane row q loads group
+// 4*st + q of its weight row (16 bytes) and that group's scale; MFMA j of the
+// step takes dword j (8 nibbles) of every lane's group, so one MFMA's K = 32
+// spans the step's 4 groups, 8 values of each, and the activations are read
+// at the same positions. Loads are issued kDepth steps ahead (activation
+// slice first, then weights) into a register ring whose slots are
+// compile-time indices, so every wait is for the oldest unit only.
+constexpr int kTok = kTM / 16;            // 16-token tiles per block
+constexpr int kWavesG = 8;               // waves per GEMM block
+constexpr int kThreadsGemm = kWavesG * kWave;
+constexpr int kStage = kTM * 16 / kThreadsGemm;  // 16-byte activation chunks per thread and step
+constexpr int kStepK = 4 * kGroup;       // 128
+constexpr int kBRow = kStepK * 2 + 16;   // LDS bytes per activation row of a step (padded)
+constexpr int kDepth = 4;
+constexpr int kMR = 2;
+
+// Byte B of x as a float (v_cvt_f32_ubyteB; written out because the compiler
+// folds the surrounding masks and then loses the byte-select forms).
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  float r;
+  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  return r;
 }
 
-// Dequantises 16 consecutive K values (8 bytes of nibbles, one fp16 scale) of
-// one weight row to bf16 and stores them to LDS.
-__device__ __forceinline__ void dequant16(uint2 q, uint16_t s, __bf16* dst) {
-  const float sc = h2f(s);
-  __attribute__((aligned(16))) __bf16 v[16];
-  const uint32_t w[2] = {q.x, q.y};
+// bf16(n * s) for the 8 signed nibbles of w (k = 0..7 in bits 4k..4k+3), in
+// k order: the product (n + 8) * s - 8 * s is exact in fp32 (at most 15
+// significant bits), so the single rounding is the one to bf16.
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
+  const uint32_t x = w ^ 0x88888888u;          // nibble n -> n + 8
+  const uint32_t lo = x & 0x0F0F0F0Fu;         // byte b: k = 2b
+  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // byte b: k = 2b + 1
+  const float m8 = -8.0f * s;
+  bf16x8 r;
+  r[0] = static_cast<__bf16>(fmaf(ubyte_f32<0>(lo), s, m8));
+  r[1] = static_cast<__bf16>(fmaf(ubyte_f32<0>(hi), s, m8));
+  r[2] = static_cast<__bf16>(fmaf(ubyte_f32<1>(lo), s, m8));
+  r[3] = static_cast<__bf16>(fmaf(ubyte_f32<1>(hi), s, m8));
+  r[4] = static_cast<__bf16>(fmaf(ubyte_f32<2>(lo), s, m8));
+  r[5] = static_cast<__bf16>(fmaf(ubyte_f32<2>(hi), s, m8));
+  r[6] = static_cast<__bf16>(fmaf(ubyte_f32<3>(lo), s, m8));
+  r[7] = static_cast<__bf16>(fmaf(ubyte_f32<3>(hi), s, m8));
+  return r;
+}
+
+struct WStep {
+  uint4 q[kMR];
+  uint32_t s[kMR];
+};
+
+__device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow,
+                                          const uint16_t* const* srow, int ngk, int st, int q) {
+  int g = 4 * st + q;
+  g = g < ngk ? g : ngk - 1;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int nib = static_cast<int>((w[h] >> (4 * i)) & 15u);
-      const int sv = nib >= 8 ? nib - 16 : nib;
-      v[8 * h + i] = static_cast<__bf16>(static_cast<float>(sv) * sc);  // exact product, RNE to bf16
-    }
+  for (int m = 0; m < kMR; ++m) {
+    b.q[m] = *reinterpret_cast<const uint4*>(qrow[m] + 16 * static_cast<size_t>(g));
+    b.s[m] = srow[m][g];
   }
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
-  *reinterpret_cast<uint4*>(dst + 8) = *reinterpret_cast<const uint4*>(v + 8);
 }
 
 struct GemmArgs {
-  // A rows: row r of a tile = A + row_index * lda (bf16), where row_index is
-  // rmap[r_global] / rdiv when rmap is given, else r_global
+  // activation rows: row r of the tile = A + index * lda (bf16), where index
+  // is rmap[r] / rdiv when rmap is given, else r
   const __bf16* A;
   int lda;
   const int32_t* rmap;
@@ -137,7 +185,7 @@ struct GemmArgs {
   const uint8_t* experts;
   size_t blob_e;
   int H, inter;
-  // routed tiles from the table (tiles/n_tiles/seg), or a dense M x N job
+  // routed tiles from the table (tiles/n_tiles/seg), or a dense job of M_dense rows
   const int2* tiles;
   const int32_t* n_tiles;
   const int32_t* seg;
@@ -153,15 +201,12 @@ struct GemmArgs {
   int k;
 };
 
-// GATEUP: tile = 64 rows x (64 gate + 64 up) columns of one source; a wave
-//   owns gate sub-tile w and the matching up sub-tile, so each lane holds g
-//   and v of the same (row, column) and applies GeGLU in registers.
-// DOWN:   tile = 64 rows x 128 output columns; a wave owns 2 column sub-tiles.
 template <bool GATEUP, bool ROUTED>
-__global__ __launch_bounds__(kThreadsG) void k_gemm(GemmArgs G) {
-  __shared__ __attribute__((aligned(16))) __bf16 As[kTM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[128 * kLdsRow];
-  const int n_tiles_n = GATEUP ? G.inter / 64 : G.H / 128;
+__global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+  constexpr int rows_per_block = GATEUP ? kWavesG * 16 : kWavesG * kMR * 16;
+  const int nrows = GATEUP ? G.inter : G.H;
+  const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
   const int mt = blockIdx.x / n_tiles_n;
   const int nt = blockIdx.x % n_tiles_n;
   int r0, r_end;
@@ -170,100 +215,167 @@ __global__ __launch_bounds__(kThreadsG) void k_gemm(GemmArgs G) {
     if (mt >= *G.n_tiles) return;
     const int2 td = G.tiles[mt];
     r0 = td.y;
-    r_end = G.seg[td.x + 1];
+    const int e_end = G.seg[td.x + 1];
+    r_end = r0 + kTM < e_end ? r0 + kTM : e_end;
     blob = G.experts + static_cast<size_t>(td.x) * G.blob_e;
   } else {
     r0 = mt * kTM;
-    r_end = G.M_dense;
-    if (r0 >= r_end) return;
+    if (r0 >= G.M_dense) return;
+    r_end = r0 + kTM < G.M_dense ? r0 + kTM : G.M_dense;
     blob = G.blob;
   }
+  const int mtok = r_end - r0;
   const BlobOffsets o = blob_offsets(G.H, G.inter);
   const int K = GATEUP ? G.H : G.inter;
   const int ngk = K / kGroup;
+  const int nsteps = (ngk + 3) / 4;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-
-  // A loader: thread t loads row t/4, 8 bf16 at k offset 8*(t%4)
-  const int ar = threadIdx.x >> 2;
-  const int ak = 8 * (threadIdx.x & 3);
-  const int arow_g = r0 + ar < r_end ? r0 + ar : r_end - 1;
-  const int aidx = G.rmap ? G.rmap[arow_g] / G.rdiv : arow_g;
-  const __bf16* arow = G.A + static_cast<size_t>(aidx) * G.lda + ak;
-  // B loader: thread t dequantises column t/2 (of 128), K half t%2 (16 values)
-  const int bc = threadIdx.x >> 1;
-  const int bh = threadIdx.x & 1;
-  const uint8_t* bq;
-  const uint16_t* bs;
-  if (GATEUP) {
-    const int n = nt * 64 + (bc & 63);
-    const bool up = bc >= 64;
-    bq = blob + (up ? o.up_q : o.gate_q) + static_cast<size_t>(n) * (K / 2) + 8 * bh;
-    bs = reinterpret_cast<const uint16_t*>(blob + (up ? o.up_s : o.gate_s)) + static_cast<size_t>(n) * ngk;
-  } else {
-    const int n = nt * 128 + bc;
-    bq = blob + o.down_q + static_cast<size_t>(n) * (K / 2) + 8 * bh;
-    bs = reinterpret_cast<const uint16_t*>(blob + o.down_s) + static_cast<size_t>(n) * ngk;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const int rbase = nt * rows_per_block + wave * (GATEUP ? 16 : kMR * 16);
+  const bool live = rbase < nrows;  // waves past the last row only stage and sync
+  const uint8_t* qrow[kMR];
+  const uint16_t* srow[kMR];
+#pragma unroll
+  for (int mr = 0; mr < kMR; ++mr) {
+    int row = (GATEUP ? rbase : rbase + 16 * mr) + l16;
+    row = live && row < nrows ? row : l16;
+    const size_t qo = GATEUP ? (mr == 0 ? o.gate_q : o.up_q) : o.down_q;
+    const size_t so = GATEUP ? (mr == 0 ? o.gate_s : o.up_s) : o.down_s;
+    qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
+    srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
+  }
+  // this thread's 16-byte chunks of an activation slice (row = c / 16)
+  const __bf16* brow[kStage];
+  int boff[kStage], loff[kStage];
+#pragma unroll
+  for (int r = 0; r < kStage; ++r) {
+    int c = threadIdx.x + kThreadsGemm * r;
+    c = c < mtok * 16 ? c : mtok * 16 - 1;
+    const int row = r0 + (c >> 4);
+    const int idx = G.rmap ? G.rmap[row] / G.rdiv : row;
+    brow[r] = G.A + static_cast<size_t>(idx) * G.lda;
+    boff[r] = 8 * (c & 15);
+    loff[r] = (c >> 4) * kBRow + 16 * (c & 15);
   }
 
-  f32x4 acc[4][2];
+  f32x4 acc[kMR][kTok];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int mr = 0; mr < kMR; ++mr)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < kTok; ++tt) acc[mr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = 0; g < ngk; ++g) {
-    const uint4 av = *reinterpret_cast<const uint4*>(arow + g * kTK);
-    const uint2 qv = *reinterpret_cast<const uint2*>(bq + 16 * static_cast<size_t>(g));
-    const uint16_t sv = bs[g];
-    __syncthreads();  // previous step's fragments have been read
-    *reinterpret_cast<uint4*>(As + ar * kLdsRow + ak) = av;
-    dequant16(qv, sv, Bs + bc * kLdsRow + 16 * bh);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  WStep w[kDepth];
+  u32x4 bs[kDepth][kStage];
+  // st past the last step re-reads the last step: every step issues the same
+  // loads, so the wait counts are the same on every path
+  auto issue = [&](int st, WStep& wd, u32x4* bd) __attribute__((always_inline)) {
+    st = st < nsteps ? st : nsteps - 1;
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) {
+      int kk = st * kStepK + boff[r];
+      kk = kk < K ? kk : K - 8;  // past the end: any finite values (their weights are 0)
+      bd[r] = *reinterpret_cast<const u32x4*>(brow[r] + kk);
+    }
+    load_step(wd, qrow, srow, ngk, st, q);
+  };
+  auto stage_store = [&](int bi, const u32x4* bd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < kStage; ++r) *reinterpret_cast<u32x4*>(lds_b[bi] + loff[r]) = bd[r];
+  };
+  auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
+    constexpr int D = decltype(slot)::value;
+    const int st = s0 + D;
+    if (tail && st >= nsteps) return;  // uniform over the block
+    stage_store((st + 1) & 1, bs[(D + 1) % kDepth]);  // past the end: unused
+    const uint8_t* lb = lds_b[st & 1];
+    const bool gv = 4 * st + q < ngk;  // groups past K weigh 0
+    bf16x8 a[kMR][4];
+#pragma unroll
+    for (int mr = 0; mr < kMR; ++mr) {
+      const float sc = gv ? h2f(static_cast<uint16_t>(w[D].s[mr])) : 0.0f;
+      a[mr][0] = dequant8_bf16(w[D].q[mr].x, sc);
+      a[mr][1] = dequant8_bf16(w[D].q[mr].y, sc);
+      a[mr][2] = dequant8_bf16(w[D].q[mr].z, sc);
+      a[mr][3] = dequant8_bf16(w[D].q[mr].w, sc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // every token tile, also past mtok: an output column depends on its
+      // own activation row only, and the columns of absent rows are dropped
+#pragma unroll
+      for (int tt = 0; tt < kTok; ++tt) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + (tt * 16 + l16) * kBRow + 64 * q + 16 * j);
+#pragma unroll
+        for (int mr = 0; mr < kMR; ++mr)
+          acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mr][j], bv, acc[mr][tt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st + kDepth, w[D], bs[D]);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    bf16x8 bfr[2];
-    if (GATEUP) {
-      bfr[0] = lds_frag(Bs, 16 * wave + (lane & 15), lane);
-      bfr[1] = lds_frag(Bs, 64 + 16 * wave + (lane & 15), lane);
-    } else {
-      bfr[0] = lds_frag(Bs, 32 * wave + (lane & 15), lane);
-      bfr[1] = lds_frag(Bs, 32 * wave + 16 + (lane & 15), lane);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 afr = lds_frag(As, 16 * i + (lane & 15), lane);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[0], acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[1], acc[i][1], 0, 0, 0);
-    }
+  };
+  issue(0, w[0], bs[0]);
+  issue(1, w[1], bs[1]);
+  issue(2, w[2], bs[2]);
+  issue(3, w[3], bs[3]);
+  stage_store(0, bs[0]);
+  __syncthreads();
+  int s0 = 0;
+  for (; s0 + kDepth <= nsteps; s0 += kDepth) {
+    step(std::integral_constant<int, 0>{}, s0, false);
+    step(std::integral_constant<int, 1>{}, s0, false);
+    step(std::integral_constant<int, 2>{}, s0, false);
+    step(std::integral_constant<int, 3>{}, s0, false);
+  }
+  if (s0 < nsteps) {
+    step(std::integral_constant<int, 0>{}, s0, true);
+    step(std::integral_constant<int, 1>{}, s0, true);
+    step(std::integral_constant<int, 2>{}, s0, true);
   }
 
-  // epilogue: lane holds rows 16i + 4*(lane/16) + r, column (lane % 16) of each sub-tile
+  // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token row
+  // l16 of each token tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int tt = 0; tt < kTok; ++tt) {
+    const int m = r0 + tt * 16 + l16;
+    if (m >= r_end || !live) continue;
+    if (GATEUP) {
+      __attribute__((aligned(8))) __bf16 av[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = r0 + 16 * i + 4 * (lane >> 4) + r;
-      if (m >= r_end) continue;
-      if (GATEUP) {
-        const int n = nt * 64 + 16 * wave + (lane & 15);
-        const float a = gelu_tanh(acc[i][0][r]) * acc[i][1][r];
-        G.act[static_cast<size_t>(m) * G.inter + n] = static_cast<__bf16>(a);
-      } else {
+      for (int i = 0; i < 4; ++i) av[i] = static_cast<__bf16>(gelu_tanh(acc[0][tt][i]) * acc[1][tt][i]);
+      *reinterpret_cast<uint2*>(G.act + static_cast<size_t>(m) * G.inter + rbase + 4 * q) =
+          *reinterpret_cast<const uint2*>(av);
+    } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = nt * 128 + 32 * wave + 16 * j + (lane & 15);
-          float v = acc[i][j][r];
-          if (ROUTED) {
-            G.out[static_cast<size_t>(m) * G.H + n] = v * G.wrow[G.perm[m]];
-          } else {
-            // shared expert output plus the token's routed rows in rank order
-            for (int jj = 0; jj < G.k; ++jj)
-              v += G.out_r[static_cast<size_t>(G.pos_of[m * G.k + jj]) * G.H + n];
-            G.out[static_cast<size_t>(m) * G.H + n] = v;
+      for (int mr = 0; mr < kMR; ++mr) {
+        const int n = rbase + 16 * mr + 4 * q;
+        float4 v = make_float4(acc[mr][tt][0], acc[mr][tt][1], acc[mr][tt][2], acc[mr][tt][3]);
+        if (ROUTED) {
+          const float wr = G.wrow[G.perm[m]];
+          v = make_float4(v.x * wr, v.y * wr, v.z * wr, v.w * wr);
+        } else {
+          // shared expert output plus the token's routed rows in rank order
+          for (int jj = 0; jj < G.k; ++jj) {
+            const float4 r = *reinterpret_cast<const float4*>(
+                G.out_r + static_cast<size_t>(G.pos_of[m * G.k + jj]) * G.H + n);
+            v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
           }
         }
+        *reinterpret_cast<float4*>(G.out + static_cast<size_t>(m) * G.H + n) = v;
       }
     }
   }
+}
+
+// Blocks along the weight rows of one GEMM (gate/up: row pairs; down: rows).
+int gemm_row_tiles(bool gateup, int H, int inter) {
+  const int rows = gateup ? inter : H;
+  const int per = gateup ? kWavesG * 16 : kWavesG * kMR * 16;
+  return (rows + per - 1) / per;
 }
 
 __global__ void k_bf16_to_f32(const uint16_t* __restrict__ x, size_t n, float* __restrict__ y) {
@@ -371,7 +483,7 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
   g.n_tiles = n_tiles;
   g.seg = seg;
   g.act = act_r;
-  hipLaunchKernelGGL((k_gemm<true, true>), dim3(L.max_tiles * (I / 64)), dim3(kThreadsG), 0, s, g);
+  hipLaunchKernelGGL((k_gemm<true, true>), dim3(L.max_tiles * gemm_row_tiles(true, H, I)), dim3(kThreadsGemm), 0, s, g);
   // shared gate/up: dense over tokens
   GemmArgs gs = g;
   gs.rmap = nullptr;
@@ -379,7 +491,7 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
   gs.inter = Is;
   gs.M_dense = T;
   gs.act = act_s;
-  hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * (Is / 64)), dim3(kThreadsG), 0, s, gs);
+  hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
   // routed down: rows are the permuted activations, weighted by their routing weight
   GemmArgs d = g;
   d.A = act_r;
@@ -388,7 +500,7 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
   d.out = out_r;
   d.wrow = w;
   d.perm = perm;
-  hipLaunchKernelGGL((k_gemm<false, true>), dim3(L.max_tiles * (H / 128)), dim3(kThreadsG), 0, s, d);
+  hipLaunchKernelGGL((k_gemm<false, true>), dim3(L.max_tiles * gemm_row_tiles(false, H, I)), dim3(kThreadsGemm), 0, s, d);
   // shared down + combine into y
   GemmArgs ds = gs;
   ds.A = act_s;
@@ -396,7 +508,7 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
   ds.out = y;
   ds.out_r = out_r;
   ds.pos_of = pos_of;
-  hipLaunchKernelGGL((k_gemm<false, false>), dim3(((T + kTM - 1) / kTM) * (H / 128)), dim3(kThreadsG), 0, s, ds);
+  hipLaunchKernelGGL((k_gemm<false, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
   return hipGetLastError();
 }
 
