@@ -39,11 +39,89 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-resident", action="store_true", help="skip the all-resident variant")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
+                    help="short run for hardware counters: 'gateup' decodes a few cache-mode "
+                         "tokens (the measured kernel included), 'copy' copies 1 GiB once")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("GU_FETCH", "GU_WRITE", "CP_FETCH", "CP_WRITE"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of a "
+                         "'--probe gateup' and a '--probe copy' run) into the traffic summary (JSON)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gateup_routed_gemma_layer.json")
+# sources that define the measured kernel: the summary is void once one changes
+KERNEL_SOURCES = ["bit_quantized_expert_softmax_amd/csrc/decode.hip",
+                  "bit_quantized_expert_softmax_amd/csrc/device_common.h",
+                  "bit_quantized_expert_softmax_amd/csrc/launch.h"]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def routed_gateup_grid(sh):
+    """Launch size (work-items) of the routed gate/up kernel at B=1."""
+    return sh.top_k * (sh.inter // 32) * 1024
+
+
+def summarize_pmc(dirs):
+    """Per-dispatch HBM bytes of the routed gate/up kernel from FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter's reading for a plain copy of
+    COPY_BYTES (so the counters' unit and coverage cancel out)."""
+    import csv
+    import glob
+
+    from synth.configs import C2
+
+    def rows(d):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    grid = routed_gateup_grid(C2.shape)
+
+    def kernel_avg(d, counter):
+        v = [float(r["Counter_Value"]) for r in rows(d)
+             if r["Counter_Name"] == counter and "k_gateup" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid]
+        return sum(v) / len(v), len(v)
+
+    def copy_max(d, counter):
+        # the 1 GiB copy is the largest dispatch of the probe
+        return max(float(r["Counter_Value"]) for r in rows(d) if r["Counter_Name"] == counter)
+
+    f_kib, nf = kernel_avg(dirs[0], "FETCH_SIZE")
+    w_kib, nw = kernel_avg(dirs[1], "WRITE_SIZE")
+    cf = COPY_BYTES / copy_max(dirs[2], "FETCH_SIZE")
+    cw = COPY_BYTES / copy_max(dirs[3], "WRITE_SIZE")
+    return {"kernel": "k_gateup (routed experts, cache mode)", "grid": grid,
+            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+            "dispatches": [nf, nw], "copy_bytes_per_fetch_unit": cf, "copy_bytes_per_write_unit": cw,
+            "fetch_bytes": f_kib * cf, "write_bytes": w_kib * cw,
+            "traffic_bytes": f_kib * cf + w_kib * cw, "source_hash": kernel_source_hash()}
+
+
+def load_traffic():
+    """The committed counter summary if it was taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_hash") == kernel_source_hash() else None
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -57,6 +135,14 @@ def main():
     from synth import gen
     from synth.configs import C2
 
+    if args.probe == "copy":
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+        b = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+        torch.cuda.synchronize()
+        a.copy_(b)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+        return
     sh = C2.shape
     H, E, k, I, Is = sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter
     Lyr, T, S = args.layers, args.tokens, args.slots
@@ -119,6 +205,11 @@ def main():
     for t in range(args.warmup):
         token(t, handles, stats)
     torch.cuda.synchronize()
+    if args.probe == "gateup":
+        print(f"[bench] probe: {args.warmup} cache-mode tokens decoded", file=sys.stderr, flush=True)
+        for d in layers:
+            api.moe_layer_destroy(d["h"])
+        return
     warm = [(s.hits, s.misses, s.h2d_bytes) for s in stats]
     for d in layers:
         api.moe_layer_profile(d["h"], True)
@@ -234,22 +325,24 @@ def main():
             api.moe_layer_destroy(h)
 
         # batched decode (B tokens per step, grouped by expert) and 2048-token
-        # prefill on one layer of the same shape, unbiased routing
-        d0 = layers[0]
+        # prefill, unbiased routing. Consecutive steps use consecutive layers
+        # (routers, shared and routed experts of all 30 layers resident, one
+        # workspace shared by the handles as calls are in stream order), so no
+        # step finds its weights in the last-level cache.
         for B in (16, 64):
             wsb = torch.zeros(api.moe_layer_workspace_bytes(sh, B, 0), dtype=torch.uint8, device=devn)
-            hb = api.moe_layer_create(sh, router=d0["router"], shared_blob=d0["shared"], workspace=wsb,
-                                      experts_dev=d0["experts_dev"], max_B=B)
+            hbs = [api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"], workspace=wsb,
+                                        experts_dev=d["experts_dev"], max_B=B) for d in layers]
             xb = torch.from_numpy(gen.x_fp32(B * 8, H, 3, sub=B)).to(devn)
             yb = torch.empty((B, H), device=devn)
             idsb = torch.empty((B, k), dtype=torch.int32, device=devn)
 
             def bstep(i):
-                api.moe_layer_decode(hb, xb[(i % 8) * B:(i % 8 + 1) * B], None, B, 0, yb, idsb)
+                api.moe_layer_decode(hbs[i % Lyr], xb[(i % 8) * B:(i % 8 + 1) * B], None, B, 0, yb, idsb)
             for i in range(5):
                 bstep(i)
             torch.cuda.synchronize()
-            n_it = 40
+            n_it = 60
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record()
             touched = 0
@@ -265,30 +358,32 @@ def main():
             detail[f"batched_B{B}"] = {"tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms,
                                        "distinct_experts": touched / 8,
                                        "GBps": step_bytes / (ms * 1e-3) / 1e9}
-            api.moe_layer_destroy(hb)
+            for hb in hbs:
+                api.moe_layer_destroy(hb)
             del wsb
         Tp = 2048
         wsp = torch.zeros(api.moe_layer_workspace_bytes(sh, 1, Tp), dtype=torch.uint8, device=devn)
-        hp_ = api.moe_layer_create(sh, router=d0["router"], shared_blob=d0["shared"], workspace=wsp,
-                                   experts_dev=d0["experts_dev"], max_T=Tp)
+        hps = [api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"], workspace=wsp,
+                                    experts_dev=d["experts_dev"], max_T=Tp) for d in layers]
         xp = torch.from_numpy(gen.x_bf16(Tp, H, 4).view(np.int16)).to(devn)
         lp = torch.from_numpy(gen.logits_uniform(Tp, E, 4)).to(devn)
         yp = torch.empty((Tp, H), device=devn)
         for i in range(3):
-            api.moe_layer_prefill(hp_, xp, lp, Tp, yp)
+            api.moe_layer_prefill(hps[i % Lyr], xp, lp, Tp, yp)
         torch.cuda.synchronize()
-        n_it = 10
+        n_it = 20
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         for i in range(n_it):
-            api.moe_layer_prefill(hp_, xp, lp, Tp, yp)
+            api.moe_layer_prefill(hps[i % Lyr], xp, lp, Tp, yp)
         ev1.record()
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / n_it
         flops = 2.0 * Tp * (k * 3 * H * I + 3 * H * Is)
         detail["prefill_2048"] = {"ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
                                   "mfma_bf16_frac": flops / (ms * 1e-3) / 2.5e15, "GFLOP": flops / 1e9}
-        api.moe_layer_destroy(hp_)
+        for hp_ in hps:
+            api.moe_layer_destroy(hp_)
         del wsp
         for d in layers:
             del d["experts_dev"]
@@ -316,6 +411,9 @@ def main():
                "sample": f"{units} random (token, layer) units of the 30-layer stack at full shape, "
                          f"fp64 numpy, {el_c:.1f}s; tokens/s = units/s / {Lyr}"}
 
+    traffic = load_traffic()
+    if traffic:
+        detail["traffic_vs_algorithmic"] = traffic["traffic_bytes"] / gu_bytes
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -333,8 +431,9 @@ def main():
                    "inter": I, "shared_inter": Is, "slots_per_layer": S, "batch": 1,
                    "expert_store": "pinned host memory", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gbps_gu, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps_gu / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_ffn_gateup (routed experts)", "bytes_per_launch": gu_bytes,
+                     "frac": gbps_gu / HBM_PEAK_GBPS,
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "kernel": "k_gateup (routed experts, cache mode)", "bytes_per_launch": gu_bytes,
                      "mean_us": us_gu, "launches": n_gu},
         "cpu_baseline": cpu,
         "detail": detail,

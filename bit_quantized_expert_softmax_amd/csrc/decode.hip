@@ -22,6 +22,8 @@
 //   all k+1 sources as one virtual row of (k*I + I_s)/32 chunks, the routing
 //   weight folded into each group's scale; the row sum is the weighted
 //   combine, in a fixed order, without atomics.
+#include <hip/hip_ext.h>
+
 #include "launch.h"
 #include "topk.h"
 
@@ -256,7 +258,7 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
 
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
-                             hipStream_t s) {
+                             hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int routed = src.k * (src.I / kGroupRows);
   const int shared = src.Is / kGroupRows;
   const int lo = do_routed ? 0 : routed;
@@ -268,7 +270,11 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
                      (src.z ? sizeof(double) * src.E : 0);
   const int ntask = 2 * kGroupRows * ngu;
   const int need = (ntask + kThreads - 1) / kThreads;
-#define MOE_GATEUP(NT) hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, lo, udig, usc, adig, asc)
+#define MOE_GATEUP(NT)                                                                                   \
+  do {                                                                                                   \
+    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, lo, udig, usc, adig, asc); \
+    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, lo, udig, usc, adig, asc);               \
+  } while (0)
   if (need <= 1) MOE_GATEUP(1);
   else if (need <= 2) MOE_GATEUP(2);
   else if (need <= 4) MOE_GATEUP(4);
@@ -283,13 +289,17 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
 
 hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig, const float* asc,
                            const float* x, const uint16_t* add_in, bool residual, float* y,
-                           hipStream_t s) {
+                           hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int nga = src.k * (src.I / kGroup) + src.Is / kGroup;
   const size_t lds = static_cast<size_t>(nga) * sizeof(DigitGroup) + (((nga + 3) & ~3) * 4) +
                      static_cast<size_t>(kOutPerBlock) * nga * 4;
   const int blocks = (src.H + kOutPerBlock - 1) / kOutPerBlock;
   const int need = (kOutPerBlock * nga + kThreads - 1) / kThreads;
-#define MOE_DOWN(NT) hipLaunchKernelGGL(k_down<NT>, dim3(blocks), dim3(kThreads), lds, s, src, w, adig, asc, x, add_in, residual ? 1 : 0, y)
+#define MOE_DOWN(NT)                                                                                     \
+  do {                                                                                                   \
+    if (t0) hipExtLaunchKernelGGL(k_down<NT>, dim3(blocks), dim3(kThreads), lds, s, t0, t1, 0, src, w, adig, asc, x, add_in, residual ? 1 : 0, y); \
+    else hipLaunchKernelGGL(k_down<NT>, dim3(blocks), dim3(kThreads), lds, s, src, w, adig, asc, x, add_in, residual ? 1 : 0, y);               \
+  } while (0)
   if (need <= 1) MOE_DOWN(1);
   else if (need <= 2) MOE_DOWN(2);
   else if (need <= 3) MOE_DOWN(3);

@@ -71,14 +71,16 @@ struct SourceSet {
 // Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k) (do_routed)
 // and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
 // as digit planes, one DigitGroup and one scale per 32 activations.
+// t0/t1 (optional, both or neither): events stamped by the dispatch itself at
+// the kernel's start and end (kernel time without the cost of separate records).
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
-                             hipStream_t s);
+                             hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
 // optional residual x' = x + add_in, y [H].
 hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,
                            const float* asc, const float* x, const uint16_t* add_in, bool residual,
-                           float* y, hipStream_t s);
+                           float* y, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // Largest LDS footprint of the one-token kernels for a shape (bytes).
 size_t decode_lds_bytes(int H, int E, int k, int I, int Is);
 

@@ -148,6 +148,27 @@ void prof_end(moe_layer* L, int kind, hipEvent_t b, hipStream_t s) {
   L->rec[kind].emplace_back(b, e);
 }
 
+// Events for a single-kernel stage, stamped by the kernel's own dispatch
+// (start and end of the kernel), so the figure is the kernel's duration.
+struct ProfPair {
+  hipEvent_t a = nullptr, b = nullptr;
+};
+
+ProfPair prof_pair(moe_layer* L) {
+  if (!L->prof) return {};
+  hipEvent_t a = pool_get(L);
+  hipEvent_t b = a ? pool_get(L) : nullptr;
+  if (!b) {
+    if (a) L->pool.push_back(a);
+    return {};
+  }
+  return {a, b};
+}
+
+void prof_add(moe_layer* L, int kind, ProfPair p) {
+  if (p.a) L->rec[kind].emplace_back(p.a, p.b);
+}
+
 moe::SourceSet make_sources(const moe_layer* L) {
   moe::SourceSet S{};
   S.shared = L->d.shared_blob;
@@ -365,16 +386,16 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       G.w2 = w_out ? w_out + ko : nullptr;
       auto* adb = reinterpret_cast<moe::DigitGroup*>(adig + static_cast<size_t>(b) * npos);
       float* asb = asc + static_cast<size_t>(b) * npos;
-      hipEvent_t p1 = prof_begin(L, s);
+      const ProfPair p1 = prof_pair(L);
       HIP_OR_FAIL(moe::launch_ffn_gateup(G, true, true, udig + static_cast<size_t>(b) * ngu,
-                                         usc + static_cast<size_t>(b) * ngu, adb, asb, s), fn);
-      prof_end(L, 2, p1, s);
+                                         usc + static_cast<size_t>(b) * ngu, adb, asb, s, p1.a, p1.b), fn);
+      prof_add(L, 2, p1);
       S.ids = ids + ko;
-      hipEvent_t p2 = prof_begin(L, s);
+      const ProfPair p2 = prof_pair(L);
       HIP_OR_FAIL(moe::launch_ffn_down(S, w + ko, adb, asb, x + static_cast<size_t>(b) * H,
                                        add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
-                                       y + static_cast<size_t>(b) * H, s), fn);
-      prof_end(L, 3, p2, s);
+                                       y + static_cast<size_t>(b) * H, s, p2.a, p2.b), fn);
+      prof_add(L, 3, p2);
     }
     if (stats) stats->calls += 1;
     return MOE_OK;
@@ -385,10 +406,10 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   HIP_OR_FAIL(hipEventRecord(L->ev_ids, s), fn);
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
-  hipEvent_t p1 = prof_begin(L, s);
+  const ProfPair p1 = prof_pair(L);
   auto* adg = reinterpret_cast<moe::DigitGroup*>(adig);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s), fn);
-  prof_end(L, 1, p1, s);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b), fn);
+  prof_add(L, 1, p1);
   HIP_OR_FAIL(hipEventSynchronize(L->ev_ids), fn);
 
   // LFU step; the pre-step state is kept so that a failed copy enqueue leaves
@@ -415,12 +436,12 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
   }
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
-  hipEvent_t p2 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s), fn);
-  prof_end(L, 2, p2, s);
-  hipEvent_t p3 = prof_begin(L, s);
-  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s), fn);
-  prof_end(L, 3, p3, s);
+  const ProfPair p2 = prof_pair(L);
+  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+  prof_add(L, 2, p2);
+  const ProfPair p3 = prof_pair(L);
+  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
+  prof_add(L, 3, p3);
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
   if (stats) {
     stats->hits += k - n_miss;

@@ -217,15 +217,17 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
 
 /* Prefill T tokens (resident mode). x is bf16 [T][H]; routing uses
  * logits_in (dev fp32 [T][E]) when given, else x . router. Tokens are grouped
- * by expert; expert weights are converted to bf16 tile by tile and multiplied
- * on the matrix cores with fp32 accumulation; the GeGLU activation is rounded
+ * by expert; expert weights are dequantised to bf16 (one rounding of the
+ * exact product) and multiplied on the matrix cores with fp32 accumulation; the GeGLU activation is rounded
  * to bf16 before the down projection. y dev fp32 [T][H]. ids_out / w_out
  * optional as in decode. Asynchronous on stream. */
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in,
                              int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
 
-/* Per-kernel GPU time of the handle's calls, measured with HIP events placed
- * around each launch on the launch stream while profiling is enabled.
+/* Per-kernel GPU time of the handle's calls, measured with HIP events on the
+ * launch stream while profiling is enabled: the one-kernel stages 1-3 of the
+ * one-token paths take events stamped by the kernel's own dispatch (start and
+ * end of the kernel); the other stages take events recorded around them.
  * kind: 0 = routing (input prep, logits, top-k), 1 = shared-expert gate/up
  * launched ahead of the miss copies (cache mode), 2 = gate/up of the routed
  * experts (resident mode: together with the shared expert), 3 = down
