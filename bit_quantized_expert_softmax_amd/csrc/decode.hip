@@ -66,7 +66,7 @@ __device__ __forceinline__ void stage_to_lds(const uint4* __restrict__ g16, uint
 
 // Gate/up of one group of 32 (gate row i, up row i) pairs; NT tasks per lane.
 template <int NT>
-__global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int group_lo,
+__global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_blocks,
                                                      const DigitGroup* __restrict__ udig,
                                                      const float* __restrict__ usc,
                                                      DigitGroup* __restrict__ adig,
@@ -81,8 +81,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int group_lo,
   float* part = xs + ((ngu + 3) & ~3);                                      // [64][ngu]
   double* zs = reinterpret_cast<double*>(part + 2 * kGroupRows * ngu + 2);  // [E]
 
-  const int grp = group_lo + blockIdx.x;  // group of 32 activations in [0, (k*I + I_s)/32)
-  const int routed_groups = S.k * (S.I / kGroupRows);
+  // blocks [0, n_routed_blocks): groups of the routed ranks (all k, or the
+  // selected ones); the rest: groups of the shared expert
+  const int gpr = S.I / kGroupRows;
+  const int routed_groups = S.k * gpr;
+  int grp;  // group of 32 activations in [0, (k*I + I_s)/32)
+  if (static_cast<int>(blockIdx.x) < n_routed_blocks) {
+    const int ls = blockIdx.x / gpr;
+    grp = (S.nsel > 0 ? S.rsel.v[ls] : ls) * gpr + blockIdx.x % gpr;
+  } else {
+    grp = routed_groups + (blockIdx.x - n_routed_blocks);
+  }
   int src, i0, inter;
   if (grp < routed_groups) {
     src = grp / (S.I / kGroupRows);
@@ -259,10 +268,9 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
                              hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-  const int routed = src.k * (src.I / kGroupRows);
+  const int nr = do_routed ? (src.nsel > 0 ? src.nsel : src.k) * (src.I / kGroupRows) : 0;
   const int shared = src.Is / kGroupRows;
-  const int lo = do_routed ? 0 : routed;
-  const int n = (do_routed ? routed : 0) + (do_shared ? shared : 0);
+  const int n = nr + (do_shared ? shared : 0);
   if (n == 0) return hipSuccess;
   const int ngu = src.H / kGroup;
   const size_t lds = static_cast<size_t>(ngu) * sizeof(DigitGroup) + (((ngu + 3) & ~3) * 4) +
@@ -272,8 +280,8 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
   const int need = (ntask + kThreads - 1) / kThreads;
 #define MOE_GATEUP(NT)                                                                                   \
   do {                                                                                                   \
-    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, lo, udig, usc, adig, asc); \
-    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, lo, udig, usc, adig, asc);               \
+    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc); \
+    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc);               \
   } while (0)
   if (need <= 1) MOE_GATEUP(1);
   else if (need <= 2) MOE_GATEUP(2);

@@ -33,11 +33,14 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 // digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
 // finish. cnt must be zero before the launch and is zero after it.
 // Grid: (E/4 blocks) x B tokens; the top-k variant (ids != nullptr) needs B == 1.
+// With seq_host (top-k variant only) the last block also writes the ids to
+// ids_host (host-coherent memory) and then seq to *seq_host (system-scope
+// release), so the host can wait for them without a copy or an event.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              hipStream_t s);
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
@@ -55,6 +58,8 @@ struct SourceSet {
   const uint8_t* experts;  // resident expert array or slot pool
   const int32_t* ids;      // device ids [k] of this token, or nullptr (slots / in-kernel top-k)
   SlotList slot;           // cache mode: slot of each rank
+  SlotList rsel;           // gate/up: routed ranks to compute (rsel.v[0..nsel)); nsel 0 = all k
+  int nsel;
   const uint8_t* shared;   // shared expert blob
   size_t blob_e, blob_s;
   int H, I, Is, k;
@@ -68,8 +73,8 @@ struct SourceSet {
   float* w2;
 };
 
-// Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k) (do_routed)
-// and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
+// Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k), or the ranks
+// src.rsel selects (do_routed), and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
 // as digit planes, one DigitGroup and one scale per 32 activations.
 // t0/t1 (optional, both or neither): events stamped by the dispatch itself at
 // the kernel's start and end (kernel time without the cost of separate records).

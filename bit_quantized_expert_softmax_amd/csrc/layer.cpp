@@ -11,14 +11,17 @@
 // pinned host memory, and each miss is one host->HBM copy on a side stream.
 // The ids must reach the host before any copy can be issued (the routing of
 // a layer depends on the previous layer's output), so a cache-mode call
-// synchronises once, on an event recorded right after the 32-byte ids copy;
-// the shared-expert gate/up kernel is enqueued before that wait so the GPU is
-// busy meanwhile. A slot overwritten for token t was last read by the
-// previous call's kernels, which precede this call's routing kernels on the
-// same stream and so have finished when the ids event fires.
+// waits once: the routing kernel's last block writes the ids to
+// host-coherent memory and then a sequence word (system-scope release), and
+// the host spins on that word (bounded) instead of a device->host copy and an
+// event; the shared-expert gate/up kernel is enqueued before the wait so the
+// GPU is busy meanwhile. A slot overwritten for token t was last read by the
+// previous call's kernels, which precede this call's routing kernel on the
+// same stream and so have finished when the ids are published.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <chrono>
 #include <new>
 #include <vector>
 
@@ -100,8 +103,10 @@ struct moe_layer {
   size_t blob_e = 0, blob_s = 0;
   moe::WsLayout ws{};
   uint8_t* wsb = nullptr;
-  int32_t* ids_host = nullptr;  // pinned, [top_k]
-  hipEvent_t ev_ids = nullptr, ev_fill = nullptr;
+  int32_t* ids_host = nullptr;  // host-coherent, [kMaxTopK] ids then the sequence word
+  int32_t* seq_host = nullptr;
+  int32_t seq = 0;              // sequence number of the last routing published
+  hipEvent_t ev_fill = nullptr;
   // profiling
   bool prof = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kProfKinds];
@@ -167,6 +172,22 @@ ProfPair prof_pair(moe_layer* L) {
 
 void prof_add(moe_layer* L, int kind, ProfPair p) {
   if (p.a) L->rec[kind].emplace_back(p.a, p.b);
+}
+
+// Waits until the routing kernel has published the ids of call L->seq (it
+// writes them to host-coherent memory, then the sequence word with release
+// semantics). Bounded: false after 10 s without it (a failed or stalled launch).
+bool wait_routing(moe_layer* L) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (uint32_t spin = 0;; ++spin) {
+    if (__atomic_load_n(L->seq_host, __ATOMIC_ACQUIRE) == L->seq) return true;
+    if ((spin & 1023u) == 1023u &&
+        std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10))
+      return false;
+#if defined(__x86_64__)
+    __builtin_ia32_pause();
+#endif
+  }
 }
 
 moe::SourceSet make_sources(const moe_layer* L) {
@@ -255,11 +276,15 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
-    e = hipHostMalloc(reinterpret_cast<void**>(&L->ids_host), sizeof(int32_t) * moe::kMaxTopK,
-                      hipHostMallocDefault);
-    if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned ids buffer", e);
-    e = hipEventCreateWithFlags(&L->ev_ids, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
+    // the routing kernel writes the ids here and then bumps the sequence word
+    // with a system-scope release store; coherent memory makes both visible
+    // to the host without a copy
+    e = hipHostMalloc(reinterpret_cast<void**>(&L->ids_host), sizeof(int32_t) * (moe::kMaxTopK + 16),
+                      hipHostMallocCoherent | hipHostMallocMapped);
+    if (e != hipSuccess) return cleanup(MOE_EHIP, "host-coherent ids buffer", e);
+    L->seq_host = L->ids_host + moe::kMaxTopK;
+    *L->seq_host = 0;
+    e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
     moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
     if (!cs) cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache_backup);
@@ -275,7 +300,6 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
 void moe_layer_destroy(moe_layer* L) {
   if (!L) return;
   if (L->ids_host) (void)hipHostFree(L->ids_host);
-  if (L->ev_ids) (void)hipEventDestroy(L->ev_ids);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   for (auto& v : L->rec)
     for (auto& p : v) {
@@ -339,11 +363,15 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   const bool grouped = !L->cache_mode && B > 1;
   uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
   float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
+  const int32_t seq = L->cache_mode ? L->seq + 1 : 0;
   HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
                                       grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
                                       in_kernel_topk ? nullptr : ids,
                                       in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
-                                      in_kernel_topk ? nullptr : w_out, s), fn);
+                                      in_kernel_topk ? nullptr : w_out,
+                                      L->cache_mode ? L->ids_host : nullptr,
+                                      L->cache_mode ? L->seq_host : nullptr, seq, s), fn);
+  if (L->cache_mode) L->seq = seq;
   prof_end(L, 0, pb, s);
 
   moe::SourceSet S = make_sources(L);
@@ -402,15 +430,13 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   }
 
   // ---- cache mode, one token
-  HIP_OR_FAIL(hipMemcpyAsync(L->ids_host, ids, sizeof(int32_t) * k, hipMemcpyDeviceToHost, s), fn);
-  HIP_OR_FAIL(hipEventRecord(L->ev_ids, s), fn);
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
   const ProfPair p1 = prof_pair(L);
   auto* adg = reinterpret_cast<moe::DigitGroup*>(adig);
   HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b), fn);
   prof_add(L, 1, p1);
-  HIP_OR_FAIL(hipEventSynchronize(L->ev_ids), fn);
+  if (!wait_routing(L)) return fail(MOE_EHIP, "%s: timed out waiting for the routing kernel", fn);
 
   // LFU step; the pre-step state is kept so that a failed copy enqueue leaves
   // the cache unchanged (no slot is marked resident with stale bytes)

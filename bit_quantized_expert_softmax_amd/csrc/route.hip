@@ -42,6 +42,11 @@ struct RouteArgs {
   int32_t* cnt;       // arrival counter, zero between calls
   int32_t *ids, *ids2;
   float *w, *w2;
+  // optional (top-k variant, B == 1): the ids also go to host-coherent memory,
+  // then seq_host is set to seq with a system-scope release store
+  int32_t* ids_host;
+  int32_t* seq_host;
+  int32_t seq;
 };
 
 // Per wave: one expert's router row and the whole token input x' are loaded
@@ -241,6 +246,13 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
     topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids + o, A.w + o, A.ids2 ? A.ids2 + o : nullptr,
                A.w2 ? A.w2 + o : nullptr);
   }
+  if (A.seq_host && threadIdx.x == 0) {
+    // one thread writes the ids and then publishes them: the release store
+    // orders its own earlier stores before the sequence number
+    for (int j = 0; j < A.k; ++j)
+      __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 constexpr int kLogitWaves = 4;
@@ -299,9 +311,10 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              hipStream_t s) {
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s) {
+  if (seq_host && (B != 1 || !ids)) return hipErrorInvalidValue;
   RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, u16, tsc, z, cnt,
-              ids, ids2, w, w2};
+              ids, ids2, w, w2, ids_host, seq_host, seq};
   const int blocks = (E + kWaves - 1) / kWaves;
   const size_t lds = sizeof(double) * E;
   const bool topk = ids != nullptr;
