@@ -9,10 +9,10 @@
 //
 // The work is HBM-bound (~3.5 flop per weight byte) and short (tens of MB per
 // token), so both kernels are shaped for latency: 1024-thread blocks (16 waves
-// per CU), a flat task list in which every lane owns a few (row, 16-byte
-// chunk) tasks and issues all of its loads before any is consumed, per-chunk
-// partial products reduced in LDS in a fixed order, and no cross-block
-// synchronisation.
+// per CU); every lane owns one 16-byte chunk column and a few rows of it,
+// loads that chunk's activation digits once into registers and issues all of
+// its loads before any is consumed; per-chunk partial products are reduced in
+// LDS in a fixed order; no cross-block synchronisation.
 //
 // gate/up kernel: one block per group of 32 activations of one source: the 32
 //   gate rows and 32 up rows (contiguous in the blob) are streamed as one
@@ -31,37 +31,12 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kGroupRows = 32;  // activations per gate/up block
 
 __device__ __forceinline__ const uint8_t* source_base(const SourceSet& S, int j) {
   if (j >= S.k) return S.shared;
   const int e = S.ids ? S.ids[j] : S.slot.v[j];
   return S.experts + static_cast<size_t>(e) * S.blob_e;
-}
-
-// Copies n16 uint4 and nf floats from global memory to LDS with every load of
-// a thread issued before its first store.
-__device__ __forceinline__ void stage_to_lds(const uint4* __restrict__ g16, uint4* l16, int n16,
-                                             const float* __restrict__ gf, float* lf, int nf) {
-  constexpr int U = 2;
-  for (int i0 = 0; i0 < n16; i0 += kThreads * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + threadIdx.x + kThreads * u;
-      v[u] = g16[i < n16 ? i : n16 - 1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // unconditional stores (clamped index): lanes past the end rewrite the last
-    // element with its own value, which keeps the loads ahead of the first wait
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + threadIdx.x + kThreads * u;
-      l16[i < n16 ? i : n16 - 1] = v[u];
-    }
-  }
-  for (int i = threadIdx.x; i < nf; i += kThreads) lf[i] = gf[i];
 }
 
 // Gate/up of one group of 32 (gate row i, up row i) pairs; NT tasks per lane.
@@ -76,9 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   __shared__ int sel_e[kMaxTopK];
   __shared__ float rowsum[2 * kGroupRows];
   const int ngu = S.H / kGroup;
-  DigitGroup* xd = reinterpret_cast<DigitGroup*>(lds_raw);
-  float* xs = reinterpret_cast<float*>(xd + ngu);
-  float* part = xs + ((ngu + 3) & ~3);                                      // [64][ngu]
+  float* part = reinterpret_cast<float*>(lds_raw);                          // [64][ngu]
   double* zs = reinterpret_cast<double*>(part + 2 * kGroupRows * ngu + 2);  // [E]
 
   // blocks [0, n_routed_blocks): groups of the routed ranks (all k, or the
@@ -117,37 +90,37 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   }
   const BlobOffsets o = blob_offsets(S.H, inter);
   const size_t rowb = static_cast<size_t>(S.H) / 2;
-  // tasks: tau in [0, 64 * ngu): gate rows first, then up rows, chunk c =
-  // tau % ngu. Gate rows i0..i0+31 are one contiguous span and so are the up
-  // rows, so consecutive lanes read consecutive 16-byte chunks.
-  const int ntask = 2 * kGroupRows * ngu;
-  const uint8_t* gq = base + o.gate_q + static_cast<size_t>(i0) * rowb;
-  const uint8_t* uq = base + o.up_q + static_cast<size_t>(i0) * rowb;
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(base + o.gate_s) + static_cast<size_t>(i0) * ngu;
-  const uint16_t* us = reinterpret_cast<const uint16_t*>(base + o.up_s) + static_cast<size_t>(i0) * ngu;
-  const int half = kGroupRows * ngu;
+  // Lane (r0, c) = (threadIdx / ngu, threadIdx % ngu) owns chunk column c of
+  // rows r0, r0 + R, ... (R = kThreads / ngu; rows 0..31 gate, 32..63 up).
+  // It loads that chunk's activation digits once into registers, next to its
+  // weights, so no staging pass and no per-chunk LDS reads are needed;
+  // consecutive lanes read consecutive 16-byte chunks of a row.
+  const int R = kThreads / ngu;
+  const int c = threadIdx.x % ngu;
+  const int r0 = threadIdx.x / ngu;
+  const uint8_t* gq = base + o.gate_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(c);
+  const uint8_t* uq = base + o.up_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(c);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(base + o.gate_s) + static_cast<size_t>(i0) * ngu + c;
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(base + o.up_s) + static_cast<size_t>(i0) * ngu + c;
   uint4 wv[NT];
   uint16_t sw[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int tau = threadIdx.x + kThreads * t;
-    tau = tau < ntask ? tau : ntask - 1;
-    const bool up = tau >= half;
-    const int off = up ? tau - half : tau;
-    wv[t] = load_w16((up ? uq : gq) + 16 * static_cast<size_t>(off));
-    sw[t] = (up ? us : gs)[off];
+    int r = r0 + R * t;
+    r = r < 2 * kGroupRows ? r : 2 * kGroupRows - 1;  // clamped: loaded, not stored
+    const bool up = r >= kGroupRows;
+    const int rr = up ? r - kGroupRows : r;
+    wv[t] = load_w16((up ? uq : gq) + static_cast<size_t>(rr) * rowb);
+    sw[t] = (up ? us : gs)[static_cast<size_t>(rr) * ngu];
   }
-  // the activation digits are staged while the weight loads are in flight
-  stage_to_lds(reinterpret_cast<const uint4*>(udig), reinterpret_cast<uint4*>(xd), ngu * 4, usc, xs, ngu);
-  __syncthreads();
+  const DigitGroup xd = udig[c];
+  const float xs = usc[c];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int tau = threadIdx.x + kThreads * t;
-    const int tc = tau < ntask ? tau : ntask - 1;
-    const int c = tc % ngu;
-    const float p = static_cast<float>(chunk_dot(wv[t], xd[c])) * (h2f(sw[t]) * xs[c]);
-    if (tau < ntask) part[tau] = p;
+    const int r = r0 + R * t;
+    const float p = static_cast<float>(chunk_dot(wv[t], xd)) * (h2f(sw[t]) * xs);
+    if (r < 2 * kGroupRows) part[r * ngu + c] = p;
   }
   __syncthreads();
   // 64 row sums: 16 lanes per row, 4 rows per wave, fixed order
@@ -186,9 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
   const int gi = S.I / kGroup;
   const int gsh = S.Is / kGroup;
   const int nga = S.k * gi + gsh;  // chunks of the virtual row
-  DigitGroup* xd = reinterpret_cast<DigitGroup*>(lds_raw);
-  float* xs = reinterpret_cast<float*>(xd + nga);
-  float* part = xs + ((nga + 3) & ~3);  // [kOutPerBlock][nga]
+  float* part = reinterpret_cast<float*>(lds_raw);  // [kOutPerBlock][nga]
   const int n0 = blockIdx.x * kOutPerBlock;
   const int nout = S.H - n0 < kOutPerBlock ? S.H - n0 : kOutPerBlock;
   if (threadIdx.x <= static_cast<unsigned>(S.k)) {
@@ -197,45 +168,45 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     wsh[j] = j < S.k ? w[j] : 1.0f;
   }
   __syncthreads();
-  // tasks: tau = o * nga + c (output o of the block, chunk c of its virtual row)
-  const int ntask = nout * nga;
+  // Lane (o0, c) = (threadIdx / nga, threadIdx % nga) owns chunk c of the
+  // virtual row for outputs o0, o0 + R, ... (R = kThreads / nga); it loads
+  // that chunk's activation digits once, with the routing weight of the
+  // chunk's source folded into the scale.
+  const int R = kThreads / nga;
+  const int c = threadIdx.x % nga;
+  const int o0 = threadIdx.x / nga;
+  const bool on = o0 < R;
+  int j, cc, inter;
+  if (c < S.k * gi) {
+    j = c / gi;
+    cc = c - j * gi;
+    inter = S.I;
+  } else {
+    j = S.k;
+    cc = c - S.k * gi;
+    inter = S.Is;
+  }
+  const BlobOffsets o = blob_offsets(S.H, inter);
+  const uint8_t* qb = srcb[j] + o.down_q + 16 * static_cast<size_t>(cc);
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(srcb[j] + o.down_s) + cc;
   uint4 wv[NT];
   uint16_t sw[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    int tau = threadIdx.x + kThreads * t;
-    tau = tau < ntask ? tau : ntask - 1;
-    const int ob = tau / nga;
-    const int c = tau - ob * nga;
-    int j, cc, inter;
-    if (c < S.k * gi) {
-      j = c / gi;
-      cc = c - j * gi;
-      inter = S.I;
-    } else {
-      j = S.k;
-      cc = c - S.k * gi;
-      inter = S.Is;
-    }
-    const BlobOffsets o = blob_offsets(S.H, inter);
+    int ob = o0 + R * t;
+    ob = ob < nout ? ob : nout - 1;  // clamped: loaded, not stored
     const size_t n = static_cast<size_t>(n0 + ob);
-    wv[t] = load_w16(srcb[j] + o.down_q + n * (inter / 2) + 16 * static_cast<size_t>(cc));
-    sw[t] = reinterpret_cast<const uint16_t*>(srcb[j] + o.down_s)[n * (inter / kGroup) + cc];
+    wv[t] = load_w16(qb + n * (inter / 2));
+    sw[t] = sb[n * (inter / kGroup)];
   }
-  // activations and their scales are staged while the weights stream in
-  stage_to_lds(reinterpret_cast<const uint4*>(adig), reinterpret_cast<uint4*>(xd), nga * 4, asc, xs, nga);
-  __syncthreads();
-  // fold the routing weight of each source into its groups' scales
-  for (int g = threadIdx.x; g < nga; g += kThreads) xs[g] *= wsh[g < S.k * gi ? g / gi : S.k];
-  __syncthreads();
+  const DigitGroup xd = adig[c];
+  const float xs = asc[c] * wsh[j];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int tau = threadIdx.x + kThreads * t;
-    const int tc = tau < ntask ? tau : ntask - 1;
-    const int c = tc % nga;
-    const float p = static_cast<float>(chunk_dot(wv[t], xd[c])) * (h2f(sw[t]) * xs[c]);
-    if (tau < ntask) part[tau] = p;
+    const int ob = o0 + R * t;
+    const float p = static_cast<float>(chunk_dot(wv[t], xd)) * (h2f(sw[t]) * xs);
+    if (on && ob < nout) part[ob * nga + c] = p;
   }
   __syncthreads();
   // one wave per output: fixed-order sum of its nga partials
@@ -258,10 +229,8 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
 
 size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
   const size_t ngu = H / kGroup, nga = (static_cast<size_t>(k) * I + Is) / kGroup;
-  const size_t gu = ngu * sizeof(DigitGroup) + ((ngu + 3) & ~static_cast<size_t>(3)) * 4 +
-                    (2 * kGroupRows * ngu + 2) * 4 + sizeof(double) * E;
-  const size_t dn = nga * sizeof(DigitGroup) + ((nga + 3) & ~static_cast<size_t>(3)) * 4 +
-                    static_cast<size_t>(kOutPerBlock) * nga * 4;
+  const size_t gu = (2 * kGroupRows * ngu + 2) * 4 + sizeof(double) * E;
+  const size_t dn = static_cast<size_t>(kOutPerBlock) * nga * 4;
   return gu > dn ? gu : dn;
 }
 
@@ -273,11 +242,10 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
   const int n = nr + (do_shared ? shared : 0);
   if (n == 0) return hipSuccess;
   const int ngu = src.H / kGroup;
-  const size_t lds = static_cast<size_t>(ngu) * sizeof(DigitGroup) + (((ngu + 3) & ~3) * 4) +
-                     static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 +
-                     (src.z ? sizeof(double) * src.E : 0);
-  const int ntask = 2 * kGroupRows * ngu;
-  const int need = (ntask + kThreads - 1) / kThreads;
+  const size_t lds = static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 + (src.z ? sizeof(double) * src.E : 0);
+  if (ngu > kThreads) return hipErrorInvalidValue;
+  const int rows_per_pass = kThreads / ngu;
+  const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
 #define MOE_GATEUP(NT)                                                                                   \
   do {                                                                                                   \
     if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc); \
@@ -299,10 +267,11 @@ hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGrou
                            const float* x, const uint16_t* add_in, bool residual, float* y,
                            hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int nga = src.k * (src.I / kGroup) + src.Is / kGroup;
-  const size_t lds = static_cast<size_t>(nga) * sizeof(DigitGroup) + (((nga + 3) & ~3) * 4) +
-                     static_cast<size_t>(kOutPerBlock) * nga * 4;
+  const size_t lds = static_cast<size_t>(kOutPerBlock) * nga * 4;
+  if (nga > kThreads) return hipErrorInvalidValue;
   const int blocks = (src.H + kOutPerBlock - 1) / kOutPerBlock;
-  const int need = (kOutPerBlock * nga + kThreads - 1) / kThreads;
+  const int outs_per_pass = kThreads / nga;
+  const int need = (kOutPerBlock + outs_per_pass - 1) / outs_per_pass;
 #define MOE_DOWN(NT)                                                                                     \
   do {                                                                                                   \
     if (t0) hipExtLaunchKernelGGL(k_down<NT>, dim3(blocks), dim3(kThreads), lds, s, t0, t1, 0, src, w, adig, asc, x, add_in, residual ? 1 : 0, y); \
