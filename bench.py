@@ -3,9 +3,11 @@
 cache per layer, B=1, on one MI355X.
 
 One step = one token through all layers of the stack (per layer: routing,
-LFU lookup, host->HBM copies of the missing experts on a side stream
-overlapped with the shared-expert gate/up GEMV, routed gate/up GEMVs with
-GeGLU, down GEMVs with the weighted combine and the residual). Inputs are
+LFU lookup, host->HBM copies of the missing experts overlapped with the
+shared-expert gate/up GEMV -- by hipMemcpyAsync on a side stream, or with
+--fill kernel by fill blocks of the shared-expert launch --, routed gate/up
+GEMVs with GeGLU, down GEMVs with the weighted combine and the residual). The
+fill variant not chosen is timed afterwards and reported in detail. Inputs are
 seeded and synthetic (no trained weights); the experts of all layers sit in
 pinned host memory, the slot pools, routers and shared experts in HBM.
 
@@ -38,6 +40,10 @@ def parse():
     ap.add_argument("--slots", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-resident", action="store_true", help="skip the all-resident variant")
+    ap.add_argument("--fill", choices=["kernel", "copy-engine"], default="copy-engine",
+                    help="how the timed (headline) run fills cache misses; the other way is "
+                         "timed afterwards and reported in detail")
+    ap.add_argument("--no-variant", action="store_true", help="skip the other fill variant")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
@@ -54,6 +60,7 @@ KERNEL_SOURCES = ["bit_quantized_expert_softmax_amd/csrc/decode.hip",
                   "bit_quantized_expert_softmax_amd/csrc/device_common.h",
                   "bit_quantized_expert_softmax_amd/csrc/launch.h"]
 COPY_BYTES = 1 << 30
+PROFILE_EVERY = 8
 
 
 def kernel_source_hash():
@@ -151,7 +158,9 @@ def main():
     torch.cuda.set_device(0)
     lib = api.lib()
     blob = gen.blob_bytes(H, I)
-    flags = api.MOE_F_RMSNORM_IN | api.MOE_F_RESIDUAL
+    flags_base = api.MOE_F_RMSNORM_IN | api.MOE_F_RESIDUAL
+    fill_flag = {"kernel": api.MOE_F_FILL_KERNEL, "copy-engine": 0}
+    flags = flags_base | fill_flag[args.fill]
 
     # ---------------------------------------------------------------- inputs
     t_gen = time.perf_counter()
@@ -211,8 +220,11 @@ def main():
             api.moe_layer_destroy(d["h"])
         return
     warm = [(s.hits, s.misses, s.h2d_bytes) for s in stats]
+    # only the measured kernel (routed gate/up, kind 2) is timed during the
+    # timed region, on one token in PROFILE_EVERY, with its events created
+    # beforehand (timing every launch costs the stack about 10%)
     for d in layers:
-        api.moe_layer_profile(d["h"], True)
+        api.moe_layer_profile_kinds(d["h"], 1 << 2, PROFILE_EVERY, 2 * args.steps // PROFILE_EVERY + 16)
     print("[bench] warmup done, timing the cache-mode stack", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -226,6 +238,19 @@ def main():
     hits = sum(s.hits - w[0] for s, w in zip(stats, warm))
     misses = sum(s.misses - w[1] for s, w in zip(stats, warm))
     h2d = sum(s.h2d_bytes - w[2] for s, w in zip(stats, warm))
+    # per-stage times of all kinds come from a short profiled pass afterwards
+    # (out of the timed region: events around every stage slow the stack)
+    n_gu, ms_gu = 0, 0.0
+    for d in layers:
+        a, b = api.moe_layer_profile_read(d["h"], 2)
+        n_gu += a
+        ms_gu += b
+        api.moe_layer_profile(d["h"], True)
+    for t in range(args.warmup + args.steps, args.warmup + args.steps + 16):
+        token(t, handles, None)
+    torch.cuda.synchronize()
+    for d in layers:
+        api.moe_layer_profile(d["h"], False)
     kinds = {}
     for kind in range(4):
         n = ms = 0
@@ -239,7 +264,6 @@ def main():
     # plus the fp32 input vector read and the fp32 activations written
     gu_bytes = k * 2 * I * (H // 2 + 2 * (H // 32)) + H * 4 + k * I * 4
     down_bytes = H * (k * (I // 2 + 2 * (I // 32)) + Is // 2 + 2 * (Is // 32)) + (k * I + Is) * 4 + H * 4 * 2
-    n_gu, ms_gu = kinds[2]
     us_gu = 1e3 * ms_gu / max(n_gu, 1)
     gbps_gu = gu_bytes / (us_gu * 1e-6) / 1e9
     n_dn, ms_dn = kinds[3]
@@ -256,6 +280,31 @@ def main():
         },
         "down_combine_GBps": down_bytes / (us_dn * 1e-6) / 1e9 if us_dn > 0 else None,
     }
+
+    # ---------------------------------------------------------------- other fill variant
+    # Same stack, caches emptied, misses filled the other way (fill blocks of
+    # the shared-expert launch vs hipMemcpyAsync on the side stream).
+    if not args.no_variant:
+        other = "copy-engine" if args.fill == "kernel" else "kernel"
+        for d in layers:
+            api.moe_cache_reset(api.moe_layer_cache(d["h"]))
+        stats_f = [api.moe_decode_stats() for _ in range(Lyr)]
+        flags = flags_base | fill_flag[other]
+        for t in range(args.warmup):
+            token(t, handles, stats_f)
+        torch.cuda.synchronize()
+        warm_f = [(s.hits, s.misses) for s in stats_f]
+        t0 = time.perf_counter()
+        for t in range(args.warmup, args.warmup + args.steps):
+            token(t, handles, stats_f)
+        torch.cuda.synchronize()
+        el_f = time.perf_counter() - t0
+        flags = flags_base | fill_flag[args.fill]
+        hf = sum(s.hits - w[0] for s, w in zip(stats_f, warm_f))
+        mf = sum(s.misses - w[1] for s, w in zip(stats_f, warm_f))
+        detail["fill_" + other.replace("-", "_")] = {
+            "tokens_per_s": args.steps / el_f, "ms_per_step": 1e3 * el_f / args.steps,
+            "hit_rate_timed": hf / max(hf + mf, 1)}
 
     # ---------------------------------------------------------------- all experts resident
     if not args.no_resident:
@@ -275,7 +324,7 @@ def main():
             src = x_in.data_ptr()
             for l in range(Lyr):
                 dst = hp[l & 1]
-                rc = decode(res[l], src, e_in.data_ptr() + l * H * 2, 1, flags, dst, None, None, None,
+                rc = decode(res[l], src, e_in.data_ptr() + l * H * 2, 1, flags_base, dst, None, None, None,
                             None, None, s)
                 if rc:
                     raise api.MoeError(rc, "moe_layer_decode", api.moe_last_error())
@@ -429,7 +478,10 @@ def main():
         "data": "synthetic (seeded; no trained weights)",
         "config": {"workload": C2.name, "layers": Lyr, "hidden": H, "experts": E, "top_k": k,
                    "inter": I, "shared_inter": Is, "slots_per_layer": S, "batch": 1,
-                   "expert_store": "pinned host memory", "parallelism": "none (1 GPU)"},
+                   "expert_store": "pinned host memory",
+                   "miss_fill": ("fill blocks in the shared-expert gate/up launch" if args.fill == "kernel"
+                                 else "hipMemcpyAsync on a side stream"),
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": gbps_gu, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps_gu / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,

@@ -15,6 +15,7 @@ from . import _lib as L
 
 MOE_F_RMSNORM_IN = 1
 MOE_F_RESIDUAL = 2
+MOE_F_FILL_KERNEL = 4
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EALIGN", -4: "MOE_EHIP",
           -5: "MOE_ENOMEM", -6: "MOE_ESTATE"}
 
@@ -203,6 +204,10 @@ def moe_layer_prefill(h, x_bf16, logits_in, T, y, ids_out=None, w_out=None, stre
 
 def moe_layer_profile(h, enable: bool) -> None:
     _check(lib().moe_layer_profile(h, 1 if enable else 0), "moe_layer_profile")
+
+
+def moe_layer_profile_kinds(h, mask: int, every: int = 1, reserve_events: int = 0) -> None:
+    _check(lib().moe_layer_profile_kinds(h, mask, every, reserve_events), "moe_layer_profile_kinds")
 
 
 def moe_layer_profile_read(h, kind: int):

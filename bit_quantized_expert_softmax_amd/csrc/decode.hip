@@ -45,7 +45,39 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
                                                      const DigitGroup* __restrict__ udig,
                                                      const float* __restrict__ usc,
                                                      DigitGroup* __restrict__ adig,
-                                                     float* __restrict__ asc) {
+                                                     float* __restrict__ asc, FillList F) {
+  // fill blocks first (cache mode, fill-kernel option): block f copies its
+  // share of blob f / blocks_per_blob from the pinned host store to the slot,
+  // while the compute blocks of the same launch run
+  const int nfill = F.n * F.blocks_per_blob;
+  if (static_cast<int>(blockIdx.x) < nfill) {
+    const int m = blockIdx.x / F.blocks_per_blob;
+    const size_t n16 = F.bytes / 16;
+    const size_t per = (n16 + F.blocks_per_blob - 1) / F.blocks_per_blob;
+    const size_t lo = (blockIdx.x % F.blocks_per_blob) * per;
+    const size_t hi = lo + per < n16 ? lo + per : n16;
+    const uint4* __restrict__ src = reinterpret_cast<const uint4*>(F.src[m]);
+    uint4* __restrict__ dst = reinterpret_cast<uint4*>(F.dst[m]);
+    constexpr int U = 4;
+    for (size_t i0 = lo; i0 < hi; i0 += static_cast<size_t>(kThreads) * U) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = i0 + threadIdx.x + static_cast<size_t>(kThreads) * u;
+        v[u] = src[i < hi ? i : hi - 1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // streaming stores: the blob is read next from memory by the expert
+      // kernels, so it need not stay in (and be written back from) the L2
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t i = i0 + threadIdx.x + static_cast<size_t>(kThreads) * u;
+        if (i < hi) store_nt16(dst + i, v[u]);
+      }
+    }
+    return;
+  }
+  const int bid = blockIdx.x - nfill;
   extern __shared__ uint4 lds_raw[];
   __shared__ double sel_z[kMaxTopK];
   __shared__ int sel_e[kMaxTopK];
@@ -59,11 +91,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   const int gpr = S.I / kGroupRows;
   const int routed_groups = S.k * gpr;
   int grp;  // group of 32 activations in [0, (k*I + I_s)/32)
-  if (static_cast<int>(blockIdx.x) < n_routed_blocks) {
-    const int ls = blockIdx.x / gpr;
-    grp = (S.nsel > 0 ? S.rsel.v[ls] : ls) * gpr + blockIdx.x % gpr;
+  if (bid < n_routed_blocks) {
+    const int ls = bid / gpr;
+    grp = (S.nsel > 0 ? S.rsel.v[ls] : ls) * gpr + bid % gpr;
   } else {
-    grp = routed_groups + (blockIdx.x - n_routed_blocks);
+    grp = routed_groups + (bid - n_routed_blocks);
   }
   int src, i0, inter;
   if (grp < routed_groups) {
@@ -236,10 +268,15 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
 
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
-                             hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+                             hipStream_t s, hipEvent_t t0, hipEvent_t t1, const FillList* fill) {
+  FillList F{};
+  if (fill && fill->n > 0) {
+    if (fill->n > kMaxTopK || fill->blocks_per_blob < 1 || fill->bytes % 16) return hipErrorInvalidValue;
+    F = *fill;
+  }
   const int nr = do_routed ? (src.nsel > 0 ? src.nsel : src.k) * (src.I / kGroupRows) : 0;
   const int shared = src.Is / kGroupRows;
-  const int n = nr + (do_shared ? shared : 0);
+  const int n = F.n * F.blocks_per_blob + nr + (do_shared ? shared : 0);
   if (n == 0) return hipSuccess;
   const int ngu = src.H / kGroup;
   const size_t lds = static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 + (src.z ? sizeof(double) * src.E : 0);
@@ -248,8 +285,8 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
   const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
 #define MOE_GATEUP(NT)                                                                                   \
   do {                                                                                                   \
-    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc); \
-    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc);               \
+    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F); \
+    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F);               \
   } while (0)
   if (need <= 1) MOE_GATEUP(1);
   else if (need <= 2) MOE_GATEUP(2);

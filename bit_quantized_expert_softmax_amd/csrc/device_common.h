@@ -158,4 +158,9 @@ __device__ __forceinline__ uint4 load_w16(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming 16-byte store (data not read again by this kernel).
+__device__ __forceinline__ void store_nt16(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 }  // namespace moe

@@ -73,14 +73,25 @@ struct SourceSet {
   float* w2;
 };
 
+// Misses to copy host -> slot by fill blocks (cache mode, fill-kernel option).
+struct FillList {
+  const uint8_t* src[kMaxTopK];  // device-accessible pinned host blobs
+  uint8_t* dst[kMaxTopK];        // slots in HBM
+  int n;                         // number of blobs
+  int blocks_per_blob;
+  size_t bytes;                  // blob size, a multiple of 16
+};
+
 // Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k), or the ranks
 // src.rsel selects (do_routed), and/or the shared expert (do_shared). The activations a [k*I + I_s] leave
 // as digit planes, one DigitGroup and one scale per 32 activations.
 // t0/t1 (optional, both or neither): events stamped by the dispatch itself at
 // the kernel's start and end (kernel time without the cost of separate records).
+// fill (optional): blobs copied by extra blocks of the same launch.
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
-                             hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+                             hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr,
+                             const FillList* fill = nullptr);
 // Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
 // optional residual x' = x + add_in, y [H].
 hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,

@@ -106,9 +106,14 @@ struct moe_layer {
   int32_t* ids_host = nullptr;  // host-coherent, [kMaxTopK] ids then the sequence word
   int32_t* seq_host = nullptr;
   int32_t seq = 0;              // sequence number of the last routing published
+  const uint8_t* host_dev = nullptr;  // device address of experts_host (fill-kernel option)
   hipEvent_t ev_fill = nullptr;
   // profiling
   bool prof = false;
+  uint32_t prof_mask = 0;  // kinds recorded while profiling (bit i = kind i)
+  uint32_t prof_every = 1; // record one call in prof_every
+  uint32_t prof_calls = 0;
+  bool prof_now = false;   // this call is recorded
   std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[kProfKinds];
   std::vector<hipEvent_t> pool;
   int64_t prof_launches[kProfKinds] = {};
@@ -132,8 +137,8 @@ hipEvent_t pool_get(moe_layer* L) {
 }
 
 // Records an event before a launch when profiling; returns it (or nullptr).
-hipEvent_t prof_begin(moe_layer* L, hipStream_t s) {
-  if (!L->prof) return nullptr;
+hipEvent_t prof_begin(moe_layer* L, int kind, hipStream_t s) {
+  if (!L->prof_now || !(L->prof_mask & (1u << kind))) return nullptr;
   hipEvent_t e = pool_get(L);
   if (e && hipEventRecord(e, s) != hipSuccess) {
     L->pool.push_back(e);
@@ -159,8 +164,8 @@ struct ProfPair {
   hipEvent_t a = nullptr, b = nullptr;
 };
 
-ProfPair prof_pair(moe_layer* L) {
-  if (!L->prof) return {};
+ProfPair prof_pair(moe_layer* L, int kind) {
+  if (!L->prof_now || !(L->prof_mask & (1u << kind))) return {};
   hipEvent_t a = pool_get(L);
   hipEvent_t b = a ? pool_get(L) : nullptr;
   if (!b) {
@@ -284,6 +289,13 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     if (e != hipSuccess) return cleanup(MOE_EHIP, "host-coherent ids buffer", e);
     L->seq_host = L->ids_host + moe::kMaxTopK;
     *L->seq_host = 0;
+    // the fill-kernel option reads the store from the device; pinned memory
+    // from hipHostMalloc has a device address, other memory has none
+    hipPointerAttribute_t pa{};
+    if (hipPointerGetAttributes(&pa, d->experts_host) == hipSuccess && pa.type == hipMemoryTypeHost &&
+        pa.devicePointer)
+      L->host_dev = static_cast<const uint8_t*>(pa.devicePointer);
+    (void)hipGetLastError();  // a failed query leaves the option unavailable, not an error
     e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
     moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
@@ -329,10 +341,16 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   moe::clear_error();
   const char* fn = "moe_layer_decode";
   if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
-  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL)) return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL | MOE_F_FILL_KERNEL))
+    return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const bool fill_kernel = flags & MOE_F_FILL_KERNEL;
+  if (fill_kernel && !L->cache_mode) return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs a cache-mode handle", fn);
+  if (fill_kernel && !L->host_dev)
+    return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs experts_host in device-accessible pinned memory", fn);
   if (B < 0 || B > L->max_B) return fail(MOE_ESHAPE, "%s: B=%d outside [0, max_B=%d]", fn, B, L->max_B);
   if (B == 0) return MOE_OK;
   if (!x || !y) return fail(MOE_EINVAL, "%s: x and y are required", fn);
+  L->prof_now = L->prof && (L->prof_calls++ % L->prof_every) == 0;
   if (x == y) return fail(MOE_EINVAL, "%s: y must not alias x", fn);
   if (!moe::aligned16(x) || (add_in && !moe::aligned16(add_in)))
     return fail(MOE_EALIGN, "%s: x and add_in must be 16-byte aligned", fn);
@@ -354,7 +372,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   const bool rms = flags & MOE_F_RMSNORM_IN;
   const bool res = flags & MOE_F_RESIDUAL;
 
-  hipEvent_t pb = prof_begin(L, s);
+  hipEvent_t pb = prof_begin(L, 0, s);
   // resident mode: the router only produces logits; each gate/up block takes
   // the top-k itself (no cross-block handshake on the critical path)
   const bool in_kernel_topk = !L->cache_mode;
@@ -378,7 +396,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   if (grouped) {
     // batched: per-token top-k, stable sort of the B*k assignments by expert,
     // grouped GEMVs that read each touched expert once, ordered combine
-    hipEvent_t pt = prof_begin(L, s);
+    hipEvent_t pt = prof_begin(L, 0, s);
     HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, E, k, ids, w, ids_out, w_out, s), fn);
     const int A = B * k;
     int32_t* seg = L->at<int32_t>(L->ws.seg);
@@ -392,7 +410,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     uint16_t* act = L->at<uint16_t>(L->ws.act);
     moe::BatchedBuffers bb{seg, perm, pos_of, act, act + static_cast<size_t>(A) * sh.inter,
                            L->at<float>(L->ws.out_r), L->at<float>(L->ws.out_s)};
-    hipEvent_t p1 = prof_begin(L, s);
+    hipEvent_t p1 = prof_begin(L, 2, s);
     HIP_OR_FAIL(moe::launch_batched(bb, L->d.experts_dev, L->d.shared_blob, L->blob_e, H, sh.inter,
                                     sh.shared_inter, E, k, B, u16, tsc, w, x, add_in, res, y, s), fn);
     prof_end(L, 2, p1, s);
@@ -414,12 +432,12 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       G.w2 = w_out ? w_out + ko : nullptr;
       auto* adb = reinterpret_cast<moe::DigitGroup*>(adig + static_cast<size_t>(b) * npos);
       float* asb = asc + static_cast<size_t>(b) * npos;
-      const ProfPair p1 = prof_pair(L);
+      const ProfPair p1 = prof_pair(L, 2);
       HIP_OR_FAIL(moe::launch_ffn_gateup(G, true, true, udig + static_cast<size_t>(b) * ngu,
                                          usc + static_cast<size_t>(b) * ngu, adb, asb, s, p1.a, p1.b), fn);
       prof_add(L, 2, p1);
       S.ids = ids + ko;
-      const ProfPair p2 = prof_pair(L);
+      const ProfPair p2 = prof_pair(L, 3);
       HIP_OR_FAIL(moe::launch_ffn_down(S, w + ko, adb, asb, x + static_cast<size_t>(b) * H,
                                        add_in ? add_in + static_cast<size_t>(b) * H : nullptr, res,
                                        y + static_cast<size_t>(b) * H, s, p2.a, p2.b), fn);
@@ -432,10 +450,14 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   // ---- cache mode, one token
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
-  const ProfPair p1 = prof_pair(L);
   auto* adg = reinterpret_cast<moe::DigitGroup*>(adig);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b), fn);
-  prof_add(L, 1, p1);
+  if (!fill_kernel) {
+    // the shared-expert gate/up runs while the host waits for the ids and
+    // while the copy engine fills the misses
+    const ProfPair p1 = prof_pair(L, 1);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b), fn);
+    prof_add(L, 1, p1);
+  }
   if (!wait_routing(L)) return fail(MOE_EHIP, "%s: timed out waiting for the routing kernel", fn);
 
   // LFU step; the pre-step state is kept so that a failed copy enqueue leaves
@@ -445,27 +467,43 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   moe::cache_assign(L->cache_backup, L->cache);
   moe_status cs = moe_cache_step(L->cache, L->ids_host, k, ev, &n_miss);
   if (cs) return cs;
-  hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
   hipError_t ce = hipSuccess;
-  for (int j = 0; j < k && ce == hipSuccess; ++j) {
-    if (ev[j].hit) continue;
-    ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e,
-                        L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e, L->blob_e,
-                        hipMemcpyHostToDevice, cp);
-  }
-  if (ce == hipSuccess && n_miss > 0) {
-    ce = hipEventRecord(L->ev_fill, cp);
-    if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+  if (fill_kernel) {
+    // the misses are copied by fill blocks of the shared-expert gate/up launch
+    moe::FillList F{};
+    F.blocks_per_blob = 16;
+    F.bytes = L->blob_e;
+    for (int j = 0; j < k; ++j) {
+      if (ev[j].hit) continue;
+      F.src[F.n] = L->host_dev + static_cast<size_t>(ev[j].expert) * L->blob_e;
+      F.dst[F.n] = L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e;
+      ++F.n;
+    }
+    const ProfPair p1 = prof_pair(L, 1);
+    ce = moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
+    if (ce == hipSuccess) prof_add(L, 1, p1);
+  } else {
+    hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
+    for (int j = 0; j < k && ce == hipSuccess; ++j) {
+      if (ev[j].hit) continue;
+      ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e,
+                          L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e, L->blob_e,
+                          hipMemcpyHostToDevice, cp);
+    }
+    if (ce == hipSuccess && n_miss > 0) {
+      ce = hipEventRecord(L->ev_fill, cp);
+      if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+    }
   }
   if (ce != hipSuccess) {
     moe::cache_assign(L->cache, L->cache_backup);
     return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
   }
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
-  const ProfPair p2 = prof_pair(L);
+  const ProfPair p2 = prof_pair(L, 2);
   HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
   prof_add(L, 2, p2);
-  const ProfPair p3 = prof_pair(L);
+  const ProfPair p3 = prof_pair(L, 3);
   HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
   prof_add(L, 3, p3);
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
@@ -487,6 +525,7 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
   if (T < 0 || T > L->max_T) return fail(MOE_ESHAPE, "%s: T=%d outside [0, max_T=%d]", fn, T, L->max_T);
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !y) return fail(MOE_EINVAL, "%s: x_bf16 and y are required", fn);
+  L->prof_now = L->prof && (L->prof_calls++ % L->prof_every) == 0;
   if (!moe::aligned16(x_bf16)) return fail(MOE_EALIGN, "%s: x_bf16 must be 16-byte aligned", fn);
   const moe_shape& sh = L->sh;
   if (sh.inter % 64 || sh.shared_inter % 64 || sh.hidden % 128)
@@ -494,7 +533,7 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::PrefillLayout P = moe::prefill_layout(L->max_T, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                                    sh.shared_inter);
-  hipEvent_t pb = prof_begin(L, s);
+  hipEvent_t pb = prof_begin(L, 4, s);
   HIP_OR_FAIL(moe::launch_prefill(P, L->wsb + L->ws.pre, x_bf16, logits_in, L->d.router, L->d.bias, T,
                                   sh.n_experts, sh.top_k, sh.hidden, sh.inter, sh.shared_inter,
                                   L->d.experts_dev, L->blob_e, L->d.shared_blob, y, ids_out, w_out, s),
@@ -507,6 +546,28 @@ moe_status moe_layer_profile(moe_layer* L, int32_t enable) {
   moe::clear_error();
   if (!L) return fail(MOE_EINVAL, "moe_layer_profile: NULL handle");
   L->prof = enable != 0;
+  L->prof_mask = (1u << kProfKinds) - 1;
+  L->prof_every = 1;
+  return MOE_OK;
+}
+
+moe_status moe_layer_profile_kinds(moe_layer* L, uint32_t mask, int32_t every, int32_t reserve_events) {
+  moe::clear_error();
+  const char* fn = "moe_layer_profile_kinds";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (every < 1) return fail(MOE_EINVAL, "%s: every = %d, must be >= 1", fn, every);
+  if (mask >> kProfKinds) return fail(MOE_EINVAL, "%s: mask 0x%x has kinds beyond %d", fn, mask, kProfKinds - 1);
+  if (reserve_events < 0 || reserve_events > (1 << 20))
+    return fail(MOE_EINVAL, "%s: reserve_events %d outside [0, 2^20]", fn, reserve_events);
+  while (static_cast<int32_t>(L->pool.size()) < reserve_events) {
+    hipEvent_t e = nullptr;
+    HIP_OR_FAIL(hipEventCreate(&e), fn);
+    L->pool.push_back(e);
+  }
+  L->prof_mask = mask;
+  L->prof_every = static_cast<uint32_t>(every);
+  L->prof_calls = 0;
+  L->prof = mask != 0;
   return MOE_OK;
 }
 

@@ -107,7 +107,10 @@ __global__ __launch_bounds__(kChunk) void k_perm_scatter(const int32_t* __restri
 // block's 128 activation rows are staged in LDS per K step (double buffered)
 // and shared by its 8 waves. A wave owns two 16-row weight tiles (GATEUP: 16
 // gate rows and the matching 16 up rows; else 32 consecutive down rows) and
-// all 8 16-row token tiles, so each dequantised weight feeds 8 MFMAs.
+// all 8 16-row token tiles, so each dequantised weight feeds 8 MFMAs. (Four
+// tiles per wave halve the LDS reads per flop but need one wave per SIMD;
+// measured slower, 1.04 vs 0.83 ms, as dequant, LDS reads and MFMAs of one
+// wave then overlap too little.)
 //
 // K step = 4 quant groups (128 values). The lane of 16-lane row q loads group
 // 4*st + q of its weight row (16 bytes) and that group's scale; MFMA j of the
@@ -123,7 +126,8 @@ constexpr int kStage = kTM * 16 / kThreadsGemm;  // 16-byte activation chunks pe
 constexpr int kStepK = 4 * kGroup;       // 128
 constexpr int kBRow = kStepK * 2 + 16;   // LDS bytes per activation row of a step (padded)
 constexpr int kDepth = 4;
-constexpr int kMR = 2;
+constexpr int kMR = 2;                   // 16-row weight tiles per wave (GATEUP: half gate, half up)
+constexpr int kHalf = kMR / 2;
 
 // Byte B of x as a float (v_cvt_f32_ubyteB; written out because the compiler
 // folds the surrounding masks and then loses the byte-select forms).
@@ -204,7 +208,7 @@ struct GemmArgs {
 template <bool GATEUP, bool ROUTED>
 __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
-  constexpr int rows_per_block = GATEUP ? kWavesG * 16 : kWavesG * kMR * 16;
+  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
   const int nrows = GATEUP ? G.inter : G.H;
   const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
   const int mt = blockIdx.x / n_tiles_n;
@@ -233,16 +237,17 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = lane >> 4;
   const int l16 = lane & 15;
-  const int rbase = nt * rows_per_block + wave * (GATEUP ? 16 : kMR * 16);
+  const int rbase = nt * rows_per_block + wave * (GATEUP ? kHalf * 16 : kMR * 16);
   const bool live = rbase < nrows;  // waves past the last row only stage and sync
   const uint8_t* qrow[kMR];
   const uint16_t* srow[kMR];
 #pragma unroll
   for (int mr = 0; mr < kMR; ++mr) {
-    int row = (GATEUP ? rbase : rbase + 16 * mr) + l16;
+    int row = (GATEUP ? rbase + 16 * (mr % kHalf) : rbase + 16 * mr) + l16;
     row = live && row < nrows ? row : l16;
-    const size_t qo = GATEUP ? (mr == 0 ? o.gate_q : o.up_q) : o.down_q;
-    const size_t so = GATEUP ? (mr == 0 ? o.gate_s : o.up_s) : o.down_s;
+    const bool up = mr >= kHalf;
+    const size_t qo = GATEUP ? (up ? o.up_q : o.gate_q) : o.down_q;
+    const size_t so = GATEUP ? (up ? o.up_s : o.gate_s) : o.down_s;
     qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
     srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
   }
@@ -318,10 +323,12 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
+  static_assert(kDepth == 3 || kDepth == 4, "the step sequence below is written out for 3 or 4 slots");
+  constexpr int kD3 = kDepth > 3 ? 3 : 0;
   issue(0, w[0], bs[0]);
   issue(1, w[1], bs[1]);
   issue(2, w[2], bs[2]);
-  issue(3, w[3], bs[3]);
+  if constexpr (kDepth > 3) issue(3, w[kD3], bs[kD3]);
   stage_store(0, bs[0]);
   __syncthreads();
   int s0 = 0;
@@ -329,12 +336,12 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
     step(std::integral_constant<int, 0>{}, s0, false);
     step(std::integral_constant<int, 1>{}, s0, false);
     step(std::integral_constant<int, 2>{}, s0, false);
-    step(std::integral_constant<int, 3>{}, s0, false);
+    if constexpr (kDepth > 3) step(std::integral_constant<int, kD3>{}, s0, false);
   }
-  if (s0 < nsteps) {
+  if (s0 < nsteps) {  // the last 1..kDepth-1 steps
     step(std::integral_constant<int, 0>{}, s0, true);
     step(std::integral_constant<int, 1>{}, s0, true);
-    step(std::integral_constant<int, 2>{}, s0, true);
+    if constexpr (kDepth > 3) step(std::integral_constant<int, 2>{}, s0, true);
   }
 
   // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token row
@@ -344,11 +351,15 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
     const int m = r0 + tt * 16 + l16;
     if (m >= r_end || !live) continue;
     if (GATEUP) {
-      __attribute__((aligned(8))) __bf16 av[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = static_cast<__bf16>(gelu_tanh(acc[0][tt][i]) * acc[1][tt][i]);
-      *reinterpret_cast<uint2*>(G.act + static_cast<size_t>(m) * G.inter + rbase + 4 * q) =
-          *reinterpret_cast<const uint2*>(av);
+      for (int mr = 0; mr < kHalf; ++mr) {
+        __attribute__((aligned(8))) __bf16 av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          av[i] = static_cast<__bf16>(gelu_tanh(acc[mr][tt][i]) * acc[mr + kHalf][tt][i]);
+        *reinterpret_cast<uint2*>(G.act + static_cast<size_t>(m) * G.inter + rbase + 16 * mr + 4 * q) =
+            *reinterpret_cast<const uint2*>(av);
+      }
     } else {
 #pragma unroll
       for (int mr = 0; mr < kMR; ++mr) {
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
 // Blocks along the weight rows of one GEMM (gate/up: row pairs; down: rows).
 int gemm_row_tiles(bool gateup, int H, int inter) {
   const int rows = gateup ? inter : H;
-  const int per = gateup ? kWavesG * 16 : kWavesG * kMR * 16;
+  const int per = gateup ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
   return (rows + per - 1) / per;
 }
 

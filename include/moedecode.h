@@ -184,6 +184,12 @@ typedef struct moe_decode_stats {
 
 #define MOE_F_RMSNORM_IN 1u /* u = x' / sqrt(mean(x'^2) + 1e-6) feeds router and FFN */
 #define MOE_F_RESIDUAL 2u   /* y = x' + MoE(u) instead of y = MoE(u)                 */
+/* Cache mode: the misses are copied from experts_host to their slots by fill
+ * blocks that run in the same launch as the shared-expert gate/up, on the
+ * call's stream, after the LFU step (no copy engine, no copy_stream, no
+ * cross-stream event). experts_host must then be device-accessible pinned
+ * memory (hipHostMalloc); copy_stream is unused. Same cache trace, same bits. */
+#define MOE_F_FILL_KERNEL 4u
 
 /* Workspace for up to max_B decode tokens per call and max_T prefill tokens. */
 moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
@@ -201,7 +207,8 @@ moe_cache* moe_layer_cache(moe_layer* L);
 /* Decode B tokens through the layer.
  *   x       dev fp32 [B][H] layer input
  *   add_in  dev fp16 [B][H] added first, x' = x + add_in, or NULL (x' = x)
- *   flags   MOE_F_RMSNORM_IN | MOE_F_RESIDUAL (u = x' without RMSNORM_IN)
+ *   flags   MOE_F_RMSNORM_IN | MOE_F_RESIDUAL (u = x' without RMSNORM_IN),
+ *           MOE_F_FILL_KERNEL (cache mode only)
  *   y       dev fp32 [B][H] output; must not alias x
  *   ids_out dev int32 [B][k], w_out dev fp32 [B][k], u_out dev fp32 [B][H]:
  *           optional copies of the routing and of u (NULL to skip)
@@ -210,7 +217,9 @@ moe_cache* moe_layer_cache(moe_layer* L);
  * Resident mode is asynchronous on stream. Cache mode requires B == 1 and
  * blocks the calling thread once, until the token's ids are on the host; it
  * returns with the miss copies and the expert kernels enqueued (the copies on
- * copy_stream, ordered before the expert kernels by an event). */
+ * copy_stream, ordered before the expert kernels by an event; with
+ * MOE_F_FILL_KERNEL the copies are fill blocks of the shared-expert launch on
+ * stream). */
 moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in, int32_t B,
                             uint32_t flags, float* y, int32_t* ids_out, float* w_out, float* u_out,
                             moe_cache_event* trace, moe_decode_stats* stats, void* stream);
@@ -228,6 +237,8 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
  * launch stream while profiling is enabled: the one-kernel stages 1-3 of the
  * one-token paths take events stamped by the kernel's own dispatch (start and
  * end of the kernel); the other stages take events recorded around them.
+ * The stamps bracket the dispatch, so a stage is charged a little more than
+ * the kernel-execution time a kernel trace reports (about 1 us at B=1).
  * kind: 0 = routing (input prep, logits, top-k), 1 = shared-expert gate/up
  * launched ahead of the miss copies (cache mode), 2 = gate/up of the routed
  * experts (resident mode: together with the shared expert), 3 = down
@@ -238,6 +249,11 @@ typedef struct moe_kernel_time {
   double ms_total;
 } moe_kernel_time;
 moe_status moe_layer_profile(moe_layer* L, int32_t enable);
+/* Profile only the kinds in mask (bit i = kind i; 0 turns profiling off), on
+ * one call in `every` (>= 1), and pre-create reserve_events events (0..2^20),
+ * so that a timed region pays neither for event creation (two events per
+ * profiled stage and call) nor for timing every call. */
+moe_status moe_layer_profile_kinds(moe_layer* L, uint32_t mask, int32_t every, int32_t reserve_events);
 moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* out);
 
 /* ---------------------------------------------------------------- test support

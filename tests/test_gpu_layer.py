@@ -95,8 +95,9 @@ def test_norm_residual_perturbation(shape, cid):
     L.close()
 
 
+@pytest.mark.parametrize("fill", [0, api.MOE_F_FILL_KERNEL], ids=["copy_engine", "fill_kernel"])
 @pytest.mark.parametrize("shape,cid,slots,tokens", [(SMALL_LAYER, 0, 10, 60), (GEMMA_LAYER, 2, 16, 10)])
-def test_cache_mode_trace_and_output(shape, cid, slots, tokens):
+def test_cache_mode_trace_and_output(shape, cid, slots, tokens, fill):
     d = layer_data(shape, cid)
     bias = gen.zipf_bias(shape.n_experts, cid, 0)
     L = Layer(shape, d, bias=bias, cache_slots=slots)
@@ -105,7 +106,7 @@ def test_cache_mode_trace_and_output(shape, cid, slots, tokens):
     stats = api.moe_decode_stats()
     check = set(range(0, tokens, max(1, tokens // 6))) | {tokens - 1}
     for t in range(tokens):
-        y, ids, w, u, tr = run_decode(L, dev(xs[t:t + 1]), trace_k=shape.top_k, stats=stats)
+        y, ids, w, u, tr = run_decode(L, dev(xs[t:t + 1]), flags=fill, trace_k=shape.top_k, stats=stats)
         r_ids, r_w, _ = moe.route(xs[t:t + 1].astype(np.float64), d["router"], shape.top_k, bias)
         assert np.array_equal(ids, r_ids), t
         want = sim.step(ids[0])
@@ -124,6 +125,34 @@ def test_cache_mode_trace_and_output(shape, cid, slots, tokens):
             assert np.array_equal(pool[s_], d["experts"][e]), (s_, e)
     ex, fr, la = api.moe_cache_slots(api.moe_layer_cache(L.h), slots)
     assert ex.tolist() == sim.expert and fr.tolist() == sim.freq
+    L.close()
+
+
+def test_fill_kernel_matches_copy_engine_bitwise():
+    """Both fill paths leave the same slots and give the same bits."""
+    sh = GEMMA_LAYER
+    d = layer_data(sh, 2)
+    bias = gen.zipf_bias(sh.n_experts, 2, 0)
+    La = Layer(sh, d, bias=bias, cache_slots=16)
+    Lb = Layer(sh, d, bias=bias, cache_slots=16)
+    xs = gen.x_fp32(6, sh.hidden, 2, sub=12)
+    for t in range(6):
+        ya, ida, _, _, tra = run_decode(La, dev(xs[t:t + 1]), trace_k=sh.top_k)
+        yb, idb, _, _, trb = run_decode(Lb, dev(xs[t:t + 1]), flags=api.MOE_F_FILL_KERNEL, trace_k=sh.top_k)
+        assert np.array_equal(ida, idb) and np.array_equal(tra, trb), t
+        assert np.array_equal(ya, yb), t
+    assert np.array_equal(La.pool.cpu().numpy(), Lb.pool.cpu().numpy())
+    La.close()
+    Lb.close()
+
+
+def test_fill_kernel_needs_cache_mode():
+    sh = SMALL_LAYER
+    d = layer_data(sh, 0)
+    L = Layer(sh, d)
+    y = poisoned((1, sh.hidden))
+    with pytest.raises(api.MoeError):
+        api.moe_layer_decode(L.h, dev(gen.x_fp32(1, sh.hidden, 0)), None, 1, api.MOE_F_FILL_KERNEL, y)
     L.close()
 
 
