@@ -31,16 +31,22 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 // ---------------------------------------------------------------- routing
 // Layer router, one launch: x' = x (+ add_in); u = x' or rmsnorm(x'); u's
 // digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
-// finish. cnt must be zero before the launch and is zero after it.
-// Grid: (E/4 blocks) x B tokens; the top-k variant (ids != nullptr) needs B == 1.
-// With seq_host (top-k variant only) the last block also writes the ids to
-// ids_host (host-coherent memory) and then seq to *seq_host (system-scope
-// release), so the host can wait for them without a copy or an event.
+// finish. Grid: (E/4 blocks) x B tokens. cnt holds B + 1 arrival counters
+// (B per-token, one for the sort), zero before the launch and after it.
+// Top-k variant (ids != nullptr): the last block of each token's grid row
+// takes that token's top-k. With seq_host (B == 1 only) it also writes the
+// ids to ids_host (host-coherent memory) and then seq to *seq_host
+// (system-scope release), so the host can wait for them without a copy or an
+// event. With seg/perm/pos_of (top-k variant) the block whose token finishes
+// last sorts the B*k assignments a = token*k + rank stably by expert:
+// seg[e]..seg[e+1] is expert e's range of sorted positions, perm[p] the
+// assignment at position p and pos_of[a] its position.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s);
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, int32_t* seg,
+                              int32_t* perm, int32_t* pos_of, hipStream_t s);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);

@@ -62,7 +62,7 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.w = take(B * k * 4);
   L.adig = take(B * npos * 16);
   L.asc = take(B * npos * 4);
-  L.cnt = take(256);  // router arrival counter
+  L.cnt = take((B + 1) * 4);  // router arrival counters: one per token, one for the sort
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
@@ -277,7 +277,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     moe_layer_destroy(L);
     return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
   };
-  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, 256);
+  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, (static_cast<size_t>(max_B) + 1) * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
@@ -373,14 +373,19 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   const bool res = flags & MOE_F_RESIDUAL;
 
   hipEvent_t pb = prof_begin(L, 0, s);
-  // resident mode: the router only produces logits; each gate/up block takes
-  // the top-k itself (no cross-block handshake on the critical path)
-  const bool in_kernel_topk = !L->cache_mode;
   // grouped path (B > 1, all experts resident): every touched expert is read
-  // once per call by the matrix-core kernels, which take fp16 inputs
+  // once per call by the matrix-core kernels, which take fp16 inputs; the
+  // router also takes each token's top-k and sorts the B*k assignments by
+  // expert
   const bool grouped = !L->cache_mode && B > 1;
+  // one token, resident: the router only produces logits; each gate/up block
+  // takes the top-k itself (no cross-block handshake on the critical path)
+  const bool in_kernel_topk = !L->cache_mode && !grouped;
   uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
   float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
+  int32_t* seg = grouped ? L->at<int32_t>(L->ws.seg) : nullptr;
+  int32_t* perm = grouped ? L->at<int32_t>(L->ws.perm) : nullptr;
+  int32_t* pos_of = grouped ? L->at<int32_t>(L->ws.pos_of) : nullptr;
   const int32_t seq = L->cache_mode ? L->seq + 1 : 0;
   HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
                                       grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
@@ -388,25 +393,14 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                                       in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
                                       in_kernel_topk ? nullptr : w_out,
                                       L->cache_mode ? L->ids_host : nullptr,
-                                      L->cache_mode ? L->seq_host : nullptr, seq, s), fn);
+                                      L->cache_mode ? L->seq_host : nullptr, seq, seg, perm, pos_of, s), fn);
   if (L->cache_mode) L->seq = seq;
   prof_end(L, 0, pb, s);
 
   moe::SourceSet S = make_sources(L);
   if (grouped) {
-    // batched: per-token top-k, stable sort of the B*k assignments by expert,
-    // grouped GEMVs that read each touched expert once, ordered combine
-    hipEvent_t pt = prof_begin(L, 0, s);
-    HIP_OR_FAIL(moe::launch_route_topk(z, nullptr, B, E, k, ids, w, ids_out, w_out, s), fn);
+    // batched: grouped GEMVs that read each touched expert once, ordered combine
     const int A = B * k;
-    int32_t* seg = L->at<int32_t>(L->ws.seg);
-    int32_t* perm = L->at<int32_t>(L->ws.perm);
-    int32_t* pos_of = L->at<int32_t>(L->ws.pos_of);
-    HIP_OR_FAIL(moe::launch_permute(ids, A, E, L->ws.chunks, L->at<int32_t>(L->ws.hist),
-                                    L->at<int32_t>(L->ws.lrank), L->at<int32_t>(L->ws.base), seg,
-                                    L->at<int2>(L->ws.tiles), L->at<int32_t>(L->ws.n_tiles), perm, pos_of,
-                                    s), fn);
-    prof_end(L, 0, pt, s);
     uint16_t* act = L->at<uint16_t>(L->ws.act);
     moe::BatchedBuffers bb{seg, perm, pos_of, act, act + static_cast<size_t>(A) * sh.inter,
                            L->at<float>(L->ws.out_r), L->at<float>(L->ws.out_s)};

@@ -37,7 +37,17 @@ __device__ inline void topk_block(const double* zs, int E, int k, double* sel_z,
     int rank = 0;
     const int f0 = part * per;
     const int f1 = f0 + per < E ? f0 + per : E;
-    for (int f = f0; f < f1; ++f) rank += key_better(zs[f], f, v, e) ? 1 : 0;
+    // eight logits per batch, so that the batch's LDS reads are in flight
+    // together instead of one read latency per comparison
+    int f = f0;
+    for (; f + 8 <= f1; f += 8) {
+      double zf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zf[i] = zs[f + i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rank += key_better(zf[i], f + i, v, e) ? 1 : 0;
+    }
+    for (; f < f1; ++f) rank += key_better(zs[f], f, v, e) ? 1 : 0;
     for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
     if (valid && part == 0 && rank < k) {
       sel_z[rank] = v;

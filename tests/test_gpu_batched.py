@@ -35,9 +35,10 @@ def decode(L, x, flags=0, add_in=None):
 
 # B covers one ragged token tile (5, 7), exactly one tile (16), two and four
 # tiles per pass (33, 64) and a shared segment of more than 64 tokens, which
-# takes two passes over the weights (100); the tiny shape has K tails (2 of the
+# takes two passes over the weights (100), and 160 tokens (1280 assignments:
+# top-k and sort in separate launches instead of one block); the tiny shape has K tails (2 of the
 # 4 groups of a step are past K) and idle waves (32 rows per block of 64)
-@pytest.mark.parametrize("shape,cid,B", [(SMALL_LAYER, 0, 5), (SMALL_LAYER, 0, 16), (SMALL_LAYER, 0, 100),
+@pytest.mark.parametrize("shape,cid,B", [(SMALL_LAYER, 0, 5), (SMALL_LAYER, 0, 16), (SMALL_LAYER, 0, 100), (SMALL_LAYER, 0, 160),
                                          (TINY_LAYER, 99, 7), (GEMMA_LAYER, 3, 16), (GEMMA_LAYER, 3, 33),
                                          (GEMMA_LAYER, 3, 64)])
 def test_batched_decode_matches_per_token_oracle(shape, cid, B):
