@@ -37,6 +37,7 @@
 // assignment; the combine adds, per token and in rank order, w_j times its
 // routed rows to the shared expert's row (and the residual).
 #include <type_traits>
+#include <utility>
 
 #include "launch.h"
 
@@ -90,34 +91,37 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 }
 
 struct WStep {
-  uint4 q[kMR];       // group 4*st + q (16-lane row q of the wave) of the lane's row
-  uint32_t s[kMR];    // its fp16 scale
+  u32x4 q[kMR];  // group 4*st + q (16-lane row q of the wave) of the lane's row
 };
 
 // Weights of K step st: group 4*st + q of the lane's row in each tile (16
 // bytes; a 16-lane row of the wave reads 64 contiguous bytes of each of its 16
-// weight rows) and that group's scale. Groups past K are clamped to the last
-// one (their scale is zeroed when used). No loaded value is used here, so the
-// loads stay in flight.
-__device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow,
-                                          const uint16_t* const* srow, int ngk, int st, int q) {
+// weight rows). Groups past K are clamped to the last one (their scale is
+// zeroed when used). No loaded value is used here, so the loads stay in
+// flight. The scales come from LDS (staged once per block).
+__device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow, int ngk, int st, int q) {
   int g = 4 * st + q;
   g = g < ngk ? g : ngk - 1;
 #pragma unroll
-  for (int m = 0; m < kMR; ++m) {
+  for (int m = 0; m < kMR; ++m)
     // cached load: the other half of each 128-byte line is read one step later
-    b.q[m] = *reinterpret_cast<const uint4*>(qrow[m] + 16 * static_cast<size_t>(g));
-    b.s[m] = srow[m][g];
-  }
+    b.q[m] = *reinterpret_cast<const u32x4*>(qrow[m] + 16 * static_cast<size_t>(g));
 }
 
 // One launch covers all segments: tiles_r blocks per routed expert (blocks of
 // untouched experts exit at once), then tiles_s blocks of the shared expert.
 // GATEUP: a wave's weight tiles are 16 gate rows and the 16 matching up rows;
 // else 32 consecutive down rows. NTT 16-token tiles share one pass over K.
+// f(integral_constant<int, D>) for D = 0, 1, ...: ring slots as compile-time
+// constants, so the ring stays in registers
+template <class F, int... D>
+__device__ __forceinline__ void for_slots(std::integer_sequence<int, D...>, F&& f) {
+  (f(std::integral_constant<int, D>{}), ...);
+}
+
 template <bool GATEUP, int NTT, int DEPTH>
 __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
-  static_assert(DEPTH == 3 || DEPTH == 4, "the step sequence below is written out for 3 or 4 slots");
+  static_assert(DEPTH >= 2 && DEPTH <= 8, "ring of 2..8 load units");
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][NTT * kTile * kBRow];
   int s, tile;
   {
@@ -144,15 +148,28 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   const int rbase = (tile * kWaves + wave) * (GATEUP ? kTile : kMR * kTile);
   const bool live = rbase < nrows;
   const uint8_t* qrow[kMR];
-  const uint16_t* srow[kMR];
+  // The wave's scales, [kMR][16 rows][ngk], staged once: a tile's 16 rows
+  // are consecutive, so its scales are one contiguous run of 32*ngk bytes,
+  // read in 16-byte chunks (per step, scattered 2-byte loads would touch 16
+  // cache lines per instruction for 128 bytes). Chunks are clamped to the
+  // matrix's scale array; rows past it (and idle waves, which take the first
+  // tile) get finite scales of other rows, whose results are not stored.
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_scales[];
+  uint16_t* ssc = reinterpret_cast<uint16_t*>(lds_scales) + static_cast<size_t>(wave) * kMR * kTile * ngk;
 #pragma unroll
   for (int mr = 0; mr < kMR; ++mr) {
-    int row = (GATEUP ? rbase : rbase + kTile * mr) + l16;
+    const int t0r = GATEUP ? rbase : rbase + kTile * mr;  // first row of the tile
+    const int t0 = live && t0r < nrows ? t0r : 0;
+    int row = t0 + l16;
     row = live && row < nrows ? row : l16;
     const size_t qo = GATEUP ? (mr == 0 ? o.gate_q : o.up_q) : o.down_q;
     const size_t so = GATEUP ? (mr == 0 ? o.gate_s : o.up_s) : o.down_s;
     qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
-    srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
+    const u32x4* src = reinterpret_cast<const u32x4*>(blob + so + static_cast<size_t>(t0) * ngk * 2);
+    u32x4* dst = reinterpret_cast<u32x4*>(ssc + mr * kTile * ngk);
+    const int t_rows = nrows - t0 < kTile ? nrows - t0 : kTile;  // 16: nrows, t0 multiples of 16
+    const int cmax = t_rows * ngk / 8 - 1;                       // last chunk inside the scale array
+    for (int c = lane; c < 2 * ngk; c += kWave) dst[c] = src[c < cmax ? c : cmax];
   }
 
   for (int p0 = 0; p0 < m; p0 += NTT * kTile) {
@@ -182,25 +199,28 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) acc[mr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Load unit y = (activation slice of step y, weights of step y), issued in
-    // that order DEPTH steps ahead into ring slot y % DEPTH. Loads retire in
-    // issue order, so waiting for the slice of step x+1 (stored to LDS during
-    // step x) only waits for units issued at least DEPTH-1 steps earlier.
-    // Every ring index below is a compile-time constant, so the ring lives
-    // in registers.
+    // Load unit y = (activation slice of step y+1, weights of step y), issued
+    // in that order DEPTH steps ahead into ring slot y % DEPTH. Step x needs
+    // its weights and stores the slice of step x+1 to LDS, both from unit x:
+    // as loads retire in issue order, a step waits for its own unit only and
+    // the DEPTH-1 later units stay in flight. Every ring index below is a
+    // compile-time constant, so the ring lives in registers.
     WStep w[DEPTH];
     u32x4 bs[DEPTH][NTT];
-    // st past the last step re-reads the last step: every step issues the
-    // same loads, so the wait counts are the same on every path
-    auto issue = [&](int st, WStep& wd, u32x4* bd) __attribute__((always_inline)) {
-      st = st < nsteps ? st : nsteps - 1;
+    auto load_slice = [&](int st, u32x4* bd) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < NTT; ++r) {
         int kk = st * kStepK + boff[r];
         kk = kk < K ? kk : K - 8;  // past the end: any finite values (their weights are 0)
         bd[r] = *reinterpret_cast<const u32x4*>(brow[r] + kk);
       }
-      load_step(wd, qrow, srow, ngk, st, q);
+    };
+    // st past the last step re-reads the last step: every step issues the
+    // same loads, so the wait counts are the same on every path
+    auto issue = [&](int st, WStep& wd, u32x4* bd) __attribute__((always_inline)) {
+      st = st < nsteps ? st : nsteps - 1;
+      load_slice(st + 1 < nsteps ? st + 1 : nsteps - 1, bd);
+      load_step(wd, qrow, ngk, st, q);
     };
     auto stage_store = [&](int bi, const u32x4* bd) __attribute__((always_inline)) {
 #pragma unroll
@@ -210,31 +230,31 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
       constexpr int D = decltype(slot)::value;
       const int st = s0 + D;
       if (tail && st >= nsteps) return;  // uniform over the block
-      stage_store((st + 1) & 1, bs[(D + 1) % DEPTH]);  // past the end: unused
+      stage_store((st + 1) & 1, bs[D]);  // past the end: unused
       const uint8_t* lb = lds_b[st & 1];
       // MFMA j takes dword j (8 nibbles) of every lane's group: the 4
       // 16-lane rows contribute groups 4*st .. 4*st+3, each dequantised with
       // its own scale, and the activations at the same positions
       const bool gv = 4 * st + q < ngk;  // groups past K weigh 0
-      f16x8 a[kMR][4];
+      const int gs = gv ? 4 * st + q : ngk - 1;
+      _Float16 sc[kMR];
 #pragma unroll
-      for (int mr = 0; mr < kMR; ++mr) {
-        const _Float16 sc = gv ? __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[D].s[mr]))
-                               : static_cast<_Float16>(0.0f);
-        a[mr][0] = dequant8(w[D].q[mr].x, sc);
-        a[mr][1] = dequant8(w[D].q[mr].y, sc);
-        a[mr][2] = dequant8(w[D].q[mr].z, sc);
-        a[mr][3] = dequant8(w[D].q[mr].w, sc);
-      }
+      for (int mr = 0; mr < kMR; ++mr)
+        sc[mr] = gv ? __builtin_bit_cast(_Float16, ssc[(mr * kTile + l16) * ngk + gs]) : static_cast<_Float16>(0.0f);
+      // dequantised one dword (K slice of the MFMA) at a time: few live
+      // operand registers leave room for a deeper load ring
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        f16x8 a[kMR];
+#pragma unroll
+        for (int mr = 0; mr < kMR; ++mr) a[mr] = dequant8(w[D].q[mr][j], sc[mr]);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
           if (tt * kTile < mt) {
             const f16x8 bv = *reinterpret_cast<const f16x8*>(lb + (tt * kTile + l16) * kBRow + 64 * q + 16 * j);
 #pragma unroll
             for (int mr = 0; mr < kMR; ++mr)
-              acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mr][j], bv, acc[mr][tt], 0, 0, 0);
+              acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mr], bv, acc[mr][tt], 0, 0, 0);
           }
         }
       }
@@ -245,26 +265,25 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
-    issue(0, w[0], bs[0]);
-    issue(1, w[1], bs[1]);
-    issue(2, w[2], bs[2]);
-    if constexpr (DEPTH > 3) issue(3, w[DEPTH > 3 ? 3 : 0], bs[DEPTH > 3 ? 3 : 0]);
-    stage_store(0, bs[0]);
+    {
+      u32x4 b0[NTT];  // the slice of step 0, ahead of the ring
+      load_slice(0, b0);
+      for_slots(std::make_integer_sequence<int, DEPTH>{}, [&](auto slot) __attribute__((always_inline)) {
+        constexpr int D = decltype(slot)::value;
+        issue(D, w[D], bs[D]);
+      });
+      stage_store(0, b0);
+    }
     __syncthreads();
     // whole groups of DEPTH steps: straight-line code with the same loads on
     // every path, so each wait is only for the unit it needs
     int s0 = 0;
-    for (; s0 + DEPTH <= nsteps; s0 += DEPTH) {
-      step(std::integral_constant<int, 0>{}, s0, false);
-      step(std::integral_constant<int, 1>{}, s0, false);
-      step(std::integral_constant<int, 2>{}, s0, false);
-      if constexpr (DEPTH > 3) step(std::integral_constant<int, (DEPTH > 3 ? 3 : 0)>{}, s0, false);
-    }
-    if (s0 < nsteps) {  // the last 1..DEPTH-1 steps
-      step(std::integral_constant<int, 0>{}, s0, true);
-      step(std::integral_constant<int, 1>{}, s0, true);
-      step(std::integral_constant<int, 2>{}, s0, true);
-    }
+    for (; s0 + DEPTH <= nsteps; s0 += DEPTH)
+      for_slots(std::make_integer_sequence<int, DEPTH>{},
+                [&](auto slot) __attribute__((always_inline)) { step(slot, s0, false); });
+    if (s0 < nsteps)  // the last 1..DEPTH-1 steps
+      for_slots(std::make_integer_sequence<int, DEPTH - 1>{},
+                [&](auto slot) __attribute__((always_inline)) { step(slot, s0, true); });
 
     // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token
     // column l16 of each token tile (columns past mt hold garbage, unused)
@@ -328,16 +347,30 @@ __global__ void k_bcombine(const float* __restrict__ out_s, const float* __restr
   }
 }
 
+// LDS of one k_mfma block: the double-buffered activation slices (static)
+// and the staged scales of its 4 waves (dynamic, 2 tiles x 16 rows x K/32).
+size_t mfma_static_lds(int ntt) { return 2 * static_cast<size_t>(ntt) * kTile * kBRow; }
+size_t mfma_scale_lds(int K) { return static_cast<size_t>(kWaves) * kMR * kTile * (K / kGroup) * 2; }
+int tiles_per_pass(int B) { return B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4); }
+constexpr size_t kMaxBlockLds = 65536;
+
 template <bool GATEUP>
 hipError_t launch_mfma(const MArgs& A, int ntt, hipStream_t s) {
   const dim3 grid(A.E * A.tiles_r + A.tiles_s);
-  if (ntt <= 1) hipLaunchKernelGGL((k_mfma<GATEUP, 1, 4>), grid, dim3(kThreads), 0, s, A);
-  else if (ntt == 2) hipLaunchKernelGGL((k_mfma<GATEUP, 2, 4>), grid, dim3(kThreads), 0, s, A);
-  else hipLaunchKernelGGL((k_mfma<GATEUP, 4, 3>), grid, dim3(kThreads), 0, s, A);
+  const size_t lds = mfma_scale_lds(GATEUP ? A.H : (A.I > A.Is ? A.I : A.Is));
+  if (mfma_static_lds(ntt) + lds > kMaxBlockLds) return hipErrorInvalidValue;
+  if (ntt <= 1) hipLaunchKernelGGL((k_mfma<GATEUP, 1, 4>), grid, dim3(kThreads), lds, s, A);
+  else if (ntt == 2) hipLaunchKernelGGL((k_mfma<GATEUP, 2, 4>), grid, dim3(kThreads), lds, s, A);
+  else hipLaunchKernelGGL((k_mfma<GATEUP, 4, 3>), grid, dim3(kThreads), lds, s, A);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool batched_lds_fits(int H, int I, int Is, int max_B) {
+  const size_t st = mfma_static_lds(tiles_per_pass(max_B));
+  return st + mfma_scale_lds(H) <= kMaxBlockLds && st + mfma_scale_lds(I > Is ? I : Is) <= kMaxBlockLds;
+}
 
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
@@ -347,7 +380,7 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
           bb.act_r, bb.act_s, bb.out_r, bb.out_s, 0, 0};
   // tokens per pass over a segment's weights: up to 64; a larger shared or
   // expert segment takes several passes
-  const int ntt = B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4);
+  const int ntt = tiles_per_pass(B);
   // gate/up: 64 row pairs per block
   A.tiles_r = (I + kWaves * kTile - 1) / (kWaves * kTile);
   A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile);

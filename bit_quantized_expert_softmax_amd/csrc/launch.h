@@ -143,6 +143,9 @@ struct BatchedBuffers {
 };
 // Grouped gate/up and down products over the expert segments on the matrix
 // cores (inputs: u16/tsc of launch_route_layer), then the combine.
+// Whether the matrix-core kernels' LDS (activation slices for up to max_B
+// tokens per pass plus the staged scales of a block's rows) fits one block.
+bool batched_lds_fits(int H, int I, int Is, int max_B);
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
                           const uint16_t* u16, const float* tsc, const float* w, const float* x,

@@ -7,50 +7,72 @@
 
 namespace moe {
 
-__device__ __forceinline__ bool key_better(double v1, int e1, double v2, int e2) {
-  return v1 > v2 || (v1 == v2 && e1 < e2);
+// Order-preserving 64-bit key of an fp64 logit: the unsigned order of the
+// keys is the numeric order of the logits (-0 is taken as +0; a NaN gets key
+// 0, below every number), so the rank loop compares integers instead of fp64
+// values (measured faster on gfx950).
+__device__ __forceinline__ unsigned long long logit_key(double z) {
+  if (z != z) return 0ull;
+  const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(z + 0.0));
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double key_logit(unsigned long long key) {
+  const unsigned long long b = (key >> 63) ? (key & 0x7FFFFFFFFFFFFFFFull) : ~key;
+  return __longlong_as_double(static_cast<long long>(b));
+}
+
+// (key f, expert f) ranks before (key e, expert e): a larger key, or the same
+// key and a lower expert id. Keys as (low word, high word).
+__device__ __forceinline__ bool key_better(uint2 kf, int f, uint2 ke, int e) {
+  const unsigned long long a = static_cast<unsigned long long>(kf.y) << 32 | kf.x;
+  const unsigned long long b = static_cast<unsigned long long>(ke.y) << 32 | ke.x;
+  return a > b || (a == b && f < e);
 }
 
 // Top-k of E logits held in LDS (zs), by rank: an expert's rank is the number
-// of experts with a larger (z, -id) key; ranks below k are the selection in
-// rank order. Writes ids / w (and the optional copies). All block threads call.
-__device__ inline void topk_block(const double* zs, int E, int k, double* sel_z, int* sel_e,
-                           int32_t* ids, float* w, int32_t* ids2, float* w2) {
+// of experts ranking before it; ranks below k are the selection in rank order.
+// zs is overwritten with the logits' keys. Writes ids / w (and the optional
+// copies). All block threads call.
+__device__ inline void topk_block(double* zs, int E, int k, double* sel_z, int* sel_e,
+                                  int32_t* ids, float* w, int32_t* ids2, float* w2) {
   // every rank slot starts with a valid id, so non-finite logits cannot
   // produce an out-of-range expert index downstream
   if (threadIdx.x < static_cast<unsigned>(k)) {
     sel_e[threadIdx.x] = threadIdx.x;
     sel_z[threadIdx.x] = 0.0;
   }
+  // each thread converts the logits it reads back, so no barrier between
+  unsigned long long* kz64 = reinterpret_cast<unsigned long long*>(zs);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) kz64[e] = logit_key(zs[e]);
   __syncthreads();
-  // P threads share one expert's comparisons (P = largest power of two with
-  // P * E <= blockDim, at most 8); their partial ranks are summed in-wave
+  const uint2* kz = reinterpret_cast<const uint2*>(zs);
+  // P threads (adjacent lanes) share one expert's comparisons (P = largest
+  // power of two with P * E <= blockDim, at most 8); part p takes the keys
+  // p, p + P, ..., so at each step the parts of a wave read adjacent words
+  // (no bank conflicts) and the experts of a part share one address
   int P = 1;
   while (P < 8 && 2 * P * E <= static_cast<int>(blockDim.x)) P *= 2;
-  const int per = (E + P - 1) / P;
   for (int t0 = 0; t0 < E * P; t0 += blockDim.x) {
     const int t = t0 + threadIdx.x;
     const int e = t / P;
     const int part = t % P;
     const bool valid = e < E;
-    const double v = zs[valid ? e : 0];
+    const uint2 ke = kz[valid ? e : 0];
     int rank = 0;
-    const int f0 = part * per;
-    const int f1 = f0 + per < E ? f0 + per : E;
-    // eight logits per batch, so that the batch's LDS reads are in flight
-    // together instead of one read latency per comparison
-    int f = f0;
-    for (; f + 8 <= f1; f += 8) {
-      double zf[8];
+    // eight keys per batch, so that the batch's LDS reads are in flight together
+    int f = part;
+    for (; f + 7 * P < E; f += 8 * P) {
+      uint2 kf[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) zf[i] = zs[f + i];
+      for (int i = 0; i < 8; ++i) kf[i] = kz[f + i * P];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rank += key_better(zf[i], f + i, v, e) ? 1 : 0;
+      for (int i = 0; i < 8; ++i) rank += key_better(kf[i], f + i * P, ke, e) ? 1 : 0;
     }
-    for (; f < f1; ++f) rank += key_better(zs[f], f, v, e) ? 1 : 0;
+    for (; f < E; f += P) rank += key_better(kz[f], f, ke, e) ? 1 : 0;
     for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
     if (valid && part == 0 && rank < k) {
-      sel_z[rank] = v;
+      sel_z[rank] = key_logit(static_cast<unsigned long long>(ke.y) << 32 | ke.x);
       sel_e[rank] = e;
     }
   }
