@@ -156,6 +156,54 @@ __device__ void sort_by_expert(const RouteArgs& A, unsigned long long* mk) {
   }
 }
 
+// Top-k variant, after the block's logit stores (agent scope): the block
+// bumps its token's counter; the last of the token's gridDim.x blocks takes
+// the token's top-k (and publishes it to the host, B == 1); with a sort, the
+// block whose token completes last sorts the assignments. All threads call.
+__device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
+  int& is_last = *is_last_p;
+  const int nb = gridDim.x;
+  // every logit store of this block has completed before the block arrives
+  const int tok = blockIdx.y;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == nb - 1;
+    if (is_last) __hip_atomic_store(A.cnt + tok, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  for (int f = threadIdx.x; f < A.E; f += kThreads)
+    zs[f] = __hip_atomic_load(A.z + static_cast<size_t>(tok) * A.E + f, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const size_t o = static_cast<size_t>(tok) * A.k;
+  // the sort reads the ids of every token, so they go out with agent-scope
+  // stores below instead of the plain ones
+  topk_block(zs, A.E, A.k, sel_z, sel_e, A.seg ? nullptr : A.ids + o, A.w + o,
+             A.ids2 ? A.ids2 + o : nullptr, A.w2 ? A.w2 + o : nullptr);
+  if (A.seq_host && threadIdx.x == 0) {
+    // one thread writes the ids and then publishes them: the release store
+    // orders its own earlier stores before the sequence number
+    for (int j = 0; j < A.k; ++j)
+      __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  if (!A.seg) return;
+  if (threadIdx.x < static_cast<unsigned>(A.k))
+    __hip_atomic_store(A.ids + o + threadIdx.x, sel_e[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(A.cnt + A.B, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == A.B - 1;
+    if (is_last) __hip_atomic_store(A.cnt + A.B, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (is_last) sort_by_expert(A, reinterpret_cast<unsigned long long*>(zs + A.E));
+}
+
 template <bool HAS_ADD, bool RMS, bool TOPK>
 __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
   extern __shared__ double zs[];  // [E] for the top-k of the last block
@@ -326,45 +374,122 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
     }
   }
   if (!TOPK) return;
-  // every logit store of this block has completed before the block arrives
-  const int tok = blockIdx.y;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == nb - 1;
-    if (is_last) __hip_atomic_store(A.cnt + tok, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  route_tail(A, zs, sel_z, sel_e, &is_last);
+}
+
+// Batched router (B > 1, matrix-core path: fp16 inputs, no digit planes).
+// A wave holds one token's whole input in registers (STEPS steps of 8
+// consecutive values per lane) and computes kEW experts' logits from it, so
+// a token's input is read E / kEW times instead of E times and a token takes
+// E / (4 kEW) blocks. Per expert the fp64 products and their order are those
+// of k_route_fused, so the logits (and the ids) are the same bits.
+constexpr int kEW = 4;
+
+template <bool HAS_ADD, bool RMS, int STEPS>
+__global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
+  extern __shared__ double zs[];  // top-k tail: [E] logits, then the sort's scratch
+  __shared__ double sel_z[kMaxTopK];
+  __shared__ int sel_e[kMaxTopK];
+  __shared__ int is_last;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int H = A.H, n8 = H / 8;
+  const int b = blockIdx.y;
+  const int e0 = (blockIdx.x * kWaves + wave) * kEW;
+  const float* xb = A.x + static_cast<size_t>(b) * H;
+  const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
+
+  float u[STEPS][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < STEPS; ++t) {
+    int c = lane + kWave * t;
+    const bool valid = c < n8;
+    c = valid ? c : n8 - 1;
+    const float4 x0 = *reinterpret_cast<const float4*>(xb + 8 * c);
+    const float4 x1 = *reinterpret_cast<const float4*>(xb + 8 * c + 4);
+    const uint4 av = HAS_ADD ? *reinterpret_cast<const uint4*>(ab + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint32_t ap[4] = {av.x, av.y, av.z, av.w};
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u[t][2 * i] = xv[2 * i] + h2f(static_cast<uint16_t>(ap[i] & 0xFFFFu));
+      u[t][2 * i + 1] = xv[2 * i + 1] + h2f(static_cast<uint16_t>(ap[i] >> 16));
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part = fmaf(u[t][i], u[t][i], part);
+    ss += valid ? part : 0.f;
   }
-  __syncthreads();
-  if (!is_last) return;
-  for (int f = threadIdx.x; f < A.E; f += kThreads)
-    zs[f] = __hip_atomic_load(A.z + static_cast<size_t>(tok) * A.E + f, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const size_t o = static_cast<size_t>(tok) * A.k;
-  // the sort reads the ids of every token, so they go out with agent-scope
-  // stores below instead of the plain ones
-  topk_block(zs, A.E, A.k, sel_z, sel_e, A.seg ? nullptr : A.ids + o, A.w + o,
-             A.ids2 ? A.ids2 + o : nullptr, A.w2 ? A.w2 + o : nullptr);
-  if (A.seq_host && threadIdx.x == 0) {
-    // one thread writes the ids and then publishes them: the release store
-    // orders its own earlier stores before the sequence number
-    for (int j = 0; j < A.k; ++j)
-      __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  ss = seg_sum<kWave>(ss);
+  const float r = RMS ? 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f) : 1.0f;
+  // token scale of the fp16 copy: a power of two, so scaling is exact
+  float tsc = 1.0f;
+  {
+    const float nrm = sqrtf(ss) * r;
+    if (nrm > 0.f && nrm <= FLT_MAX) {
+      int ex;
+      frexpf(nrm, &ex);
+      tsc = ldexpf(1.0f, ex - 4);
+    }
   }
-  if (!A.seg) return;
-  if (threadIdx.x < static_cast<unsigned>(A.k))
-    __hip_atomic_store(A.ids + o + threadIdx.x, sel_e[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + A.B, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == A.B - 1;
-    if (is_last) __hip_atomic_store(A.cnt + A.B, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (RMS) {
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[t][i] *= r;
   }
-  __syncthreads();
-  if (is_last) sort_by_expert(A, reinterpret_cast<unsigned long long*>(zs + A.E));
+  if (blockIdx.x == 0) {
+    // the token's fp16 copy (and u), one step per wave
+    if (threadIdx.x == 0) A.tsc[b] = tsc;
+    const float inv_t = 1.0f / tsc;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const int c = lane + kWave * t;
+      if (t % kWaves != wave || c >= n8) continue;
+      uint32_t hw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 lo = static_cast<_Float16>(u[t][i] * inv_t);
+        const _Float16 hi = static_cast<_Float16>(u[t][i + 4] * inv_t);
+        hw[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(A.u16 + static_cast<size_t>(b) * H + 8 * c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if (A.u_out) {
+        float* uo = A.u_out + static_cast<size_t>(b) * H + 8 * c;
+        *reinterpret_cast<float4*>(uo) = make_float4(u[t][0], u[t][1], u[t][2], u[t][3]);
+        *reinterpret_cast<float4*>(uo + 4) = make_float4(u[t][4], u[t][5], u[t][6], u[t][7]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kEW; ++j) {
+    const int e = e0 + j < A.E ? e0 + j : A.E - 1;
+    const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
+    double acc = 0.0;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      int c = lane + kWave * t;
+      const bool valid = c < n8;
+      c = valid ? c : n8 - 1;
+      const uint4 wv = *reinterpret_cast<const uint4*>(row + 8 * c);
+      const uint32_t wp[4] = {wv.x, wv.y, wv.z, wv.w};
+      double part = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = fma(static_cast<double>(u[t][2 * i]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu))), part);
+        part = fma(static_cast<double>(u[t][2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), part);
+      }
+      acc += valid ? part : 0.0;
+    }
+    acc = seg_sum_f64<kWave>(acc);
+    if (lane == 0 && e0 + j < A.E) {
+      const double zv = acc + (A.bias ? static_cast<double>(A.bias[e]) : 0.0);
+      __hip_atomic_store(A.z + static_cast<size_t>(b) * A.E + e, zv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  route_tail(A, zs, sel_z, sel_e, &is_last);
 }
 
 constexpr int kLogitWaves = 4;
@@ -433,6 +558,25 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
   const int blocks = (E + kWaves - 1) / kWaves;
   // logits of one token; the sort adds a mask and a counter per expert
   const size_t lds = sizeof(double) * E + (sort ? (sizeof(unsigned long long) + sizeof(int)) * E : 0);
+  // a batch with its top-k, for the matrix-core path (no digit planes): the
+  // batched router, a token's input held in registers (H <= 4096)
+  const int steps = (H / 8 + kWave - 1) / kWave;
+  if (B > 1 && ids && !udig && u16 && tsc && steps <= kMaxSteps) {
+    const dim3 grid((E + kWaves * kEW - 1) / (kWaves * kEW), B);
+#define MOE_ROUTE_TOK(A_, R_)                                                                        \
+  do {                                                                                             \
+    if (steps <= 2) hipLaunchKernelGGL((k_route_tok<A_, R_, 2>), grid, dim3(kThreads), lds, s, A); \
+    else if (steps <= 4) hipLaunchKernelGGL((k_route_tok<A_, R_, 4>), grid, dim3(kThreads), lds, s, A); \
+    else if (steps <= 6) hipLaunchKernelGGL((k_route_tok<A_, R_, 6>), grid, dim3(kThreads), lds, s, A); \
+    else hipLaunchKernelGGL((k_route_tok<A_, R_, 8>), grid, dim3(kThreads), lds, s, A);             \
+  } while (0)
+    if (add_in && rmsnorm) MOE_ROUTE_TOK(true, true);
+    else if (add_in) MOE_ROUTE_TOK(true, false);
+    else if (rmsnorm) MOE_ROUTE_TOK(false, true);
+    else MOE_ROUTE_TOK(false, false);
+#undef MOE_ROUTE_TOK
+    return hipGetLastError();
+  }
   const bool topk = ids != nullptr;
 #define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks, B), dim3(kThreads), lds, s, A)
   if (topk) {
