@@ -8,10 +8,12 @@
 // token); grouping rows per loaded expert follows the same page's section
 // "Desempenho no mundo real".
 //
-// After routing, the B*k assignments are sorted by expert (stable: expert,
-// token, rank) and each expert becomes a segment of rows; the shared expert is
-// one more segment holding every token. Per segment the projection is a small
-// dense product W [rows x K] * X [K x m], so it runs on 16x16x32 fp16 MFMA:
+// After routing, each expert's segment of rows is its assignments a =
+// token*k + rank in increasing a (token order); a block finds them itself by
+// scanning the B*k ids, so no sort and no permutation arrays are needed, and
+// per-assignment rows are stored by a. The shared expert is one more segment
+// holding every token. Per segment the projection is a small dense product
+// W [rows x K] * X [K x m], so it runs on 16x16x32 fp16 MFMA:
 //
 //   * a wave streams 16 weight rows per tile, 4 quant groups (64 contiguous
 //     bytes of each row) per K step, prefetched DEPTH steps ahead in
@@ -61,11 +63,11 @@ struct MArgs {
   const uint8_t* shared;
   size_t blob_e;
   int H, I, Is, E, k, B;
-  const int32_t* seg;    // [E+1] segment starts in the sorted assignment list
-  const int32_t* perm;   // sorted position -> assignment (token*k + rank)
+  const int32_t* ids;   // [B][k] experts of each token, in rank order
+  int nA;                // B*k assignments a = token*k + rank
   const uint16_t* u16;   // [B][H] fp16 inputs / tsc
   const float* tsc;      // [B]
-  uint16_t* act_r;       // [B*k][I]  routed GeGLU activations by sorted position
+  uint16_t* act_r;       // [B*k][I]  routed GeGLU activations by assignment
   uint16_t* act_s;       // [B][Is]   shared activations by token
   float* out_r;          // [B*k][H]
   float* out_s;          // [B][H]
@@ -131,8 +133,46 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
     tile = bx < nr ? bx % A.tiles_r : bx - nr;
   }
   const bool routed = s < A.E;
-  const int r0 = routed ? A.seg[s] : 0;
-  const int m = routed ? A.seg[s + 1] - r0 : A.B;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  // A routed segment's rows are the assignments a with ids[a] == s, in
+  // increasing a (so in token order: a token holds an expert at most once).
+  // scan() counts them and puts those of rows [p0, p0 + cap) in alist: a
+  // ballot per wave, the waves' counts through LDS, ids read in batches.
+  __shared__ int alist[NTT * kTile];
+  __shared__ int wcnt[kWaves];
+  auto scan = [&](int p0, int cap) __attribute__((always_inline)) {
+    constexpr int kBatch = 4;
+    int total = 0;
+    for (int c0 = 0; c0 < A.nA; c0 += kBatch * kThreads) {
+      int v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int a = c0 + u * kThreads + threadIdx.x;
+        v[u] = a < A.nA ? A.ids[a] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c0 + u * kThreads >= A.nA) break;  // uniform
+        const bool hit = v[u] == s;
+        const unsigned long long bal = __ballot(hit);
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int base = total, chunk = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+          base += w2 < wave ? wcnt[w2] : 0;
+          chunk += wcnt[w2];
+        }
+        const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+        if (hit && pos >= p0 && pos < p0 + cap) alist[pos - p0] = c0 + u * kThreads + threadIdx.x;
+        total += chunk;
+        __syncthreads();  // wcnt is rewritten by the next batch
+      }
+    }
+    return total;
+  };
+  const int m = routed ? scan(0, NTT * kTile) : A.B;
   if (m == 0) return;  // uniform over the block
   const uint8_t* blob = routed ? A.experts + static_cast<size_t>(s) * A.blob_e : A.shared;
   const int inter = routed ? A.I : A.Is;
@@ -140,8 +180,6 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   const int nrows = GATEUP ? inter : A.H;
   const int ngk = K / kGroup;
   const int nsteps = (ngk + 3) / 4;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
   const int q = lane >> 4;
   const int l16 = lane & 15;
   const BlobOffsets o = blob_offsets(A.H, inter);
@@ -174,6 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
 
   for (int p0 = 0; p0 < m; p0 += NTT * kTile) {
     const int mt = m - p0 < NTT * kTile ? m - p0 : NTT * kTile;
+    if (routed && p0 > 0) scan(p0, NTT * kTile);  // this pass's assignments
     // this thread's 16-byte chunks of a step slice (token = c / 16)
     const uint16_t* brow[NTT];
     int boff[NTT], loff[NTT];
@@ -185,10 +224,10 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
       boff[r] = 8 * (c & 15);
       loff[r] = (c >> 4) * kBRow + 16 * (c & 15);
       if (GATEUP) {
-        const int t = routed ? A.perm[r0 + row] / A.k : row;
+        const int t = routed ? alist[row - p0] / A.k : row;
         brow[r] = A.u16 + static_cast<size_t>(t) * A.H;
       } else {
-        brow[r] = routed ? A.act_r + static_cast<size_t>(r0 + row) * A.I
+        brow[r] = routed ? A.act_r + static_cast<size_t>(alist[row - p0]) * A.I
                          : A.act_s + static_cast<size_t>(row) * A.Is;
       }
     }
@@ -293,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
       const int col = tt * kTile + l16;
       const bool valid = live && col < mt;
       const int row = p0 + (col < mt ? col : mt - 1);  // row of the segment
-      const int tok = routed ? A.perm[r0 + row] / A.k : row;
+      const int asg = routed ? alist[row - p0] : row;    // its assignment (routed) or token
+      const int tok = routed ? asg / A.k : row;
       const float ts = A.tsc[tok];
       if (GATEUP) {
         float av[4];
@@ -314,13 +354,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
           out.y = (recv >> 16) | (hi & 0xFFFF0000u);
         }
         if (valid) {
-          uint16_t* dst = routed ? A.act_r + static_cast<size_t>(r0 + row) * A.I
+          uint16_t* dst = routed ? A.act_r + static_cast<size_t>(asg) * A.I
                                  : A.act_s + static_cast<size_t>(row) * A.Is;
           *reinterpret_cast<uint2*>(dst + rbase + 8 * (q >> 1) + 4 * (q & 1)) = out;
         }
       } else if (valid) {
         const float f = ts * ts;
-        float* dst = routed ? A.out_r + static_cast<size_t>(r0 + row) * A.H
+        float* dst = routed ? A.out_r + static_cast<size_t>(asg) * A.H
                             : A.out_s + static_cast<size_t>(row) * A.H;
 #pragma unroll
         for (int mr = 0; mr < kMR; ++mr)
@@ -331,16 +371,16 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   }
 }
 
-// y[t] = (x'[t] if residual) + out_s[t] + sum_j w[t][j] * out_r[pos_of[t*k + j]]
+// y[t] = (x'[t] if residual) + out_s[t] + sum_j w[t][j] * out_r[t*k + j]
 __global__ void k_bcombine(const float* __restrict__ out_s, const float* __restrict__ out_r,
-                           const int32_t* __restrict__ pos_of, const float* __restrict__ w,
+                           const float* __restrict__ w,
                            const float* __restrict__ x, const uint16_t* __restrict__ add_in,
                            int residual, int H, int k, float* __restrict__ y) {
   const int t = blockIdx.y;
   for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < H; n += gridDim.x * blockDim.x) {
     float v = out_s[static_cast<size_t>(t) * H + n];
     for (int j = 0; j < k; ++j)
-      v = fmaf(w[t * k + j], out_r[static_cast<size_t>(pos_of[t * k + j]) * H + n], v);
+      v = fmaf(w[t * k + j], out_r[(static_cast<size_t>(t) * k + j) * H + n], v);
     float r = 0.f;
     if (residual) r = x[static_cast<size_t>(t) * H + n] + (add_in ? h2f(add_in[static_cast<size_t>(t) * H + n]) : 0.f);
     y[static_cast<size_t>(t) * H + n] = r + v;
@@ -374,9 +414,9 @@ bool batched_lds_fits(int H, int I, int Is, int max_B) {
 
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
-                          const uint16_t* u16, const float* tsc, const float* w, const float* x,
-                          const uint16_t* add_in, bool residual, float* y, hipStream_t s) {
-  MArgs A{experts, shared, blob_e, H, I, Is, E, k, B, bb.seg, bb.perm, u16, tsc,
+                          const uint16_t* u16, const float* tsc, const int32_t* ids, const float* w,
+                          const float* x, const uint16_t* add_in, bool residual, float* y, hipStream_t s) {
+  MArgs A{experts, shared, blob_e, H, I, Is, E, k, B, ids, B * k, u16, tsc,
           bb.act_r, bb.act_s, bb.out_r, bb.out_s, 0, 0};
   // tokens per pass over a segment's weights: up to 64; a larger shared or
   // expert segment takes several passes
@@ -389,7 +429,7 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
   // down: 128 output rows per block
   A.tiles_r = A.tiles_s = (H + kWaves * kMR * kTile - 1) / (kWaves * kMR * kTile);
   if ((e = launch_mfma<false>(A, ntt, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bcombine, dim3((H + 255) / 256, B), dim3(256), 0, s, bb.out_s, bb.out_r, bb.pos_of, w,
+  hipLaunchKernelGGL(k_bcombine, dim3((H + 255) / 256, B), dim3(256), 0, s, bb.out_s, bb.out_r, w,
                      x, add_in, residual ? 1 : 0, H, k, y);
   return hipGetLastError();
 }

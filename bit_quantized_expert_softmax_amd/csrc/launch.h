@@ -31,22 +31,19 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
 // ---------------------------------------------------------------- routing
 // Layer router, one launch: x' = x (+ add_in); u = x' or rmsnorm(x'); u's
 // digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
-// finish. Grid: (E/4 blocks) x B tokens. cnt holds B + 1 arrival counters
-// (B per-token, one for the sort), zero before the launch and after it.
+// finish. Grid: (E/4 blocks) x B tokens (with u16 and no digit planes, B > 1:
+// E/16 blocks, four experts per wave). cnt holds B arrival counters, zero
+// before the launch and after it.
 // Top-k variant (ids != nullptr): the last block of each token's grid row
 // takes that token's top-k. With seq_host (B == 1 only) it also writes the
 // ids to ids_host (host-coherent memory) and then seq to *seq_host
 // (system-scope release), so the host can wait for them without a copy or an
-// event. With seg/perm/pos_of (top-k variant) the block whose token finishes
-// last sorts the B*k assignments a = token*k + rank stably by expert:
-// seg[e]..seg[e+1] is expert e's range of sorted positions, perm[p] the
-// assignment at position p and pos_of[a] its position.
+// event.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, int32_t* seg,
-                              int32_t* perm, int32_t* pos_of, hipStream_t s);
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
@@ -133,23 +130,21 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int chunks, int32_t*
 int permute_chunks(int A);
 
 struct BatchedBuffers {
-  const int32_t* seg;
-  const int32_t* perm;
-  const int32_t* pos_of;
-  uint16_t* act_r;  // [B*k][I] fp16 GeGLU activations by sorted position
+  uint16_t* act_r;  // [B*k][I] fp16 GeGLU activations by assignment token*k + rank
   uint16_t* act_s;  // [B][Is]
   float* out_r;     // [B*k][H]
   float* out_s;     // [B][H]
 };
-// Grouped gate/up and down products over the expert segments on the matrix
-// cores (inputs: u16/tsc of launch_route_layer), then the combine.
 // Whether the matrix-core kernels' LDS (activation slices for up to max_B
 // tokens per pass plus the staged scales of a block's rows) fits one block.
 bool batched_lds_fits(int H, int I, int Is, int max_B);
+// Grouped gate/up and down products per expert on the matrix cores (inputs:
+// u16/tsc of launch_route_layer and the ids [B][k]; every block finds its
+// expert's tokens in the ids), then the combine.
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
-                          const uint16_t* u16, const float* tsc, const float* w, const float* x,
-                          const uint16_t* add_in, bool residual, float* y, hipStream_t s);
+                          const uint16_t* u16, const float* tsc, const int32_t* ids, const float* w,
+                          const float* x, const uint16_t* add_in, bool residual, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------- standalone GEMV
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,

@@ -37,9 +37,8 @@ namespace {
 
 struct WsLayout {
   size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre;
-  // batched decode (max_B > 1): expert sort and per-assignment outputs
-  size_t hist, base, lrank, seg, tiles, n_tiles, perm, pos_of, out_r, out_s, u16, tsc, act;
-  int chunks;
+  // batched decode (max_B > 1): fp16 inputs and per-assignment outputs
+  size_t out_r, out_s, u16, tsc, act;
   size_t total;
 };
 
@@ -62,20 +61,11 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.w = take(B * k * 4);
   L.adig = take(B * npos * 16);
   L.asc = take(B * npos * 4);
-  L.cnt = take((B + 1) * 4);  // router arrival counters: one per token, one for the sort
+  L.cnt = take(B * 4);  // router arrival counters, one per token
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
   const size_t A = B > 1 ? B * k : 0;
-  L.chunks = permute_chunks(static_cast<int>(A));
-  L.hist = take(static_cast<size_t>(L.chunks) * E * 4);
-  L.base = take(static_cast<size_t>(L.chunks) * E * 4);
-  L.lrank = take(A * 4);
-  L.seg = take((E + 1) * 4);
-  L.tiles = take((A / 64 + E + 1) * 8);
-  L.n_tiles = take(4);
-  L.perm = take(A * 4);
-  L.pos_of = take(A * 4);
   L.out_r = take(A * H * 4);
   L.out_s = take(B > 1 ? B * H * 4 : 0);
   L.u16 = take(B > 1 ? B * H * 2 : 0);
@@ -279,7 +269,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     moe_layer_destroy(L);
     return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
   };
-  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, (static_cast<size_t>(max_B) + 1) * 4);
+  hipError_t e = hipMemset(L->wsb + ws.cnt, 0, static_cast<size_t>(max_B) * 4);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
@@ -376,18 +366,15 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
 
   hipEvent_t pb = prof_begin(L, 0, s);
   // grouped path (B > 1, all experts resident): every touched expert is read
-  // once per call by the matrix-core kernels, which take fp16 inputs; the
-  // router also takes each token's top-k and sorts the B*k assignments by
-  // expert
+  // once per call by the matrix-core kernels, which take fp16 inputs and
+  // find each expert's tokens in the ids; the router also takes each token's
+  // top-k
   const bool grouped = !L->cache_mode && B > 1;
   // one token, resident: the router only produces logits; each gate/up block
   // takes the top-k itself (no cross-block handshake on the critical path)
   const bool in_kernel_topk = !L->cache_mode && !grouped;
   uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
   float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
-  int32_t* seg = grouped ? L->at<int32_t>(L->ws.seg) : nullptr;
-  int32_t* perm = grouped ? L->at<int32_t>(L->ws.perm) : nullptr;
-  int32_t* pos_of = grouped ? L->at<int32_t>(L->ws.pos_of) : nullptr;
   const int32_t seq = L->cache_mode ? L->seq + 1 : 0;
   HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
                                       grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
@@ -395,7 +382,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                                       in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
                                       in_kernel_topk ? nullptr : w_out,
                                       L->cache_mode ? L->ids_host : nullptr,
-                                      L->cache_mode ? L->seq_host : nullptr, seq, seg, perm, pos_of, s), fn);
+                                      L->cache_mode ? L->seq_host : nullptr, seq, s), fn);
   if (L->cache_mode) L->seq = seq;
   prof_end(L, 0, pb, s);
 
@@ -404,11 +391,11 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     // batched: grouped GEMVs that read each touched expert once, ordered combine
     const int A = B * k;
     uint16_t* act = L->at<uint16_t>(L->ws.act);
-    moe::BatchedBuffers bb{seg, perm, pos_of, act, act + static_cast<size_t>(A) * sh.inter,
-                           L->at<float>(L->ws.out_r), L->at<float>(L->ws.out_s)};
+    moe::BatchedBuffers bb{act, act + static_cast<size_t>(A) * sh.inter, L->at<float>(L->ws.out_r),
+                           L->at<float>(L->ws.out_s)};
     hipEvent_t p1 = prof_begin(L, 2, s);
     HIP_OR_FAIL(moe::launch_batched(bb, L->d.experts_dev, L->d.shared_blob, L->blob_e, H, sh.inter,
-                                    sh.shared_inter, E, k, B, u16, tsc, w, x, add_in, res, y, s), fn);
+                                    sh.shared_inter, E, k, B, u16, tsc, ids, w, x, add_in, res, y, s), fn);
     prof_end(L, 2, p1, s);
     if (stats) stats->calls += 1;
     return MOE_OK;

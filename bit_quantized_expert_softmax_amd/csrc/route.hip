@@ -11,10 +11,9 @@
 // digit planes for the expert GEMVs, and computes the logits of 4 experts in
 // fp64. The logits are written with agent-scope (L2-bypassing) stores; after
 // its stores have completed each block bumps its token's counter, and the
-// block that arrives last takes that token's top-k. For a batch, the block
-// whose token completes last also sorts the assignments by expert (a stable
-// counting sort). No block waits for another and no cache writeback is
-// needed, so the launch costs little more than its loads.
+// block that arrives last takes that token's top-k. No block waits for
+// another and no cache writeback is needed, so the launch costs little more
+// than its loads.
 #include <float.h>
 #include <math.h>
 
@@ -49,8 +48,6 @@ struct RouteArgs {
   int32_t* ids_host;
   int32_t* seq_host;
   int32_t seq;
-  // optional (top-k variant): stable sort of the B*k assignments by expert
-  int32_t *seg, *perm, *pos_of;
 };
 
 // Per wave: one expert's router row and the whole token input x' are loaded
@@ -61,105 +58,9 @@ struct RouteArgs {
 // digit planes straight from registers.
 constexpr int kMaxSteps = 8;  // H <= 8 * 64 * 8 = 4096 in one batch
 
-// Stable counting sort of the A = B*k assignments a = token*k + rank by
-// expert, token order kept within an expert. Counts by LDS atomics, offsets
-// by a wave scan; positions chunk by chunk of 64 tokens (one per lane of wave
-// 0): each lane sets its bit in a 64-bit mask per expert it selected, and its
-// position is the expert's running offset plus the number of lower lanes in
-// that mask (the k experts of a token are distinct). All threads call.
-// lds: E masks (u64) then E counters (int).
-__device__ void sort_by_expert(const RouteArgs& A, unsigned long long* mk) {
-  const int E = A.E, k = A.k, B = A.B, n = B * k;
-  int* off = reinterpret_cast<int*>(mk + E);
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    off[e] = 0;
-    mk[e] = 0ull;
-  }
-  __syncthreads();
-  // the ids come from memory (agent scope): issue a thread's loads together,
-  // at clamped addresses, and use only the valid ones
-  constexpr int kU = 4;
-  for (int a0 = 0; a0 < n; a0 += kU * kThreads) {
-    int v[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int a = a0 + u * kThreads + threadIdx.x;
-      v[u] = __hip_atomic_load(A.ids + (a < n ? a : n - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (a0 + u * kThreads + threadIdx.x < n) atomicAdd(off + v[u], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int c = e < E ? off[e] : 0;
-      int incl = c;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(incl, d, kWave);
-        incl += lane >= d ? y : 0;
-      }
-      if (e < E) {
-        off[e] = carry + incl - c;
-        A.seg[e] = carry + incl - c;
-      }
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (lane == 0) A.seg[E] = carry;
-  }
-  __syncthreads();
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int t0 = 0; t0 < B; t0 += kWave) {
-    const int t = t0 + lane;
-    int id[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) id[j] = -1;
-    if (wave == 0) {
-      const int tc = t < B ? t : B - 1;
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
-        id[j] = __hip_atomic_load(A.ids + static_cast<size_t>(tc) * k + (j < k ? j : k - 1),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) id[j] = t < B && j < k ? id[j] : -1;
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (id[j] >= 0) atomicOr(mk + id[j], 1ull << lane);
-    __syncthreads();
-    bool first[kMaxTopK];
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      first[j] = false;
-      if (id[j] < 0) continue;
-      const unsigned long long m = mk[id[j]];
-      const int p = off[id[j]] + __popcll(m & below);
-      const int a = t * k + j;
-      A.perm[p] = a;
-      A.pos_of[a] = p;
-      first[j] = (m & below) == 0ull;
-    }
-    __syncthreads();
-    // the lowest lane holding an expert advances its offset and clears it
-#pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
-      if (first[j]) {
-        off[id[j]] += __popcll(mk[id[j]]);
-        mk[id[j]] = 0ull;
-      }
-    __syncthreads();
-  }
-}
-
 // Top-k variant, after the block's logit stores (agent scope): the block
 // bumps its token's counter; the last of the token's gridDim.x blocks takes
-// the token's top-k (and publishes it to the host, B == 1); with a sort, the
-// block whose token completes last sorts the assignments. All threads call.
+// the token's top-k (and publishes it to the host, B == 1). All threads call.
 __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
   int& is_last = *is_last_p;
   const int nb = gridDim.x;
@@ -179,10 +80,8 @@ __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* s
                               __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const size_t o = static_cast<size_t>(tok) * A.k;
-  // the sort reads the ids of every token, so they go out with agent-scope
-  // stores below instead of the plain ones
-  topk_block(zs, A.E, A.k, sel_z, sel_e, A.seg ? nullptr : A.ids + o, A.w + o,
-             A.ids2 ? A.ids2 + o : nullptr, A.w2 ? A.w2 + o : nullptr);
+  topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids + o, A.w + o, A.ids2 ? A.ids2 + o : nullptr,
+             A.w2 ? A.w2 + o : nullptr);
   if (A.seq_host && threadIdx.x == 0) {
     // one thread writes the ids and then publishes them: the release store
     // orders its own earlier stores before the sequence number
@@ -190,18 +89,6 @@ __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* s
       __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  if (!A.seg) return;
-  if (threadIdx.x < static_cast<unsigned>(A.k))
-    __hip_atomic_store(A.ids + o + threadIdx.x, sel_e[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + A.B, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == A.B - 1;
-    if (is_last) __hip_atomic_store(A.cnt + A.B, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (is_last) sort_by_expert(A, reinterpret_cast<unsigned long long*>(zs + A.E));
 }
 
 template <bool HAS_ADD, bool RMS, bool TOPK>
@@ -387,7 +274,7 @@ constexpr int kEW = 4;
 
 template <bool HAS_ADD, bool RMS, int STEPS>
 __global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
-  extern __shared__ double zs[];  // top-k tail: [E] logits, then the sort's scratch
+  extern __shared__ double zs[];  // [E] for the top-k of the last block
   __shared__ double sel_z[kMaxTopK];
   __shared__ int sel_e[kMaxTopK];
   __shared__ int is_last;
@@ -548,16 +435,12 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, int32_t* seg,
-                              int32_t* perm, int32_t* pos_of, hipStream_t s) {
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s) {
   if (seq_host && (B != 1 || !ids)) return hipErrorInvalidValue;
-  const bool sort = seg != nullptr;
-  if (sort && (!ids || !w || !perm || !pos_of || k > kMaxTopK)) return hipErrorInvalidValue;
   RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, u16, tsc, z, cnt,
-              ids, ids2, w, w2, ids_host, seq_host, seq, seg, perm, pos_of};
+              ids, ids2, w, w2, ids_host, seq_host, seq};
   const int blocks = (E + kWaves - 1) / kWaves;
-  // logits of one token; the sort adds a mask and a counter per expert
-  const size_t lds = sizeof(double) * E + (sort ? (sizeof(unsigned long long) + sizeof(int)) * E : 0);
+  const size_t lds = sizeof(double) * E;  // one token's logits, for the top-k
   // a batch with its top-k, for the matrix-core path (no digit planes): the
   // batched router, a token's input held in registers (H <= 4096)
   const int steps = (H / 8 + kWave - 1) / kWave;
