@@ -247,7 +247,12 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
   if (wave < nout) {
     float acc = 0.f;
     for (int c = lane; c < nga; c += kWave) acc += part[wave * nga + c];
-    acc = dpp_sum<64>(acc);
+    // row sums by DPP, then the four rows through scalar reads (lane 0 writes)
+    acc = dpp_sum<16>(acc);
+    acc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
     if (lane == 0) {
       const int n = n0 + wave;
       float r = 0.f;

@@ -59,6 +59,10 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
 __device__ __forceinline__ double dpp(double v) {
   const long long b = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b & 0xffffffffll), CTRL, 0xF, 0xF, true);
@@ -94,9 +98,14 @@ __device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, Di
   const int lane = threadIdx.x & (kWave - 1);
   const int g = g0 + (lane >> 5);
   const int i = lane & 31;
+  // max over the 32 lanes: DPP within 16 lanes, one shuffle across (max and
+  // OR below are exact, so the order of the steps does not matter)
   float m = fabsf(v);
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  m = fmaxf(m, dpp<0xB1>(m));
+  m = fmaxf(m, dpp<0x4E>(m));
+  m = fmaxf(m, dpp<0x141>(m));
+  m = fmaxf(m, dpp<0x140>(m));
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
   const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
   int q = static_cast<int>(rintf(v * inv));
   q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
@@ -111,13 +120,19 @@ __device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, Di
   uint32_t w1 = static_cast<uint32_t>(d1 & 15) << sh;
   uint32_t w2 = static_cast<uint32_t>(d2 & 15) << sh;
   uint32_t w3 = static_cast<uint32_t>(d3 & 15) << sh;
-#pragma unroll
-  for (int o = 4; o > 0; o >>= 1) {
-    w0 |= __shfl_xor(w0, o, kWave);
-    w1 |= __shfl_xor(w1, o, kWave);
-    w2 |= __shfl_xor(w2, o, kWave);
-    w3 |= __shfl_xor(w3, o, kWave);
-  }
+  // OR over each aligned 8 lanes: quads, then the mirrored quad
+  w0 |= dpp<0xB1>(w0);
+  w1 |= dpp<0xB1>(w1);
+  w2 |= dpp<0xB1>(w2);
+  w3 |= dpp<0xB1>(w3);
+  w0 |= dpp<0x4E>(w0);
+  w1 |= dpp<0x4E>(w1);
+  w2 |= dpp<0x4E>(w2);
+  w3 |= dpp<0x4E>(w3);
+  w0 |= dpp<0x141>(w0);
+  w1 |= dpp<0x141>(w1);
+  w2 |= dpp<0x141>(w2);
+  w3 |= dpp<0x141>(w3);
   if (g < ng) {
     if ((i & 7) == 0) dig[g].p[i >> 3] = make_uint4(w0, w1, w2, w3);
     if (i == 0) sc[g] = m / static_cast<float>(kQmax);

@@ -96,6 +96,10 @@ def test_route_given_logits_and_ties():
     logits = gen.logits_uniform(T, sh.n_experts, 4)
     logits[0] = 0.0                              # all tied: ids 0..7, w = 1/8
     logits[1, 5] = logits[1, 9] = 2.0            # a tie at the top goes to the lower id
+    logits[2] = -1.0                             # -0.0 and +0.0 are equal: ties by id
+    logits[2, 12], logits[2, 7], logits[2, 3] = -0.0, 0.0, -0.0
+    logits[3] = -3.5                             # negative ties, one larger value
+    logits[3, 40] = -2.0
     ids = poisoned((T, sh.top_k), torch.int32)
     w = poisoned((T, sh.top_k))
     api.moe_route(sh, None, None, None, dev(logits), T, ids, w, None)
@@ -104,4 +108,6 @@ def test_route_given_logits_and_ties():
     assert np.array_equal(ids.cpu().numpy(), r_ids)
     assert ids[0].tolist() == list(range(8)) and torch.all(w[0] == 0.125)
     assert ids[1, :2].tolist() == [5, 9]
+    assert ids[2].tolist() == [3, 7, 12, 0, 1, 2, 4, 5]
+    assert ids[3].tolist() == [40, 0, 1, 2, 3, 4, 5, 6]
     assert_close(w.cpu().numpy(), r_w, "w")
