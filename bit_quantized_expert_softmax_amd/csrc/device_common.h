@@ -83,6 +83,29 @@ __device__ __forceinline__ T dpp_sum(T v) {
   return v;
 }
 
+// Sum over the whole wave, in every lane: DPP within each 16-lane row, then
+// the four row sums through lane reads (a fixed order, no LDS shuffles).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_sum<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ double wave_sum(double v) {
+  v = dpp_sum<16>(v);
+  double r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffll), 16 * i);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 16 * i);
+    r[i] = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+  }
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+
 // GELU, tanh form: z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
           ss = fmaf(v1, v1, ss);
         }
       }
-      ss_all = seg_sum<kWave>(ss);
+      ss_all = wave_sum(ss);
       if (RMS) r_all = 1.0f / sqrtf(ss_all / static_cast<float>(H) + 1e-6f);
     }
     double acc = 0.0;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
       }
       float r = r_all;
       if ((RMS || A.u16) && !multi) {
-        ss = seg_sum<kWave>(ss);
+        ss = wave_sum(ss);
         if (RMS) r = 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f);
       } else {
         ss = ss_all;
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(u[t][i]));
-        m = fmaxf(m, __shfl_xor(m, 1, kWave));
-        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        m = fmaxf(m, dpp<0xB1>(m));  // the group's 4 lanes (an aligned quad)
+        m = fmaxf(m, dpp<0x4E>(m));
         if (own) {
           const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
           uint32_t wd[4] = {0u, 0u, 0u, 0u};
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
         }
       }
     }
-    acc = seg_sum_f64<kWave>(acc);
+    acc = wave_sum(acc);
     if (lane == 0 && gw < A.E) {
       const double zv = acc + (A.bias ? static_cast<double>(A.bias[e]) : 0.0);
       if (TOPK)
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
     for (int i = 0; i < 8; ++i) part = fmaf(u[t][i], u[t][i], part);
     ss += valid ? part : 0.f;
   }
-  ss = seg_sum<kWave>(ss);
+  ss = wave_sum(ss);
   const float r = RMS ? 1.0f / sqrtf(ss / static_cast<float>(H) + 1e-6f) : 1.0f;
   // token scale of the fp16 copy: a power of two, so scaling is exact
   float tsc = 1.0f;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
       }
       acc += valid ? part : 0.0;
     }
-    acc = seg_sum_f64<kWave>(acc);
+    acc = wave_sum(acc);
     if (lane == 0 && e0 + j < A.E) {
       const double zv = acc + (A.bias ? static_cast<double>(A.bias[e]) : 0.0);
       __hip_atomic_store(A.z + static_cast<size_t>(b) * A.E + e, zv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kLogitWaves* kWave) void k_route_logits(
         acc = fma(static_cast<double>(uv[2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), acc);
       }
     }
-    acc = seg_sum_f64<kWave>(acc);
+    acc = wave_sum(acc);
     if (lane == 0) z[static_cast<size_t>(b) * E + e] = acc + (bias ? static_cast<double>(bias[e]) : 0.0);
   }
 }

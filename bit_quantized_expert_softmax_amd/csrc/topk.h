@@ -70,7 +70,11 @@ __device__ inline void topk_block(double* zs, int E, int k, double* sel_z, int* 
       for (int i = 0; i < 8; ++i) rank += key_better(kf[i], f + i * P, ke, e) ? 1 : 0;
     }
     for (; f < E; f += P) rank += key_better(kz[f], f, ke, e) ? 1 : 0;
-    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    // partial ranks of the P lanes (an aligned group of 2, 4 or 8) by DPP:
+    // lane ^ 1, lane ^ 2, then the mirrored quad
+    if (P >= 2) rank += static_cast<int>(dpp<0xB1>(static_cast<uint32_t>(rank)));
+    if (P >= 4) rank += static_cast<int>(dpp<0x4E>(static_cast<uint32_t>(rank)));
+    if (P >= 8) rank += static_cast<int>(dpp<0x141>(static_cast<uint32_t>(rank)));
     if (valid && part == 0 && rank < k) {
       sel_z[rank] = key_logit(static_cast<unsigned long long>(ke.y) << 32 | ke.x);
       sel_e[rank] = e;
