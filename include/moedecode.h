@@ -194,7 +194,11 @@ typedef struct moe_decode_stats {
 /* Workspace for up to max_B decode tokens per call and max_T prefill tokens. */
 moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
                                      size_t* out);
-/* Validates, clears the workspace counters (synchronously) and returns a handle. */
+/* Validates, clears the workspace counters (synchronously) and returns a handle.
+ * max_B > 1 (batched decode, resident mode) also needs the batched kernels'
+ * per-block LDS (the staged group scales of 128 weight rows of length H, and
+ * the activation slices of up to 64 tokens) to fit 64 KiB: MOE_ESHAPE if not
+ * (max_B <= 16: H up to 7104; max_B > 32: H up to 3840). */
 moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_t max_B,
                             int32_t max_T, moe_layer** out);
 void moe_layer_destroy(moe_layer* L);
@@ -214,7 +218,11 @@ moe_cache* moe_layer_cache(moe_layer* L);
  *           optional copies of the routing and of u (NULL to skip)
  *   trace   host [B][k] cache events (cache mode) or NULL
  *   stats   host, accumulated (cache mode counters) or NULL
- * Resident mode is asynchronous on stream. Cache mode requires B == 1 and
+ * Resident mode is asynchronous on stream. With B > 1 (resident) the tokens
+ * are grouped by expert: each touched expert's weights are read once per call
+ * and multiplied on the matrix cores (fp16 weights and activations, fp32
+ * accumulation); each token's result is its own B = 1 layer output within the
+ * same tolerance, and its ids are the same. Cache mode requires B == 1 and
  * blocks the calling thread once, until the token's ids are on the host; it
  * returns with the miss copies and the expert kernels enqueued (the copies on
  * copy_stream, ordered before the expert kernels by an event; with
