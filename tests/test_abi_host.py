@@ -148,4 +148,13 @@ def test_gpu_entry_points_reject_bad_arguments_before_enqueue():
     d.experts_dev = None
     d.experts_host, d.slot_pool, d.n_slots, d.workspace_bytes = 16, 16, 4, out.value
     assert lib.moe_layer_create(C.byref(sh), C.byref(d), 1, 0, C.byref(h)) == -2
+    # batched decode of a shape whose staged scales and 64-token slices exceed
+    # 64 KiB of LDS per block: refused at create (with max_B = 1 it passes
+    # this check and fails later, on the missing descriptor fields)
+    wide = api.make_shape(SMALL_LAYER)
+    wide.hidden = 3872
+    d2 = _lib.moe_layer_desc()
+    assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 64, 0, C.byref(h)) == -2
+    assert "LDS" in api.moe_last_error()
+    assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 1, 0, C.byref(h)) == -1
     assert lib.moe_layer_decode(None, 16, None, 1, 0, 32, None, None, None, None, None, None) == -1
