@@ -52,41 +52,78 @@ __global__ __launch_bounds__(kChunk) void k_perm_count(const int32_t* __restrict
 }
 
 // Single block: expert offsets (seg [E+1]), per-(chunk, expert) bases, and the
-// routed tile table (expert, first row) with its length in *n_tiles.
+// routed tile table (expert, first row) with its length in *n_tiles. P
+// threads per expert (P = 1024 / E) each take a contiguous range of chunks;
+// their partial counts meet in LDS, and the expert offsets and tile starts
+// come from one block-wide scan (wave scans, then the waves' totals).
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ hist, int C, int E,
                                                     int32_t* __restrict__ base, int32_t* __restrict__ seg,
                                                     int2* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  constexpr int kT = 1024;
+  __shared__ int part[kT];
   __shared__ int tot[MOE_MAX_EXPERTS + 1];
-  __shared__ int tstart[MOE_MAX_EXPERTS + 1];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0;
-    for (int c = 0; c < C; ++c) s += hist[static_cast<size_t>(c) * E + e];
-    tot[e] = s;
-  }
+  __shared__ int tst[MOE_MAX_EXPERTS + 1];
+  __shared__ int wsum[kT / kWave][2];
+  const int t = threadIdx.x;
+  const int wave = t / kWave, lane = t % kWave;
+  const int P = kT / E;  // E <= MOE_MAX_EXPERTS = 1024
+  const int e = t / P, p = t % P;
+  const bool on = e < E;
+  const int per = (C + P - 1) / P;
+  const int c0 = p * per;
+  const int c1 = c0 + per < C ? c0 + per : C;
+  int s = 0;
+  if (on)
+    for (int c = c0; c < c1; ++c) s += hist[static_cast<size_t>(c) * E + e];
+  part[t] = s;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0, t = 0;
-    for (int e = 0; e < E; ++e) {
-      const int n = tot[e];
-      tot[e] = s;  // becomes the exclusive prefix
-      tstart[e] = t;
-      s += n;
-      t += (n + kTM - 1) / kTM;
+  int off = 0;  // this thread's first row within its expert
+  if (on)
+    for (int q = 0; q < p; ++q) off += part[e * P + q];
+  // expert t's rows and tiles, exclusive prefix over experts
+  int n = 0;
+  if (t < E)
+    for (int q = 0; q < P; ++q) n += part[t * P + q];
+  const int nt = (n + kTM - 1) / kTM;
+  int a = n, b = nt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int ya = __shfl_up(a, d, kWave);
+    const int yb = __shfl_up(b, d, kWave);
+    if (lane >= d) {
+      a += ya;
+      b += yb;
     }
-    tot[E] = s;
-    tstart[E] = t;
-    *n_tiles = t;
+  }
+  if (lane == kWave - 1) {
+    wsum[wave][0] = a;
+    wsum[wave][1] = b;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) seg[e] = tot[e];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = tot[e];
-    for (int c = 0; c < C; ++c) {
-      base[static_cast<size_t>(c) * E + e] = s;
-      s += hist[static_cast<size_t>(c) * E + e];
+  int wa = 0, wb = 0;
+  for (int w = 0; w < wave; ++w) {
+    wa += wsum[w][0];
+    wb += wsum[w][1];
+  }
+  if (t < E) {
+    tot[t] = wa + a - n;
+    tst[t] = wb + b - nt;
+  }
+  if (t == E - 1) {
+    tot[E] = wa + a;
+    tst[E] = wb + b;
+    *n_tiles = wb + b;
+  }
+  __syncthreads();
+  for (int f = t; f <= E; f += kT) seg[f] = tot[f];
+  if (on) {
+    int r = tot[e] + off;
+    for (int c = c0; c < c1; ++c) {
+      base[static_cast<size_t>(c) * E + e] = r;
+      r += hist[static_cast<size_t>(c) * E + e];
     }
     const int rows = tot[e + 1] - tot[e];
-    for (int m = 0; m < rows; m += kTM) tiles[tstart[e] + m / kTM] = make_int2(e, tot[e] + m);
+    for (int m = p * kTM; m < rows; m += P * kTM) tiles[tst[e] + m / kTM] = make_int2(e, tot[e] + m);
   }
 }
 
