@@ -44,6 +44,8 @@ def parse():
                     help="how the timed (headline) run fills cache misses; the other way is "
                          "timed afterwards and reported in detail")
     ap.add_argument("--no-variant", action="store_true", help="skip the other fill variant")
+    ap.add_argument("--sweep-slots", default="8,32,64",
+                    help="slot counts per layer for the cache-size sweep in the detail ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
@@ -305,6 +307,46 @@ def main():
         detail["fill_" + other.replace("-", "_")] = {
             "tokens_per_s": args.steps / el_f, "ms_per_step": 1e3 * el_f / args.steps,
             "hit_rate_timed": hf / max(hf + mf, 1)}
+
+    # ---------------------------------------------------------------- slot-count sweep
+    # The same stack with other pool sizes (fresh caches, the headline's fill
+    # path, half the timed tokens): hit rate, bytes over PCIe and tokens/s per
+    # slot count.
+    sweep = [int(v) for v in args.sweep_slots.split(",") if v.strip()]
+    if sweep:
+        detail["slot_sweep"] = {}
+        n_sw = max(args.steps // 2, 8)
+        for S2 in sweep:
+            if S2 < k or S2 > E:
+                continue
+            hs = []
+            for d in layers:
+                d["pool2"] = torch.empty((S2, blob), dtype=torch.uint8, device=devn)
+                d["ws2"] = torch.zeros_like(d["ws"])
+                hs.append(api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"],
+                                               workspace=d["ws2"], bias=d["bias"], experts_host=d["host"],
+                                               slot_pool=d["pool2"], n_slots=S2, copy_stream=copy_stream))
+            st2 = [api.moe_decode_stats() for _ in range(Lyr)]
+            for t in range(args.warmup):
+                token(t, hs, st2)
+            torch.cuda.synchronize()
+            w2 = [(s.hits, s.misses, s.h2d_bytes) for s in st2]
+            t0 = time.perf_counter()
+            for t in range(args.warmup, args.warmup + n_sw):
+                token(t, hs, st2)
+            torch.cuda.synchronize()
+            el2 = time.perf_counter() - t0
+            h2 = sum(s.hits - w[0] for s, w in zip(st2, w2))
+            m2 = sum(s.misses - w[1] for s, w in zip(st2, w2))
+            b2 = sum(s.h2d_bytes - w[2] for s, w in zip(st2, w2))
+            detail["slot_sweep"][str(S2)] = {"tokens_per_s": n_sw / el2, "hit_rate": h2 / max(h2 + m2, 1),
+                                             "h2d_MB_per_token": b2 / n_sw / 1e6, "tokens": n_sw}
+            for h_ in hs:
+                api.moe_layer_destroy(h_)
+            for d in layers:
+                del d["pool2"], d["ws2"]
+            torch.cuda.synchronize()
+        print("[bench] slot sweep done", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- all experts resident
     if not args.no_resident:

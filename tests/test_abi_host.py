@@ -60,10 +60,13 @@ def _traces():
     out.append((8, 128, 8, [[(8 * t + j) % 128 for j in range(8)] for t in range(50)]))
     out.append((2, 16, 1, [[x] for x in rng.integers(0, 4, 300)]))
     out.append((9, 32, 8, [rng.choice(10, 8, replace=False) for _ in range(300)]))
+    # the slot counts of the benchmark's sweep, on the Zipf-biased trace
+    out.append((32, 128, 8, [rng.choice(128, 8, replace=False, p=p) for _ in range(400)]))
+    out.append((64, 128, 8, [rng.choice(128, 8, replace=False, p=p) for _ in range(400)]))
     return out
 
 
-@pytest.mark.parametrize("case", range(5))
+@pytest.mark.parametrize("case", range(7))
 def test_native_lfu_matches_simulator(case):
     S, E, k, rows = _traces()[case]
     ref, sim = simulate(rows, S, E)
