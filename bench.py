@@ -44,6 +44,10 @@ def parse():
                     help="how the timed (headline) run fills cache misses; the other way is "
                          "timed afterwards and reported in detail")
     ap.add_argument("--no-variant", action="store_true", help="skip the other fill variant")
+    ap.add_argument("--no-file-store", action="store_true",
+                    help="skip the variant whose misses are read from an expert file with parallel pread")
+    ap.add_argument("--store-threads", type=int, default=8, help="reader threads of the expert file store")
+    ap.add_argument("--store-tokens", type=int, default=48, help="tokens timed with the expert file store")
     ap.add_argument("--sweep-slots", default="8,32,64",
                     help="slot counts per layer for the cache-size sweep in the detail ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -347,6 +351,70 @@ def main():
                 del d["pool2"], d["ws2"]
             torch.cuda.synchronize()
         print("[bench] slot sweep done", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- expert file store
+    # The same stack with the misses read from a file of all layers' experts
+    # (each blob padded to 16 KiB pages) by parallel pread, unbuffered where
+    # the file system allows, then copied like the host-memory misses. The
+    # file is written and synced first, so the reads come from the disk.
+    if not args.no_file_store:
+        import shutil
+        tmpdir = os.environ.get("TMPDIR", "/tmp")
+        stride = api.moe_store_stride(blob)
+        need = Lyr * E * stride
+        if shutil.disk_usage(tmpdir).free < need + (8 << 30):
+            detail["file_store"] = {"skipped": f"less than {need / 1e9 + 8:.1f} GB free in {tmpdir}"}
+        else:
+            path = os.path.join(tmpdir, f"moe_experts_{os.getpid()}.bin")
+            t_w = time.perf_counter()
+            try:
+                pad = np.zeros((E, stride), np.uint8)
+                with open(path, "wb") as fh:
+                    for d in layers:
+                        pad[:, :blob] = d["host"].numpy()
+                        fh.write(pad.data)
+                    fh.flush()
+                    os.fsync(fh.fileno())
+                t_w = time.perf_counter() - t_w
+                store = api.moe_store_open(path, Lyr, E, blob, args.store_threads, True)
+                hs = []
+                for l, d in enumerate(layers):
+                    d["pool3"] = torch.empty((S, blob), dtype=torch.uint8, device=devn)
+                    d["ws3"] = torch.zeros_like(d["ws"])
+                    hs.append(api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"],
+                                                   workspace=d["ws3"], bias=d["bias"], slot_pool=d["pool3"],
+                                                   n_slots=S, copy_stream=copy_stream, store=store,
+                                                   store_layer=l))
+                st3 = [api.moe_decode_stats() for _ in range(Lyr)]
+                n_w3 = min(args.warmup, 16)
+                for t in range(n_w3):
+                    token(t, hs, st3)
+                torch.cuda.synchronize()
+                w3 = [(s.hits, s.misses, s.h2d_bytes) for s in st3]
+                n3 = args.store_tokens
+                t0 = time.perf_counter()
+                for t in range(n_w3, n_w3 + n3):
+                    token(t, hs, st3)
+                torch.cuda.synchronize()
+                el3 = time.perf_counter() - t0
+                h3 = sum(s.hits - w[0] for s, w in zip(st3, w3))
+                m3 = sum(s.misses - w[1] for s, w in zip(st3, w3))
+                b3 = sum(s.h2d_bytes - w[2] for s, w in zip(st3, w3))
+                detail["file_store"] = {
+                    "tokens_per_s": n3 / el3, "ms_per_step": 1e3 * el3 / n3, "tokens": n3,
+                    "hit_rate": h3 / max(h3 + m3, 1), "misses_per_token": m3 / n3,
+                    "expert_GBps_wall": b3 / el3 / 1e9, "unbuffered": api.moe_store_is_direct(store),
+                    "reader_threads": args.store_threads, "file_GB": need / 1e9,
+                    "file_write_and_sync_s": t_w}
+                for h_ in hs:
+                    api.moe_layer_destroy(h_)
+                api.moe_store_close(store)
+                for d in layers:
+                    del d["pool3"], d["ws3"]
+            finally:
+                if os.path.exists(path):
+                    os.remove(path)
+        print("[bench] file store done", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- all experts resident
     if not args.no_resident:

@@ -34,7 +34,8 @@ class moe_cache_event(C.Structure):
 class moe_layer_desc(C.Structure):
     _fields_ = [("router", vp), ("bias", vp), ("shared_blob", vp), ("experts_dev", vp),
                 ("experts_host", vp), ("slot_pool", vp), ("n_slots", C.c_int32),
-                ("copy_stream", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("copy_stream", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t),
+                ("store", vp), ("store_layer", C.c_int32)]
 
 
 class moe_decode_stats(C.Structure):
@@ -74,6 +75,11 @@ SIGNATURES = {
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
+    "moe_store_stride": (C.c_int64, [C.c_int64]),
+    "moe_store_open": (c_status, [C.c_char_p, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(vp)]),
+    "moe_store_is_direct": (C.c_int32, [vp]),
+    "moe_store_close": (None, [vp]),
+    "moe_store_read": (c_status, [vp, C.c_int32, P(C.c_int32), C.c_int32, P(vp)]),
 }
 
 _lib = None

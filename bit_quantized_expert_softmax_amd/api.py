@@ -163,12 +163,12 @@ def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
 
 def moe_layer_create(sh, *, router, shared_blob, workspace, bias=None, experts_dev=None,
                      experts_host=None, slot_pool=None, n_slots=0, copy_stream=None, max_B=1,
-                     max_T=0) -> int:
+                     max_T=0, store=None, store_layer=0) -> int:
     s = make_shape(sh)
     d = L.moe_layer_desc(_p(router), _p(bias), _p(shared_blob), _p(experts_dev), _p(experts_host),
                          _p(slot_pool), n_slots,
                          None if copy_stream is None else _stream(copy_stream),
-                         _p(workspace), workspace.numel() * workspace.element_size())
+                         _p(workspace), workspace.numel() * workspace.element_size(), store, store_layer)
     h = C.c_void_p()
     _check(lib().moe_layer_create(C.byref(s), C.byref(d), max_B, max_T, C.byref(h)), "moe_layer_create")
     return h.value
@@ -214,3 +214,33 @@ def moe_layer_profile_read(h, kind: int):
     out = L.moe_kernel_time()
     _check(lib().moe_layer_profile_read(h, kind, C.byref(out)), "moe_layer_profile_read")
     return out.launches, out.ms_total
+
+
+# ---------------------------------------------------------------- expert file store
+def moe_store_stride(blob_bytes: int) -> int:
+    return int(lib().moe_store_stride(blob_bytes))
+
+
+def moe_store_open(path: str, n_layers: int, n_experts: int, blob_bytes: int, threads: int = 8,
+                   direct: bool = True) -> int:
+    h = C.c_void_p()
+    _check(lib().moe_store_open(path.encode(), n_layers, n_experts, blob_bytes, threads, 1 if direct else 0,
+                                C.byref(h)), "moe_store_open")
+    return h.value
+
+
+def moe_store_is_direct(h) -> bool:
+    return bool(lib().moe_store_is_direct(h))
+
+
+def moe_store_close(h) -> None:
+    lib().moe_store_close(h)
+
+
+def moe_store_read(h, layer: int, experts, dst_ptrs) -> None:
+    """Reads the padded blobs of `experts` (ints) of `layer` into host buffers
+    at the addresses dst_ptrs (one stride each)."""
+    n = len(experts)
+    ids = (C.c_int32 * max(n, 1))(*experts)
+    ptrs = (C.c_void_p * max(n, 1))(*dst_ptrs)
+    _check(lib().moe_store_read(h, layer, ids, n, ptrs), "moe_store_read")

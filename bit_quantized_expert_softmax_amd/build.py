@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoedecode.so")
 
 # plain C++ (no HIP headers)
-HOST_SOURCES = ["lfu.cpp"]
+HOST_SOURCES = ["lfu.cpp", "store.cpp"]
 # compiled as HIP: kernels, and host code that calls the HIP runtime
 HIP_SOURCES = ["abi.cpp", "layer.cpp", "route.hip", "decode.hip", "gemv.hip", "prefill.hip", "batched.hip"]
 ARCH = "gfx950"

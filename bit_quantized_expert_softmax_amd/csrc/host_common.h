@@ -29,6 +29,9 @@ void cache_assign(moe_cache* dst, const moe_cache* src);
 
 inline void clear_error() { last_error_text().clear(); }
 
+// Whether a store holds layer `layer` of n_experts blobs of blob_bytes each.
+bool store_fits(const moe_store* s, int layer, int n_experts, int64_t blob_bytes);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace moe

@@ -98,6 +98,11 @@ struct moe_layer {
   int32_t seq = 0;              // sequence number of the last routing published
   const uint8_t* host_dev = nullptr;  // device address of experts_host (fill-kernel option)
   hipEvent_t ev_fill = nullptr;
+  // file store (cache mode): the misses are read into pinned staging first
+  uint8_t* staging = nullptr;            // [kMaxTopK][stride]
+  const uint8_t* staging_dev = nullptr;  // its device address (fill-kernel option)
+  int64_t stride = 0;
+  bool staging_busy = false;  // copies out of the staging may still run (ev_fill)
   // profiling
   bool prof = false;
   uint32_t prof_mask = 0;  // kinds recorded while profiling (bit i = kind i)
@@ -239,8 +244,12 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     return fail(MOE_EINVAL, "%s: router, shared_blob and workspace are required", fn);
   const bool cache_mode = d->experts_dev == nullptr;
   if (cache_mode) {
-    if (!d->experts_host || !d->slot_pool)
-      return fail(MOE_EINVAL, "%s: cache mode needs experts_host and slot_pool", fn);
+    if (!d->slot_pool || (!d->experts_host) == (!d->store))
+      return fail(MOE_EINVAL, "%s: cache mode needs slot_pool and exactly one of experts_host and store", fn);
+    if (d->store &&
+        !moe::store_fits(d->store, d->store_layer, sh->n_experts, moe_expert_bytes(sh->hidden, sh->inter)))
+      return fail(MOE_ESHAPE, "%s: the store has no layer %d of %d blobs of this shape", fn, d->store_layer,
+                  sh->n_experts);
     if (d->n_slots < sh->top_k || d->n_slots > sh->n_experts)
       return fail(MOE_ESHAPE, "%s: n_slots %d outside [top_k=%d, n_experts=%d]", fn, d->n_slots,
                   sh->top_k, sh->n_experts);
@@ -283,11 +292,22 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     *L->seq_host = 0;
     // the fill-kernel option reads the store from the device; pinned memory
     // from hipHostMalloc has a device address, other memory has none
-    hipPointerAttribute_t pa{};
-    if (hipPointerGetAttributes(&pa, d->experts_host) == hipSuccess && pa.type == hipMemoryTypeHost &&
-        pa.devicePointer)
-      L->host_dev = static_cast<const uint8_t*>(pa.devicePointer);
-    (void)hipGetLastError();  // a failed query leaves the option unavailable, not an error
+    if (d->store) {
+      // staging for one token's misses, page aligned (unbuffered reads)
+      L->stride = moe_store_stride(static_cast<int64_t>(L->blob_e));
+      e = hipHostMalloc(reinterpret_cast<void**>(&L->staging), static_cast<size_t>(L->stride) * moe::kMaxTopK,
+                        hipHostMallocDefault);
+      if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned staging for the store", e);
+      void* dp = nullptr;
+      if (hipHostGetDevicePointer(&dp, L->staging, 0) == hipSuccess) L->staging_dev = static_cast<const uint8_t*>(dp);
+      (void)hipGetLastError();
+    } else {
+      hipPointerAttribute_t pa{};
+      if (hipPointerGetAttributes(&pa, d->experts_host) == hipSuccess && pa.type == hipMemoryTypeHost &&
+          pa.devicePointer)
+        L->host_dev = static_cast<const uint8_t*>(pa.devicePointer);
+      (void)hipGetLastError();  // a failed query leaves the option unavailable, not an error
+    }
     e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
     moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
@@ -304,6 +324,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
 void moe_layer_destroy(moe_layer* L) {
   if (!L) return;
   if (L->ids_host) (void)hipHostFree(L->ids_host);
+  if (L->staging) (void)hipHostFree(L->staging);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   for (auto& v : L->rec)
     for (auto& p : v) {
@@ -337,7 +358,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
   const bool fill_kernel = flags & MOE_F_FILL_KERNEL;
   if (fill_kernel && !L->cache_mode) return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs a cache-mode handle", fn);
-  if (fill_kernel && !L->host_dev)
+  if (fill_kernel && !(L->d.store ? L->staging_dev : L->host_dev))
     return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs experts_host in device-accessible pinned memory", fn);
   if (B < 0 || B > L->max_B) return fail(MOE_ESHAPE, "%s: B=%d outside [0, max_B=%d]", fn, B, L->max_B);
   if (B == 0) return MOE_OK;
@@ -450,6 +471,46 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   moe::cache_assign(L->cache_backup, L->cache);
   moe_status cs = moe_cache_step(L->cache, L->ids_host, k, ev, &n_miss);
   if (cs) return cs;
+  // where each miss's bytes come from (host and device addresses): the host
+  // store, or the staging that the file store reads them into
+  const uint8_t* src_h[moe::kMaxTopK];
+  const uint8_t* src_d[moe::kMaxTopK];
+  if (L->d.store && n_miss > 0) {
+    // the staging's previous copies (this handle's last call) must be done
+    if (L->staging_busy) {
+      const hipError_t se = hipEventSynchronize(L->ev_fill);
+      if (se != hipSuccess) {
+        moe::cache_assign(L->cache, L->cache_backup);
+        return fail(MOE_EHIP, "%s: waiting for the staging: %s", fn, hipGetErrorString(se));
+      }
+      L->staging_busy = false;
+    }
+    int32_t mexp[moe::kMaxTopK];
+    void* mdst[moe::kMaxTopK];
+    int nm = 0;
+    for (int j = 0; j < k; ++j)
+      if (!ev[j].hit) {
+        mexp[nm] = ev[j].expert;
+        mdst[nm] = L->staging + static_cast<size_t>(nm) * L->stride;
+        ++nm;
+      }
+    const moe_status rs = moe_store_read(L->d.store, L->d.store_layer, mexp, nm, mdst);
+    if (rs) {
+      moe::cache_assign(L->cache, L->cache_backup);
+      return rs;
+    }
+  }
+  for (int j = 0, m = 0; j < k; ++j) {
+    if (ev[j].hit) continue;
+    if (L->d.store) {
+      src_h[j] = L->staging + static_cast<size_t>(m) * L->stride;
+      src_d[j] = L->staging_dev ? L->staging_dev + static_cast<size_t>(m) * L->stride : nullptr;
+      ++m;
+    } else {
+      src_h[j] = L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e;
+      src_d[j] = L->host_dev ? L->host_dev + static_cast<size_t>(ev[j].expert) * L->blob_e : nullptr;
+    }
+  }
   hipError_t ce = hipSuccess;
   if (fill_kernel) {
     // the misses are copied by fill blocks of the shared-expert gate/up launch
@@ -458,24 +519,28 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     F.bytes = L->blob_e;
     for (int j = 0; j < k; ++j) {
       if (ev[j].hit) continue;
-      F.src[F.n] = L->host_dev + static_cast<size_t>(ev[j].expert) * L->blob_e;
+      F.src[F.n] = src_d[j];
       F.dst[F.n] = L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e;
       ++F.n;
     }
     const ProfPair p1 = prof_pair(L, 1);
     ce = moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
     if (ce == hipSuccess) prof_add(L, 1, p1);
+    if (ce == hipSuccess && L->d.store && n_miss > 0) {
+      ce = hipEventRecord(L->ev_fill, s);
+      L->staging_busy = ce == hipSuccess;
+    }
   } else {
     hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
     for (int j = 0; j < k && ce == hipSuccess; ++j) {
       if (ev[j].hit) continue;
-      ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e,
-                          L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e, L->blob_e,
+      ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src_h[j], L->blob_e,
                           hipMemcpyHostToDevice, cp);
     }
     if (ce == hipSuccess && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, cp);
       if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+      L->staging_busy = ce == hipSuccess && L->d.store;
     }
   }
   if (ce != hipSuccess) {

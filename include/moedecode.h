@@ -164,6 +164,33 @@ moe_status moe_expert_gemv_q4(const moe_q4* W, int32_t N, int32_t K, const float
  * All pointers are borrowed and must stay valid and unmodified until
  * moe_layer_destroy. */
 typedef struct moe_layer moe_layer;
+/* ---------------------------------------------------------------- expert file store
+ * Source: "Show HN: mecanismo de código aberto executando Gemma 4 26B em 2 GB
+ * de RAM em qualquer Mac com série M", section "Abordagem técnica (MoE +
+ * streaming por SSD)": experts are streamed from the SSD with parallel pread.
+ * The file holds expert blobs in the order [layer][expert], each padded to
+ * moe_store_stride(blob) bytes (a whole number of 16 KiB pages; the padding is
+ * not read into the slot). */
+typedef struct moe_store moe_store;
+int64_t moe_store_stride(int64_t blob_bytes);
+/* Opens path with `threads` reader threads (1..64). direct != 0 asks for
+ * unbuffered reads (O_DIRECT); where the file system refuses them the store
+ * reads through the page cache (moe_store_is_direct tells which). The file
+ * must hold n_layers * n_experts strides: MOE_ESHAPE otherwise, MOE_EINVAL if
+ * it cannot be opened. */
+moe_status moe_store_open(const char* path, int32_t n_layers, int32_t n_experts, int64_t blob_bytes,
+                          int32_t threads, int32_t direct, moe_store** out);
+int32_t moe_store_is_direct(const moe_store* s);
+/* Joins the readers and closes the file (NULL: no-op). */
+void moe_store_close(moe_store* s);
+/* Reads the padded blobs of experts[0..n) of one layer into dst[i] (host
+ * memory of at least one stride each; 4096-byte aligned for unbuffered
+ * reads, MOE_EALIGN otherwise). Each blob is split into one page-aligned part
+ * per reader; returns when every part is in. Calls on one store are
+ * serialised. Errors: MOE_EINVAL (bad layer, expert or pointer, read error),
+ * MOE_ESHAPE (file shorter than a blob). */
+moe_status moe_store_read(moe_store* s, int32_t layer, const int32_t* experts, int32_t n, void* const* dst);
+
 typedef struct moe_layer_desc {
   const uint16_t* router;       /* dev fp16 [E][H]                               */
   const float* bias;            /* dev fp32 [E] added to the logits, or NULL     */
@@ -175,6 +202,11 @@ typedef struct moe_layer_desc {
   void* copy_stream;            /* cache mode: hipStream_t for the miss copies   */
   void* workspace;              /* dev, moe_layer_workspace_bytes bytes          */
   size_t workspace_bytes;
+  /* cache mode, instead of experts_host: the misses are read from this store
+   * (layer store_layer) into pinned staging owned by the handle, then copied
+   * to their slots like host-memory misses. Not owned by the handle. */
+  moe_store* store;
+  int32_t store_layer;
 } moe_layer_desc;
 
 typedef struct moe_decode_stats {

@@ -46,7 +46,8 @@ def assert_close(gpu, ref, what="", rel=1e-3, abs_=1e-5):
 class Layer:
     """Owns the device copies of one layer's inputs and a libmoedecode handle."""
 
-    def __init__(self, shape, d, *, bias=None, cache_slots=0, max_B=1, max_T=0, copy_stream=None):
+    def __init__(self, shape, d, *, bias=None, cache_slots=0, max_B=1, max_T=0, copy_stream=None,
+                 store=None, store_layer=0):
         self.shape = shape
         self.router = dev_u16(d["router"])
         self.shared = dev(d["shared"])
@@ -54,13 +55,15 @@ class Layer:
         self.ws = torch.zeros(api.moe_layer_workspace_bytes(shape, max_B, max_T), dtype=torch.uint8,
                               device=DEV)
         if cache_slots:
-            self.host = pinned(d["experts"])
+            # misses from pinned host memory, or (store given) from an expert file
+            self.host = pinned(d["experts"]) if store is None else None
             self.pool = torch.zeros((cache_slots, d["experts"].shape[1]), dtype=torch.uint8, device=DEV)
             self.copy_stream = copy_stream or torch.cuda.Stream()
             self.h = api.moe_layer_create(shape, router=self.router, shared_blob=self.shared,
                                           workspace=self.ws, bias=self.bias, experts_host=self.host,
                                           slot_pool=self.pool, n_slots=cache_slots,
-                                          copy_stream=self.copy_stream, max_B=max_B, max_T=max_T)
+                                          copy_stream=self.copy_stream, max_B=max_B, max_T=max_T,
+                                          store=store, store_layer=store_layer)
         else:
             self.experts = dev(d["experts"])
             self.h = api.moe_layer_create(shape, router=self.router, shared_blob=self.shared,

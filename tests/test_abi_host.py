@@ -123,7 +123,7 @@ def test_lfu_under_sanitizers(tmp_path):
         assert r.stdout.splitlines()[-1] == f"END {sim.hits} {sim.misses} {len(rows)}"
 
 
-def test_gpu_entry_points_reject_bad_arguments_before_enqueue():
+def test_gpu_entry_points_reject_bad_arguments_before_enqueue(tmp_path):
     import ctypes as C
     lib = _lib.load()
     sh = api.make_shape(SMALL_LAYER)
@@ -151,6 +151,22 @@ def test_gpu_entry_points_reject_bad_arguments_before_enqueue():
     d.experts_dev = None
     d.experts_host, d.slot_pool, d.n_slots, d.workspace_bytes = 16, 16, 4, out.value
     assert lib.moe_layer_create(C.byref(sh), C.byref(d), 1, 0, C.byref(h)) == -2
+    # cache mode takes exactly one miss source, and a store must hold the layer
+    import numpy as np
+    from synth import gen
+    blob = gen.blob_bytes(SMALL_LAYER.hidden, SMALL_LAYER.inter)
+    f = tmp_path / "one_layer.bin"
+    np.zeros(SMALL_LAYER.n_experts * api.moe_store_stride(blob), np.uint8).tofile(str(f))
+    st = api.moe_store_open(str(f), 1, SMALL_LAYER.n_experts, blob, 2, False)
+    try:
+        d.store = st
+        assert lib.moe_layer_create(C.byref(sh), C.byref(d), 1, 0, C.byref(h)) == -1   # host and store
+        d.experts_host, d.store_layer = None, 1
+        assert lib.moe_layer_create(C.byref(sh), C.byref(d), 1, 0, C.byref(h)) == -2   # no layer 1
+        assert "store" in api.moe_last_error()
+    finally:
+        d.store, d.store_layer = None, 0
+        api.moe_store_close(st)
     # batched decode of a shape whose staged scales and 64-token slices exceed
     # 64 KiB of LDS per block: refused at create (with max_B = 1 it passes
     # this check and fails later, on the missing descriptor fields)

@@ -146,6 +146,39 @@ def test_fill_kernel_matches_copy_engine_bitwise():
     Lb.close()
 
 
+@pytest.mark.parametrize("flags", [0, api.MOE_F_FILL_KERNEL], ids=["copy_engine", "fill_kernel"])
+def test_file_store_matches_host_memory_bitwise(tmp_path, flags):
+    """Misses read from an expert file (parallel pread into pinned staging,
+    layer 1 of a 2-layer file) leave the same slots and give the same bits as
+    misses copied from pinned host memory, with the simulator's cache trace."""
+    sh = SMALL_LAYER
+    d = layer_data(sh, 2)
+    bias = gen.zipf_bias(sh.n_experts, 2, 0)
+    blob = d["experts"].shape[1]
+    stride = api.moe_store_stride(blob)
+    padded = np.zeros((2, sh.n_experts, stride), np.uint8)
+    padded[0, :, :blob] = np.random.default_rng(3).integers(0, 256, (sh.n_experts, blob), dtype=np.uint8)
+    padded[1, :, :blob] = d["experts"]
+    path = str(tmp_path / "experts.bin")
+    padded.tofile(path)
+    store = api.moe_store_open(path, 2, sh.n_experts, blob, 4, True)
+    La = Layer(sh, d, bias=bias, cache_slots=8)
+    Lb = Layer(sh, d, bias=bias, cache_slots=8, store=store, store_layer=1)
+    sim = lfu.LFUCache(8, sh.n_experts)
+    xs = gen.x_fp32(12, sh.hidden, 2, sub=5)
+    for t in range(12):
+        ya, ida, _, _, tra = run_decode(La, dev(xs[t:t + 1]), flags=flags, trace_k=sh.top_k)
+        yb, idb, _, _, trb = run_decode(Lb, dev(xs[t:t + 1]), flags=flags, trace_k=sh.top_k)
+        assert np.array_equal(ida, idb) and np.array_equal(tra, trb), t
+        assert [tuple(e) for e in trb.tolist()] == [tuple(e) for e in sim.step(idb[0])], t
+        assert np.array_equal(ya, yb), t
+    assert sim.misses > 8 and sim.hits > 0
+    assert np.array_equal(La.pool.cpu().numpy(), Lb.pool.cpu().numpy())
+    La.close()
+    Lb.close()
+    api.moe_store_close(store)
+
+
 def test_fill_kernel_needs_cache_mode():
     sh = SMALL_LAYER
     d = layer_data(sh, 0)
