@@ -105,6 +105,14 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is);
 
 // ---------------------------------------------------------------- prefill
 // Workspace layout of a prefill of up to T tokens (byte offsets).
+// Experts of one slot-pool group and their slots (prefill through the pool).
+constexpr int kMaxGroup = 16;
+struct SlotGroup {
+  int32_t expert[kMaxGroup];
+  int32_t slot[kMaxGroup];
+  int32_t n;
+};
+
 struct PrefillLayout {
   size_t ids, w, hist, base, local_rank, seg, tiles, n_tiles, perm, pos_of, act_r, act_s, out_r, xf, z,
       total;
@@ -119,6 +127,19 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
                           int E, int k, int H, int I, int Is, const uint8_t* experts, size_t blob_e,
                           const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
                           hipStream_t s);
+// Its stages, for prefill through the slot pool: routing and the stable sort
+// of the assignments (seg / tiles / perm / pos_of in the layout); the routed
+// GEMMs (group == nullptr: every expert, experts + id * blob_e; else only the
+// group's experts, experts + slot * blob_e); the shared expert and the
+// combine into y.
+hipError_t launch_prefill_route(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
+                                const float* logits_in, const uint16_t* router, const float* bias, int T,
+                                int E, int k, int H, int32_t* ids_out, float* w_out, hipStream_t s);
+hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int k, int H,
+                                 int I, const uint8_t* experts, size_t blob_e, const SlotGroup* group,
+                                 hipStream_t s);
+hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
+                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s);
 
 // ---------------------------------------------------------------- batched decode
 // Stable sort of A assignments (token*k + rank, expert ids[a]) by expert:

@@ -103,6 +103,9 @@ struct moe_layer {
   const uint8_t* staging_dev = nullptr;  // its device address (fill-kernel option)
   int64_t stride = 0;
   bool staging_busy = false;  // copies out of the staging may still run (ev_fill)
+  // prefill through the slot pool (cache mode)
+  int32_t* seg_host = nullptr;    // pinned, the chunk's expert offsets [E+1]
+  hipEvent_t ev_pool = nullptr;   // the pool's readers (kernels on the call's stream) are done
   // profiling
   bool prof = false;
   uint32_t prof_mask = 0;  // kinds recorded while profiling (bit i = kind i)
@@ -309,7 +312,13 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
       (void)hipGetLastError();  // a failed query leaves the option unavailable, not an error
     }
     e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_pool, hipEventDisableTiming);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
+    if (max_T > 0) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&L->seg_host), sizeof(int32_t) * (sh->n_experts + 1),
+                        hipHostMallocDefault);
+      if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned expert offsets", e);
+    }
     moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
     if (!cs) cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache_backup);
     if (cs) {
@@ -325,6 +334,8 @@ void moe_layer_destroy(moe_layer* L) {
   if (!L) return;
   if (L->ids_host) (void)hipHostFree(L->ids_host);
   if (L->staging) (void)hipHostFree(L->staging);
+  if (L->seg_host) (void)hipHostFree(L->seg_host);
+  if (L->ev_pool) (void)hipEventDestroy(L->ev_pool);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   for (auto& v : L->rec)
     for (auto& p : v) {
@@ -564,12 +575,114 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   return MOE_OK;
 }
 
+namespace {
+
+constexpr int kPrefillChunk = 128;  // tokens per chunk through the slot pool
+
+// Prefill through the slot pool (cache mode). "Como executar um modelo de 26
+// bilhões de parâmetros em dois gigabytes de memória em um Mac comum",
+// section "Desempenho no mundo real": prompt processing in chunks of 128
+// tokens, so that one loaded expert serves a group of rows at once. Per chunk:
+// routing and the stable sort of its assignments; the chunk's experts (from
+// the sorted offsets, read back to the host) in groups of up to
+// min(n_slots, 16), each an LFU step whose misses are copied into their slots
+// after the previous group's kernels, then the group's routed GEMMs on the
+// slots; last the shared expert and the combine. Each output row is the same
+// sum as in the resident prefill, so the result is the same bits.
+moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logits_in, int T, float* y,
+                        int32_t* ids_out, float* w_out, hipStream_t s, const char* fn) {
+  const moe_shape& sh = L->sh;
+  const int E = sh.n_experts, k = sh.top_k, H = sh.hidden;
+  const int chunk = L->max_T < kPrefillChunk ? L->max_T : kPrefillChunk;
+  const moe::PrefillLayout P = moe::prefill_layout(chunk, E, k, H, sh.inter, sh.shared_inter);
+  uint8_t* pw = L->wsb + L->ws.pre;
+  hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
+  const int gmax = L->d.n_slots < moe::kMaxGroup ? L->d.n_slots : moe::kMaxGroup;
+  for (int c0 = 0; c0 < T; c0 += chunk) {
+    const int Tc = T - c0 < chunk ? T - c0 : chunk;
+    const uint16_t* xc = x_bf16 + static_cast<size_t>(c0) * H;
+    HIP_OR_FAIL(moe::launch_prefill_route(P, pw, xc, logits_in ? logits_in + static_cast<size_t>(c0) * E : nullptr,
+                                          L->d.router, L->d.bias, Tc, E, k, H,
+                                          ids_out ? ids_out + static_cast<size_t>(c0) * k : nullptr,
+                                          w_out ? w_out + static_cast<size_t>(c0) * k : nullptr, s), fn);
+    HIP_OR_FAIL(hipMemcpyAsync(L->seg_host, pw + P.seg, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToHost, s), fn);
+    HIP_OR_FAIL(hipStreamSynchronize(s), fn);
+    int32_t experts[MOE_MAX_EXPERTS];
+    int nx = 0;
+    for (int e = 0; e < E; ++e)
+      if (L->seg_host[e + 1] > L->seg_host[e]) experts[nx++] = e;
+    for (int g0 = 0; g0 < nx; g0 += gmax) {
+      const int n = nx - g0 < gmax ? nx - g0 : gmax;
+      moe_cache_event ev[moe::kMaxGroup];
+      int32_t n_miss = 0;
+      moe::cache_assign(L->cache_backup, L->cache);
+      moe_status cs = moe_cache_step(L->cache, experts + g0, n, ev, &n_miss);
+      if (cs) return cs;
+      auto undo = [&](moe_status code, const char* what, const char* detail) {
+        moe::cache_assign(L->cache, L->cache_backup);
+        return fail(code, "%s: %s: %s", fn, what, detail);
+      };
+      if (n_miss > 0) {
+        // a miss may evict a slot that earlier kernels on s still read
+        hipError_t ce = hipEventRecord(L->ev_pool, s);
+        if (ce == hipSuccess) ce = hipStreamWaitEvent(cp, L->ev_pool, 0);
+        const uint8_t* src[moe::kMaxGroup];
+        if (ce == hipSuccess && L->d.store) {
+          if (L->staging_busy) {
+            ce = hipEventSynchronize(L->ev_fill);
+            L->staging_busy = false;
+          }
+          int32_t mexp[moe::kMaxGroup];
+          void* mdst[moe::kMaxGroup];
+          int nm = 0;
+          for (int j = 0; j < n; ++j)
+            if (!ev[j].hit) {
+              mexp[nm] = ev[j].expert;
+              mdst[nm] = L->staging + static_cast<size_t>(nm) * L->stride;
+              src[j] = static_cast<const uint8_t*>(mdst[nm]);
+              ++nm;
+            }
+          if (ce == hipSuccess) {
+            const moe_status rs = moe_store_read(L->d.store, L->d.store_layer, mexp, nm, mdst);
+            if (rs) {
+              moe::cache_assign(L->cache, L->cache_backup);
+              return rs;
+            }
+          }
+        } else {
+          for (int j = 0; j < n; ++j)
+            if (!ev[j].hit) src[j] = L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e;
+        }
+        for (int j = 0; j < n && ce == hipSuccess; ++j)
+          if (!ev[j].hit)
+            ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src[j], L->blob_e,
+                                hipMemcpyHostToDevice, cp);
+        if (ce == hipSuccess) ce = hipEventRecord(L->ev_fill, cp);
+        if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+        if (ce != hipSuccess) return undo(MOE_EHIP, "miss copy", hipGetErrorString(ce));
+        L->staging_busy = L->d.store != nullptr;
+      }
+      moe::SlotGroup grp{};
+      grp.n = n;
+      for (int j = 0; j < n; ++j) {
+        grp.expert[j] = ev[j].expert;
+        grp.slot[j] = ev[j].slot;
+      }
+      HIP_OR_FAIL(moe::launch_prefill_routed(P, pw, xc, k, H, sh.inter, L->d.slot_pool, L->blob_e, &grp, s), fn);
+    }
+    HIP_OR_FAIL(moe::launch_prefill_shared(P, pw, xc, Tc, k, H, sh.shared_inter, L->d.shared_blob,
+                                           y + static_cast<size_t>(c0) * H, s), fn);
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in, int32_t T,
                              float* y, int32_t* ids_out, float* w_out, void* stream) {
   moe::clear_error();
   const char* fn = "moe_layer_prefill";
   if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
-  if (L->cache_mode) return fail(MOE_ESTATE, "%s: prefill needs a resident-mode handle", fn);
   if (T < 0 || T > L->max_T) return fail(MOE_ESHAPE, "%s: T=%d outside [0, max_T=%d]", fn, T, L->max_T);
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !y) return fail(MOE_EINVAL, "%s: x_bf16 and y are required", fn);
@@ -582,6 +695,12 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
   const moe::PrefillLayout P = moe::prefill_layout(L->max_T, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                                    sh.shared_inter);
   hipEvent_t pb = prof_begin(L, 4, s);
+  if (L->cache_mode) {
+    const moe_status ps = prefill_pool(L, x_bf16, logits_in, T, y, ids_out, w_out, s, fn);
+    if (ps) return ps;
+    prof_end(L, 4, pb, s);
+    return MOE_OK;
+  }
   HIP_OR_FAIL(moe::launch_prefill(P, L->wsb + L->ws.pre, x_bf16, logits_in, L->d.router, L->d.bias, T,
                                   sh.n_experts, sh.top_k, sh.hidden, sh.inter, sh.shared_inter,
                                   L->d.experts_dev, L->blob_e, L->d.shared_blob, y, ids_out, w_out, s),

@@ -240,6 +240,9 @@ struct GemmArgs {
   const float* out_r;
   const int32_t* pos_of;
   int k;
+  // routed, slot pool: only the tiles of these experts run, each expert's
+  // weights at experts + slot * blob_e (n_group == 0: every expert, at its id)
+  SlotGroup group;
 };
 
 template <bool GATEUP, bool ROUTED>
@@ -255,10 +258,17 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
   if (ROUTED) {
     if (mt >= *G.n_tiles) return;
     const int2 td = G.tiles[mt];
+    int where = td.x;  // expert id (resident) or its slot (slot pool)
+    if (G.group.n > 0) {
+      where = -1;
+      for (int i = 0; i < G.group.n; ++i)
+        if (G.group.expert[i] == td.x) where = G.group.slot[i];
+      if (where < 0) return;  // uniform over the block: not this group's expert
+    }
     r0 = td.y;
     const int e_end = G.seg[td.x + 1];
     r_end = r0 + kTM < e_end ? r0 + kTM : e_end;
-    blob = G.experts + static_cast<size_t>(td.x) * G.blob_e;
+    blob = G.experts + static_cast<size_t>(where) * G.blob_e;
   } else {
     r0 = mt * kTM;
     if (r0 >= G.M_dense) return;
@@ -476,11 +486,9 @@ PrefillLayout prefill_layout(int T, int E, int k, int H, int I, int Is) {
   return L;
 }
 
-hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
-                          const float* logits_in, const uint16_t* router, const float* bias, int T,
-                          int E, int k, int H, int I, int Is, const uint8_t* experts, size_t blob_e,
-                          const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
-                          hipStream_t s) {
+hipError_t launch_prefill_route(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
+                                const float* logits_in, const uint16_t* router, const float* bias, int T,
+                                int E, int k, int H, int32_t* ids_out, float* w_out, hipStream_t s) {
   auto at = [&](size_t off) { return ws + off; };
   int32_t* ids = reinterpret_cast<int32_t*>(at(L.ids));
   float* w = reinterpret_cast<float*>(at(L.w));
@@ -498,66 +506,90 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
       e = launch_route_topk(reinterpret_cast<double*>(at(L.z)), nullptr, T, E, k, ids, w, ids_out, w_out, s);
   }
   if (e != hipSuccess) return e;
-  const int A = T * k;
-  int32_t* hist = reinterpret_cast<int32_t*>(at(L.hist));
-  int32_t* base = reinterpret_cast<int32_t*>(at(L.base));
-  int32_t* lrank = reinterpret_cast<int32_t*>(at(L.local_rank));
-  int32_t* seg = reinterpret_cast<int32_t*>(at(L.seg));
-  int2* tiles = reinterpret_cast<int2*>(at(L.tiles));
-  int32_t* n_tiles = reinterpret_cast<int32_t*>(at(L.n_tiles));
-  int32_t* perm = reinterpret_cast<int32_t*>(at(L.perm));
-  int32_t* pos_of = reinterpret_cast<int32_t*>(at(L.pos_of));
-  if ((e = launch_permute(ids, A, E, L.chunks, hist, lrank, base, seg, tiles, n_tiles, perm, pos_of, s)) !=
-      hipSuccess)
-    return e;
+  return launch_permute(ids, T * k, E, L.chunks, reinterpret_cast<int32_t*>(at(L.hist)),
+                        reinterpret_cast<int32_t*>(at(L.local_rank)), reinterpret_cast<int32_t*>(at(L.base)),
+                        reinterpret_cast<int32_t*>(at(L.seg)), reinterpret_cast<int2*>(at(L.tiles)),
+                        reinterpret_cast<int32_t*>(at(L.n_tiles)), reinterpret_cast<int32_t*>(at(L.perm)),
+                        reinterpret_cast<int32_t*>(at(L.pos_of)), s);
+}
 
-  const __bf16* x = reinterpret_cast<const __bf16*>(x_bf16);
-  __bf16* act_r = reinterpret_cast<__bf16*>(at(L.act_r));
-  __bf16* act_s = reinterpret_cast<__bf16*>(at(L.act_s));
-  float* out_r = reinterpret_cast<float*>(at(L.out_r));
-
+namespace {
+GemmArgs routed_args(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int k, int H, int I,
+                     const uint8_t* experts, size_t blob_e) {
+  auto at = [&](size_t off) { return ws + off; };
   GemmArgs g{};
   g.H = H;
   g.k = k;
   // routed gate/up: rows are assignments in expert order, A row = token = perm / k
-  g.A = x;
+  g.A = reinterpret_cast<const __bf16*>(x_bf16);
   g.lda = H;
-  g.rmap = perm;
+  g.rmap = reinterpret_cast<const int32_t*>(at(L.perm));
   g.rdiv = k;
   g.experts = experts;
   g.blob_e = blob_e;
   g.inter = I;
-  g.tiles = tiles;
-  g.n_tiles = n_tiles;
-  g.seg = seg;
-  g.act = act_r;
+  g.tiles = reinterpret_cast<const int2*>(at(L.tiles));
+  g.n_tiles = reinterpret_cast<const int32_t*>(at(L.n_tiles));
+  g.seg = reinterpret_cast<const int32_t*>(at(L.seg));
+  g.act = reinterpret_cast<__bf16*>(at(L.act_r));
+  return g;
+}
+}  // namespace
+
+hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int k, int H,
+                                 int I, const uint8_t* experts, size_t blob_e, const SlotGroup* group,
+                                 hipStream_t s) {
+  GemmArgs g = routed_args(L, ws, x_bf16, k, H, I, experts, blob_e);
+  if (group) {
+    if (group->n < 1 || group->n > kMaxGroup) return hipErrorInvalidValue;
+    g.group = *group;
+  }
   hipLaunchKernelGGL((k_gemm<true, true>), dim3(L.max_tiles * gemm_row_tiles(true, H, I)), dim3(kThreadsGemm), 0, s, g);
-  // shared gate/up: dense over tokens
-  GemmArgs gs = g;
-  gs.rmap = nullptr;
+  // routed down: rows are the permuted activations, weighted by their routing weight
+  GemmArgs d = g;
+  d.A = reinterpret_cast<const __bf16*>(ws + L.act_r);
+  d.lda = I;
+  d.rmap = nullptr;
+  d.out = reinterpret_cast<float*>(ws + L.out_r);
+  d.wrow = reinterpret_cast<const float*>(ws + L.w);
+  d.perm = reinterpret_cast<const int32_t*>(ws + L.perm);
+  hipLaunchKernelGGL((k_gemm<false, true>), dim3(L.max_tiles * gemm_row_tiles(false, H, I)), dim3(kThreadsGemm), 0, s, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
+                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s) {
+  GemmArgs gs{};
+  gs.H = H;
+  gs.k = k;
+  gs.A = reinterpret_cast<const __bf16*>(x_bf16);
+  gs.lda = H;
   gs.blob = shared;
   gs.inter = Is;
   gs.M_dense = T;
-  gs.act = act_s;
+  gs.act = reinterpret_cast<__bf16*>(ws + L.act_s);
+  // shared gate/up: dense over tokens
   hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
-  // routed down: rows are the permuted activations, weighted by their routing weight
-  GemmArgs d = g;
-  d.A = act_r;
-  d.lda = I;
-  d.rmap = nullptr;
-  d.out = out_r;
-  d.wrow = w;
-  d.perm = perm;
-  hipLaunchKernelGGL((k_gemm<false, true>), dim3(L.max_tiles * gemm_row_tiles(false, H, I)), dim3(kThreadsGemm), 0, s, d);
-  // shared down + combine into y
+  // shared down + combine into y (each token's routed rows in rank order)
   GemmArgs ds = gs;
-  ds.A = act_s;
+  ds.A = reinterpret_cast<const __bf16*>(ws + L.act_s);
   ds.lda = Is;
   ds.out = y;
-  ds.out_r = out_r;
-  ds.pos_of = pos_of;
+  ds.out_r = reinterpret_cast<const float*>(ws + L.out_r);
+  ds.pos_of = reinterpret_cast<const int32_t*>(ws + L.pos_of);
   hipLaunchKernelGGL((k_gemm<false, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
+                          const float* logits_in, const uint16_t* router, const float* bias, int T,
+                          int E, int k, int H, int I, int Is, const uint8_t* experts, size_t blob_e,
+                          const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
+                          hipStream_t s) {
+  hipError_t e = launch_prefill_route(L, ws, x_bf16, logits_in, router, bias, T, E, k, H, ids_out, w_out, s);
+  if (e == hipSuccess) e = launch_prefill_routed(L, ws, x_bf16, k, H, I, experts, blob_e, nullptr, s);
+  if (e == hipSuccess) e = launch_prefill_shared(L, ws, x_bf16, T, k, H, Is, shared, y, s);
+  return e;
 }
 
 }  // namespace moe

@@ -264,12 +264,21 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                             uint32_t flags, float* y, int32_t* ids_out, float* w_out, float* u_out,
                             moe_cache_event* trace, moe_decode_stats* stats, void* stream);
 
-/* Prefill T tokens (resident mode). x is bf16 [T][H]; routing uses
+/* Prefill T tokens (T <= max_T). x is bf16 [T][H]; routing uses
  * logits_in (dev fp32 [T][E]) when given, else x . router. Tokens are grouped
  * by expert; expert weights are dequantised to bf16 (one rounding of the
  * exact product) and multiplied on the matrix cores with fp32 accumulation; the GeGLU activation is rounded
  * to bf16 before the down projection. y dev fp32 [T][H]. ids_out / w_out
- * optional as in decode. Asynchronous on stream. */
+ * optional as in decode.
+ * Resident mode: asynchronous on stream.
+ * Cache mode (source: "Como executar um modelo de 26 bilhões de parâmetros em
+ * dois gigabytes de memória em um Mac comum", section "Desempenho no mundo
+ * real"): the tokens go through the slot pool in chunks of 128 (or max_T): per
+ * chunk, its experts in groups of min(n_slots, 16), each an LFU step of the
+ * handle's cache whose misses are copied (from experts_host or the store) on
+ * copy_stream after the previous group's kernels, then the group's routed
+ * products on the slots. The calling thread waits once per chunk (for the
+ * chunk's expert list) and for store reads. Same bits as resident mode. */
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in,
                              int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
 

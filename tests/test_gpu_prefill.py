@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from bit_quantized_expert_softmax_amd import api
-from oracle import moe
+from oracle import lfu, moe
 from synth import gen
 from synth.configs import GEMMA_LAYER, SMALL_LAYER
 from tests.gpu_util import DEV, Layer, assert_close, dev, dev_u16, poisoned
@@ -78,7 +78,54 @@ def test_prefill_full_2048_tokens():
     L.close()
 
 
-def test_prefill_rejects_cache_mode_and_empty_is_noop():
+@pytest.mark.parametrize("shape,slots,T,source", [(SMALL_LAYER, 8, 300, "host"), (SMALL_LAYER, 8, 300, "store"),
+                                                   (GEMMA_LAYER, 16, 260, "host")])
+def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, source):
+    """Chunks of 128 tokens through the LFU slot pool (ragged last chunk) give
+    the resident prefill's bits, ids and weights; the cache ends in the
+    simulator's state after one step per group of each chunk's experts, and
+    every slot holds its expert's blob; the handle then still decodes."""
+    sh = shape
+    d = layer_data(sh, 5)
+    xb = gen.x_bf16(T, sh.hidden, 77)
+    logits = gen.logits_uniform(T, sh.n_experts, 77)
+    R = Layer(sh, d, max_T=T)
+    y_r, ids_r, w_r = run_prefill(R, xb, logits, T)
+    R.close()
+    store = None
+    if source == "store":
+        blob = d["experts"].shape[1]
+        padded = np.zeros((sh.n_experts, api.moe_store_stride(blob)), np.uint8)
+        padded[:, :blob] = d["experts"]
+        path = str(tmp_path / "experts.bin")
+        padded.tofile(path)
+        store = api.moe_store_open(path, 1, sh.n_experts, blob, 4, True)
+    Cm = Layer(sh, d, cache_slots=slots, max_T=T, store=store)
+    y_c, ids_c, w_c = run_prefill(Cm, xb, logits, T)
+    assert np.array_equal(ids_c, ids_r) and np.array_equal(w_c, w_r)
+    assert np.array_equal(y_c, y_r)
+    sim = lfu.LFUCache(slots, sh.n_experts)
+    g = min(slots, 16)
+    for c0 in range(0, T, 128):
+        ex = sorted(set(ids_r[c0:c0 + 128].reshape(-1).tolist()))
+        for i in range(0, len(ex), g):
+            sim.step(np.array(ex[i:i + g]))
+    ex_n, fr_n, la_n = api.moe_cache_slots(api.moe_layer_cache(Cm.h), slots)
+    assert ex_n.tolist() == sim.expert and fr_n.tolist() == sim.freq and la_n.tolist() == sim.last
+    pool = Cm.pool.cpu().numpy()
+    for s_, e in enumerate(sim.expert):
+        if e >= 0:
+            assert np.array_equal(pool[s_], d["experts"][e]), (s_, e)
+    y = poisoned((1, sh.hidden))
+    api.moe_layer_decode(Cm.h, dev(gen.x_fp32(1, sh.hidden, 5)), None, 1, 0, y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    Cm.close()
+    if store is not None:
+        api.moe_store_close(store)
+
+
+def test_prefill_needs_max_T_and_empty_is_noop():
     sh = SMALL_LAYER
     d = layer_data(sh, 0)
     L = Layer(sh, d, max_T=16)
