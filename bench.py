@@ -547,6 +547,43 @@ def main():
         for d in layers:
             del d["experts_dev"]
 
+    # ---------------------------------------------------------------- prefill through the slot pool
+    # 2048 tokens of one layer in 128-token chunks through a cold 16-slot pool
+    # (cache mode, misses from pinned host memory): the time to the first
+    # token's layer output when the experts do not fit in HBM.
+    Tq = 2048
+    wsq = torch.zeros(api.moe_layer_workspace_bytes(sh, 1, Tq), dtype=torch.uint8, device=devn)
+    xq = torch.from_numpy(gen.x_bf16(Tq, H, 4).view(np.int16)).to(devn)
+    lq = torch.from_numpy(gen.logits_uniform(Tq, E, 4)).to(devn)
+    yq = torch.empty((Tq, H), device=devn)
+    detail["prefill_2048_slot_pool"] = {}
+    for chunk_q in (128, Tq):
+        runs = []
+        for l in range(3):
+            d = layers[l]
+            poolq = torch.empty((S, blob), dtype=torch.uint8, device=devn)
+            hq = api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"], workspace=wsq,
+                                      bias=d["bias"], experts_host=d["host"], slot_pool=poolq, n_slots=S,
+                                      copy_stream=copy_stream, max_T=Tq)
+            api.moe_layer_prefill_chunk(hq, chunk_q)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            api.moe_layer_prefill(hq, xq, lq, Tq, yq)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            hits_q, misses_q, _ = api.moe_cache_counters(api.moe_layer_cache(hq))
+            runs.append((el, hits_q, misses_q))
+            api.moe_layer_destroy(hq)
+            del poolq
+        ms_q = 1e3 * sum(r[0] for r in runs[1:]) / len(runs[1:])  # the first run also warms the kernels
+        miss_q = sum(r[2] for r in runs[1:]) / len(runs[1:])
+        hit_q = sum(r[1] for r in runs[1:]) / len(runs[1:])
+        detail["prefill_2048_slot_pool"][f"chunk_{chunk_q}"] = {
+            "ms": ms_q, "misses": miss_q, "hits": hit_q, "h2d_GB": miss_q * blob / 1e9,
+            "h2d_GBps_wall": miss_q * blob / (ms_q * 1e-3) / 1e9, "slots": S}
+    del wsq
+    print("[bench] slot-pool prefill done", file=sys.stderr, flush=True)
+
     # ---------------------------------------------------------------- oracle on host cores
     cpu = None
     if not args.no_cpu:

@@ -71,6 +71,7 @@ SIGNATURES = {
     "moe_layer_decode": (c_status, [vp, vp, vp, C.c_int32, C.c_uint32, vp, vp, vp, vp,
                                     P(moe_cache_event), P(moe_decode_stats), vp]),
     "moe_layer_prefill": (c_status, [vp, vp, vp, C.c_int32, vp, vp, vp, vp]),
+    "moe_layer_prefill_chunk": (c_status, [vp, C.c_int32]),
     "moe_layer_profile": (c_status, [vp, C.c_int32]),
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),

@@ -197,6 +197,10 @@ def moe_layer_decode(h, x, add_in, B, flags, y, ids_out=None, w_out=None, u_out=
     return events_to_array(ev, B * trace_k) if trace_k else None
 
 
+def moe_layer_prefill_chunk(h, tokens: int) -> None:
+    _check(lib().moe_layer_prefill_chunk(h, tokens), "moe_layer_prefill_chunk")
+
+
 def moe_layer_prefill(h, x_bf16, logits_in, T, y, ids_out=None, w_out=None, stream=None):
     _check(lib().moe_layer_prefill(h, _p(x_bf16), _p(logits_in), T, _p(y), _p(ids_out), _p(w_out),
                                    _stream(stream)), "moe_layer_prefill")

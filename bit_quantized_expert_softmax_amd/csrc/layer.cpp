@@ -105,6 +105,7 @@ struct moe_layer {
   bool staging_busy = false;  // copies out of the staging may still run (ev_fill)
   // prefill through the slot pool (cache mode)
   int32_t* seg_host = nullptr;    // pinned, the chunk's expert offsets [E+1]
+  int32_t prefill_chunk = 128;    // tokens per chunk (the pages' value), at most max_T
   hipEvent_t ev_pool = nullptr;   // the pool's readers (kernels on the call's stream) are done
   // profiling
   bool prof = false;
@@ -577,12 +578,11 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
 
 namespace {
 
-constexpr int kPrefillChunk = 128;  // tokens per chunk through the slot pool
-
 // Prefill through the slot pool (cache mode). "Como executar um modelo de 26
 // bilhões de parâmetros em dois gigabytes de memória em um Mac comum",
 // section "Desempenho no mundo real": prompt processing in chunks of 128
-// tokens, so that one loaded expert serves a group of rows at once. Per chunk:
+// tokens, so that one loaded expert serves a group of rows at once (the chunk
+// is settable; a longer chunk loads each expert for more rows). Per chunk:
 // routing and the stable sort of its assignments; the chunk's experts (from
 // the sorted offsets, read back to the host) in groups of up to
 // min(n_slots, 16), each an LFU step whose misses are copied into their slots
@@ -593,7 +593,7 @@ moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logit
                         int32_t* ids_out, float* w_out, hipStream_t s, const char* fn) {
   const moe_shape& sh = L->sh;
   const int E = sh.n_experts, k = sh.top_k, H = sh.hidden;
-  const int chunk = L->max_T < kPrefillChunk ? L->max_T : kPrefillChunk;
+  const int chunk = L->max_T < L->prefill_chunk ? L->max_T : L->prefill_chunk;
   const moe::PrefillLayout P = moe::prefill_layout(chunk, E, k, H, sh.inter, sh.shared_inter);
   uint8_t* pw = L->wsb + L->ws.pre;
   hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
@@ -706,6 +706,16 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
                                   L->d.experts_dev, L->blob_e, L->d.shared_blob, y, ids_out, w_out, s),
               fn);
   prof_end(L, 4, pb, s);
+  return MOE_OK;
+}
+
+moe_status moe_layer_prefill_chunk(moe_layer* L, int32_t tokens) {
+  moe::clear_error();
+  const char* fn = "moe_layer_prefill_chunk";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (tokens < 1 || tokens > L->max_T)
+    return fail(MOE_ESHAPE, "%s: %d tokens outside [1, max_T=%d]", fn, tokens, L->max_T);
+  L->prefill_chunk = tokens;
   return MOE_OK;
 }
 

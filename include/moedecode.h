@@ -273,7 +273,8 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
  * Resident mode: asynchronous on stream.
  * Cache mode (source: "Como executar um modelo de 26 bilhões de parâmetros em
  * dois gigabytes de memória em um Mac comum", section "Desempenho no mundo
- * real"): the tokens go through the slot pool in chunks of 128 (or max_T): per
+ * real"): the tokens go through the slot pool in chunks of 128 tokens (see
+ * moe_layer_prefill_chunk; at most max_T): per
  * chunk, its experts in groups of min(n_slots, 16), each an LFU step of the
  * handle's cache whose misses are copied (from experts_host or the store) on
  * copy_stream after the previous group's kernels, then the group's routed
@@ -281,6 +282,10 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
  * chunk's expert list) and for store reads. Same bits as resident mode. */
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in,
                              int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
+/* Cache-mode prefill: tokens per chunk through the slot pool, 1..max_T
+ * (default 128, the pages' value; a longer chunk loads each expert once for
+ * more rows). MOE_ESHAPE outside that range. */
+moe_status moe_layer_prefill_chunk(moe_layer* L, int32_t tokens);
 
 /* Per-kernel GPU time of the handle's calls, measured with HIP events on the
  * launch stream while profiling is enabled: the one-kernel stages 1-3 of the

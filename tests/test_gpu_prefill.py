@@ -78,10 +78,12 @@ def test_prefill_full_2048_tokens():
     L.close()
 
 
-@pytest.mark.parametrize("shape,slots,T,source", [(SMALL_LAYER, 8, 300, "host"), (SMALL_LAYER, 8, 300, "store"),
-                                                   (GEMMA_LAYER, 16, 260, "host")])
-def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, source):
-    """Chunks of 128 tokens through the LFU slot pool (ragged last chunk) give
+@pytest.mark.parametrize("shape,slots,T,source,chunk", [(SMALL_LAYER, 8, 300, "host", 128),
+                                                         (SMALL_LAYER, 8, 300, "store", 128),
+                                                         (GEMMA_LAYER, 16, 260, "host", 128),
+                                                         (SMALL_LAYER, 8, 300, "host", 300)])
+def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, source, chunk):
+    """Chunks of 128 tokens (or one chunk) through the LFU slot pool (ragged last chunk) give
     the resident prefill's bits, ids and weights; the cache ends in the
     simulator's state after one step per group of each chunk's experts, and
     every slot holds its expert's blob; the handle then still decodes."""
@@ -101,13 +103,18 @@ def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, s
         padded.tofile(path)
         store = api.moe_store_open(path, 1, sh.n_experts, blob, 4, True)
     Cm = Layer(sh, d, cache_slots=slots, max_T=T, store=store)
+    with pytest.raises(api.MoeError):
+        api.moe_layer_prefill_chunk(Cm.h, T + 1)
+    with pytest.raises(api.MoeError):
+        api.moe_layer_prefill_chunk(Cm.h, 0)
+    api.moe_layer_prefill_chunk(Cm.h, chunk)
     y_c, ids_c, w_c = run_prefill(Cm, xb, logits, T)
     assert np.array_equal(ids_c, ids_r) and np.array_equal(w_c, w_r)
     assert np.array_equal(y_c, y_r)
     sim = lfu.LFUCache(slots, sh.n_experts)
     g = min(slots, 16)
-    for c0 in range(0, T, 128):
-        ex = sorted(set(ids_r[c0:c0 + 128].reshape(-1).tolist()))
+    for c0 in range(0, T, chunk):
+        ex = sorted(set(ids_r[c0:c0 + chunk].reshape(-1).tolist()))
         for i in range(0, len(ex), g):
             sim.step(np.array(ex[i:i + g]))
     ex_n, fr_n, la_n = api.moe_cache_slots(api.moe_layer_cache(Cm.h), slots)
