@@ -316,11 +316,12 @@ def main():
     # The same stack with other pool sizes (fresh caches, the headline's fill
     # path, half the timed tokens): hit rate, bytes over PCIe and tokens/s per
     # slot count.
+    # The last run is the headline's slot count with the LRU policy variant.
     sweep = [int(v) for v in args.sweep_slots.split(",") if v.strip()]
     if sweep:
         detail["slot_sweep"] = {}
         n_sw = max(args.steps // 2, 8)
-        for S2 in sweep:
+        for S2, pol in [(v, api.MOE_POLICY_LFU) for v in sweep] + [(S, api.MOE_POLICY_LRU)]:
             if S2 < k or S2 > E:
                 continue
             hs = []
@@ -329,7 +330,8 @@ def main():
                 d["ws2"] = torch.zeros_like(d["ws"])
                 hs.append(api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"],
                                                workspace=d["ws2"], bias=d["bias"], experts_host=d["host"],
-                                               slot_pool=d["pool2"], n_slots=S2, copy_stream=copy_stream))
+                                               slot_pool=d["pool2"], n_slots=S2, copy_stream=copy_stream,
+                                               cache_policy=pol))
             st2 = [api.moe_decode_stats() for _ in range(Lyr)]
             for t in range(args.warmup):
                 token(t, hs, st2)
@@ -343,8 +345,9 @@ def main():
             h2 = sum(s.hits - w[0] for s, w in zip(st2, w2))
             m2 = sum(s.misses - w[1] for s, w in zip(st2, w2))
             b2 = sum(s.h2d_bytes - w[2] for s, w in zip(st2, w2))
-            detail["slot_sweep"][str(S2)] = {"tokens_per_s": n_sw / el2, "hit_rate": h2 / max(h2 + m2, 1),
-                                             "h2d_MB_per_token": b2 / n_sw / 1e6, "tokens": n_sw}
+            key = str(S2) if pol == api.MOE_POLICY_LFU else f"{S2}_lru"
+            detail["slot_sweep"][key] = {"tokens_per_s": n_sw / el2, "hit_rate": h2 / max(h2 + m2, 1),
+                                         "h2d_MB_per_token": b2 / n_sw / 1e6, "tokens": n_sw}
             for h_ in hs:
                 api.moe_layer_destroy(h_)
             for d in layers:

@@ -35,7 +35,7 @@ class moe_layer_desc(C.Structure):
     _fields_ = [("router", vp), ("bias", vp), ("shared_blob", vp), ("experts_dev", vp),
                 ("experts_host", vp), ("slot_pool", vp), ("n_slots", C.c_int32),
                 ("copy_stream", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t),
-                ("store", vp), ("store_layer", C.c_int32)]
+                ("store", vp), ("store_layer", C.c_int32), ("cache_policy", C.c_int32)]
 
 
 class moe_decode_stats(C.Structure):
@@ -57,6 +57,7 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (C.c_size_t, [P(moe_shape), C.c_int32]),
     "moe_route": (c_status, [P(moe_shape), vp, vp, vp, vp, C.c_int32, vp, vp, vp, C.c_size_t, vp]),
     "moe_cache_create": (c_status, [C.c_int32, C.c_int32, P(vp)]),
+    "moe_cache_create_policy": (c_status, [C.c_int32, C.c_int32, C.c_int32, P(vp)]),
     "moe_cache_destroy": (None, [vp]),
     "moe_cache_step": (c_status, [vp, P(C.c_int32), C.c_int32, P(moe_cache_event), P(C.c_int32)]),
     "moe_cache_reset": (c_status, [vp]),

@@ -16,6 +16,8 @@ from . import _lib as L
 MOE_F_RMSNORM_IN = 1
 MOE_F_RESIDUAL = 2
 MOE_F_FILL_KERNEL = 4
+MOE_POLICY_LFU = 0
+MOE_POLICY_LRU = 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EALIGN", -4: "MOE_EHIP",
           -5: "MOE_ENOMEM", -6: "MOE_ESTATE"}
 
@@ -95,9 +97,12 @@ def moe_route(sh, x, wr, bias, logits_in, B, ids, w, workspace=None, stream=None
 
 
 # ------------------------------------------------------------------ LFU cache
-def moe_cache_create(n_slots: int, n_experts: int) -> int:
+def moe_cache_create(n_slots: int, n_experts: int, policy: int = 0) -> int:
     h = C.c_void_p()
-    _check(lib().moe_cache_create(n_slots, n_experts, C.byref(h)), "moe_cache_create")
+    if policy == MOE_POLICY_LFU:
+        _check(lib().moe_cache_create(n_slots, n_experts, C.byref(h)), "moe_cache_create")
+    else:
+        _check(lib().moe_cache_create_policy(n_slots, n_experts, policy, C.byref(h)), "moe_cache_create_policy")
     return h.value
 
 
@@ -163,12 +168,13 @@ def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
 
 def moe_layer_create(sh, *, router, shared_blob, workspace, bias=None, experts_dev=None,
                      experts_host=None, slot_pool=None, n_slots=0, copy_stream=None, max_B=1,
-                     max_T=0, store=None, store_layer=0) -> int:
+                     max_T=0, store=None, store_layer=0, cache_policy=0) -> int:
     s = make_shape(sh)
     d = L.moe_layer_desc(_p(router), _p(bias), _p(shared_blob), _p(experts_dev), _p(experts_host),
                          _p(slot_pool), n_slots,
                          None if copy_stream is None else _stream(copy_stream),
-                         _p(workspace), workspace.numel() * workspace.element_size(), store, store_layer)
+                         _p(workspace), workspace.numel() * workspace.element_size(), store, store_layer,
+                         cache_policy)
     h = C.c_void_p()
     _check(lib().moe_layer_create(C.byref(s), C.byref(d), max_B, max_T, C.byref(h)), "moe_layer_create")
     return h.value

@@ -254,6 +254,8 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
         !moe::store_fits(d->store, d->store_layer, sh->n_experts, moe_expert_bytes(sh->hidden, sh->inter)))
       return fail(MOE_ESHAPE, "%s: the store has no layer %d of %d blobs of this shape", fn, d->store_layer,
                   sh->n_experts);
+    if (d->cache_policy != MOE_POLICY_LFU && d->cache_policy != MOE_POLICY_LRU)
+      return fail(MOE_EINVAL, "%s: unknown cache_policy %d", fn, d->cache_policy);
     if (d->n_slots < sh->top_k || d->n_slots > sh->n_experts)
       return fail(MOE_ESHAPE, "%s: n_slots %d outside [top_k=%d, n_experts=%d]", fn, d->n_slots,
                   sh->top_k, sh->n_experts);
@@ -320,8 +322,8 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
                         hipHostMallocDefault);
       if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned expert offsets", e);
     }
-    moe_status cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache);
-    if (!cs) cs = moe_cache_create(d->n_slots, sh->n_experts, &L->cache_backup);
+    moe_status cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache);
+    if (!cs) cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache_backup);
     if (cs) {
       moe_layer_destroy(L);
       return cs;

@@ -14,7 +14,8 @@
 //          (frequency, last use, slot index) among slots holding none of the
 //          current token's ids; the new entry starts at frequency 1;
 //   hits are applied before misses; events are reported in the ids' order.
-// Plain C++ with no HIP dependency.
+// A policy variant for comparisons (LRU) takes the smallest (last use, slot
+// index) instead. Plain C++ with no HIP dependency.
 #include <string.h>
 
 #include <vector>
@@ -23,6 +24,7 @@
 
 struct moe_cache {
   int32_t n_slots = 0, n_experts = 0;
+  int32_t policy = MOE_POLICY_LFU;
   std::vector<int32_t> expert;  // slot -> expert, -1 = empty
   std::vector<int32_t> freq;
   std::vector<int64_t> last;
@@ -47,8 +49,14 @@ const char* moe_last_error(void) { return moe::last_error_text().c_str(); }
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
 moe_status moe_cache_create(int32_t n_slots, int32_t n_experts, moe_cache** out) {
+  return moe_cache_create_policy(n_slots, n_experts, MOE_POLICY_LFU, out);
+}
+
+moe_status moe_cache_create_policy(int32_t n_slots, int32_t n_experts, int32_t policy, moe_cache** out) {
   moe::clear_error();
   if (!out) return fail(MOE_EINVAL, "moe_cache_create: out is NULL");
+  if (policy != MOE_POLICY_LFU && policy != MOE_POLICY_LRU)
+    return fail(MOE_EINVAL, "moe_cache_create: unknown policy %d", policy);
   if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
     return fail(MOE_ESHAPE, "moe_cache_create: n_experts %d outside [1, %d]", n_experts, MOE_MAX_EXPERTS);
   if (n_slots < 1 || n_slots > n_experts)
@@ -57,6 +65,7 @@ moe_status moe_cache_create(int32_t n_slots, int32_t n_experts, moe_cache** out)
   if (!c) return fail(MOE_ENOMEM, "moe_cache_create: out of host memory");
   c->n_slots = n_slots;
   c->n_experts = n_experts;
+  c->policy = policy;
   c->expert.assign(n_slots, -1);
   c->freq.assign(n_slots, 0);
   c->last.assign(n_slots, -1);
@@ -115,9 +124,15 @@ moe_status moe_cache_step(moe_cache* c, const int32_t* ids, int32_t k, moe_cache
     if (victim < 0) {
       for (int s = 0; s < c->n_slots; ++s) {
         if (seen[c->expert[s]]) continue;  // holds an id of this token
-        if (victim < 0 || c->freq[s] < c->freq[victim] ||
-            (c->freq[s] == c->freq[victim] && c->last[s] < c->last[victim]))
-          victim = s;  // scanning upward keeps the lower index on full ties
+        if (victim < 0) {
+          victim = s;
+          continue;
+        }
+        const bool better = c->policy == MOE_POLICY_LRU
+                                ? c->last[s] < c->last[victim]
+                                : c->freq[s] < c->freq[victim] ||
+                                      (c->freq[s] == c->freq[victim] && c->last[s] < c->last[victim]);
+        if (better) victim = s;  // scanning upward keeps the lower index on full ties
       }
     }
     const int old = c->expert[victim];

@@ -128,12 +128,20 @@ moe_status moe_route(const moe_shape* sh, const float* x, const uint16_t* wr, co
  *   - ev[j] (host, k entries, out) describes ids[j]: expert, slot, hit (1/0),
  *     evicted expert or -1; *n_miss (out, may be NULL) counts misses.
  * The step counter advances by one per successful call. Errors (k > n_slots,
- * id out of range, duplicate id) leave the cache unchanged. */
+ * id out of range, duplicate id) leave the cache unchanged.
+ * Replacement policy variant (not the pages' policy; for comparisons):
+ * MOE_POLICY_LRU takes the slot with the smallest (last use, slot index)
+ * instead; everything else is the same (frequencies are still counted). */
+#define MOE_POLICY_LFU 0
+#define MOE_POLICY_LRU 1
 typedef struct moe_cache moe_cache;
 typedef struct moe_cache_event {
   int32_t expert, slot, hit, evicted;
 } moe_cache_event;
+/* An LFU cache (the pages' policy). */
 moe_status moe_cache_create(int32_t n_slots, int32_t n_experts, moe_cache** out);
+/* A cache with the given policy (MOE_POLICY_*); MOE_EINVAL for others. */
+moe_status moe_cache_create_policy(int32_t n_slots, int32_t n_experts, int32_t policy, moe_cache** out);
 void moe_cache_destroy(moe_cache* c);
 moe_status moe_cache_step(moe_cache* c, const int32_t* ids, int32_t k, moe_cache_event* ev,
                           int32_t* n_miss);
@@ -207,6 +215,7 @@ typedef struct moe_layer_desc {
    * to their slots like host-memory misses. Not owned by the handle. */
   moe_store* store;
   int32_t store_layer;
+  int32_t cache_policy;         /* cache mode: MOE_POLICY_LFU (0) or MOE_POLICY_LRU */
 } moe_layer_desc;
 
 typedef struct moe_decode_stats {

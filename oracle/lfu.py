@@ -17,6 +17,9 @@ They do not fix tie-breaks. Reading taken (so that a trace is unique):
   ageing; the cache starts empty; the tick is the step number;
 * hits are settled before misses, but events are reported in rank order.
 
+Policy variant for comparisons (not the pages' policy): with policy="lru" the
+victim minimises (last, slot index) instead; everything else is unchanged.
+
 Test infrastructure only (see the package docstring).
 """
 from __future__ import annotations
@@ -25,9 +28,12 @@ EMPTY = -1
 
 
 class LFUCache:
-    def __init__(self, n_slots: int, n_experts: int):
+    def __init__(self, n_slots: int, n_experts: int, policy: str = "lfu"):
         if n_slots < 1:
             raise ValueError("need at least one slot")
+        if policy not in ("lfu", "lru"):
+            raise ValueError("policy must be 'lfu' or 'lru'")
+        self.policy = policy
         self.n_slots = n_slots
         self.n_experts = n_experts
         self.expert = [EMPTY] * n_slots
@@ -74,7 +80,10 @@ class LFUCache:
                 victim = empties[0]
             else:
                 cands = [s for s in range(self.n_slots) if self.expert[s] not in wanted]
-                victim = min(cands, key=lambda s: (self.freq[s], self.last[s], s))
+                if self.policy == "lru":
+                    victim = min(cands, key=lambda s: (self.last[s], s))
+                else:
+                    victim = min(cands, key=lambda s: (self.freq[s], self.last[s], s))
             old = self.expert[victim]
             self.expert[victim] = e
             self.freq[victim] = 1
@@ -85,7 +94,7 @@ class LFUCache:
         return events
 
 
-def simulate(id_rows, n_slots: int, n_experts: int):
+def simulate(id_rows, n_slots: int, n_experts: int, policy: str = "lfu"):
     """Run a whole id trace; returns (events per step, cache)."""
-    c = LFUCache(n_slots, n_experts)
+    c = LFUCache(n_slots, n_experts, policy)
     return [c.step(r) for r in id_rows], c

@@ -66,11 +66,12 @@ def _traces():
     return out
 
 
+@pytest.mark.parametrize("policy", ["lfu", "lru"])
 @pytest.mark.parametrize("case", range(7))
-def test_native_lfu_matches_simulator(case):
+def test_native_lfu_matches_simulator(case, policy):
     S, E, k, rows = _traces()[case]
-    ref, sim = simulate(rows, S, E)
-    h = api.moe_cache_create(S, E)
+    ref, sim = simulate(rows, S, E, policy)
+    h = api.moe_cache_create(S, E, api.MOE_POLICY_LRU if policy == "lru" else api.MOE_POLICY_LFU)
     try:
         for t, r in enumerate(rows):
             ev, nm = api.moe_cache_step(h, r)

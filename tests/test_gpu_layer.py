@@ -179,6 +179,36 @@ def test_file_store_matches_host_memory_bitwise(tmp_path, flags):
     api.moe_store_close(store)
 
 
+def test_lru_policy_layer_trace_and_bits():
+    """A layer with the LRU policy variant follows the simulator's LRU trace
+    and gives the same bits as the LFU layer (the policy only decides which
+    slot holds an expert)."""
+    sh = SMALL_LAYER
+    d = layer_data(sh, 4)
+    bias = gen.zipf_bias(sh.n_experts, 4, 0)
+    La = Layer(sh, d, bias=bias, cache_slots=8)
+    Lr = Layer(sh, d, bias=bias, cache_slots=8)
+    api.moe_layer_destroy(Lr.h)
+    Lr.h = api.moe_layer_create(sh, router=Lr.router, shared_blob=Lr.shared, workspace=Lr.ws, bias=Lr.bias,
+                                experts_host=Lr.host, slot_pool=Lr.pool, n_slots=8, copy_stream=Lr.copy_stream,
+                                cache_policy=api.MOE_POLICY_LRU)
+    sim = lfu.LFUCache(8, sh.n_experts, policy="lru")
+    xs = gen.x_fp32(16, sh.hidden, 4, sub=9)
+    differs = False
+    for t in range(16):
+        ya, ida, _, _, tra = run_decode(La, dev(xs[t:t + 1]), trace_k=sh.top_k)
+        yr, idr, _, _, trr = run_decode(Lr, dev(xs[t:t + 1]), trace_k=sh.top_k)
+        assert np.array_equal(ida, idr) and np.array_equal(ya, yr), t
+        assert [tuple(e) for e in trr.tolist()] == [tuple(e) for e in sim.step(idr[0])], t
+        differs |= not np.array_equal(tra, trr)
+    assert differs  # the two policies did take different slots on this trace
+    with pytest.raises(api.MoeError):
+        api.moe_layer_create(sh, router=Lr.router, shared_blob=Lr.shared, workspace=Lr.ws, experts_host=Lr.host,
+                             slot_pool=Lr.pool, n_slots=8, copy_stream=Lr.copy_stream, cache_policy=7)
+    La.close()
+    Lr.close()
+
+
 def test_fill_kernel_needs_cache_mode():
     sh = SMALL_LAYER
     d = layer_data(sh, 0)

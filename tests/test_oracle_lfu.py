@@ -106,3 +106,52 @@ def test_frequency_beats_recency():
     # A is used twice, B once but more recently: the miss evicts B
     ev, _ = simulate([[A], [A], [B], [C]], n_slots=2, n_experts=16)
     assert ev[3] == [(C, 1, 0, B)]
+
+
+# ---------------------------------------------------------------- LRU variant
+def test_lru_hand_trace_differs_from_lfu():
+    # A is used twice, then B once, then C arrives: LFU evicts B (freq 1 < 2),
+    # LRU evicts A (used at step 1, B at step 2)
+    rows = [[A], [A], [B], [C]]
+    ev_lfu, _ = simulate(rows, n_slots=2, n_experts=16)
+    ev_lru, _ = simulate(rows, n_slots=2, n_experts=16, policy="lru")
+    assert ev_lfu[3] == [(C, 1, 0, B)]
+    assert ev_lru[3] == [(C, 0, 0, A)]
+
+
+def textbook_lru(trace, capacity):
+    """Hits / misses of a plain single-key LRU cache (recency list)."""
+    from collections import OrderedDict
+    od, hits = OrderedDict(), 0
+    out = []
+    for x in trace:
+        if x in od:
+            od.move_to_end(x)
+            hits += 1
+            out.append(True)
+        else:
+            if len(od) == capacity:
+                od.popitem(last=False)
+            od[x] = None
+            out.append(False)
+    return out, list(od.keys())
+
+
+@pytest.mark.parametrize("seed,cap", [(0, 2), (1, 4), (2, 7)])
+def test_lru_one_id_per_step_is_textbook_lru(seed, cap):
+    rng = np.random.default_rng(seed)
+    trace = [int(v) for v in rng.integers(0, 3 * cap, 400)]
+    want_hit, want_resident = textbook_lru(trace, cap)
+    c = LFUCache(cap, 3 * cap, policy="lru")
+    got = [bool(c.step([x])[0][2]) for x in trace]
+    assert got == want_hit
+    assert sorted(e for e in c.expert if e >= 0) == sorted(want_resident)
+
+
+def test_lru_pins_the_current_token_and_fills_empty_slots_first():
+    c = LFUCache(3, 16, policy="lru")
+    assert [e[1] for e in c.step([A, B])] == [0, 1]
+    c.step([C])                       # the empty slot 2
+    c.step([A])                       # A recent again; B now least recent
+    out = c.step([B, D])              # B hits; D must not evict B although it is the oldest
+    assert out[0] == (B, 1, 1, -1) and out[1] == (D, 2, 0, C)
