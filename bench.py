@@ -486,6 +486,27 @@ def main():
         for h in res:
             api.moe_layer_destroy(h)
 
+        # floor of one launch streaming the routed gate/up's bytes with no
+        # arithmetic (same event method), rotating over one layer's 428 MB of
+        # experts so that no launch finds its bytes in the last-level cache
+        src = layers[0]["experts_dev"]
+        fb = gu_bytes // 16 * 16
+        stride = (fb + 255) // 256 * 256
+        nreg = src.numel() // stride
+        fout = torch.zeros(2048 * 16, dtype=torch.int32, device=devn)
+        floor = {"bytes": fb, "regions": nreg}
+        for blocks in (176, 256, 512, 1024):
+            api.moe_debug_read_floor(src, fb, blocks, fout, region_stride=stride, regions=nreg, reps=nreg)
+            us_f = api.moe_debug_read_floor(src, fb, blocks, fout, region_stride=stride, regions=nreg,
+                                            reps=10 * nreg, timed=True)
+            floor[f"grid_{blocks}x1024"] = {"us": us_f, "frac": fb / (us_f * 1e-6) / 8e12}
+        one = 176 * 1024 * 16
+        us_1 = api.moe_debug_read_floor(src, one, 176, fout, region_stride=stride, regions=nreg,
+                                        reps=10 * nreg, timed=True)
+        floor["one_load_per_lane_176x1024_us"] = us_1
+        detail["launch_floor"] = floor
+        print(f"[bench] launch floor: {floor}", file=sys.stderr, flush=True)
+
         # batched decode (B tokens per step, grouped by expert) and 2048-token
         # prefill, unbiased routing. Consecutive steps use consecutive layers
         # (routers, shared and routed experts of all 30 layers resident, one

@@ -77,6 +77,8 @@ SIGNATURES = {
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
+    "moe_debug_read_floor": (c_status, [vp, C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int32, vp,
+                                        P(C.c_double), vp]),
     "moe_store_stride": (C.c_int64, [C.c_int64]),
     "moe_store_open": (c_status, [C.c_char_p, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32, P(vp)]),
     "moe_store_is_direct": (C.c_int32, [vp]),

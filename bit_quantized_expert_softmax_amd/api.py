@@ -157,6 +157,17 @@ def moe_debug_unpack_q4(q, N, K, out, stream=None):
     _check(lib().moe_debug_unpack_q4(C.byref(W), N, K, _p(out), _stream(stream)), "moe_debug_unpack_q4")
 
 
+def moe_debug_read_floor(src, nbytes, blocks, out, *, region_stride=0, regions=1, reps=1, timed=False,
+                         stream=None):
+    """Streams nbytes per launch (reps launches rotating over regions); returns
+    the mean µs per launch when timed, else None (launches only enqueued)."""
+    us = C.c_double(0.0)
+    _check(lib().moe_debug_read_floor(_p(src), nbytes, region_stride, regions, blocks, reps, _p(out),
+                                      C.byref(us) if timed else None, _stream(stream)),
+           "moe_debug_read_floor")
+    return us.value if timed else None
+
+
 # ------------------------------------------------------------------ layer
 def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
     s = make_shape(sh)

@@ -3,6 +3,8 @@
 // before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "host_common.h"
 #include "launch.h"
 
@@ -114,6 +116,56 @@ moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* ou
   if (N == 0) return MOE_OK;
   HIP_OR_FAIL(moe::launch_unpack_q4(W->q, N, K, out, static_cast<hipStream_t>(stream)), fn);
   return MOE_OK;
+}
+
+moe_status moe_debug_read_floor(const void* src, int64_t bytes, int64_t region_stride, int32_t regions,
+                                int32_t blocks, int32_t reps, uint32_t* out, double* mean_us, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_debug_read_floor";
+  if (!src || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (bytes < 16 || bytes % 16 || regions < 1 || reps < 1 || blocks < 1 || blocks > 65536)
+    return fail(MOE_ESHAPE, "%s: bytes %lld, regions %d, blocks %d, reps %d out of range", fn,
+                static_cast<long long>(bytes), regions, blocks, reps);
+  if (regions > 1 && (region_stride < bytes || region_stride % 16))
+    return fail(MOE_ESHAPE, "%s: region_stride %lld must be a multiple of 16 and >= bytes", fn,
+                static_cast<long long>(region_stride));
+  if (moe::read_floor_loads(bytes, blocks) > 16)
+    return fail(MOE_ESHAPE, "%s: %lld bytes need more than 16 loads per lane on %d blocks", fn,
+                static_cast<long long>(bytes), blocks);
+  if (!moe::aligned16(src)) return fail(MOE_EALIGN, "%s: src must be 16-byte aligned", fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* base = static_cast<const uint8_t*>(src);
+  std::vector<hipEvent_t> ev;
+  if (mean_us) {
+    ev.resize(2 * static_cast<size_t>(reps), nullptr);
+    for (auto& e : ev) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        for (auto& f : ev)
+          if (f) (void)hipEventDestroy(f);
+        return fail(MOE_EHIP, "%s: hipEventCreate failed", fn);
+      }
+    }
+  }
+  moe_status st = MOE_OK;
+  for (int i = 0; i < reps && st == MOE_OK; ++i) {
+    const uint8_t* p = base + static_cast<int64_t>(i % regions) * region_stride;
+    const hipError_t e = moe::launch_read_floor(p, bytes, blocks, out, mean_us ? ev[2 * i] : nullptr,
+                                                mean_us ? ev[2 * i + 1] : nullptr, s);
+    if (e != hipSuccess) st = fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  }
+  if (mean_us && st == MOE_OK) {
+    double tot = 0.0;
+    for (int i = 0; i < reps && st == MOE_OK; ++i) {
+      float ms = 0.f;
+      hipError_t e = hipEventSynchronize(ev[2 * i + 1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+      if (e != hipSuccess) st = fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
+      tot += ms;
+    }
+    *mean_us = 1000.0 * tot / reps;
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);
+  return st;
 }
 
 }  // extern "C"

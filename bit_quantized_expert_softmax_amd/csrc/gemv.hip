@@ -1,10 +1,13 @@
-// Standalone int4 g32 GEMV for M token rows sharing one weight matrix, and
-// the nibble unpack used for bit-exact checks.
+// Standalone int4 g32 GEMV for M token rows sharing one weight matrix, the
+// nibble unpack used for bit-exact checks, and a read-only stream that sets
+// the floor one launch of a given size takes.
 //
 // Weights are 4-bit with custom quantisation and GEMV kernels ("Como
 // executar um modelo de 26 bilhões de parâmetros em dois gigabytes de memória
 // em um Mac comum", section "Sem dependências do llama.cpp e MLX").
 // y[m][n] = sum_k x[m][k] * nibble(n,k) * s[n][k/32].
+#include <hip/hip_ext.h>
+
 #include "launch.h"
 
 namespace moe {
@@ -94,7 +97,58 @@ __global__ void k_unpack_q4(const uint8_t* __restrict__ q, size_t nbytes, int8_t
   }
 }
 
+// Read-only stream of n16 16-byte words: lane i of the grid loads words
+// i, i + G, i + 2G, ... (G = grid threads; L of them, every load issued before
+// any is used, the last word re-read where the range ends), folds them by XOR
+// and the wave writes one word. It does no arithmetic on the data, so its
+// duration is the floor for one launch that streams the same bytes on the same
+// grid.
+template <int L>
+__global__ __launch_bounds__(1024) void k_read_floor(const uint8_t* __restrict__ src, int64_t n16,
+                                                     uint32_t* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint4 v[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const int64_t i = i0 + j * stride;
+    v[j] = load_w16(src + 16 * (i < n16 ? i : n16 - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < L; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  for (int o = kWave / 2; o >= 1; o >>= 1) x ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o));
+  if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave] = x;
+}
+
 }  // namespace
+
+int read_floor_loads(int64_t bytes, int blocks) {
+  const int64_t threads = static_cast<int64_t>(blocks) * 1024;
+  return static_cast<int>((bytes / 16 + threads - 1) / threads);
+}
+
+hipError_t launch_read_floor(const uint8_t* src, int64_t bytes, int blocks, uint32_t* out, hipEvent_t t0,
+                             hipEvent_t t1, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  switch (read_floor_loads(bytes, blocks)) {
+#define MOE_FLOOR(L)                                                                                  \
+  case L:                                                                                             \
+    if (t0)                                                                                           \
+      hipExtLaunchKernelGGL(k_read_floor<L>, dim3(blocks), dim3(1024), 0, s, t0, t1, 0, src, n16, out); \
+    else                                                                                              \
+      hipLaunchKernelGGL(k_read_floor<L>, dim3(blocks), dim3(1024), 0, s, src, n16, out);             \
+    break;
+    MOE_FLOOR(1) MOE_FLOOR(2) MOE_FLOOR(3) MOE_FLOOR(4) MOE_FLOOR(5) MOE_FLOOR(6) MOE_FLOOR(7) MOE_FLOOR(8)
+    MOE_FLOOR(9) MOE_FLOOR(10) MOE_FLOOR(11) MOE_FLOOR(12) MOE_FLOOR(13) MOE_FLOOR(14) MOE_FLOOR(15)
+    MOE_FLOOR(16)
+#undef MOE_FLOOR
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,
                           float* y, hipStream_t s) {

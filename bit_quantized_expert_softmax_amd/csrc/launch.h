@@ -171,5 +171,11 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
 hipError_t launch_gemv_q4(const uint8_t* q, const uint16_t* sc, int N, int K, const float* x, int M,
                           float* y, hipStream_t s);
 hipError_t launch_unpack_q4(const uint8_t* q, int N, int K, int8_t* out, hipStream_t s);
+// Read-only stream of `bytes` (a multiple of 16) on blocks x 1024 threads;
+// loads per lane = read_floor_loads(bytes, blocks), at most 16. With t0/t1 the
+// dispatch stamps the events at its start and end.
+int read_floor_loads(int64_t bytes, int blocks);
+hipError_t launch_read_floor(const uint8_t* src, int64_t bytes, int blocks, uint32_t* out, hipEvent_t t0,
+                             hipEvent_t t1, hipStream_t s);
 
 }  // namespace moe

@@ -323,6 +323,20 @@ moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* o
  * Unpacks the nibbles of W to int8 [N][K] (dev) for bit-exact comparison. */
 moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* out, void* stream);
 
+/* Measurement support: the floor of one launch that streams `bytes` from HBM
+ * with no arithmetic, to set a GEMV launch of the same bytes against. Each of
+ * reps launches (blocks x 1024 threads) reads `bytes` (a multiple of 16, at
+ * most 16 x 16 B per lane) at src + (i % regions) * region_stride (dev,
+ * 16-byte aligned; region_stride >= bytes when regions > 1, so that rotating
+ * over a range larger than the last-level cache defeats it); every lane issues
+ * all its 16-byte loads before using any, and each wave writes the XOR of its
+ * words to out (dev uint32 [blocks * 16]). With mean_us non-NULL every launch
+ * takes events stamped by its own dispatch, the call synchronises the stream
+ * and *mean_us receives the mean duration; with NULL the launches are only
+ * enqueued. MOE_ESHAPE for sizes out of range. */
+moe_status moe_debug_read_floor(const void* src, int64_t bytes, int64_t region_stride, int32_t regions,
+                                int32_t blocks, int32_t reps, uint32_t* out, double* mean_us, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

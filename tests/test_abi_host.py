@@ -178,3 +178,9 @@ def test_gpu_entry_points_reject_bad_arguments_before_enqueue(tmp_path):
     assert "LDS" in api.moe_last_error()
     assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 1, 0, C.byref(h)) == -1
     assert lib.moe_layer_decode(None, 16, None, 1, 0, 32, None, None, None, None, None, None) == -1
+    # read floor: sizes are checked before any launch
+    assert lib.moe_debug_read_floor(16, 24, 0, 1, 1, 1, 16, None, None) == -2          # not 16-byte words
+    assert lib.moe_debug_read_floor(16, 16 * 1024 * 17, 0, 1, 1, 1, 16, None, None) == -2  # 17 loads per lane
+    assert lib.moe_debug_read_floor(16, 1024, 512, 2, 1, 1, 16, None, None) == -2       # regions overlap
+    assert lib.moe_debug_read_floor(8, 1024, 0, 1, 1, 1, 16, None, None) == -3
+    assert lib.moe_debug_read_floor(None, 1024, 0, 1, 1, 1, 16, None, None) == -1

@@ -28,6 +28,26 @@ def test_unpack_bit_exact_all_bytes():
     assert np.array_equal(out.cpu().numpy(), q4.unpack_nibbles(q))
 
 
+@pytest.mark.parametrize("n16,blocks", [(2 * 1024 * 3 + 5, 2), (1024, 1), (16 * 1024 * 3, 3)])
+def test_read_floor_reads_every_word(n16, blocks):
+    """Each wave's word is the XOR of the 16-byte words its lanes load (word
+    i + j * grid threads for lane i, the last word re-read past the end)."""
+    data = np.random.default_rng(n16).integers(0, 2**32, (n16, 4), dtype=np.uint32)
+    out = torch.zeros(blocks * 16, dtype=torch.int32, device=DEV)
+    api.moe_debug_read_floor(dev(data.view(np.int32)), 16 * n16, blocks, out)
+    torch.cuda.synchronize()
+    G = blocks * 1024
+    L = -(-n16 // G)
+    fold = np.bitwise_xor.reduce(data, axis=1)
+    idx = np.minimum(np.arange(G)[:, None] + G * np.arange(L)[None, :], n16 - 1)
+    want = np.bitwise_xor.reduce(fold[idx], axis=1).reshape(-1, 64)
+    want = np.bitwise_xor.reduce(want, axis=1)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+    us = api.moe_debug_read_floor(dev(np.tile(data, (3, 1)).view(np.int32)), 16 * n16, blocks, out, region_stride=16 * n16,
+                                  regions=3, reps=6, timed=True)
+    assert 0.0 < us < 1e5
+
+
 @pytest.mark.parametrize("N,K,M", [(128, 512, 1), (256, 512, 3), (37, 32, 2), (704, 2816, 1),
                                    (2816, 704, 1), (2816, 2112, 1), (300, 2816, 8), (64, 1024, 17),
                                    (5, 16384, 1)])
