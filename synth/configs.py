@@ -43,10 +43,39 @@ class Workload:
     notes: dict = field(default_factory=dict)
 
 
+@dataclass(frozen=True)
+class AttnShape:
+    """Attention step next to the MoE layer of one decoder layer. The pages
+    name the attention, RoPE and RMSNorm kernels and an fp16 KV cache but no
+    head counts; the Gemma-shaped reading below is 16 query heads sharing 8
+    key/value heads (2 per group) of width 256."""
+    hidden: int          # H
+    n_heads: int         # query heads
+    n_kv_heads: int      # key/value heads (n_heads / n_kv_heads query heads share one)
+    head_dim: int        # d
+    max_ctx: int         # positions the KV cache holds
+    rope_theta: float = 10000.0
+    eps: float = 1e-6    # RMSNorm epsilon
+    group: int = 32
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    @property
+    def attn_width(self) -> int:
+        return self.n_heads * self.head_dim
+
+
 GEMMA_LAYER = Shape(hidden=2816, n_experts=128, top_k=8, inter=704, shared_inter=2112)
 SMALL_LAYER = Shape(hidden=512, n_experts=32, top_k=8, inter=128, shared_inter=256)
 # A hand-checkable shape for brute-force tests (explicit Python loops).
 TINY_LAYER = Shape(hidden=64, n_experts=4, top_k=2, inter=32, shared_inter=64)
+
+GEMMA_ATTN = AttnShape(hidden=2816, n_heads=16, n_kv_heads=8, head_dim=256, max_ctx=4096)
+SMALL_ATTN = AttnShape(hidden=512, n_heads=4, n_kv_heads=2, head_dim=64, max_ctx=512)
+# hand-checkable shape for the explicit-loop pins of the attention oracle
+TINY_ATTN = AttnShape(hidden=64, n_heads=4, n_kv_heads=2, head_dim=8, max_ctx=6)
 
 C0 = Workload("small_layer_decode_b1", 0, SMALL_LAYER, "decode", tokens=1)
 C1 = Workload("gemma_layer_decode_b1", 1, GEMMA_LAYER, "decode", tokens=1000)

@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import Shape
+from .configs import AttnShape, Shape
 
 SEED = 0
 
@@ -38,6 +38,12 @@ TAG_EPS = 7
 TAG_ZIPF = 8
 TAG_LOGITS = 9
 TAG_X_BF16 = 10
+TAG_ATTN_NORM = 11
+TAG_ATTN_QKV_BYTES = 12
+TAG_ATTN_QKV_SCALES = 13
+TAG_ATTN_O_BYTES = 14
+TAG_ATTN_O_SCALES = 15
+TAG_KV = 16
 
 SCALE_LO, SCALE_HI = 0.005, 0.02
 ROUTER_STD = 0.02
@@ -178,3 +184,34 @@ def layer_inputs(shape: Shape, config_id: int, layer: int = 0) -> dict:
         "shared": shared_blob(shape, config_id, layer),
         "experts": expert_blobs(shape, config_id, layer),
     }
+
+
+# --------------------------------------------------------------------------- attention step
+def q4_matrix(rows: int, cols: int, config_id: int, byte_tag: int, scale_tag: int, *sub: int,
+              group: int = 32):
+    """int4 g32 matrix [rows][cols]: uniform random nibbles (uint8 [rows][cols/2])
+    and U(0.005, 0.02) fp16 scales [rows][cols/32], as for the experts."""
+    q = np.frombuffer(stream(config_id, byte_tag, *sub).bytes(rows * cols // 2), np.uint8).reshape(rows, cols // 2)
+    s = stream(config_id, scale_tag, *sub).uniform(SCALE_LO, SCALE_HI, size=(rows, cols // group))
+    return q.copy(), s.astype(np.float16)
+
+
+def attn_weights(a: AttnShape, config_id: int, layer: int = 0) -> dict:
+    """Weights of one attention step: RMSNorm weight fp32 [H] = 1 + N(0, 0.1);
+    the fused projection [q rows | k rows | v rows] x H and the output
+    projection H x (n_heads * d), both int4 g32."""
+    norm_w = (1.0 + 0.1 * stream(config_id, TAG_ATTN_NORM, layer).standard_normal(a.hidden)).astype(np.float32)
+    qkv_q, qkv_s = q4_matrix(a.qkv_rows, a.hidden, config_id, TAG_ATTN_QKV_BYTES, TAG_ATTN_QKV_SCALES, layer)
+    o_q, o_s = q4_matrix(a.hidden, a.attn_width, config_id, TAG_ATTN_O_BYTES, TAG_ATTN_O_SCALES, layer)
+    return {"norm_w": norm_w, "qkv_q": qkv_q, "qkv_s": qkv_s, "o_q": o_q, "o_s": o_s}
+
+
+def kv_cache(a: AttnShape, n_filled: int, config_id: int, layer: int = 0):
+    """fp16 K and V caches [n_kv_heads][max_ctx][d]: positions < n_filled hold
+    N(0, 1) values (the keys and values of earlier tokens), the rest zero."""
+    k = np.zeros((a.n_kv_heads, a.max_ctx, a.head_dim), np.float16)
+    v = np.zeros_like(k)
+    r = stream(config_id, TAG_KV, layer)
+    k[:, :n_filled] = r.standard_normal((a.n_kv_heads, n_filled, a.head_dim)).astype(np.float16)
+    v[:, :n_filled] = r.standard_normal((a.n_kv_heads, n_filled, a.head_dim)).astype(np.float16)
+    return k, v

@@ -82,3 +82,53 @@ def layer_loops(u, E, k, H, I, Is, router, shared, experts, bias=None):
     for j, e in enumerate(order):
         y = y + w[j] * ffn_loops(*expert_weights_bruteforce(experts[e], H, I), u)
     return order, w, y
+
+
+# --------------------------------------------------------------------------- attention step
+def q4_matrix_loops(q, s):
+    """W[r][c] of an int4 g32 matrix (q uint8 [N][K/2], s fp16 [N][K/32]), element by element."""
+    N, K = q.shape[0], 2 * q.shape[1]
+    W = np.zeros((N, K))
+    for r in range(N):
+        for c in range(K):
+            W[r, c] = _nibble(int(q[r, c // 2]), c) * float(s[r, c // 32])
+    return W
+
+
+def attn_step_loops(x, w, kc, vc, pos, nh, nkv, d, theta, eps):
+    """One decode token through the attention step by explicit loops (tiny
+    shapes only). kc/vc (fp16 [nkv][ctx][d]) receive the token's key/value at
+    pos. Returns y (list of floats)."""
+    H = len(x)
+    ss = sum(float(v) * float(v) for v in x) / H
+    r = 1.0 / math.sqrt(ss + eps)
+    h = [float(x[i]) * r * float(w["norm_w"][i]) for i in range(H)]
+    Wqkv = q4_matrix_loops(w["qkv_q"], w["qkv_s"])
+    proj = [sum(Wqkv[n, i] * h[i] for i in range(H)) for n in range(Wqkv.shape[0])]
+
+    def rot(vec):
+        out = list(vec)
+        for i in range(d // 2):
+            ang = pos * theta ** (-2.0 * i / d)
+            c, s = math.cos(ang), math.sin(ang)
+            out[i] = vec[i] * c - vec[i + d // 2] * s
+            out[i + d // 2] = vec[i + d // 2] * c + vec[i] * s
+        return out
+
+    q = [rot(proj[hh * d:(hh + 1) * d]) for hh in range(nh)]
+    for g in range(nkv):
+        k = rot(proj[nh * d + g * d: nh * d + (g + 1) * d])
+        v = proj[(nh + nkv) * d + g * d: (nh + nkv) * d + (g + 1) * d]
+        for i in range(d):
+            kc[g, pos, i] = np.float16(k[i])
+            vc[g, pos, i] = np.float16(v[i])
+    att = []
+    for hh in range(nh):
+        g = hh // (nh // nkv)
+        sc = [sum(q[hh][i] * float(kc[g, t, i]) for i in range(d)) / math.sqrt(d) for t in range(pos + 1)]
+        m = max(sc)
+        e = [math.exp(v - m) for v in sc]
+        tot = sum(e)
+        att += [sum(e[t] / tot * float(vc[g, t, i]) for t in range(pos + 1)) for i in range(d)]
+    Wo = q4_matrix_loops(w["o_q"], w["o_s"])
+    return [float(x[n]) + sum(Wo[n, j] * att[j] for j in range(len(att))) for n in range(H)]
