@@ -31,6 +31,15 @@ class moe_cache_event(C.Structure):
     _fields_ = [("expert", C.c_int32), ("slot", C.c_int32), ("hit", C.c_int32), ("evicted", C.c_int32)]
 
 
+class moe_attn_shape(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("max_ctx", C.c_int32), ("rope_theta", C.c_float), ("eps", C.c_float)]
+
+
+class moe_attn_weights(C.Structure):
+    _fields_ = [("norm_w", vp), ("qkv_q", vp), ("qkv_s", vp), ("o_q", vp), ("o_s", vp)]
+
+
 class moe_layer_desc(C.Structure):
     _fields_ = [("router", vp), ("bias", vp), ("shared_blob", vp), ("experts_dev", vp),
                 ("experts_host", vp), ("slot_pool", vp), ("n_slots", C.c_int32),
@@ -77,6 +86,9 @@ SIGNATURES = {
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
+    "moe_attn_workspace_bytes": (c_status, [P(moe_attn_shape), P(C.c_size_t)]),
+    "moe_attn_decode": (c_status, [P(moe_attn_shape), P(moe_attn_weights), vp, vp, C.c_int32, vp, vp, vp,
+                                   C.c_size_t, vp]),
     "moe_debug_read_floor": (c_status, [vp, C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int32, vp,
                                         P(C.c_double), vp]),
     "moe_store_stride": (C.c_int64, [C.c_int64]),

@@ -168,6 +168,30 @@ def moe_debug_read_floor(src, nbytes, blocks, out, *, region_stride=0, regions=1
     return us.value if timed else None
 
 
+# ------------------------------------------------------------------ attention step
+def make_attn_shape(a) -> L.moe_attn_shape:
+    return L.moe_attn_shape(a.hidden, a.n_heads, a.n_kv_heads, a.head_dim, a.max_ctx, a.rope_theta, a.eps)
+
+
+def moe_attn_workspace_bytes(a) -> int:
+    s = make_attn_shape(a)
+    out = C.c_size_t(0)
+    _check(lib().moe_attn_workspace_bytes(C.byref(s), C.byref(out)), "moe_attn_workspace_bytes")
+    return out.value
+
+
+def moe_attn_decode(a, w, k_cache, v_cache, pos, x, y, workspace, stream=None):
+    """One token at position pos through the attention step. w: mapping with
+    device tensors norm_w, qkv_q, qkv_s, o_q, o_s; caches fp16 (as int16)
+    [n_kv_heads][max_ctx][d]; x, y fp32 [H]; workspace a zero-filled uint8
+    tensor of at least moe_attn_workspace_bytes bytes."""
+    s = make_attn_shape(a)
+    W = L.moe_attn_weights(_p(w["norm_w"]), _p(w["qkv_q"]), _p(w["qkv_s"]), _p(w["o_q"]), _p(w["o_s"]))
+    nbytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check(lib().moe_attn_decode(C.byref(s), C.byref(W), _p(k_cache), _p(v_cache), pos, _p(x), _p(y),
+                                 _p(workspace), nbytes, _stream(stream)), "moe_attn_decode")
+
+
 # ------------------------------------------------------------------ layer
 def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
     s = make_shape(sh)

@@ -118,6 +118,80 @@ moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* ou
   return MOE_OK;
 }
 
+static moe_status check_attn_shape(const moe_attn_shape* sh, const char* fn) {
+  if (!sh) return fail(MOE_EINVAL, "%s: shape is NULL", fn);
+  if (sh->hidden < moe::kGroup || sh->hidden > 4096 || sh->hidden % moe::kGroup)
+    return fail(MOE_ESHAPE, "%s: hidden %d must be a multiple of 32 in [32, 4096]", fn, sh->hidden);
+  if (sh->head_dim != 64 && sh->head_dim != 128 && sh->head_dim != 256)
+    return fail(MOE_ESHAPE, "%s: head_dim %d must be 64, 128 or 256", fn, sh->head_dim);
+  if (sh->n_kv_heads < 1 || sh->n_heads < sh->n_kv_heads || sh->n_heads % sh->n_kv_heads)
+    return fail(MOE_ESHAPE, "%s: n_heads %d must be a positive multiple of n_kv_heads %d", fn, sh->n_heads,
+                sh->n_kv_heads);
+  const int G = sh->n_heads / sh->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4)
+    return fail(MOE_ESHAPE, "%s: %d query heads per key/value head (1, 2 or 4 supported)", fn, G);
+  if (sh->n_heads * sh->head_dim > 8192)
+    return fail(MOE_ESHAPE, "%s: n_heads * head_dim = %d above 8192", fn, sh->n_heads * sh->head_dim);
+  const int P = moe::attn_split_positions(sh->head_dim);
+  if (sh->max_ctx < 1 || sh->max_ctx > P * P)
+    return fail(MOE_ESHAPE, "%s: max_ctx %d outside [1, %d]", fn, sh->max_ctx, P * P);
+  if (!(sh->rope_theta > 0.f) || !(sh->eps >= 0.f))
+    return fail(MOE_EINVAL, "%s: rope_theta must be > 0 and eps >= 0", fn);
+  if (!moe::attn_lds_fits(sh->hidden, sh->n_heads, sh->n_kv_heads, sh->head_dim))
+    return fail(MOE_ESHAPE, "%s: the projection blocks' LDS exceeds 64 KiB at this shape", fn);
+  return MOE_OK;
+}
+
+moe_status moe_attn_workspace_bytes(const moe_attn_shape* sh, size_t* out) {
+  moe::clear_error();
+  const char* fn = "moe_attn_workspace_bytes";
+  if (!out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  const moe_status st = check_attn_shape(sh, fn);
+  if (st != MOE_OK) return st;
+  *out = moe::attn_workspace(sh->n_heads, sh->head_dim, sh->max_ctx).total;
+  return MOE_OK;
+}
+
+moe_status moe_attn_decode(const moe_attn_shape* sh, const moe_attn_weights* W, uint16_t* k_cache,
+                           uint16_t* v_cache, int32_t pos, const float* x, float* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_attn_decode";
+  moe_status st = check_attn_shape(sh, fn);
+  if (st != MOE_OK) return st;
+  if (!W || !W->norm_w || !W->qkv_q || !W->qkv_s || !W->o_q || !W->o_s || !k_cache || !v_cache || !x || !y ||
+      !workspace)
+    return fail(MOE_EINVAL, "%s: NULL argument", fn);
+  if (pos < 0 || pos >= sh->max_ctx) return fail(MOE_EINVAL, "%s: pos %d outside [0, %d)", fn, pos, sh->max_ctx);
+  if (!moe::aligned16(W->qkv_q) || !moe::aligned16(W->o_q) || !moe::aligned16(k_cache) ||
+      !moe::aligned16(v_cache) || !moe::aligned16(workspace))
+    return fail(MOE_EALIGN, "%s: projections, caches and workspace must be 16-byte aligned", fn);
+  const size_t need = moe::attn_workspace(sh->n_heads, sh->head_dim, sh->max_ctx).total;
+  if (workspace_bytes < need)
+    return fail(MOE_ENOMEM, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+  moe::AttnLaunch L{};
+  L.H = sh->hidden;
+  L.nh = sh->n_heads;
+  L.nkv = sh->n_kv_heads;
+  L.d = sh->head_dim;
+  L.max_ctx = sh->max_ctx;
+  L.pos = pos;
+  L.theta = sh->rope_theta;
+  L.eps = sh->eps;
+  L.norm_w = W->norm_w;
+  L.qkv_q = W->qkv_q;
+  L.qkv_s = W->qkv_s;
+  L.o_q = W->o_q;
+  L.o_s = W->o_s;
+  L.kc = k_cache;
+  L.vc = v_cache;
+  L.x = x;
+  L.y = y;
+  L.workspace = workspace;
+  HIP_OR_FAIL(moe::launch_attn_decode(L, static_cast<hipStream_t>(stream)), fn);
+  return MOE_OK;
+}
+
 moe_status moe_debug_read_floor(const void* src, int64_t bytes, int64_t region_stride, int32_t regions,
                                 int32_t blocks, int32_t reps, uint32_t* out, double* mean_us, void* stream) {
   moe::clear_error();

@@ -1,0 +1,532 @@
+// Attention step of one decoder layer, one token (decode): RMSNorm with a
+// learned weight, the fused q/k/v projection, rotate-half RoPE, the append of
+// the token's key and value to the fp16 KV cache, grouped-query attention over
+// the cached positions, the output projection and the residual add.
+//
+// "Como executar um modelo de 26 bilhões de parâmetros em dois gigabytes de
+// memória em um Mac comum": section "Sem dependências do llama.cpp e MLX"
+// names hand-written attention, RMSNorm and RoPE kernels; section "Qual é o
+// principal truque da arquitetura" keeps the KV cache for the context resident
+// in FP16.
+//
+// Three launches:
+//  1. k_attn_gemv<kQkv>: every block computes the RMSNorm factor, quantises
+//     the normed input into digit planes (LDS) and takes its rows of the int4
+//     projection with v_dot8 (as the expert GEMVs). A block's rows are pairs
+//     (i, i + d/2) of one head, so its epilogue applies RoPE to q and k itself,
+//     writes q (fp32) and appends k and v to the cache (fp16, nearest even).
+//  2. k_attn_split: block (split, kv head) streams the K and V rows of its
+//     positions once for all query heads of the group: scores, a softmax over
+//     the split, the value sum; the last block of a group (arrival counter)
+//     combines the splits' partial sums in a fixed order.
+//  3. k_attn_gemv<kOut>: output projection of the attention output (quantised
+//     per group of 32 in LDS) plus the residual.
+#include <hip/hip_fp16.h>
+
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kAThreads = 1024;
+constexpr int kAWaves = kAThreads / kWave;
+constexpr int kSplitThreads = 256;
+constexpr int kSplitSteps = 8;  // position steps per split block
+
+enum { kQkv = 0, kOut = 1 };
+
+__device__ __forceinline__ uint16_t f2h_bits(float v) {
+  return __half_as_ushort(__float2half_rn(v));
+}
+
+__device__ __forceinline__ float h_lo(uint32_t w) {
+  return __half2float(__ushort_as_half(static_cast<uint16_t>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float h_hi(uint32_t w) {
+  return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)));
+}
+
+// GEMV y = W x over rows of an int4 g32 matrix with K = 32 * ng columns, input
+// quantised per group into LDS digit planes. Lane (r0, c) = (tid / ng, tid % ng)
+// owns chunk column c of local rows r0, r0 + R, ... (R = 1024 / ng); the block
+// owns RB local rows.
+template <int MODE, int NT>
+__global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
+  extern __shared__ uint4 lds_raw[];
+  __shared__ float red[kAWaves];
+  __shared__ float rowsum[64];
+  const int ng = A.K / kGroup;
+  const int RB = A.RB;
+  float* part = reinterpret_cast<float*>(lds_raw);                                // [RB][ng]
+  DigitGroup* xd = reinterpret_cast<DigitGroup*>(part + static_cast<size_t>(RB) * ng);  // [ng]
+  float* xs = reinterpret_cast<float*>(xd + ng);                                   // [ng]
+  float* xw = xs + ng;                                                             // [K] (kQkv)
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const int R = kAThreads / ng;
+  const int c = tid % ng, r0 = tid / ng;
+  const bool lane_on = r0 < R;
+  const int half = RB / 2;
+  const int d = A.d;
+
+  // global row of local row r
+  auto row_of = [&](int r) -> int {
+    if (MODE == kQkv) {
+      // pairs (i, i + d/2) of one head: local rows [0, half) are the first
+      // halves, [half, RB) the second halves
+      const int p = blockIdx.x * half + (r < half ? r : r - half);
+      const int hh = p / (d / 2), i = p % (d / 2);
+      return hh * d + i + (r < half ? 0 : d / 2);
+    } else {
+      const int n = blockIdx.x * RB + r;
+      return n < A.N ? n : A.N - 1;  // rows past the end re-read the last row
+    }
+  };
+
+  // weights first: nothing they address depends on the input
+  const size_t rowb = static_cast<size_t>(A.K) / 2;
+  uint4 wv[NT];
+  uint16_t sw[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    int r = r0 + R * t;
+    r = r < RB ? r : RB - 1;  // clamped: loaded, not stored
+    const size_t n = static_cast<size_t>(row_of(r));
+    wv[t] = load_w16(A.wq + n * rowb + 16 * static_cast<size_t>(c));
+    sw[t] = A.ws[n * ng + c];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  float inv = 1.0f;
+  if (MODE == kQkv) {
+    // RMSNorm factor of x (a fixed-order block sum), then h = x * w * factor
+    float ss = 0.f;
+    for (int i = tid; i < A.K; i += kAThreads) {
+      const float v = A.x[i];
+      ss = fmaf(v, v, ss);
+      xw[i] = v * A.norm_w[i];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAWaves; ++w) tot += red[w];
+    inv = 1.0f / sqrtf(tot / static_cast<float>(A.K) + A.eps);
+  }
+  // digit planes of the input, two groups per wave pass
+  for (int g0 = 2 * wave; g0 < ng; g0 += 2 * kAWaves) {
+    const int g = g0 + (lane >> 5);
+    const int gi = g < ng ? g : ng - 1;
+    const float v = MODE == kQkv ? xw[kGroup * gi + (lane & 31)] * inv : A.a[kGroup * gi + (lane & 31)];
+    quant_pair_of_groups(g < ng ? v : 0.f, g0, ng, xd, xs);
+  }
+  __syncthreads();
+  const DigitGroup xc = xd[c];
+  const float xsc = xs[c];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int r = r0 + R * t;
+    const float p = static_cast<float>(chunk_dot(wv[t], xc)) * (h2f(sw[t]) * xsc);
+    if (lane_on && r < RB) part[r * ng + c] = p;
+  }
+  __syncthreads();
+  {
+    // row sums: 16 lanes per row, 4 rows per wave, fixed order
+    const int r = 4 * wave + (lane >> 4);
+    const int l = lane & 15;
+    if (r < RB) {
+      float acc = 0.f;
+      for (int cc = l; cc < ng; cc += 16) acc += part[r * ng + cc];
+      acc = dpp_sum<16>(acc);
+      if (l == 0) rowsum[r] = acc;
+    }
+  }
+  __syncthreads();
+  if (MODE == kQkv) {
+    if (tid < half) {
+      const int p = blockIdx.x * half + tid;
+      const int hh = p / (d / 2), i = p % (d / 2);
+      float v0 = rowsum[tid], v1 = rowsum[tid + half];
+      if (hh < A.nh + A.nkv) {
+        // angle pos * theta^(-2i/d), in fp64, then the rotation in fp32
+        const double ang = static_cast<double>(A.pos) * pow(A.theta, -2.0 * i / d);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const float cf = static_cast<float>(cs), sf = static_cast<float>(sn);
+        const float r0v = v0 * cf - v1 * sf;
+        const float r1v = v1 * cf + v0 * sf;
+        v0 = r0v;
+        v1 = r1v;
+      }
+      if (hh < A.nh) {
+        A.q[hh * d + i] = v0;
+        A.q[hh * d + i + d / 2] = v1;
+      } else {
+        const bool is_k = hh < A.nh + A.nkv;
+        const int g = is_k ? hh - A.nh : hh - A.nh - A.nkv;
+        uint16_t* cache = is_k ? A.kc : A.vc;
+        const size_t base = (static_cast<size_t>(g) * A.max_ctx + A.pos) * d;
+        cache[base + i] = f2h_bits(v0);
+        cache[base + i + d / 2] = f2h_bits(v1);
+      }
+    }
+  } else {
+    if (tid < RB) {
+      const int n = blockIdx.x * RB + tid;
+      if (n < A.N) A.y[n] = A.x[n] + rowsum[tid];
+    }
+  }
+}
+
+// One split of the context for one key/value head and its G query heads. A
+// position's d values are spread over LP = d / 16 lanes (16 each, two 16-byte
+// loads of K and two of V); a step covers 256 / LP positions, a split
+// kSplitSteps steps. Every K and V load of the block is issued before any is
+// used.
+template <int D, int G>
+__global__ __launch_bounds__(kSplitThreads, 1) void k_attn_split(AttnSplitArgs A) {
+  constexpr int LP = D / 16;
+  constexpr int PPS = kSplitThreads / LP;
+  constexpr int P = kSplitSteps * PPS;
+  __shared__ float sc[G][P];
+  __shared__ float red[kSplitThreads / kWave][G][D];
+  __shared__ float mh[G], lh[G];
+  __shared__ int is_last;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int g = blockIdx.y, sp = blockIdx.x;
+  const int slot = tid / LP, e0 = (tid % LP) * 16;
+  const int n = A.n, lo = sp * P;
+
+  uint4 kr[kSplitSteps][2], vr[kSplitSteps][2];
+#pragma unroll
+  for (int s = 0; s < kSplitSteps; ++s) {
+    int t = lo + s * PPS + slot;
+    t = t < n ? t : n - 1;  // clamped: loaded, masked below
+    const size_t base = (static_cast<size_t>(g) * A.max_ctx + t) * D + e0;
+    kr[s][0] = *reinterpret_cast<const uint4*>(A.kc + base);
+    kr[s][1] = *reinterpret_cast<const uint4*>(A.kc + base + 8);
+    vr[s][0] = *reinterpret_cast<const uint4*>(A.vc + base);
+    vr[s][1] = *reinterpret_cast<const uint4*>(A.vc + base + 8);
+  }
+  float qv[G][16];
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float4* qp = reinterpret_cast<const float4*>(A.q + static_cast<size_t>(g * G + h) * D + e0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = qp[j];
+      qv[h][4 * j] = v.x * scale;
+      qv[h][4 * j + 1] = v.y * scale;
+      qv[h][4 * j + 2] = v.z * scale;
+      qv[h][4 * j + 3] = v.w * scale;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // scores q . k / sqrt(d): 16 products per lane, then a sum over the LP lanes
+#pragma unroll
+  for (int s = 0; s < kSplitSteps; ++s) {
+    const uint32_t kw[8] = {kr[s][0].x, kr[s][0].y, kr[s][0].z, kr[s][0].w,
+                            kr[s][1].x, kr[s][1].y, kr[s][1].z, kr[s][1].w};
+    float kf[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kf[2 * j] = h_lo(kw[j]);
+      kf[2 * j + 1] = h_hi(kw[j]);
+    }
+    const int t = lo + s * PPS + slot;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float dsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dsum = fmaf(qv[h][e], kf[e], dsum);
+      dsum = dpp_sum<LP>(dsum);
+      if (tid % LP == 0) sc[h][s * PPS + slot] = t < n ? dsum : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // softmax over the split: wave h takes query head h
+  if (wave < G) {
+    const int h = wave;
+    float m = -INFINITY;
+    for (int j = lane; j < P; j += kWave) m = fmaxf(m, sc[h][j]);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    float l = 0.f;
+    for (int j = lane; j < P; j += kWave) {
+      const float sv = sc[h][j];
+      const float e = sv == -INFINITY ? 0.f : expf(sv - m);
+      sc[h][j] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      mh[h] = m;
+      lh[h] = l;
+    }
+  }
+  __syncthreads();
+  // value sum: each lane its 16 elements over its positions
+  float acc[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSplitSteps; ++s) {
+    const uint32_t vw[8] = {vr[s][0].x, vr[s][0].y, vr[s][0].z, vr[s][0].w,
+                            vr[s][1].x, vr[s][1].y, vr[s][1].z, vr[s][1].w};
+    float vf[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      vf[2 * j] = h_lo(vw[j]);
+      vf[2 * j + 1] = h_hi(vw[j]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p = sc[h][s * PPS + slot];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+    }
+  }
+  // sum over the positions of the wave (lanes with the same elements), then
+  // over the waves through LDS
+#pragma unroll
+  for (int o = LP; o < kWave; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, kWave);
+  if (lane < LP) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave][h][e0 + e] = acc[h][e];
+  }
+  __syncthreads();
+  const int nsplit = gridDim.x;
+  for (int idx = tid; idx < G * D; idx += kSplitThreads) {
+    const int h = idx / D, e = idx % D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplitThreads / kWave; ++w) o += red[w][h][e];
+    const int qh = g * G + h;
+    if (nsplit == 1) {
+      A.out[static_cast<size_t>(qh) * D + e] = o / lh[h];
+    } else {
+      __hip_atomic_store(A.po + (static_cast<size_t>(qh) * nsplit + sp) * D + e, o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (e == 0) {
+        __hip_atomic_store(A.pm + static_cast<size_t>(qh) * nsplit + sp, mh[h], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(A.pl + static_cast<size_t>(qh) * nsplit + sp, lh[h], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (nsplit == 1) return;
+  // every partial store of this block has completed before it arrives
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(A.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = old == nsplit - 1;
+    if (is_last) __hip_atomic_store(A.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  // combine the splits of the group's heads: weights exp(m_s - M), fixed order
+  float* wsp = &sc[0][0];  // [G][nsplit] split weights (nsplit <= P)
+  for (int idx = tid; idx < G * nsplit; idx += kSplitThreads) {
+    const int h = idx / nsplit;
+    wsp[idx] = __hip_atomic_load(A.pm + static_cast<size_t>(g * G + h) * nsplit + idx % nsplit,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (wave < G) {
+    const int h = wave;
+    float m = -INFINITY;
+    for (int s = lane; s < nsplit; s += kWave) m = fmaxf(m, wsp[h * nsplit + s]);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    float l = 0.f;
+    for (int s = lane; s < nsplit; s += kWave) {
+      const float wv = expf(wsp[h * nsplit + s] - m);
+      wsp[h * nsplit + s] = wv;
+      l = fmaf(wv, __hip_atomic_load(A.pl + static_cast<size_t>(g * G + h) * nsplit + s, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT), l);
+    }
+    l = wave_sum(l);
+    if (lane == 0) lh[h] = l;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kSplitThreads) {
+    const int h = idx / D, e = idx % D;
+    const size_t qh = static_cast<size_t>(g * G + h);
+    float o = 0.f;
+    for (int s = 0; s < nsplit; ++s)
+      o = fmaf(wsp[h * nsplit + s],
+               __hip_atomic_load(A.po + (qh * nsplit + s) * D + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), o);
+    A.out[qh * D + e] = o / lh[h];
+  }
+}
+
+// rows per block of the projection: pairs of one head (a power of two that
+// divides d), at most 6 passes of R rows, and about 256 blocks where the
+// matrix has enough rows
+int qkv_rows_per_block(int K, int rows, int d) {
+  const int R = kAThreads / (K / kGroup);
+  int RB = 64;
+  while (RB > 2 && (RB > 6 * R || d % RB)) RB /= 2;
+  int rmin = 2;
+  while (rmin * 2 <= R && rmin * 2 <= RB) rmin *= 2;
+  while (RB > rmin && rows / RB < 256) RB /= 2;
+  return RB;
+}
+
+size_t gemv_lds(int K, int RB, bool with_x) {
+  const int ng = K / kGroup;
+  return static_cast<size_t>(RB) * ng * sizeof(float) + ng * sizeof(DigitGroup) + ng * sizeof(float) +
+         (with_x ? static_cast<size_t>(K) * sizeof(float) : 0);
+}
+
+hipError_t launch_gemv(int mode, const AttnGemvArgs& A, int blocks, hipStream_t s) {
+  const int R = kAThreads / (A.K / kGroup);
+  const int NT = (A.RB + R - 1) / R;
+  const size_t lds = gemv_lds(A.K, A.RB, mode == kQkv);
+#define MOE_AG(M, T) hipLaunchKernelGGL((k_attn_gemv<M, T>), dim3(blocks), dim3(kAThreads), lds, s, A)
+#define MOE_AG_NT(M)                  \
+  switch (NT) {                       \
+    case 1: MOE_AG(M, 1); break;      \
+    case 2: MOE_AG(M, 2); break;      \
+    case 3: MOE_AG(M, 3); break;      \
+    case 4: MOE_AG(M, 4); break;      \
+    case 5: MOE_AG(M, 5); break;      \
+    case 6: MOE_AG(M, 6); break;      \
+    default: return hipErrorInvalidValue; \
+  }
+  if (mode == kQkv) {
+    MOE_AG_NT(kQkv)
+  } else {
+    MOE_AG_NT(kOut)
+  }
+#undef MOE_AG_NT
+#undef MOE_AG
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attn_split_positions(int d) { return kSplitSteps * (kSplitThreads / (d / 16)); }
+
+bool attn_lds_fits(int H, int nh, int nkv, int d) {
+  const int rows = (nh + 2 * nkv) * d;
+  const int RBq = qkv_rows_per_block(H, rows, d);
+  const int Ko = nh * d;
+  const int Ro = kAThreads / (Ko / kGroup);
+  return gemv_lds(H, RBq, true) <= 65536 && gemv_lds(Ko, Ro, false) <= 65536;
+}
+
+AttnWorkspace attn_workspace(int nh, int d, int max_ctx) {
+  const int max_split = (max_ctx + attn_split_positions(d) - 1) / attn_split_positions(d);
+  AttnWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~static_cast<size_t>(255);
+    return o;
+  };
+  w.q = take(static_cast<size_t>(nh) * d * sizeof(float));
+  w.out = take(static_cast<size_t>(nh) * d * sizeof(float));
+  w.pm = take(static_cast<size_t>(nh) * max_split * sizeof(float));
+  w.pl = take(static_cast<size_t>(nh) * max_split * sizeof(float));
+  w.po = take(static_cast<size_t>(nh) * max_split * d * sizeof(float));
+  w.cnt = take(static_cast<size_t>(nh) * sizeof(int));
+  w.total = off;
+  w.max_split = max_split;
+  return w;
+}
+
+hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
+  const int H = L.H, nh = L.nh, nkv = L.nkv, d = L.d;
+  const AttnWorkspace W = attn_workspace(nh, d, L.max_ctx);
+  uint8_t* ws = static_cast<uint8_t*>(L.workspace);
+  float* q = reinterpret_cast<float*>(ws + W.q);
+  float* out = reinterpret_cast<float*>(ws + W.out);
+
+  // 1. RMSNorm + q/k/v projection + RoPE + cache append
+  AttnGemvArgs a{};
+  a.wq = L.qkv_q;
+  a.ws = L.qkv_s;
+  a.K = H;
+  a.N = (nh + 2 * nkv) * d;
+  a.RB = qkv_rows_per_block(H, a.N, d);
+  a.x = L.x;
+  a.norm_w = L.norm_w;
+  a.eps = L.eps;
+  a.d = d;
+  a.nh = nh;
+  a.nkv = nkv;
+  a.pos = L.pos;
+  a.theta = L.theta;
+  a.max_ctx = L.max_ctx;
+  a.q = q;
+  a.kc = L.kc;
+  a.vc = L.vc;
+  hipError_t e = launch_gemv(kQkv, a, a.N / a.RB, s);
+  if (e != hipSuccess) return e;
+
+  // 2. attention over positions [0, pos]
+  AttnSplitArgs b{};
+  b.q = q;
+  b.kc = L.kc;
+  b.vc = L.vc;
+  b.max_ctx = L.max_ctx;
+  b.n = L.pos + 1;
+  b.pm = reinterpret_cast<float*>(ws + W.pm);
+  b.pl = reinterpret_cast<float*>(ws + W.pl);
+  b.po = reinterpret_cast<float*>(ws + W.po);
+  b.out = out;
+  b.cnt = reinterpret_cast<int*>(ws + W.cnt);
+  const int P = attn_split_positions(d);
+  const dim3 grid((b.n + P - 1) / P, nkv);
+  const int G = nh / nkv;
+#define MOE_AS(DD, GG) hipLaunchKernelGGL((k_attn_split<DD, GG>), grid, dim3(kSplitThreads), 0, s, b)
+#define MOE_AS_G(DD)                      \
+  if (G == 1) MOE_AS(DD, 1);              \
+  else if (G == 2) MOE_AS(DD, 2);         \
+  else if (G == 4) MOE_AS(DD, 4);         \
+  else return hipErrorInvalidValue;
+  if (d == 64) {
+    MOE_AS_G(64)
+  } else if (d == 128) {
+    MOE_AS_G(128)
+  } else if (d == 256) {
+    MOE_AS_G(256)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOE_AS_G
+#undef MOE_AS
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // 3. output projection + residual
+  AttnGemvArgs c{};
+  c.wq = L.o_q;
+  c.ws = L.o_s;
+  c.K = nh * d;
+  c.N = H;
+  const int Ro = kAThreads / (c.K / kGroup);
+  int nt = H / (Ro * 256);
+  nt = nt < 1 ? 1 : (nt > 6 ? 6 : nt);
+  c.RB = Ro * nt > 64 ? 64 : Ro * nt;
+  c.a = out;
+  c.x = L.x;
+  c.y = L.y;
+  return launch_gemv(kOut, c, (H + c.RB - 1) / c.RB, s);
+}
+
+}  // namespace moe

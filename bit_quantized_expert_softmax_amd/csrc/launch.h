@@ -178,4 +178,61 @@ int read_floor_loads(int64_t bytes, int blocks);
 hipError_t launch_read_floor(const uint8_t* src, int64_t bytes, int blocks, uint32_t* out, hipEvent_t t0,
                              hipEvent_t t1, hipStream_t s);
 
+// ---------------------------------------------------------------- attention step
+struct AttnGemvArgs {
+  const uint8_t* wq;   // int4 rows [N][K/2]
+  const uint16_t* ws;  // fp16 scales [N][K/32]
+  int K, N, RB;        // columns, rows, rows per block
+  const float* x;      // projection input (RMSNorm in) or residual (output projection)
+  const float* norm_w;
+  float eps;
+  const float* a;      // output projection input [K]
+  float* y;            // output projection: y = x + W a
+  int d, nh, nkv, pos, max_ctx;
+  double theta;
+  float* q;            // rotated queries [nh][d]
+  uint16_t* kc;        // fp16 caches [nkv][max_ctx][d]
+  uint16_t* vc;
+};
+
+struct AttnSplitArgs {
+  const float* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int max_ctx, n;      // n = positions attended (pos + 1)
+  float* pm;           // per-split max [nh][nsplit]
+  float* pl;           // per-split sum of exponentials
+  float* po;           // per-split unnormalised value sums [nh][nsplit][d]
+  float* out;          // attention output [nh][d]
+  int* cnt;            // arrival counters per key/value head (zero between calls)
+};
+
+struct AttnWorkspace {
+  size_t q, out, pm, pl, po, cnt, total;
+  int max_split;
+};
+
+struct AttnLaunch {
+  int H, nh, nkv, d, max_ctx, pos;
+  double theta;
+  float eps;
+  const float* norm_w;
+  const uint8_t* qkv_q;
+  const uint16_t* qkv_s;
+  const uint8_t* o_q;
+  const uint16_t* o_s;
+  uint16_t* kc;
+  uint16_t* vc;
+  const float* x;
+  float* y;
+  void* workspace;
+};
+
+// Positions per split block of the attention kernel for head width d.
+int attn_split_positions(int d);
+// The projection kernels' LDS fits one block at this shape.
+bool attn_lds_fits(int H, int nh, int nkv, int d);
+AttnWorkspace attn_workspace(int nh, int d, int max_ctx);
+hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s);
+
 }  // namespace moe

@@ -319,6 +319,56 @@ moe_status moe_layer_profile(moe_layer* L, int32_t enable);
 moe_status moe_layer_profile_kinds(moe_layer* L, uint32_t mask, int32_t every, int32_t reserve_events);
 moe_status moe_layer_profile_read(moe_layer* L, int32_t kind, moe_kernel_time* out);
 
+/* ---------------------------------------------------------------- attention step
+ * The attention step of one decoder layer, next to the MoE FFN, for one
+ * token ("Como executar um modelo de 26 bilhões de parâmetros em dois
+ * gigabytes de memória em um Mac comum": section "Sem dependências do
+ * llama.cpp e MLX" lists attention, RMSNorm and RoPE kernels; section "Qual
+ * é o principal truque da arquitetura" keeps the KV cache for the context
+ * resident in FP16). With a = the attention output:
+ *   h = x / sqrt(mean(x^2) + eps) * norm_w
+ *   [q | k | v] = Wqkv h                (int4 g32, q rows, then k rows, then v rows)
+ *   q, k rotated by RoPE at pos: pairs (i, i + d/2), angle pos * theta^(-2i/d),
+ *       (a, b) -> (a cos - b sin, b cos + a sin)
+ *   K[g][pos] = fp16(k_g), V[g][pos] = fp16(v_g)   (round to nearest even)
+ *   a_h = softmax over t in [0, pos] of q_h . K[g][t] / sqrt(d), applied to V[g],
+ *       g = h / (n_heads / n_kv_heads)
+ *   y = x + Wo a
+ * The pages give no head counts; the Gemma-shaped configuration used with this
+ * library is 16 query heads, 8 key/value heads, d = 256. */
+typedef struct moe_attn_shape {
+  int32_t hidden;      /* H: multiple of 32 in [32, 4096] */
+  int32_t n_heads;     /* query heads; n_heads / n_kv_heads in {1, 2, 4}; n_heads * head_dim <= 8192 */
+  int32_t n_kv_heads;  /* key/value heads */
+  int32_t head_dim;    /* d: 64, 128 or 256 */
+  int32_t max_ctx;     /* positions the caches hold: 1 .. (positions per split)^2 (16384 at d = 256) */
+  float rope_theta;    /* > 0 */
+  float eps;           /* RMSNorm epsilon, >= 0 */
+} moe_attn_shape;
+
+typedef struct moe_attn_weights {
+  const float* norm_w;    /* dev fp32 [H] */
+  const uint8_t* qkv_q;   /* dev int4 g32 [(n_heads + 2 n_kv_heads) d][H/2], 16-byte aligned */
+  const uint16_t* qkv_s;  /* dev fp16 [(n_heads + 2 n_kv_heads) d][H/32] */
+  const uint8_t* o_q;     /* dev int4 g32 [H][n_heads d / 2], 16-byte aligned */
+  const uint16_t* o_s;    /* dev fp16 [H][n_heads d / 32] */
+} moe_attn_weights;
+
+/* Workspace of moe_attn_decode for this shape (queries, per-split partial
+ * results, arrival counters). MOE_ESHAPE for unsupported shapes. */
+moe_status moe_attn_workspace_bytes(const moe_attn_shape* sh, size_t* out);
+/* One token at position pos (0 <= pos < max_ctx) through the attention step,
+ * asynchronous on stream. k_cache / v_cache: dev fp16 [n_kv_heads][max_ctx][d],
+ * 16-byte aligned, owned by the caller; positions < pos hold the earlier
+ * tokens, the call writes position pos and reads [0, pos]. x, y: dev fp32 [H]
+ * (y may be x). workspace: dev, 16-byte aligned, at least
+ * moe_attn_workspace_bytes, zero-filled before its first use (the call leaves
+ * its counters at zero again); calls that share a workspace must be ordered
+ * on one stream. Checks every argument before enqueueing anything. */
+moe_status moe_attn_decode(const moe_attn_shape* sh, const moe_attn_weights* W, uint16_t* k_cache,
+                           uint16_t* v_cache, int32_t pos, const float* x, float* y, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------- test support
  * Unpacks the nibbles of W to int8 [N][K] (dev) for bit-exact comparison. */
 moe_status moe_debug_unpack_q4(const moe_q4* W, int32_t N, int32_t K, int8_t* out, void* stream);

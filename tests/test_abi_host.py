@@ -178,6 +178,28 @@ def test_gpu_entry_points_reject_bad_arguments_before_enqueue(tmp_path):
     assert "LDS" in api.moe_last_error()
     assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 1, 0, C.byref(h)) == -1
     assert lib.moe_layer_decode(None, 16, None, 1, 0, 32, None, None, None, None, None, None) == -1
+    # attention step: shapes, positions, alignment and workspace size are
+    # checked before anything is enqueued
+    from synth.configs import GEMMA_ATTN, SMALL_ATTN
+    a = api.make_attn_shape(GEMMA_ATTN)
+    nb = C.c_size_t()
+    assert lib.moe_attn_workspace_bytes(C.byref(a), C.byref(nb)) == 0 and nb.value > 0
+    for field, val in (("head_dim", 96), ("n_kv_heads", 5), ("hidden", 4128), ("max_ctx", 16385), ("max_ctx", 0)):
+        bad = api.make_attn_shape(GEMMA_ATTN)
+        setattr(bad, field, val)
+        assert lib.moe_attn_workspace_bytes(C.byref(bad), C.byref(nb)) == -2, field
+    g3 = api.make_attn_shape(GEMMA_ATTN)
+    g3.n_heads, g3.n_kv_heads = 12, 4  # 3 query heads per group
+    assert lib.moe_attn_workspace_bytes(C.byref(g3), C.byref(nb)) == -2
+    W = _lib.moe_attn_weights(16, 16, 16, 16, 16)
+    small = api.make_attn_shape(SMALL_ATTN)
+    assert lib.moe_attn_workspace_bytes(C.byref(small), C.byref(nb)) == 0
+    args = lambda pos, ws, wsb, kc=16: (C.byref(small), C.byref(W), kc, 16, pos, 16, 16, ws, wsb, None)
+    assert lib.moe_attn_decode(*args(512, 16, nb.value)) == -1     # pos = max_ctx
+    assert lib.moe_attn_decode(*args(-1, 16, nb.value)) == -1
+    assert lib.moe_attn_decode(*args(0, 16, nb.value - 1)) == -5   # workspace too small
+    assert lib.moe_attn_decode(*args(0, 16, nb.value, kc=8)) == -3  # misaligned cache
+    assert lib.moe_attn_decode(*args(0, None, nb.value)) == -1
     # read floor: sizes are checked before any launch
     assert lib.moe_debug_read_floor(16, 24, 0, 1, 1, 1, 16, None, None) == -2          # not 16-byte words
     assert lib.moe_debug_read_floor(16, 16 * 1024 * 17, 0, 1, 1, 1, 16, None, None) == -2  # 17 loads per lane
