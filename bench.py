@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--sweep-slots", default="8,32,64",
                     help="slot counts per layer for the cache-size sweep in the detail ('' to skip)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--attn-ctx", type=int, default=4096,
+                    help="context length of the attention step timed next to the MoE layers")
+    ap.add_argument("--no-attn", action="store_true", help="skip the attention-step measurements")
     ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
                          "tokens (the measured kernel included), 'copy' copies 1 GiB once")
@@ -144,9 +147,9 @@ def main():
     import numpy as np
     import torch
 
-    from bit_quantized_expert_softmax_amd import api
+    from bit_quantized_expert_softmax_amd import _lib, api
     from synth import gen
-    from synth.configs import C2
+    from synth.configs import C2, GEMMA_ATTN
 
     if args.probe == "copy":
         a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
@@ -483,6 +486,114 @@ def main():
         gu_res = gu_bytes + 2 * Is * (H // 2 + 2 * (H // 32)) + Is * 4
         detail["resident_gateup_us"] = us_r
         detail["resident_gateup_GBps"] = gu_res / (us_r * 1e-6) / 1e9
+        # attention step next to each MoE layer (RMSNorm, q/k/v, RoPE, fp16 KV
+        # cache, grouped-query attention, output projection + residual) at a
+        # context of attn_ctx positions: 30 layers with their own weights and
+        # caches (1.6 GB together, so nothing stays in the last-level cache);
+        # alone, then as full decoder layers with the resident MoE layers
+        if not args.no_attn:
+            A = GEMMA_ATTN
+            pos_a = min(args.attn_ctx, A.max_ctx) - 1
+            kc0, vc0 = gen.kv_cache(A, pos_a, 6, 0)
+            kc0, vc0 = torch.from_numpy(kc0.view(np.int16)), torch.from_numpy(vc0.view(np.int16))
+            at = []
+            for l in range(Lyr):
+                w_np = gen.attn_weights(A, 6, l)
+                at.append({"w": {"norm_w": torch.from_numpy(w_np["norm_w"]).to(devn),
+                                 "qkv_q": torch.from_numpy(w_np["qkv_q"]).to(devn),
+                                 "qkv_s": torch.from_numpy(w_np["qkv_s"].view(np.int16)).to(devn),
+                                 "o_q": torch.from_numpy(w_np["o_q"]).to(devn),
+                                 "o_s": torch.from_numpy(w_np["o_s"].view(np.int16)).to(devn)},
+                           "kc": kc0.to(devn), "vc": vc0.to(devn),
+                           "ws": torch.zeros(api.moe_attn_workspace_bytes(A), dtype=torch.uint8, device=devn)})
+            a_mid = torch.empty((1, H), device=devn)
+            Wa = A.n_heads * A.head_dim
+            attn_bytes = (A.qkv_rows * (H // 2 + 2 * (H // 32)) + H * (Wa // 2 + 2 * (Wa // 32))
+                          + 2 * A.n_kv_heads * (pos_a + 1) * A.head_dim * 2)
+
+            def step_attn(with_moe):
+                s_ = torch.cuda.current_stream()
+                src = x_in.data_ptr()
+                for l in range(Lyr):
+                    api.moe_attn_decode(A, at[l]["w"], at[l]["kc"], at[l]["vc"], pos_a, src, a_mid, at[l]["ws"],
+                                        stream=s_)
+                    if with_moe:
+                        dst = hp[l & 1]
+                        rc = decode(res[l], a_mid.data_ptr(), None, 1, flags_base, dst, None, None, None, None,
+                                    None, s_.cuda_stream)
+                        if rc:
+                            raise api.MoeError(rc, "moe_layer_decode", api.moe_last_error())
+                        src = dst
+                    else:
+                        src = a_mid.data_ptr()
+
+            attn_detail = {"ctx": pos_a + 1, "bytes_per_step": attn_bytes}
+            for with_moe in (False, True):
+                with torch.cuda.stream(cap):
+                    step_attn(with_moe)
+                torch.cuda.synchronize()
+                ga = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(ga, stream=cap):
+                    step_attn(with_moe)
+                torch.cuda.synchronize()
+                for t in range(args.warmup):
+                    x_in.copy_(x[t % T:t % T + 1])
+                    ga.replay()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for t in range(args.warmup, args.warmup + args.steps):
+                    x_in.copy_(x[t % T:t % T + 1])
+                    ga.replay()
+                torch.cuda.synchronize()
+                el_a = time.perf_counter() - t0
+                if with_moe:
+                    attn_detail["decoder_layers_with_resident_moe_tokens_per_s"] = args.steps / el_a
+                else:
+                    us_a = 1e6 * el_a / (args.steps * Lyr)
+                    attn_detail["us_per_step"] = us_a
+                    attn_detail["GBps"] = attn_bytes / (us_a * 1e-6) / 1e9
+                    attn_detail["frac_of_8TBps"] = attn_bytes / (us_a * 1e-6) / 8e12
+                del ga
+            # the cache-mode stack (16-slot LFU per layer, misses over PCIe) with
+            # the attention step in place of the seeded perturbation
+            a_sh = api.make_attn_shape(A)
+            a_w = [_lib.moe_attn_weights(*(a["w"][k].data_ptr() for k in ("norm_w", "qkv_q", "qkv_s", "o_q", "o_s")))
+                   for a in at]
+            a_ptr = [(a["kc"].data_ptr(), a["vc"].data_ptr(), a["ws"].data_ptr(), a["ws"].numel()) for a in at]
+            st_a = [api.moe_decode_stats() for _ in range(Lyr)]
+            attn_call = lib.moe_attn_decode
+
+            def token_attn(t):
+                src = xp0 + (t % T) * H * 4
+                for l in range(Lyr):
+                    kcp, vcp, wsp, wsb = a_ptr[l]
+                    rc = attn_call(C.byref(a_sh), C.byref(a_w[l]), kcp, vcp, pos_a, src, a_mid.data_ptr(), wsp, wsb,
+                                   sp)
+                    if rc:
+                        raise api.MoeError(rc, "moe_attn_decode", api.moe_last_error())
+                    dst = hp[l & 1]
+                    rc = decode(handles[l], a_mid.data_ptr(), None, 1, flags, dst, None, None, None, None,
+                                C.byref(st_a[l]), sp)
+                    if rc:
+                        raise api.MoeError(rc, "moe_layer_decode", api.moe_last_error())
+                    src = dst
+            n_at = max(args.steps // 4, 16)
+            for t in range(16):
+                token_attn(t)
+            torch.cuda.synchronize()
+            w_a = [(s_.hits, s_.misses) for s_ in st_a]
+            t0 = time.perf_counter()
+            for t in range(16, 16 + n_at):
+                token_attn(t)
+            torch.cuda.synchronize()
+            el_a = time.perf_counter() - t0
+            h_a = sum(s_.hits - w_[0] for s_, w_ in zip(st_a, w_a))
+            m_a = sum(s_.misses - w_[1] for s_, w_ in zip(st_a, w_a))
+            attn_detail["decoder_layers_with_lfu16_moe"] = {"tokens_per_s": n_at / el_a, "tokens": n_at,
+                                                           "hit_rate": h_a / max(h_a + m_a, 1)}
+            detail["attention_step"] = attn_detail
+            print(f"[bench] attention step: {attn_detail}", file=sys.stderr, flush=True)
+
         for h in res:
             api.moe_layer_destroy(h)
 

@@ -183,8 +183,8 @@ def moe_attn_workspace_bytes(a) -> int:
 def moe_attn_decode(a, w, k_cache, v_cache, pos, x, y, workspace, stream=None):
     """One token at position pos through the attention step. w: mapping with
     device tensors norm_w, qkv_q, qkv_s, o_q, o_s; caches fp16 (as int16)
-    [n_kv_heads][max_ctx][d]; x, y fp32 [H]; workspace a zero-filled uint8
-    tensor of at least moe_attn_workspace_bytes bytes."""
+    [n_kv_heads][max_ctx][d]; x, y fp32 [H]; workspace a uint8 tensor of at
+    least moe_attn_workspace_bytes bytes."""
     s = make_attn_shape(a)
     W = L.moe_attn_weights(_p(w["norm_w"]), _p(w["qkv_q"]), _p(w["qkv_s"]), _p(w["o_q"]), _p(w["o_s"]))
     nbytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0

@@ -17,11 +17,17 @@
 //     writes q (fp32) and appends k and v to the cache (fp16, nearest even).
 //  2. k_attn_split: block (split, kv head) streams the K and V rows of its
 //     positions once for all query heads of the group: scores, a softmax over
-//     the split, the value sum; the last block of a group (arrival counter)
-//     combines the splits' partial sums in a fixed order.
-//  3. k_attn_gemv<kOut>: output projection of the attention output (quantised
-//     per group of 32 in LDS) plus the residual.
+//     the split, the value sum. With one split it writes the attention output
+//     as digit planes per group of 32; with more, its partial results, and
+//  2b. k_attn_combine merges them in split order (a last-block combine inside
+//     k_attn_split, behind an arrival counter, measured 7 us slower at 4096
+//     positions: its store drain, counter round trip and L2-bypassing loads
+//     are serial).
+//  3. k_attn_gemv<kOut>: output projection of those digit planes (each lane
+//     loads its column's group next to its weights) plus the residual.
 #include <hip/hip_fp16.h>
+
+#include <cmath>
 
 #include "launch.h"
 
@@ -30,8 +36,8 @@ namespace {
 
 constexpr int kAThreads = 1024;
 constexpr int kAWaves = kAThreads / kWave;
-constexpr int kSplitThreads = 256;
-constexpr int kSplitSteps = 8;  // position steps per split block
+constexpr int kSplitThreads = 512;
+constexpr int kSplitSteps = 4;  // position steps per split block
 
 enum { kQkv = 0, kOut = 1 };
 
@@ -46,8 +52,9 @@ __device__ __forceinline__ float h_hi(uint32_t w) {
   return __half2float(__ushort_as_half(static_cast<uint16_t>(w >> 16)));
 }
 
-// GEMV y = W x over rows of an int4 g32 matrix with K = 32 * ng columns, input
-// quantised per group into LDS digit planes. Lane (r0, c) = (tid / ng, tid % ng)
+// GEMV y = W x over rows of an int4 g32 matrix with K = 32 * ng columns, the
+// input as digit planes per group of 32 (kQkv: the normed input, quantised by
+// every block into LDS; kOut: read from global memory). Lane (r0, c) = (tid / ng, tid % ng)
 // owns chunk column c of local rows r0, r0 + R, ... (R = 1024 / ng); the block
 // owns RB local rows.
 template <int MODE, int NT>
@@ -97,6 +104,14 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  DigitGroup xc;
+  float xsc;
+  if (MODE == kOut) {
+    xc = A.adig[c];
+    xsc = A.asc[c];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   float inv = 1.0f;
   if (MODE == kQkv) {
     // RMSNorm factor of x (a fixed-order block sum), then h = x * w * factor
@@ -114,16 +129,18 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
     for (int w = 0; w < kAWaves; ++w) tot += red[w];
     inv = 1.0f / sqrtf(tot / static_cast<float>(A.K) + A.eps);
   }
-  // digit planes of the input, two groups per wave pass
-  for (int g0 = 2 * wave; g0 < ng; g0 += 2 * kAWaves) {
-    const int g = g0 + (lane >> 5);
-    const int gi = g < ng ? g : ng - 1;
-    const float v = MODE == kQkv ? xw[kGroup * gi + (lane & 31)] * inv : A.a[kGroup * gi + (lane & 31)];
-    quant_pair_of_groups(g < ng ? v : 0.f, g0, ng, xd, xs);
+  if (MODE == kQkv) {
+    // digit planes of the normed input, two groups per wave pass
+    for (int g0 = 2 * wave; g0 < ng; g0 += 2 * kAWaves) {
+      const int g = g0 + (lane >> 5);
+      const int gi = g < ng ? g : ng - 1;
+      const float v = xw[kGroup * gi + (lane & 31)] * inv;
+      quant_pair_of_groups(g < ng ? v : 0.f, g0, ng, xd, xs);
+    }
+    __syncthreads();
+    xc = xd[c];
+    xsc = xs[c];
   }
-  __syncthreads();
-  const DigitGroup xc = xd[c];
-  const float xsc = xs[c];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int r = r0 + R * t;
@@ -149,11 +166,14 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
       const int hh = p / (d / 2), i = p % (d / 2);
       float v0 = rowsum[tid], v1 = rowsum[tid + half];
       if (hh < A.nh + A.nkv) {
-        // angle pos * theta^(-2i/d), in fp64, then the rotation in fp32
-        const double ang = static_cast<double>(A.pos) * pow(A.theta, -2.0 * i / d);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        const float cf = static_cast<float>(cs), sf = static_cast<float>(sn);
+        // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
+        // (|angle| < 2^14, so the reduction loses nothing), then sin and cos
+        // of the reduced angle and the rotation in fp32
+        const double ang = static_cast<double>(A.pos) * exp2(-2.0 * i / d * A.log2_theta);
+        const double twopi = 6.283185307179586476925286766559;
+        const float r = static_cast<float>(ang - twopi * rint(ang / twopi));
+        float sf, cf;
+        sincosf(r, &sf, &cf);
         const float r0v = v0 * cf - v1 * sf;
         const float r1v = v1 * cf + v0 * sf;
         v0 = r0v;
@@ -180,50 +200,67 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
 }
 
 // One split of the context for one key/value head and its G query heads. A
-// position's d values are spread over LP = d / 16 lanes (16 each, two 16-byte
-// loads of K and two of V); a step covers 256 / LP positions, a split
-// kSplitSteps steps. Every K and V load of the block is issued before any is
-// used.
+// position's d values are spread over LP = d / 16 lanes: lane j of a position
+// takes elements [8j, 8j + 8) and [d/2 + 8j, d/2 + 8j + 8), so each of its two
+// 16-byte loads of a K (or V) row makes, with the other LP - 1 lanes, one
+// contiguous half row. A step covers 256 / LP positions, a split kSplitSteps
+// steps. Every K and V load of the block is issued before any is used. The
+// attention output is written as digit planes per group of 32 (the input
+// format of the output projection).
 template <int D, int G>
-__global__ __launch_bounds__(kSplitThreads, 1) void k_attn_split(AttnSplitArgs A) {
+__global__ __launch_bounds__(kSplitThreads) void k_attn_split(AttnSplitArgs A) {
   constexpr int LP = D / 16;
   constexpr int PPS = kSplitThreads / LP;
   constexpr int P = kSplitSteps * PPS;
   __shared__ float sc[G][P];
   __shared__ float red[kSplitThreads / kWave][G][D];
   __shared__ float mh[G], lh[G];
-  __shared__ int is_last;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int g = blockIdx.y, sp = blockIdx.x;
-  const int slot = tid / LP, e0 = (tid % LP) * 16;
+  const int slot = tid / LP, e0 = (tid % LP) * 8;  // elements [e0, e0 + 8) and [D/2 + e0, D/2 + e0 + 8)
   const int n = A.n, lo = sp * P;
 
-  uint4 kr[kSplitSteps][2], vr[kSplitSteps][2];
+  // loads in the order of use (q, every K row, every V row): loads retire in
+  // order, so the scores of step s wait only for K row s while the later rows
+  // and all V rows are still in flight
+  float4 qraw[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float* qh = A.q + static_cast<size_t>(g * G + h) * D + e0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qraw[h][j] = *reinterpret_cast<const float4*>(qh + (j < 2 ? 4 * j : D / 2 + 4 * (j - 2)));
+  }
+  size_t base[kSplitSteps];
 #pragma unroll
   for (int s = 0; s < kSplitSteps; ++s) {
     int t = lo + s * PPS + slot;
     t = t < n ? t : n - 1;  // clamped: loaded, masked below
-    const size_t base = (static_cast<size_t>(g) * A.max_ctx + t) * D + e0;
-    kr[s][0] = *reinterpret_cast<const uint4*>(A.kc + base);
-    kr[s][1] = *reinterpret_cast<const uint4*>(A.kc + base + 8);
-    vr[s][0] = *reinterpret_cast<const uint4*>(A.vc + base);
-    vr[s][1] = *reinterpret_cast<const uint4*>(A.vc + base + 8);
+    base[s] = (static_cast<size_t>(g) * A.max_ctx + t) * D + e0;
   }
+  uint4 kr[kSplitSteps][2], vr[kSplitSteps][2];
+#pragma unroll
+  for (int s = 0; s < kSplitSteps; ++s) {
+    kr[s][0] = *reinterpret_cast<const uint4*>(A.kc + base[s]);
+    kr[s][1] = *reinterpret_cast<const uint4*>(A.kc + base[s] + D / 2);
+  }
+#pragma unroll
+  for (int s = 0; s < kSplitSteps; ++s) {
+    vr[s][0] = *reinterpret_cast<const uint4*>(A.vc + base[s]);
+    vr[s][1] = *reinterpret_cast<const uint4*>(A.vc + base[s] + D / 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float qv[G][16];
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float4* qp = reinterpret_cast<const float4*>(A.q + static_cast<size_t>(g * G + h) * D + e0);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 v = qp[j];
-      qv[h][4 * j] = v.x * scale;
-      qv[h][4 * j + 1] = v.y * scale;
-      qv[h][4 * j + 2] = v.z * scale;
-      qv[h][4 * j + 3] = v.w * scale;
+      qv[h][4 * j] = qraw[h][j].x * scale;
+      qv[h][4 * j + 1] = qraw[h][j].y * scale;
+      qv[h][4 * j + 2] = qraw[h][j].z * scale;
+      qv[h][4 * j + 3] = qraw[h][j].w * scale;
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
 
   // scores q . k / sqrt(d): 16 products per lane, then a sum over the LP lanes
 #pragma unroll
@@ -303,10 +340,12 @@ __global__ __launch_bounds__(kSplitThreads, 1) void k_attn_split(AttnSplitArgs A
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave][h][e0 + e] = acc[h][e];
+      for (int e = 0; e < 16; ++e) red[wave][h][(e < 8 ? 0 : D / 2 - 8) + e0 + e] = acc[h][e];
   }
   __syncthreads();
   const int nsplit = gridDim.x;
+  // G * D is a multiple of 64, so every wave of the loop is whole (the
+  // digit-plane writer needs all 64 lanes)
   for (int idx = tid; idx < G * D; idx += kSplitThreads) {
     const int h = idx / D, e = idx % D;
     float o = 0.f;
@@ -314,63 +353,71 @@ __global__ __launch_bounds__(kSplitThreads, 1) void k_attn_split(AttnSplitArgs A
     for (int w = 0; w < kSplitThreads / kWave; ++w) o += red[w][h][e];
     const int qh = g * G + h;
     if (nsplit == 1) {
-      A.out[static_cast<size_t>(qh) * D + e] = o / lh[h];
+      const int g0 = (g * G * D + idx - lane) / kGroup;
+      quant_pair_of_groups(o / lh[h], g0, g0 + 2, A.adig, A.asc);
     } else {
-      __hip_atomic_store(A.po + (static_cast<size_t>(qh) * nsplit + sp) * D + e, o, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      // read by the combine kernel, after the kernel boundary
+      A.po[(static_cast<size_t>(qh) * nsplit + sp) * D + e] = o;
       if (e == 0) {
-        __hip_atomic_store(A.pm + static_cast<size_t>(qh) * nsplit + sp, mh[h], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(A.pl + static_cast<size_t>(qh) * nsplit + sp, lh[h], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        A.pm[static_cast<size_t>(qh) * nsplit + sp] = mh[h];
+        A.pl[static_cast<size_t>(qh) * nsplit + sp] = lh[h];
       }
     }
   }
-  if (nsplit == 1) return;
-  // every partial store of this block has completed before it arrives
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = old == nsplit - 1;
-    if (is_last) __hip_atomic_store(A.cnt + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Combine of the splits (more than one): block h takes query head h, thread
+// e its element e. The block stages the splits' maxima and sums in LDS while
+// every thread's value loads (up to 32 splits per batch) are already in
+// flight; wave 0 forms M = max m_s, the weights exp(m_s - M) and
+// L = sum of weight * l_s; each thread then sums weight * o_s in split order.
+// Writes digit planes per group of 32.
+__global__ __launch_bounds__(256) void k_attn_combine(AttnSplitArgs A, int nsplit) {
+  extern __shared__ float cmb[];  // [2][nsplit]: maxima -> weights, sums
+  __shared__ float Lsh;
+  const int D = blockDim.x;
+  const int h = blockIdx.x, e = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float* po = A.po + static_cast<size_t>(h) * nsplit * D + e;
+  float* wm = cmb;
+  float* wl = cmb + nsplit;
+  constexpr int B = 32;
+  float ov[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) ov[j] = po[static_cast<size_t>(j < nsplit ? j : nsplit - 1) * D];
+  for (int s = e; s < nsplit; s += D) {
+    wm[s] = A.pm[static_cast<size_t>(h) * nsplit + s];
+    wl[s] = A.pl[static_cast<size_t>(h) * nsplit + s];
   }
   __syncthreads();
-  if (!is_last) return;
-  // combine the splits of the group's heads: weights exp(m_s - M), fixed order
-  float* wsp = &sc[0][0];  // [G][nsplit] split weights (nsplit <= P)
-  for (int idx = tid; idx < G * nsplit; idx += kSplitThreads) {
-    const int h = idx / nsplit;
-    wsp[idx] = __hip_atomic_load(A.pm + static_cast<size_t>(g * G + h) * nsplit + idx % nsplit,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (wave < G) {
-    const int h = wave;
+  if (threadIdx.x < kWave) {
     float m = -INFINITY;
-    for (int s = lane; s < nsplit; s += kWave) m = fmaxf(m, wsp[h * nsplit + s]);
+    for (int s = lane; s < nsplit; s += kWave) m = fmaxf(m, wm[s]);
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     float l = 0.f;
     for (int s = lane; s < nsplit; s += kWave) {
-      const float wv = expf(wsp[h * nsplit + s] - m);
-      wsp[h * nsplit + s] = wv;
-      l = fmaf(wv, __hip_atomic_load(A.pl + static_cast<size_t>(g * G + h) * nsplit + s, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT), l);
+      const float w = expf(wm[s] - m);
+      wm[s] = w;
+      l = fmaf(w, wl[s], l);
     }
     l = wave_sum(l);
-    if (lane == 0) lh[h] = l;
+    if (lane == 0) Lsh = l;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += kSplitThreads) {
-    const int h = idx / D, e = idx % D;
-    const size_t qh = static_cast<size_t>(g * G + h);
-    float o = 0.f;
-    for (int s = 0; s < nsplit; ++s)
-      o = fmaf(wsp[h * nsplit + s],
-               __hip_atomic_load(A.po + (qh * nsplit + s) * D + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), o);
-    A.out[qh * D + e] = o / lh[h];
+  float O = 0.f;
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+    if (j < nsplit) O = fmaf(wm[j], ov[j], O);
+  for (int s0 = B; s0 < nsplit; s0 += B) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) ov[j] = po[static_cast<size_t>(s0 + j < nsplit ? s0 + j : nsplit - 1) * D];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (s0 + j < nsplit) O = fmaf(wm[s0 + j], ov[j], O);
   }
+  const int g0 = (h * D + e - lane) / kGroup;
+  quant_pair_of_groups(O / Lsh, g0, g0 + 2, A.adig, A.asc);
 }
 
 // rows per block of the projection: pairs of one head (a power of two that
@@ -386,10 +433,10 @@ int qkv_rows_per_block(int K, int rows, int d) {
   return RB;
 }
 
-size_t gemv_lds(int K, int RB, bool with_x) {
+size_t gemv_lds(int K, int RB, bool staged_input) {
   const int ng = K / kGroup;
-  return static_cast<size_t>(RB) * ng * sizeof(float) + ng * sizeof(DigitGroup) + ng * sizeof(float) +
-         (with_x ? static_cast<size_t>(K) * sizeof(float) : 0);
+  return static_cast<size_t>(RB) * ng * sizeof(float) +
+         (staged_input ? ng * sizeof(DigitGroup) + ng * sizeof(float) + static_cast<size_t>(K) * sizeof(float) : 0);
 }
 
 hipError_t launch_gemv(int mode, const AttnGemvArgs& A, int blocks, hipStream_t s) {
@@ -439,11 +486,11 @@ AttnWorkspace attn_workspace(int nh, int d, int max_ctx) {
     return o;
   };
   w.q = take(static_cast<size_t>(nh) * d * sizeof(float));
-  w.out = take(static_cast<size_t>(nh) * d * sizeof(float));
+  w.adig = take(static_cast<size_t>(nh) * d / kGroup * sizeof(DigitGroup));
+  w.asc = take(static_cast<size_t>(nh) * d / kGroup * sizeof(float));
   w.pm = take(static_cast<size_t>(nh) * max_split * sizeof(float));
   w.pl = take(static_cast<size_t>(nh) * max_split * sizeof(float));
   w.po = take(static_cast<size_t>(nh) * max_split * d * sizeof(float));
-  w.cnt = take(static_cast<size_t>(nh) * sizeof(int));
   w.total = off;
   w.max_split = max_split;
   return w;
@@ -454,7 +501,8 @@ hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
   const AttnWorkspace W = attn_workspace(nh, d, L.max_ctx);
   uint8_t* ws = static_cast<uint8_t*>(L.workspace);
   float* q = reinterpret_cast<float*>(ws + W.q);
-  float* out = reinterpret_cast<float*>(ws + W.out);
+  DigitGroup* adig = reinterpret_cast<DigitGroup*>(ws + W.adig);
+  float* asc = reinterpret_cast<float*>(ws + W.asc);
 
   // 1. RMSNorm + q/k/v projection + RoPE + cache append
   AttnGemvArgs a{};
@@ -470,7 +518,7 @@ hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
   a.nh = nh;
   a.nkv = nkv;
   a.pos = L.pos;
-  a.theta = L.theta;
+  a.log2_theta = std::log2(L.theta);
   a.max_ctx = L.max_ctx;
   a.q = q;
   a.kc = L.kc;
@@ -488,8 +536,8 @@ hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
   b.pm = reinterpret_cast<float*>(ws + W.pm);
   b.pl = reinterpret_cast<float*>(ws + W.pl);
   b.po = reinterpret_cast<float*>(ws + W.po);
-  b.out = out;
-  b.cnt = reinterpret_cast<int*>(ws + W.cnt);
+  b.adig = adig;
+  b.asc = asc;
   const int P = attn_split_positions(d);
   const dim3 grid((b.n + P - 1) / P, nkv);
   const int G = nh / nkv;
@@ -512,6 +560,12 @@ hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
 #undef MOE_AS
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (grid.x > 1) {
+    hipLaunchKernelGGL(k_attn_combine, dim3(nh), dim3(d), 2 * grid.x * sizeof(float), s, b,
+                       static_cast<int>(grid.x));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   // 3. output projection + residual
   AttnGemvArgs c{};
@@ -523,7 +577,8 @@ hipError_t launch_attn_decode(const AttnLaunch& L, hipStream_t s) {
   int nt = H / (Ro * 256);
   nt = nt < 1 ? 1 : (nt > 6 ? 6 : nt);
   c.RB = Ro * nt > 64 ? 64 : Ro * nt;
-  c.a = out;
+  c.adig = adig;
+  c.asc = asc;
   c.x = L.x;
   c.y = L.y;
   return launch_gemv(kOut, c, (H + c.RB - 1) / c.RB, s);

@@ -186,10 +186,11 @@ struct AttnGemvArgs {
   const float* x;      // projection input (RMSNorm in) or residual (output projection)
   const float* norm_w;
   float eps;
-  const float* a;      // output projection input [K]
+  const DigitGroup* adig;  // output projection input [K / 32] as digit planes
+  const float* asc;        // and their scales
   float* y;            // output projection: y = x + W a
   int d, nh, nkv, pos, max_ctx;
-  double theta;
+  double log2_theta;
   float* q;            // rotated queries [nh][d]
   uint16_t* kc;        // fp16 caches [nkv][max_ctx][d]
   uint16_t* vc;
@@ -203,12 +204,12 @@ struct AttnSplitArgs {
   float* pm;           // per-split max [nh][nsplit]
   float* pl;           // per-split sum of exponentials
   float* po;           // per-split unnormalised value sums [nh][nsplit][d]
-  float* out;          // attention output [nh][d]
-  int* cnt;            // arrival counters per key/value head (zero between calls)
+  DigitGroup* adig;    // attention output [nh * d / 32] as digit planes
+  float* asc;
 };
 
 struct AttnWorkspace {
-  size_t q, out, pm, pl, po, cnt, total;
+  size_t q, adig, asc, pm, pl, po, total;
   int max_split;
 };
 

@@ -355,16 +355,16 @@ typedef struct moe_attn_weights {
 } moe_attn_weights;
 
 /* Workspace of moe_attn_decode for this shape (queries, per-split partial
- * results, arrival counters). MOE_ESHAPE for unsupported shapes. */
+ * results, the attention output). MOE_ESHAPE for unsupported shapes. */
 moe_status moe_attn_workspace_bytes(const moe_attn_shape* sh, size_t* out);
 /* One token at position pos (0 <= pos < max_ctx) through the attention step,
  * asynchronous on stream. k_cache / v_cache: dev fp16 [n_kv_heads][max_ctx][d],
  * 16-byte aligned, owned by the caller; positions < pos hold the earlier
  * tokens, the call writes position pos and reads [0, pos]. x, y: dev fp32 [H]
  * (y may be x). workspace: dev, 16-byte aligned, at least
- * moe_attn_workspace_bytes, zero-filled before its first use (the call leaves
- * its counters at zero again); calls that share a workspace must be ordered
- * on one stream. Checks every argument before enqueueing anything. */
+ * moe_attn_workspace_bytes (scratch, no contents kept between calls); calls
+ * that share a workspace must be ordered on one stream. Checks every argument
+ * before enqueueing anything. */
 moe_status moe_attn_decode(const moe_attn_shape* sh, const moe_attn_weights* W, uint16_t* k_cache,
                            uint16_t* v_cache, int32_t pos, const float* x, float* y, void* workspace,
                            size_t workspace_bytes, void* stream);

@@ -18,6 +18,8 @@ pytestmark = pytest.mark.gpu
 # d = 128 with 4 query heads per group; d = 64 with one (plain multi-head)
 WIDE_GROUP = AttnShape(hidden=1024, n_heads=8, n_kv_heads=2, head_dim=128, max_ctx=1024)
 MHA = AttnShape(hidden=256, n_heads=2, n_kv_heads=2, head_dim=64, max_ctx=2048)
+# one query head of width 64: a combine grid of one partly used block
+ONE_HEAD = AttnShape(hidden=128, n_heads=1, n_kv_heads=1, head_dim=64, max_ctx=1100)
 
 
 class Step:
@@ -76,7 +78,8 @@ def test_gemma_shape_splits(pos):
     check(st, pos, pos)
 
 
-@pytest.mark.parametrize("a,pos", [(WIDE_GROUP, 300), (WIDE_GROUP, 1023), (MHA, 1500), (MHA, 3)])
+@pytest.mark.parametrize("a,pos", [(WIDE_GROUP, 300), (WIDE_GROUP, 1023), (MHA, 1500), (MHA, 3),
+                                   (ONE_HEAD, 1099), (ONE_HEAD, 600)])
 def test_group_sizes_and_widths(a, pos):
     st = Step(a, filled=pos)
     check(st, pos, pos)
