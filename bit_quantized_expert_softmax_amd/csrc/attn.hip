@@ -10,9 +10,9 @@
 // in FP16.
 //
 // Three launches:
-//  1. k_attn_gemv<kQkv>: every block computes the RMSNorm factor, quantises
-//     the normed input into digit planes (LDS) and takes its rows of the int4
-//     projection with v_dot8 (as the expert GEMVs). A block's rows are pairs
+//  1. k_attn_gemv<kQkv>: every block quantises x * w into digit planes (LDS),
+//     takes its rows of the int4 projection with v_dot8 (as the expert GEMVs)
+//     and scales the row sums by the RMSNorm factor. A block's rows are pairs
 //     (i, i + d/2) of one head, so its epilogue applies RoPE to q and k itself,
 //     writes q (fp32) and appends k and v to the cache (fp16, nearest even).
 //  2. k_attn_split: block (split, kv head) streams the K and V rows of its
@@ -40,6 +40,9 @@ constexpr int kSplitThreads = 512;
 constexpr int kSplitSteps = 4;  // position steps per split block
 
 enum { kQkv = 0, kOut = 1 };
+// passes of two groups per wave that cover the largest input (K = 4096:
+// 128 groups over 16 waves)
+constexpr int kMaxPairPasses = 4;
 
 __device__ __forceinline__ uint16_t f2h_bits(float v) {
   return __half_as_ushort(__float2half_rn(v));
@@ -67,7 +70,6 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
   float* part = reinterpret_cast<float*>(lds_raw);                                // [RB][ng]
   DigitGroup* xd = reinterpret_cast<DigitGroup*>(part + static_cast<size_t>(RB) * ng);  // [ng]
   float* xs = reinterpret_cast<float*>(xd + ng);                                   // [ng]
-  float* xw = xs + ng;                                                             // [K] (kQkv)
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid & (kWave - 1);
   const int R = kAThreads / ng;
@@ -114,32 +116,37 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
 
   float inv = 1.0f;
   if (MODE == kQkv) {
-    // RMSNorm factor of x (a fixed-order block sum), then h = x * w * factor
+    // The projection is linear, so the RMSNorm factor multiplies the row sums
+    // at the end: the digit planes are those of x * w (two groups per wave
+    // pass, every pass's loads issued first), and the sum of squares of x is
+    // reduced alongside, in a fixed order.
+    float xv[kMaxPairPasses], wv_n[kMaxPairPasses];
+#pragma unroll
+    for (int j = 0; j < kMaxPairPasses; ++j) {
+      const int g = 2 * (wave + kAWaves * j) + (lane >> 5);
+      const int i = kGroup * (g < ng ? g : ng - 1) + (lane & 31);
+      xv[j] = A.x[i];
+      wv_n[j] = A.norm_w[i];
+    }
     float ss = 0.f;
-    for (int i = tid; i < A.K; i += kAThreads) {
-      const float v = A.x[i];
-      ss = fmaf(v, v, ss);
-      xw[i] = v * A.norm_w[i];
+#pragma unroll
+    for (int j = 0; j < kMaxPairPasses; ++j) {
+      const int g0 = 2 * (wave + kAWaves * j);
+      if (g0 < ng) {  // uniform over the wave
+        const bool on = g0 + (lane >> 5) < ng;
+        ss = on ? fmaf(xv[j], xv[j], ss) : ss;
+        quant_pair_of_groups(on ? xv[j] * wv_n[j] : 0.f, g0, ng, xd, xs);
+      }
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wave] = ss;
     __syncthreads();
+    xc = xd[c];
+    xsc = xs[c];
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < kAWaves; ++w) tot += red[w];
     inv = 1.0f / sqrtf(tot / static_cast<float>(A.K) + A.eps);
-  }
-  if (MODE == kQkv) {
-    // digit planes of the normed input, two groups per wave pass
-    for (int g0 = 2 * wave; g0 < ng; g0 += 2 * kAWaves) {
-      const int g = g0 + (lane >> 5);
-      const int gi = g < ng ? g : ng - 1;
-      const float v = xw[kGroup * gi + (lane & 31)] * inv;
-      quant_pair_of_groups(g < ng ? v : 0.f, g0, ng, xd, xs);
-    }
-    __syncthreads();
-    xc = xd[c];
-    xsc = xs[c];
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
     if (tid < half) {
       const int p = blockIdx.x * half + tid;
       const int hh = p / (d / 2), i = p % (d / 2);
-      float v0 = rowsum[tid], v1 = rowsum[tid + half];
+      float v0 = rowsum[tid] * inv, v1 = rowsum[tid + half] * inv;
       if (hh < A.nh + A.nkv) {
         // angle pos * theta^(-2i/d) and its reduction to [-pi, pi] in fp64
         // (|angle| < 2^14, so the reduction loses nothing), then sin and cos
@@ -435,8 +442,7 @@ int qkv_rows_per_block(int K, int rows, int d) {
 
 size_t gemv_lds(int K, int RB, bool staged_input) {
   const int ng = K / kGroup;
-  return static_cast<size_t>(RB) * ng * sizeof(float) +
-         (staged_input ? ng * sizeof(DigitGroup) + ng * sizeof(float) + static_cast<size_t>(K) * sizeof(float) : 0);
+  return static_cast<size_t>(RB) * ng * sizeof(float) + (staged_input ? ng * (sizeof(DigitGroup) + sizeof(float)) : 0);
 }
 
 hipError_t launch_gemv(int mode, const AttnGemvArgs& A, int blocks, hipStream_t s) {
