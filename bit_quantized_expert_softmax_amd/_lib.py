@@ -44,7 +44,8 @@ class moe_layer_desc(C.Structure):
     _fields_ = [("router", vp), ("bias", vp), ("shared_blob", vp), ("experts_dev", vp),
                 ("experts_host", vp), ("slot_pool", vp), ("n_slots", C.c_int32),
                 ("copy_stream", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t),
-                ("store", vp), ("store_layer", C.c_int32), ("cache_policy", C.c_int32)]
+                ("store", vp), ("store_layer", C.c_int32), ("cache_policy", C.c_int32),
+                ("cache_on_device", C.c_int32)]
 
 
 class moe_decode_stats(C.Structure):
@@ -86,6 +87,7 @@ SIGNATURES = {
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
+    "moe_layer_cache_state": (c_status, [vp, vp, vp, vp, C.c_int32, vp, vp, vp, vp]),
     "moe_attn_workspace_bytes": (c_status, [P(moe_attn_shape), P(C.c_size_t)]),
     "moe_attn_decode": (c_status, [P(moe_attn_shape), P(moe_attn_weights), vp, vp, C.c_int32, vp, vp, vp,
                                    C.c_size_t, vp]),

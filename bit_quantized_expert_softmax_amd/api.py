@@ -203,13 +203,13 @@ def moe_layer_workspace_bytes(sh, max_B: int, max_T: int = 0) -> int:
 
 def moe_layer_create(sh, *, router, shared_blob, workspace, bias=None, experts_dev=None,
                      experts_host=None, slot_pool=None, n_slots=0, copy_stream=None, max_B=1,
-                     max_T=0, store=None, store_layer=0, cache_policy=0) -> int:
+                     max_T=0, store=None, store_layer=0, cache_policy=0, cache_on_device=False) -> int:
     s = make_shape(sh)
     d = L.moe_layer_desc(_p(router), _p(bias), _p(shared_blob), _p(experts_dev), _p(experts_host),
                          _p(slot_pool), n_slots,
                          None if copy_stream is None else _stream(copy_stream),
                          _p(workspace), workspace.numel() * workspace.element_size(), store, store_layer,
-                         cache_policy)
+                         cache_policy, 1 if cache_on_device else 0)
     h = C.c_void_p()
     _check(lib().moe_layer_create(C.byref(s), C.byref(d), max_B, max_T, C.byref(h)), "moe_layer_create")
     return h.value
@@ -225,6 +225,18 @@ def moe_layer_set_experts(h, experts_dev) -> None:
 
 def moe_layer_cache(h):
     return lib().moe_layer_cache(h)
+
+
+def moe_layer_cache_state(h, n_slots, stream=None):
+    """(expert, freq, last, hits, misses, steps) of the handle's slot cache."""
+    ex = np.zeros(n_slots, np.int32)
+    fr = np.zeros(n_slots, np.int32)
+    la = np.zeros(n_slots, np.int64)
+    hits, misses, steps = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(lib().moe_layer_cache_state(h, ex.ctypes.data, fr.ctypes.data, la.ctypes.data, n_slots,
+                                       C.byref(hits), C.byref(misses), C.byref(steps), _stream(stream)),
+           "moe_layer_cache_state")
+    return ex, fr, la, hits.value, misses.value, steps.value
 
 
 def moe_layer_decode(h, x, add_in, B, flags, y, ids_out=None, w_out=None, u_out=None,

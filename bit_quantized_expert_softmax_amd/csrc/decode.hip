@@ -56,8 +56,17 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
     const size_t per = (n16 + F.blocks_per_blob - 1) / F.blocks_per_blob;
     const size_t lo = (blockIdx.x % F.blocks_per_blob) * per;
     const size_t hi = lo + per < n16 ? lo + per : n16;
-    const uint4* __restrict__ src = reinterpret_cast<const uint4*>(F.src[m]);
-    uint4* __restrict__ dst = reinterpret_cast<uint4*>(F.dst[m]);
+    const uint4* __restrict__ src;
+    uint4* __restrict__ dst;
+    if (F.dlist) {
+      // miss list from the device-side cache step: blobs past its count leave
+      if (m >= F.dlist[0]) return;
+      src = reinterpret_cast<const uint4*>(F.src_base + static_cast<size_t>(F.dlist[1 + m]) * F.bytes);
+      dst = reinterpret_cast<uint4*>(F.dst_base + static_cast<size_t>(F.dlist[1 + F.n + m]) * F.bytes);
+    } else {
+      src = reinterpret_cast<const uint4*>(F.src[m]);
+      dst = reinterpret_cast<uint4*>(F.dst[m]);
+    }
     constexpr int U = 4;
     for (size_t i0 = lo; i0 < hi; i0 += static_cast<size_t>(kThreads) * U) {
       uint4 v[U];

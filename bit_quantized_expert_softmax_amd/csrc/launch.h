@@ -28,6 +28,8 @@ __host__ __device__ inline BlobOffsets blob_offsets(size_t H, size_t I) {
   return o;
 }
 
+struct DevCache;  // device-stepped expert-slot cache (below)
+
 // ---------------------------------------------------------------- routing
 // Layer router, one launch: x' = x (+ add_in); u = x' or rmsnorm(x'); u's
 // digit planes; fp64 logits (+ bias); top-k + softmax by the last block to
@@ -43,7 +45,8 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s);
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s,
+                              const DevCache* dcache = nullptr);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
@@ -77,13 +80,39 @@ struct SourceSet {
 };
 
 // Misses to copy host -> slot by fill blocks (cache mode, fill-kernel option).
+// With dlist, the list is in device memory (written by the device-side cache
+// step): dlist[0] misses, experts dlist[1 .. k], slots dlist[1 + k .. 2k];
+// blob m is read at src_base + expert * bytes and written at dst_base +
+// slot * bytes, and n (= k) blobs' worth of fill blocks are launched, those
+// past the miss count leaving at once.
 struct FillList {
   const uint8_t* src[kMaxTopK];  // device-accessible pinned host blobs
   uint8_t* dst[kMaxTopK];        // slots in HBM
   int n;                         // number of blobs
   int blocks_per_blob;
   size_t bytes;                  // blob size, a multiple of 16
+  const int32_t* dlist;
+  const uint8_t* src_base;
+  uint8_t* dst_base;
 };
+
+// LFU (or LRU) expert-slot cache of one layer kept in device memory and
+// stepped by the router's last block, with the host cache's rule (lowest
+// empty slot, else the smallest (frequency, last use, slot), or (last use,
+// slot) for LRU, among slots holding none of the token's ids; hits first).
+struct DevCache {
+  int32_t* expert;    // [n_slots], -1 = empty
+  int32_t* freq;      // [n_slots]
+  int32_t* last;      // [n_slots], -1 = never
+  int32_t* where;     // [E] expert -> slot, -1 = absent
+  long long* counters;  // [3]: steps, hits, misses
+  int32_t* slot_of_rank;  // [k]
+  int32_t* miss;      // [1 + 2k], see FillList::dlist
+  int32_t* ev;        // [k][4]: expert, slot, hit, evicted
+  int n_slots, policy;
+};
+// LDS bytes the step needs beyond the router's own.
+size_t dcache_lds_bytes(int n_slots, int E);
 
 // Gate/up GEMVs with the GeGLU epilogue for routed ranks [0,k), or the ranks
 // src.rsel selects (do_routed), and/or the shared expert (do_shared). The activations a [k*I + I_s] leave

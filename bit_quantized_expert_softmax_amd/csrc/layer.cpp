@@ -37,10 +37,36 @@ namespace {
 
 struct WsLayout {
   size_t u, udig, usc, z, ids, w, adig, asc, cnt, pre;
+  // device-stepped slot cache: counters, per-slot and per-expert arrays, the
+  // call's slot per rank, miss list and events
+  size_t dc;
   // batched decode (max_B > 1): fp16 inputs and per-assignment outputs
   size_t out_r, out_s, u16, tsc, act;
   size_t total;
 };
+
+// [3] int64 counters, then int32: expert, freq, last [E] (n_slots <= E),
+// where [E], slot of rank [kMaxTopK], miss list [1 + 2 kMaxTopK], events
+// [kMaxTopK][4]
+size_t dcache_region_bytes(int E) {
+  return 32 + sizeof(int32_t) * (4 * static_cast<size_t>(E) + kMaxTopK + 1 + 2 * kMaxTopK + 4 * kMaxTopK);
+}
+
+DevCache dcache_at(uint8_t* base, int E, int n_slots, int policy) {
+  DevCache c{};
+  c.counters = reinterpret_cast<long long*>(base);
+  int32_t* p = reinterpret_cast<int32_t*>(base + 32);
+  c.expert = p;
+  c.freq = p + E;
+  c.last = p + 2 * E;
+  c.where = p + 3 * E;
+  c.slot_of_rank = p + 4 * E;
+  c.miss = c.slot_of_rank + kMaxTopK;
+  c.ev = c.miss + 1 + 2 * kMaxTopK;
+  c.n_slots = n_slots;
+  c.policy = policy;
+  return c;
+}
 
 WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   size_t off = 0;
@@ -62,6 +88,7 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.adig = take(B * npos * 16);
   L.asc = take(B * npos * 4);
   L.cnt = take(B * 4);  // router arrival counters, one per token
+  L.dc = take(dcache_region_bytes(static_cast<int>(E)));
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
@@ -87,6 +114,8 @@ struct moe_layer {
   moe_shape sh{};
   moe_layer_desc d{};
   bool cache_mode = false;
+  bool dcache = false;     // the slot cache is stepped on the device
+  moe::DevCache dc{};
   int max_B = 0, max_T = 0;
   moe_cache* cache = nullptr;
   moe_cache* cache_backup = nullptr;
@@ -260,6 +289,14 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
       return fail(MOE_ESHAPE, "%s: n_slots %d outside [top_k=%d, n_experts=%d]", fn, d->n_slots,
                   sh->top_k, sh->n_experts);
     if (!moe::aligned16(d->slot_pool)) return fail(MOE_EALIGN, "%s: slot_pool not 16-byte aligned", fn);
+    if (d->cache_on_device && d->store)
+      return fail(MOE_EINVAL, "%s: a device-stepped cache fills from experts_host, not from a store", fn);
+    if (d->cache_on_device &&
+        sizeof(double) * sh->n_experts + moe::dcache_lds_bytes(d->n_slots, sh->n_experts) > 65536)
+      return fail(MOE_ESHAPE, "%s: the device-stepped cache of %d slots and %d experts exceeds 64 KiB of LDS", fn,
+                  d->n_slots, sh->n_experts);
+  } else if (d->cache_on_device) {
+    return fail(MOE_EINVAL, "%s: cache_on_device needs a cache-mode handle", fn);
   } else if (!moe::aligned16(d->experts_dev)) {
     return fail(MOE_EALIGN, "%s: experts_dev not 16-byte aligned", fn);
   }
@@ -322,6 +359,21 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
                         hipHostMallocDefault);
       if (e != hipSuccess) return cleanup(MOE_EHIP, "pinned expert offsets", e);
     }
+    if (d->cache_on_device) {
+      // the fill blocks read the misses from experts_host through its device address
+      if (!L->host_dev) {
+        moe_layer_destroy(L);
+        return fail(MOE_EINVAL, "%s: cache_on_device needs experts_host in device-accessible pinned memory", fn);
+      }
+      const int E = sh->n_experts;
+      std::vector<uint8_t> init(moe::dcache_region_bytes(E), 0);
+      int32_t* p = reinterpret_cast<int32_t*>(init.data() + 32);
+      for (int i = 0; i < 4 * E; ++i) p[i] = (i < E || i >= 2 * E) ? -1 : 0;  // expert, last, where: -1
+      e = hipMemcpy(L->wsb + ws.dc, init.data(), init.size(), hipMemcpyHostToDevice);
+      if (e != hipSuccess) return cleanup(MOE_EHIP, "device cache state", e);
+      L->dcache = true;
+      L->dc = moe::dcache_at(L->wsb + ws.dc, E, d->n_slots, d->cache_policy);
+    }
     moe_status cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache);
     if (!cs) cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache_backup);
     if (cs) {
@@ -360,7 +412,40 @@ moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev) {
   return MOE_OK;
 }
 
-moe_cache* moe_layer_cache(moe_layer* L) { return L ? L->cache : nullptr; }
+moe_cache* moe_layer_cache(moe_layer* L) { return L && !L->dcache ? L->cache : nullptr; }
+
+moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, int64_t* last, int32_t n,
+                                 int64_t* hits, int64_t* misses, int64_t* steps, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_layer_cache_state";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (!L->cache_mode) return fail(MOE_ESTATE, "%s: resident handle has no slot cache", fn);
+  if ((expert || freq || last) && n != L->d.n_slots)
+    return fail(MOE_ESHAPE, "%s: n=%d but n_slots=%d", fn, n, L->d.n_slots);
+  if (!L->dcache) {
+    moe_status st = moe_cache_slots(L->cache, expert, freq, last, (expert || freq || last) ? n : L->d.n_slots);
+    if (st) return st;
+    return moe_cache_counters(L->cache, hits, misses, steps);
+  }
+  const int S = L->d.n_slots;
+  std::vector<int32_t> ex(S), fr(S), la(S);
+  long long cnt[3];
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(cnt, L->dc.counters, sizeof(cnt), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(ex.data(), L->dc.expert, sizeof(int32_t) * S, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(fr.data(), L->dc.freq, sizeof(int32_t) * S, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(la.data(), L->dc.last, sizeof(int32_t) * S, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  for (int s = 0; s < S; ++s) {
+    if (expert) expert[s] = ex[s];
+    if (freq) freq[s] = fr[s];
+    if (last) last[s] = la[s];
+  }
+  if (steps) *steps = cnt[0];
+  if (hits) *hits = cnt[1];
+  if (misses) *misses = cnt[2];
+  return MOE_OK;
+}
 
 moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in, int32_t B,
                             uint32_t flags, float* y, int32_t* ids_out, float* w_out, float* u_out,
@@ -416,9 +501,10 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
                                       in_kernel_topk ? nullptr : ids,
                                       in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
                                       in_kernel_topk ? nullptr : w_out,
-                                      L->cache_mode ? L->ids_host : nullptr,
-                                      L->cache_mode ? L->seq_host : nullptr, seq, s), fn);
-  if (L->cache_mode) L->seq = seq;
+                                      L->cache_mode && !L->dcache ? L->ids_host : nullptr,
+                                      L->cache_mode && !L->dcache ? L->seq_host : nullptr, seq, s,
+                                      L->dcache ? &L->dc : nullptr), fn);
+  if (L->cache_mode && !L->dcache) L->seq = seq;
   prof_end(L, 0, pb, s);
 
   moe::SourceSet S = make_sources(L);
@@ -469,6 +555,36 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   S.experts = L->d.slot_pool;
   S.ids = nullptr;
   auto* adg = reinterpret_cast<moe::DigitGroup*>(adig);
+  if (L->dcache) {
+    // the routing kernel has stepped the cache: the fill blocks take the miss
+    // list and the expert kernels each rank's slot from device memory
+    moe::FillList F{};
+    F.n = k;
+    F.blocks_per_blob = 16;
+    F.bytes = L->blob_e;
+    F.dlist = L->dc.miss;
+    F.src_base = L->host_dev;
+    F.dst_base = L->d.slot_pool;
+    const ProfPair p1 = prof_pair(L, 1);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F), fn);
+    prof_add(L, 1, p1);
+    S.ids = L->dc.slot_of_rank;
+    const ProfPair p2 = prof_pair(L, 2);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+    prof_add(L, 2, p2);
+    const ProfPair p3 = prof_pair(L, 3);
+    HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
+    prof_add(L, 3, p3);
+    if (trace) {
+      int32_t evd[4 * moe::kMaxTopK];
+      hipError_t te = hipMemcpyAsync(evd, L->dc.ev, sizeof(int32_t) * 4 * k, hipMemcpyDeviceToHost, s);
+      if (te == hipSuccess) te = hipStreamSynchronize(s);
+      if (te != hipSuccess) return fail(MOE_EHIP, "%s: reading the cache events: %s", fn, hipGetErrorString(te));
+      for (int j = 0; j < k; ++j) trace[j] = moe_cache_event{evd[4 * j], evd[4 * j + 1], evd[4 * j + 2], evd[4 * j + 3]};
+    }
+    if (stats) stats->calls += 1;
+    return MOE_OK;
+  }
   if (!fill_kernel) {
     // the shared-expert gate/up runs while the host waits for the ids and
     // while the copy engine fills the misses
@@ -685,6 +801,7 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
   moe::clear_error();
   const char* fn = "moe_layer_prefill";
   if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (L->dcache) return fail(MOE_ESTATE, "%s: the handle's slot cache is stepped on the device (decode only)", fn);
   if (T < 0 || T > L->max_T) return fail(MOE_ESHAPE, "%s: T=%d outside [0, max_T=%d]", fn, T, L->max_T);
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !y) return fail(MOE_EINVAL, "%s: x_bf16 and y are required", fn);

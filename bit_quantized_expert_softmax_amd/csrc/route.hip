@@ -18,6 +18,7 @@
 #include <math.h>
 
 #include "launch.h"
+#include "moedecode.h"
 #include "topk.h"
 
 namespace moe {
@@ -48,6 +49,10 @@ struct RouteArgs {
   int32_t* ids_host;
   int32_t* seq_host;
   int32_t seq;
+  // optional (top-k variant, B == 1): the layer's expert-slot cache is stepped
+  // on the device by the last block, right after the top-k
+  DevCache dc;
+  int use_dc;
 };
 
 // Per wave: one expert's router row and the whole token input x' are loaded
@@ -61,6 +66,121 @@ constexpr int kMaxSteps = 8;  // H <= 8 * 64 * 8 = 4096 in one batch
 // Top-k variant, after the block's logit stores (agent scope): the block
 // bumps its token's counter; the last of the token's gridDim.x blocks takes
 // the token's top-k (and publishes it to the host, B == 1). All threads call.
+// One step of the layer's expert-slot cache for the token's ids (sel_e, rank
+// order), by the whole block, on an LDS copy of the state: hits first (in
+// parallel, the ids are distinct), then the misses in rank order, each
+// taking the victim a wave finds by a (key, slot) minimum: empty slots key
+// on their index alone, so the lowest empty slot wins; the others (those
+// holding none of the token's ids) key on (frequency, last use) for LFU or
+// last use for LRU, ties to the lower slot. The same rule as the host cache.
+__device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, int32_t* lds) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int S = C.n_slots;
+  int32_t* lexp = lds;           // [S]
+  int32_t* lfreq = lexp + S;     // [S]
+  int32_t* llast = lfreq + S;    // [S]
+  int32_t* lwhere = llast + S;   // [E]
+  int32_t* lseen = lwhere + E;   // [E]
+  __shared__ int32_t hit[kMaxTopK], nm_sh, victim_sh;
+  for (int i = tid; i < S; i += kThreads) {
+    lexp[i] = C.expert[i];
+    lfreq[i] = C.freq[i];
+    llast[i] = C.last[i];
+  }
+  for (int e = tid; e < E; e += kThreads) {
+    lwhere[e] = C.where[e];
+    lseen[e] = 0;
+  }
+  const int32_t tick = static_cast<int32_t>(C.counters[0]);
+  __syncthreads();
+  if (tid < k) {
+    const int e = sel_e[tid];
+    lseen[e] = 1;
+    const int sl = lwhere[e];
+    hit[tid] = sl >= 0;
+    if (sl >= 0) {
+      lfreq[sl] += 1;
+      llast[sl] = tick;
+      C.slot_of_rank[tid] = sl;
+      int32_t* ev = C.ev + 4 * tid;
+      ev[0] = e;
+      ev[1] = sl;
+      ev[2] = 1;
+      ev[3] = -1;
+    }
+  }
+  if (tid == 0) nm_sh = 0;
+  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    if (hit[j]) continue;  // uniform: every thread reads the same LDS word
+    if (tid < kWave) {
+      unsigned long long best = ~0ull;
+      int bs = S;
+      for (int sl = lane; sl < S; sl += kWave) {
+        const int ex = lexp[sl];
+        unsigned long long key;
+        if (ex < 0) key = static_cast<unsigned long long>(sl);
+        else if (lseen[ex]) key = ~0ull;
+        else if (C.policy == MOE_POLICY_LRU) key = (1ull << 62) | static_cast<unsigned int>(llast[sl] + 1);
+        else
+          key = (1ull << 62) | (static_cast<unsigned long long>(lfreq[sl]) << 31) |
+                static_cast<unsigned int>(llast[sl] + 1);
+        if (key < best) {  // slots in increasing order: the first minimum stays
+          best = key;
+          bs = sl;
+        }
+      }
+#pragma unroll
+      for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const unsigned long long ob = static_cast<unsigned long long>(
+            __shfl_xor(static_cast<long long>(best), o, kWave));
+        const int os = __shfl_xor(bs, o, kWave);
+        if (ob < best || (ob == best && os < bs)) {
+          best = ob;
+          bs = os;
+        }
+      }
+      // a victim always exists (n_slots >= k, and fewer than k slots hold the
+      // token's ids while a miss is placed); the clamp only keeps every index
+      // inside the pool whatever the state
+      bs = bs < S ? bs : S - 1;
+      if (lane == 0) {
+        const int e = sel_e[j];
+        const int old = lexp[bs];
+        if (old >= 0) lwhere[old] = -1;
+        lexp[bs] = e;
+        lfreq[bs] = 1;
+        llast[bs] = tick;
+        lwhere[e] = bs;
+        C.slot_of_rank[j] = bs;
+        int32_t* ev = C.ev + 4 * j;
+        ev[0] = e;
+        ev[1] = bs;
+        ev[2] = 0;
+        ev[3] = old;
+        const int m = nm_sh;
+        C.miss[1 + m] = e;
+        C.miss[1 + k + m] = bs;
+        nm_sh = m + 1;
+      }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < S; i += kThreads) {
+    C.expert[i] = lexp[i];
+    C.freq[i] = lfreq[i];
+    C.last[i] = llast[i];
+  }
+  for (int e = tid; e < E; e += kThreads) C.where[e] = lwhere[e];
+  if (tid == 0) {
+    const int nm = nm_sh;
+    C.miss[0] = nm;
+    C.counters[0] += 1;
+    C.counters[1] += k - nm;
+    C.counters[2] += nm;
+  }
+}
+
 __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
   int& is_last = *is_last_p;
   const int nb = gridDim.x;
@@ -82,6 +202,7 @@ __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* s
   const size_t o = static_cast<size_t>(tok) * A.k;
   topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids + o, A.w + o, A.ids2 ? A.ids2 + o : nullptr,
              A.w2 ? A.w2 + o : nullptr);
+  if (A.use_dc) dcache_step(A.dc, sel_e, A.k, A.E, reinterpret_cast<int32_t*>(zs + A.E));
   if (A.seq_host && threadIdx.x == 0) {
     // one thread writes the ids and then publishes them: the release store
     // orders its own earlier stores before the sequence number
@@ -435,12 +556,15 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s) {
+                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s,
+                              const DevCache* dcache) {
   if (seq_host && (B != 1 || !ids)) return hipErrorInvalidValue;
+  if (dcache && (B != 1 || !ids || !udig)) return hipErrorInvalidValue;
   RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, u16, tsc, z, cnt,
-              ids, ids2, w, w2, ids_host, seq_host, seq};
+              ids, ids2, w, w2, ids_host, seq_host, seq, dcache ? *dcache : DevCache{}, dcache ? 1 : 0};
   const int blocks = (E + kWaves - 1) / kWaves;
-  const size_t lds = sizeof(double) * E;  // one token's logits, for the top-k
+  // one token's logits, for the top-k (and the cache state for its step)
+  const size_t lds = sizeof(double) * E + (dcache ? dcache_lds_bytes(dcache->n_slots, E) : 0);
   // a batch with its top-k, for the matrix-core path (no digit planes): the
   // batched router, a token's input held in registers (H <= 4096)
   const int steps = (H / 8 + kWave - 1) / kWave;
@@ -476,6 +600,8 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
 #undef MOE_ROUTE
   return hipGetLastError();
 }
+
+size_t dcache_lds_bytes(int n_slots, int E) { return sizeof(int32_t) * (3 * static_cast<size_t>(n_slots) + 2 * E); }
 
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s) {

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 #define MOE_OK 0
@@ -216,6 +216,13 @@ typedef struct moe_layer_desc {
   moe_store* store;
   int32_t store_layer;
   int32_t cache_policy;         /* cache mode: MOE_POLICY_LFU (0) or MOE_POLICY_LRU */
+  /* cache mode with experts_host in device-accessible pinned memory: 1 = the
+   * cache lives in device memory (in the workspace) and the routing kernel
+   * steps it, so a decode call waits for nothing on the host and can be
+   * captured in a graph; the misses are then always copied by fill blocks
+   * (as with MOE_F_FILL_KERNEL). Same rule, same trace, same bits as the host
+   * cache. 0 = the host steps the cache. */
+  int32_t cache_on_device;
 } moe_layer_desc;
 
 typedef struct moe_decode_stats {
@@ -246,8 +253,15 @@ void moe_layer_destroy(moe_layer* L);
 /* Resident mode only: point the handle at another resident expert array of the
  * same shape (e.g. a replica). Takes effect for calls enqueued afterwards. */
 moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev);
-/* The handle's LFU cache (cache mode), or NULL. Owned by the handle. */
+/* The handle's LFU cache (cache mode, host-stepped), or NULL. Owned by the handle. */
 moe_cache* moe_layer_cache(moe_layer* L);
+/* State of the handle's expert-slot cache, host- or device-stepped: per slot
+ * the expert (-1 empty), frequency and last use (n = n_slots), and the
+ * counters. A device-stepped cache is read after synchronising stream (the
+ * stream the decode calls run on). Any output may be NULL. MOE_ESTATE for a
+ * resident handle. */
+moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, int64_t* last, int32_t n,
+                                 int64_t* hits, int64_t* misses, int64_t* steps, void* stream);
 
 /* Decode B tokens through the layer.
  *   x       dev fp32 [B][H] layer input
@@ -257,8 +271,11 @@ moe_cache* moe_layer_cache(moe_layer* L);
  *   y       dev fp32 [B][H] output; must not alias x
  *   ids_out dev int32 [B][k], w_out dev fp32 [B][k], u_out dev fp32 [B][H]:
  *           optional copies of the routing and of u (NULL to skip)
- *   trace   host [B][k] cache events (cache mode) or NULL
- *   stats   host, accumulated (cache mode counters) or NULL
+ *   trace   host [B][k] cache events (cache mode) or NULL; with a
+ *           device-stepped cache the call then synchronises stream to read them
+ *   stats   host, accumulated (cache mode counters) or NULL; a
+ *           device-stepped cache counts on the device instead (only calls is
+ *           accumulated here; moe_layer_cache_state reads the counters)
  * Resident mode is asynchronous on stream. With B > 1 (resident) the tokens
  * are grouped by expert: each touched expert's weights are read once per call
  * and multiplied on the matrix cores (fp16 weights and activations, fp32

@@ -47,7 +47,7 @@ class Layer:
     """Owns the device copies of one layer's inputs and a libmoedecode handle."""
 
     def __init__(self, shape, d, *, bias=None, cache_slots=0, max_B=1, max_T=0, copy_stream=None,
-                 store=None, store_layer=0):
+                 store=None, store_layer=0, cache_policy=0, cache_on_device=False):
         self.shape = shape
         self.router = dev_u16(d["router"])
         self.shared = dev(d["shared"])
@@ -63,7 +63,8 @@ class Layer:
                                           workspace=self.ws, bias=self.bias, experts_host=self.host,
                                           slot_pool=self.pool, n_slots=cache_slots,
                                           copy_stream=self.copy_stream, max_B=max_B, max_T=max_T,
-                                          store=store, store_layer=store_layer)
+                                          store=store, store_layer=store_layer, cache_policy=cache_policy,
+                                          cache_on_device=cache_on_device)
         else:
             self.experts = dev(d["experts"])
             self.h = api.moe_layer_create(shape, router=self.router, shared_blob=self.shared,
