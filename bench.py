@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--attn-ctx", type=int, default=4096,
                     help="context length of the attention step timed next to the MoE layers")
     ap.add_argument("--no-attn", action="store_true", help="skip the attention-step measurements")
+    ap.add_argument("--no-device-cache", action="store_true",
+                    help="skip the stack with the slot caches stepped on the device")
     ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
                          "tokens (the measured kernel included), 'copy' copies 1 GiB once")
@@ -357,6 +359,80 @@ def main():
                 del d["pool2"], d["ws2"]
             torch.cuda.synchronize()
         print("[bench] slot sweep done", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- device-stepped cache
+    # The same stack with each layer's cache stepped on the device by the
+    # routing kernel (misses copied by fill blocks): no host wait per layer,
+    # run eagerly and as one HIP graph per token (30 layers).
+    if not args.no_device_cache:
+        hs = []
+        for d in layers:
+            d["pool3"] = torch.empty((S, blob), dtype=torch.uint8, device=devn)
+            d["ws3"] = torch.zeros_like(d["ws"])
+            hs.append(api.moe_layer_create(sh, router=d["router"], shared_blob=d["shared"], workspace=d["ws3"],
+                                           bias=d["bias"], experts_host=d["host"], slot_pool=d["pool3"], n_slots=S,
+                                           copy_stream=copy_stream, cache_on_device=True))
+
+        def dc_counts():
+            c = [api.moe_layer_cache_state(h_, S, stream=main_stream) for h_ in hs]
+            return sum(v[3] for v in c), sum(v[4] for v in c)
+
+        for t in range(args.warmup):
+            token(t, hs)
+        torch.cuda.synchronize()
+        n_dc = args.steps
+        h0, m0 = dc_counts()
+        t0 = time.perf_counter()
+        for t in range(args.warmup, args.warmup + n_dc):
+            token(t, hs)
+        torch.cuda.synchronize()
+        el_e = time.perf_counter() - t0
+        h1, m1 = dc_counts()
+        xg = torch.empty((1, H), device=devn)
+        eg = torch.empty((Lyr, 1, H), dtype=torch.int16, device=devn)
+
+        def token_graph():
+            s_ = torch.cuda.current_stream().cuda_stream
+            src = xg.data_ptr()
+            for l in range(Lyr):
+                dst = hp[l & 1]
+                rc = decode(hs[l], src, eg.data_ptr() + l * H * 2, 1, flags, dst, None, None, None, None, None, s_)
+                if rc:
+                    raise api.MoeError(rc, "moe_layer_decode", api.moe_last_error())
+                src = dst
+        cap2 = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd, stream=cap2):
+            token_graph()
+        torch.cuda.synchronize()
+        t_base = args.warmup + n_dc
+        for t in range(t_base, t_base + 16):
+            xg.copy_(x[t % T:t % T + 1])
+            eg.copy_(eps[:, t % T:t % T + 1])
+            gd.replay()
+        torch.cuda.synchronize()
+        h2, m2 = dc_counts()
+        t0 = time.perf_counter()
+        for t in range(t_base + 16, t_base + 16 + n_dc):
+            xg.copy_(x[t % T:t % T + 1])
+            eg.copy_(eps[:, t % T:t % T + 1])
+            gd.replay()
+        torch.cuda.synchronize()
+        el_g = time.perf_counter() - t0
+        h3, m3 = dc_counts()
+        detail["device_cache_step"] = {
+            "tokens_per_s_eager": n_dc / el_e, "tokens_per_s_graph": n_dc / el_g, "tokens": n_dc,
+            "hit_rate_eager": (h1 - h0) / max(h1 - h0 + m1 - m0, 1),
+            "hit_rate_graph": (h3 - h2) / max(h3 - h2 + m3 - m2, 1),
+            "h2d_MB_per_token_graph": (m3 - m2) * blob / n_dc / 1e6}
+        del gd
+        for h_ in hs:
+            api.moe_layer_destroy(h_)
+        for d in layers:
+            del d["pool3"], d["ws3"]
+        torch.cuda.synchronize()
+        print(f"[bench] device cache step: {detail['device_cache_step']}", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- expert file store
     # The same stack with the misses read from a file of all layers' experts
