@@ -87,6 +87,8 @@ SIGNATURES = {
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
+    "moe_layer_fused": (C.c_int32, [vp]),
+    "moe_layer_check": (c_status, [vp, vp]),
     "moe_layer_cache_state": (c_status, [vp, vp, vp, vp, C.c_int32, vp, vp, vp, vp]),
     "moe_attn_workspace_bytes": (c_status, [P(moe_attn_shape), P(C.c_size_t)]),
     "moe_attn_decode": (c_status, [P(moe_attn_shape), P(moe_attn_weights), vp, vp, C.c_int32, vp, vp, vp,

@@ -16,6 +16,7 @@ from . import _lib as L
 MOE_F_RMSNORM_IN = 1
 MOE_F_RESIDUAL = 2
 MOE_F_FILL_KERNEL = 4
+MOE_F_FUSED = 8
 MOE_POLICY_LFU = 0
 MOE_POLICY_LRU = 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EALIGN", -4: "MOE_EHIP",
@@ -225,6 +226,14 @@ def moe_layer_set_experts(h, experts_dev) -> None:
 
 def moe_layer_cache(h):
     return lib().moe_layer_cache(h)
+
+
+def moe_layer_fused(h) -> bool:
+    return bool(lib().moe_layer_fused(h))
+
+
+def moe_layer_check(h, stream=None) -> None:
+    _check(lib().moe_layer_check(h, _stream(stream)), "moe_layer_check")
 
 
 def moe_layer_cache_state(h, n_slots, stream=None):

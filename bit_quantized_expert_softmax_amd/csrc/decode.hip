@@ -271,7 +271,283 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
   }
 }
 
+// Routed gate/up, then the down projections of all k + 1 sources with the
+// weighted combine, in one launch (cache mode, one token; the shared expert's
+// gate/up ran in an earlier launch). Every block issues its down-weight loads
+// together with its gate/up loads, so they stream while the gate/up phase
+// computes; the GeGLU digit planes leave with agent-scope stores; a grid
+// barrier (a ticket counter in device memory, bounded spin) separates the
+// phases; after it the block stages all activation digits into LDS with
+// agent-scope loads. Needs every block resident at once: launched only where
+// the device holds the whole grid. The arithmetic and its order are those of
+// k_gateup and k_down, so the output is the same bits.
+constexpr unsigned kBarrierSpins = 1u << 20;  // about a second of polling, then the error flag
+
+template <int NTG, int NTD>
+__global__ __launch_bounds__(kThreads) void k_ffn_fused(SourceSet S, int n_units, int n_down,
+                                                        const DigitGroup* __restrict__ udig,
+                                                        const float* __restrict__ usc, DigitGroup* adig,
+                                                        float* asc, const float* __restrict__ w,
+                                                        const float* __restrict__ x,
+                                                        const uint16_t* __restrict__ add_in, int residual,
+                                                        float* __restrict__ y, unsigned long long* ctr,
+                                                        int* err) {
+  extern __shared__ uint4 lds_raw[];
+  __shared__ float rowsum[2 * kGroupRows];
+  __shared__ float wsh[kMaxTopK + 1];
+  __shared__ const uint8_t* srcb[kMaxTopK + 1];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  const int ngu = S.H / kGroup, gi = S.I / kGroup, gsh = S.Is / kGroup;
+  const int nga = S.k * gi + gsh;
+  const int part_n = 2 * kGroupRows * ngu > kOutPerBlock * nga ? 2 * kGroupRows * ngu : kOutPerBlock * nga;
+  float* part = reinterpret_cast<float*>(lds_raw);
+  DigitGroup* xdl = reinterpret_cast<DigitGroup*>(lds_raw + (part_n + 3) / 4);  // [nga]
+  float* xsl = reinterpret_cast<float*>(xdl + nga);                              // [nga]
+  if (tid <= S.k) {
+    srcb[tid] = source_base(S, tid);
+    wsh[tid] = tid < S.k ? w[tid] : 1.0f;
+  }
+  __syncthreads();
+
+  // ---- gate/up loads: group grp of 32 activations of routed rank grp / gi
+  const bool unit = static_cast<int>(blockIdx.x) < n_units;
+  const int grp = unit ? static_cast<int>(blockIdx.x) : 0;
+  const int gsrc = grp / gi, i0 = (grp % gi) * kGroupRows;
+  const BlobOffsets og = blob_offsets(S.H, S.I);
+  const size_t rowb = static_cast<size_t>(S.H) / 2;
+  const int Rg = kThreads / ngu;
+  const int cg = tid % ngu, rg0 = tid / ngu;
+  const uint8_t* gbase = srcb[gsrc];
+  const uint8_t* gq = gbase + og.gate_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(cg);
+  const uint8_t* uq = gbase + og.up_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(cg);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(gbase + og.gate_s) + static_cast<size_t>(i0) * ngu + cg;
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(gbase + og.up_s) + static_cast<size_t>(i0) * ngu + cg;
+  uint4 wv[NTG];
+  uint16_t sw[NTG];
+  if (unit) {
+#pragma unroll
+    for (int t = 0; t < NTG; ++t) {
+      int r = rg0 + Rg * t;
+      r = r < 2 * kGroupRows ? r : 2 * kGroupRows - 1;  // clamped: loaded, not stored
+      const bool up = r >= kGroupRows;
+      const int rr = up ? r - kGroupRows : r;
+      wv[t] = load_w16((up ? uq : gq) + static_cast<size_t>(rr) * rowb);
+      sw[t] = (up ? us : gs)[static_cast<size_t>(rr) * ngu];
+    }
+  }
+  // ---- down loads: outputs n0 .. n0 + nout of the virtual rows
+  const bool down = static_cast<int>(blockIdx.x) < n_down;
+  const int n0 = (down ? static_cast<int>(blockIdx.x) : 0) * kOutPerBlock;
+  const int nout = S.H - n0 < kOutPerBlock ? S.H - n0 : kOutPerBlock;
+  const int Rd = kThreads / nga;
+  const int cd = tid % nga, od0 = tid / nga;
+  const bool on = od0 < Rd;
+  int jd, ccd, interd;
+  if (cd < S.k * gi) {
+    jd = cd / gi;
+    ccd = cd - jd * gi;
+    interd = S.I;
+  } else {
+    jd = S.k;
+    ccd = cd - S.k * gi;
+    interd = S.Is;
+  }
+  const BlobOffsets od = blob_offsets(S.H, interd);
+  const uint8_t* qb = srcb[jd] + od.down_q + 16 * static_cast<size_t>(ccd);
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(srcb[jd] + od.down_s) + ccd;
+  uint4 dv[NTD];
+  uint16_t dsw[NTD];
+  if (down) {
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) {
+      int ob = od0 + Rd * t;
+      ob = ob < nout ? ob : nout - 1;  // clamped: loaded, not stored
+      const size_t n = static_cast<size_t>(n0 + ob);
+      dv[t] = load_w16(qb + n * (interd / 2));
+      dsw[t] = sb[n * (interd / kGroup)];
+    }
+  }
+  DigitGroup xd;
+  float xs = 0.f;
+  if (unit) {
+    xd = udig[cg];
+    xs = usc[cg];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- gate/up: row sums, GeGLU, digit planes (as k_gateup)
+  if (unit) {
+#pragma unroll
+    for (int t = 0; t < NTG; ++t) {
+      const int r = rg0 + Rg * t;
+      const float p = static_cast<float>(chunk_dot(wv[t], xd)) * (h2f(sw[t]) * xs);
+      if (r < 2 * kGroupRows) part[r * ngu + cg] = p;
+    }
+    __syncthreads();
+    {
+      const int r = 4 * wave + (lane >> 4);
+      const int l = lane & 15;
+      float acc = 0.f;
+      for (int c = l; c < ngu; c += 16) acc += part[r * ngu + c];
+      acc = dpp_sum<16>(acc);
+      if (l == 0) rowsum[r] = acc;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float a = 0.f;
+      if (lane < kGroupRows) a = gelu_tanh(rowsum[lane]) * rowsum[kGroupRows + lane];
+      quant_pair_of_groups<true>(a, grp, grp + 1, adig, asc);
+    }
+  }
+
+  // ---- grid barrier: every store of the block has completed before it takes
+  // its ticket; the blocks of this launch hold tickets [g * nb, (g + 1) * nb)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned long long nb = gridDim.x;
+    const unsigned long long t = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long target = (t / nb + 1) * nb;
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kBarrierSpins) {
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (!down) return;
+
+  // ---- all activation digits into LDS (agent-scope loads: other blocks wrote them)
+  for (int i = tid; i < nga * 17; i += kThreads) {
+    const int g = i / 17, q = i % 17;
+    if (q < 16) {
+      const uint32_t v = __hip_atomic_load(reinterpret_cast<const uint32_t*>(&adig[g]) + q, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      reinterpret_cast<uint32_t*>(&xdl[g])[q] = v;
+    } else {
+      xsl[g] = __hip_atomic_load(asc + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+
+  // ---- down + combine (as k_down)
+  {
+    const DigitGroup xdd = xdl[cd];
+    const float xsd = xsl[cd] * wsh[jd];
+#pragma unroll
+    for (int t = 0; t < NTD; ++t) {
+      const int ob = od0 + Rd * t;
+      const float p = static_cast<float>(chunk_dot(dv[t], xdd)) * (h2f(dsw[t]) * xsd);
+      if (on && ob < nout) part[ob * nga + cd] = p;
+    }
+  }
+  __syncthreads();
+  if (wave < nout) {
+    float acc = 0.f;
+    for (int c = lane; c < nga; c += kWave) acc += part[wave * nga + c];
+    acc = dpp_sum<16>(acc);
+    acc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 16)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 48));
+    if (lane == 0) {
+      const int n = n0 + wave;
+      float r = 0.f;
+      if (residual) r = x[n] + (add_in ? h2f(add_in[n]) : 0.f);
+      y[n] = r + acc;
+    }
+  }
+}
+
+int fused_ntg(int H) {
+  const int rows_per_pass = kThreads / (H / kGroup);
+  const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
+  return need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : need <= 8 ? 8 : 0;
+}
+int fused_ntd(int nga) {
+  const int outs_per_pass = kThreads / nga;
+  const int need = (kOutPerBlock + outs_per_pass - 1) / outs_per_pass;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 3 ? 3 : need <= 4 ? 4 : need <= 6 ? 6 : 0;
+}
+size_t fused_lds(int H, int k, int I, int Is) {
+  const int ngu = H / kGroup, nga = k * (I / kGroup) + Is / kGroup;
+  const int part_n = 2 * kGroupRows * ngu > kOutPerBlock * nga ? 2 * kGroupRows * ngu : kOutPerBlock * nga;
+  return static_cast<size_t>((part_n + 3) / 4) * 16 + static_cast<size_t>(nga) * (sizeof(DigitGroup) + 4);
+}
+
+template <int NTG, int NTD>
+const void* fused_fn() {
+  return reinterpret_cast<const void*>(&k_ffn_fused<NTG, NTD>);
+}
+
+// The instance for this shape (nullptr if none fits).
+const void* fused_kernel_of(int H, int k, int I, int Is) {
+  const int nga = k * (I / kGroup) + Is / kGroup;
+  if (H / kGroup > kThreads || nga > kThreads) return nullptr;
+  const int g = fused_ntg(H), d = fused_ntd(nga);
+#define MOE_FK(G_, D_) if (g == G_ && d == D_) return fused_fn<G_, D_>();
+  MOE_FK(2, 1) MOE_FK(2, 2) MOE_FK(2, 3) MOE_FK(2, 4) MOE_FK(2, 6)
+  MOE_FK(4, 1) MOE_FK(4, 2) MOE_FK(4, 3) MOE_FK(4, 4) MOE_FK(4, 6)
+  MOE_FK(6, 1) MOE_FK(6, 2) MOE_FK(6, 3) MOE_FK(6, 4) MOE_FK(6, 6)
+  MOE_FK(8, 1) MOE_FK(8, 2) MOE_FK(8, 3) MOE_FK(8, 4) MOE_FK(8, 6)
+#undef MOE_FK
+  return nullptr;
+}
+
 }  // namespace
+
+int ffn_fused_grid(int H, int k, int I) {
+  const int units = k * (I / kGroup);
+  const int dn = (H + kOutPerBlock - 1) / kOutPerBlock;
+  return units > dn ? units : dn;
+}
+
+bool ffn_fused_fits(int H, int k, int I, int Is) {
+  const void* fn = fused_kernel_of(H, k, I, Is);
+  const size_t lds = fused_lds(H, k, I, Is);
+  if (!fn || lds > 65536) return false;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return static_cast<long long>(cus) * per_cu >= ffn_fused_grid(H, k, I);
+}
+
+hipError_t launch_ffn_fused(const SourceSet& S, const DigitGroup* udig, const float* usc, DigitGroup* adig,
+                            float* asc, const float* w, const float* x, const uint16_t* add_in, bool residual,
+                            float* y, unsigned long long* ctr, int* err, hipStream_t s, hipEvent_t t0,
+                            hipEvent_t t1) {
+  const int nga = S.k * (S.I / kGroup) + S.Is / kGroup;
+  const int n_units = S.k * (S.I / kGroup);
+  const int n_down = (S.H + kOutPerBlock - 1) / kOutPerBlock;
+  const int grid = n_units > n_down ? n_units : n_down;
+  const size_t lds = fused_lds(S.H, S.k, S.I, S.Is);
+  const int g = fused_ntg(S.H), d = fused_ntd(nga);
+  const int res = residual ? 1 : 0;
+#define MOE_FL(G_, D_)                                                                                       \
+  if (g == G_ && d == D_) {                                                                                  \
+    if (t0)                                                                                                  \
+      hipExtLaunchKernelGGL((k_ffn_fused<G_, D_>), dim3(grid), dim3(kThreads), lds, s, t0, t1, 0, S, n_units, \
+                            n_down, udig, usc, adig, asc, w, x, add_in, res, y, ctr, err);                   \
+    else                                                                                                     \
+      hipLaunchKernelGGL((k_ffn_fused<G_, D_>), dim3(grid), dim3(kThreads), lds, s, S, n_units, n_down, udig, \
+                         usc, adig, asc, w, x, add_in, res, y, ctr, err);                                    \
+    return hipGetLastError();                                                                                \
+  }
+  MOE_FL(2, 1) MOE_FL(2, 2) MOE_FL(2, 3) MOE_FL(2, 4) MOE_FL(2, 6)
+  MOE_FL(4, 1) MOE_FL(4, 2) MOE_FL(4, 3) MOE_FL(4, 4) MOE_FL(4, 6)
+  MOE_FL(6, 1) MOE_FL(6, 2) MOE_FL(6, 3) MOE_FL(6, 4) MOE_FL(6, 6)
+  MOE_FL(8, 1) MOE_FL(8, 2) MOE_FL(8, 3) MOE_FL(8, 4) MOE_FL(8, 6)
+#undef MOE_FL
+  return hipErrorInvalidValue;
+}
 
 size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
   const size_t ngu = H / kGroup, nga = (static_cast<size_t>(k) * I + Is) / kGroup;

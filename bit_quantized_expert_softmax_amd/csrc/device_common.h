@@ -115,7 +115,9 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 
 // Quantise two groups of 32 values to digit planes; called by a whole wave.
 // Lanes 0-31 take group g0, lanes 32-63 group g0+1 (skipped when >= ng).
-// v is the lane's value (already loaded); writes dig[g] and sc[g].
+// v is the lane's value (already loaded); writes dig[g] and sc[g]. COHERENT:
+// with agent-scope stores, for readers in other blocks of the same launch.
+template <bool COHERENT = false>
 __device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, DigitGroup* dig,
                                                      float* sc) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -157,8 +159,19 @@ __device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, Di
   w2 |= dpp<0x141>(w2);
   w3 |= dpp<0x141>(w3);
   if (g < ng) {
-    if ((i & 7) == 0) dig[g].p[i >> 3] = make_uint4(w0, w1, w2, w3);
-    if (i == 0) sc[g] = m / static_cast<float>(kQmax);
+    if (COHERENT) {
+      if ((i & 7) == 0) {
+        uint32_t* p = reinterpret_cast<uint32_t*>(&dig[g].p[i >> 3]);
+        __hip_atomic_store(p, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 2, w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 3, w3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (i == 0) __hip_atomic_store(sc + g, m / static_cast<float>(kQmax), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if ((i & 7) == 0) dig[g].p[i >> 3] = make_uint4(w0, w1, w2, w3);
+      if (i == 0) sc[g] = m / static_cast<float>(kQmax);
+    }
   }
 }
 

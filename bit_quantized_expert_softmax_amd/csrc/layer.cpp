@@ -40,6 +40,8 @@ struct WsLayout {
   // device-stepped slot cache: counters, per-slot and per-expert arrays, the
   // call's slot per rank, miss list and events
   size_t dc;
+  // fused expert FFN: grid-barrier ticket counter (8 bytes) and error flag
+  size_t bar;
   // batched decode (max_B > 1): fp16 inputs and per-assignment outputs
   size_t out_r, out_s, u16, tsc, act;
   size_t total;
@@ -89,6 +91,7 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.asc = take(B * npos * 4);
   L.cnt = take(B * 4);  // router arrival counters, one per token
   L.dc = take(dcache_region_bytes(static_cast<int>(E)));
+  L.bar = take(16);
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
@@ -116,6 +119,7 @@ struct moe_layer {
   bool cache_mode = false;
   bool dcache = false;     // the slot cache is stepped on the device
   moe::DevCache dc{};
+  bool fused = false;      // MOE_F_FUSED can take effect (cache mode, B = 1)
   int max_B = 0, max_T = 0;
   moe_cache* cache = nullptr;
   moe_cache* cache_backup = nullptr;
@@ -322,6 +326,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
   };
   hipError_t e = hipMemset(L->wsb + ws.cnt, 0, static_cast<size_t>(max_B) * 4);
+  if (e == hipSuccess) e = hipMemset(L->wsb + ws.bar, 0, 16);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
@@ -374,6 +379,9 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
       L->dcache = true;
       L->dc = moe::dcache_at(L->wsb + ws.dc, E, d->n_slots, d->cache_policy);
     }
+    // the one-launch option (MOE_F_FUSED) only where the device holds the
+    // whole grid at once (its grid barrier needs that)
+    L->fused = moe::ffn_fused_fits(sh->hidden, sh->top_k, sh->inter, sh->shared_inter);
     moe_status cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache);
     if (!cs) cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache_backup);
     if (cs) {
@@ -414,6 +422,20 @@ moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev) {
 
 moe_cache* moe_layer_cache(moe_layer* L) { return L && !L->dcache ? L->cache : nullptr; }
 
+int32_t moe_layer_fused(const moe_layer* L) { return L && L->fused ? 1 : 0; }
+
+moe_status moe_layer_check(moe_layer* L, void* stream) {
+  moe::clear_error();
+  const char* fn = "moe_layer_check";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  int32_t err = 0;
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(&err, L->wsb + L->ws.bar + 8, sizeof(err), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  if (err) return fail(MOE_EHIP, "%s: a grid-barrier wait of the fused expert kernel gave up", fn);
+  return MOE_OK;
+}
+
 moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, int64_t* last, int32_t n,
                                  int64_t* hits, int64_t* misses, int64_t* steps, void* stream) {
   moe::clear_error();
@@ -453,8 +475,11 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   moe::clear_error();
   const char* fn = "moe_layer_decode";
   if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
-  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL | MOE_F_FILL_KERNEL))
+  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL | MOE_F_FILL_KERNEL | MOE_F_FUSED))
     return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const bool fused = L->fused && (flags & MOE_F_FUSED);
+  auto* bar_ctr = reinterpret_cast<unsigned long long*>(L->wsb + L->ws.bar);
+  auto* bar_err = reinterpret_cast<int*>(L->wsb + L->ws.bar + 8);
   const bool fill_kernel = flags & MOE_F_FILL_KERNEL;
   if (fill_kernel && !L->cache_mode) return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs a cache-mode handle", fn);
   if (fill_kernel && !(L->d.store ? L->staging_dev : L->host_dev))
@@ -569,12 +594,19 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F), fn);
     prof_add(L, 1, p1);
     S.ids = L->dc.slot_of_rank;
-    const ProfPair p2 = prof_pair(L, 2);
-    HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
-    prof_add(L, 2, p2);
-    const ProfPair p3 = prof_pair(L, 3);
-    HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
-    prof_add(L, 3, p3);
+    if (fused) {
+      const ProfPair p2 = prof_pair(L, 2);
+      HIP_OR_FAIL(moe::launch_ffn_fused(S, udig, usc, adg, asc, w, x, add_in, res, y, bar_ctr, bar_err, s, p2.a,
+                                        p2.b), fn);
+      prof_add(L, 2, p2);
+    } else {
+      const ProfPair p2 = prof_pair(L, 2);
+      HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+      prof_add(L, 2, p2);
+      const ProfPair p3 = prof_pair(L, 3);
+      HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
+      prof_add(L, 3, p3);
+    }
     if (trace) {
       int32_t evd[4 * moe::kMaxTopK];
       hipError_t te = hipMemcpyAsync(evd, L->dc.ev, sizeof(int32_t) * 4 * k, hipMemcpyDeviceToHost, s);
@@ -678,12 +710,19 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
   }
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
-  const ProfPair p2 = prof_pair(L, 2);
-  HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
-  prof_add(L, 2, p2);
-  const ProfPair p3 = prof_pair(L, 3);
-  HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
-  prof_add(L, 3, p3);
+  if (fused) {
+    const ProfPair p2 = prof_pair(L, 2);
+    HIP_OR_FAIL(moe::launch_ffn_fused(S, udig, usc, adg, asc, w, x, add_in, res, y, bar_ctr, bar_err, s, p2.a,
+                                      p2.b), fn);
+    prof_add(L, 2, p2);
+  } else {
+    const ProfPair p2 = prof_pair(L, 2);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+    prof_add(L, 2, p2);
+    const ProfPair p3 = prof_pair(L, 3);
+    HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
+    prof_add(L, 3, p3);
+  }
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
   if (stats) {
     stats->hits += k - n_miss;

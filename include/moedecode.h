@@ -238,6 +238,14 @@ typedef struct moe_decode_stats {
  * cross-stream event). experts_host must then be device-accessible pinned
  * memory (hipHostMalloc); copy_stream is unused. Same cache trace, same bits. */
 #define MOE_F_FILL_KERNEL 4u
+/* Cache mode, one token: run the routed gate/up and the down projections with
+ * the combine as one launch whose blocks meet at a grid barrier between the
+ * two phases (only where the device holds the whole grid at once, see
+ * moe_layer_fused; otherwise the flag is ignored). Same bits as the default
+ * two launches, but slower on MI355X: the barrier's round trips through
+ * memory across the XCDs and the re-read of the activations cost more than
+ * the kernel boundary they replace. */
+#define MOE_F_FUSED 8u
 
 /* Workspace for up to max_B decode tokens per call and max_T prefill tokens. */
 moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
@@ -255,6 +263,13 @@ void moe_layer_destroy(moe_layer* L);
 moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev);
 /* The handle's LFU cache (cache mode, host-stepped), or NULL. Owned by the handle. */
 moe_cache* moe_layer_cache(moe_layer* L);
+/* 1 if MOE_F_FUSED can take effect on this handle (cache mode, and the device
+ * holds the fused launch's whole grid at once), else 0. */
+int32_t moe_layer_fused(const moe_layer* L);
+/* Synchronises stream and reports MOE_EHIP if a grid-barrier wait of the fused
+ * launch ever gave up (about a second without all blocks arriving: the grid
+ * was not resident at once, e.g. the device was shared), else MOE_OK. */
+moe_status moe_layer_check(moe_layer* L, void* stream);
 /* State of the handle's expert-slot cache, host- or device-stepped: per slot
  * the expert (-1 empty), frequency and last use (n = n_slots), and the
  * counters. A device-stepped cache is read after synchronising stream (the

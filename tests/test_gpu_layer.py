@@ -231,7 +231,7 @@ def test_empty_call_and_errors():
     with pytest.raises(api.MoeError):
         api.moe_layer_decode(L.h, x, None, 2, 0, y)     # B above max_B
     with pytest.raises(api.MoeError):
-        api.moe_layer_decode(L.h, x, None, 1, 8, y)     # unknown flag
+        api.moe_layer_decode(L.h, x, None, 1, 16, y)    # unknown flag
     with pytest.raises(api.MoeError):
         api.moe_layer_decode(L.h, x, None, 1, 0, x)     # y aliases x
     L.close()
