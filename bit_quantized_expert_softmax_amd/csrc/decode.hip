@@ -143,6 +143,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   const uint8_t* uq = base + o.up_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(c);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(base + o.gate_s) + static_cast<size_t>(i0) * ngu + c;
   const uint16_t* us = reinterpret_cast<const uint16_t*>(base + o.up_s) + static_cast<size_t>(i0) * ngu + c;
+  // the activation digits first: loads retire in order, so chunk t can be
+  // consumed as soon as its own bytes are in while later chunks still stream
+  const DigitGroup xd = udig[c];
+  const float xs = usc[c];
   uint4 wv[NT];
   uint16_t sw[NT];
 #pragma unroll
@@ -154,8 +158,6 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
     wv[t] = load_w16((up ? uq : gq) + static_cast<size_t>(rr) * rowb);
     sw[t] = (up ? us : gs)[static_cast<size_t>(rr) * ngu];
   }
-  const DigitGroup xd = udig[c];
-  const float xs = usc[c];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -230,6 +232,8 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
   const BlobOffsets o = blob_offsets(S.H, inter);
   const uint8_t* qb = srcb[j] + o.down_q + 16 * static_cast<size_t>(cc);
   const uint16_t* sb = reinterpret_cast<const uint16_t*>(srcb[j] + o.down_s) + cc;
+  const DigitGroup xd = adig[c];  // first, as in the gate/up kernel
+  const float xsa = asc[c];
   uint4 wv[NT];
   uint16_t sw[NT];
 #pragma unroll
@@ -240,9 +244,8 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     wv[t] = load_w16(qb + n * (inter / 2));
     sw[t] = sb[n * (inter / kGroup)];
   }
-  const DigitGroup xd = adig[c];
-  const float xs = asc[c] * wsh[j];
   __builtin_amdgcn_sched_barrier(0);
+  const float xs = xsa * wsh[j];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int ob = o0 + R * t;
@@ -323,6 +326,12 @@ __global__ __launch_bounds__(kThreads) void k_ffn_fused(SourceSet S, int n_units
   const uint8_t* uq = gbase + og.up_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(cg);
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(gbase + og.gate_s) + static_cast<size_t>(i0) * ngu + cg;
   const uint16_t* us = reinterpret_cast<const uint16_t*>(gbase + og.up_s) + static_cast<size_t>(i0) * ngu + cg;
+  DigitGroup xd;
+  float xs = 0.f;
+  if (unit) {  // the activation digits first (loads retire in order)
+    xd = udig[cg];
+    xs = usc[cg];
+  }
   uint4 wv[NTG];
   uint16_t sw[NTG];
   if (unit) {
@@ -367,12 +376,6 @@ __global__ __launch_bounds__(kThreads) void k_ffn_fused(SourceSet S, int n_units
       dv[t] = load_w16(qb + n * (interd / 2));
       dsw[t] = sb[n * (interd / kGroup)];
     }
-  }
-  DigitGroup xd;
-  float xs = 0.f;
-  if (unit) {
-    xd = udig[cg];
-    xs = usc[cg];
   }
   __builtin_amdgcn_sched_barrier(0);
 
