@@ -92,7 +92,15 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
     }
   };
 
-  // weights first: nothing they address depends on the input
+  // the output projection's input digits first (loads retire in order, so a
+  // weight chunk is consumed as soon as it is in); then the weights, whose
+  // addresses do not depend on the input
+  DigitGroup xc;
+  float xsc;
+  if (MODE == kOut) {
+    xc = A.adig[c];
+    xsc = A.asc[c];
+  }
   const size_t rowb = static_cast<size_t>(A.K) / 2;
   uint4 wv[NT];
   uint16_t sw[NT];
@@ -103,14 +111,6 @@ __global__ __launch_bounds__(kAThreads) void k_attn_gemv(AttnGemvArgs A) {
     const size_t n = static_cast<size_t>(row_of(r));
     wv[t] = load_w16(A.wq + n * rowb + 16 * static_cast<size_t>(c));
     sw[t] = A.ws[n * ng + c];
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  DigitGroup xc;
-  float xsc;
-  if (MODE == kOut) {
-    xc = A.adig[c];
-    xsc = A.asc[c];
   }
   __builtin_amdgcn_sched_barrier(0);
 

@@ -12,7 +12,7 @@
 // per CU); every lane owns one 16-byte chunk column and a few rows of it,
 // loads that chunk's activation digits once into registers and issues all of
 // its loads before any is consumed; per-chunk partial products are reduced in
-// LDS in a fixed order; no cross-block synchronisation.
+// LDS in a fixed order; the two kernels do not synchronise across blocks.
 //
 // gate/up kernel: one block per group of 32 activations of one source: the 32
 //   gate rows and 32 up rows (contiguous in the blob) are streamed as one
@@ -22,6 +22,8 @@
 //   all k+1 sources as one virtual row of (k*I + I_s)/32 chunks, the routing
 //   weight folded into each group's scale; the row sum is the weighted
 //   combine, in a fixed order, without atomics.
+// fused kernel (opt-in): both phases in one launch, separated by a grid
+//   barrier; the same arithmetic, so the same bits.
 #include <hip/hip_ext.h>
 
 #include "launch.h"
