@@ -110,10 +110,6 @@ __device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow, 
     b.q[m] = *reinterpret_cast<const u32x4*>(qrow[m] + 16 * static_cast<size_t>(g));
 }
 
-// One launch covers all segments: tiles_r blocks per routed expert (blocks of
-// untouched experts exit at once), then tiles_s blocks of the shared expert.
-// GATEUP: a wave's weight tiles are 16 gate rows and the 16 matching up rows;
-// else 32 consecutive down rows. NTT 16-token tiles share one pass over K.
 // f(integral_constant<int, D>) for D = 0, 1, ...: ring slots as compile-time
 // constants, so the ring stays in registers
 template <class F, int... D>
@@ -121,17 +117,16 @@ __device__ __forceinline__ void for_slots(std::integer_sequence<int, D...>, F&& 
   (f(std::integral_constant<int, D>{}), ...);
 }
 
+// The work of one block over segment s (an expert, or s == E: the shared
+// expert) with NTT 16-token tiles per pass. GATEUP: a wave's weight tiles are
+// 16 gate rows and the 16 matching up rows; else 32 consecutive down rows.
+// lds_slices: the two activation slice buffers, NTT * kTile * kBRow bytes
+// each; alist: NTT * kTile ints.
 template <bool GATEUP, int NTT, int DEPTH>
-__global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
+__device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, uint8_t* lds_slices, int* alist,
+                                          int* wcnt) {
   static_assert(DEPTH >= 2 && DEPTH <= 8, "ring of 2..8 load units");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][NTT * kTile * kBRow];
-  int s, tile;
-  {
-    const int nr = A.E * A.tiles_r;
-    const int bx = blockIdx.x;
-    s = bx < nr ? bx / A.tiles_r : A.E;
-    tile = bx < nr ? bx % A.tiles_r : bx - nr;
-  }
+  uint8_t* const lds_b[2] = {lds_slices, lds_slices + NTT * kTile * kBRow};
   const bool routed = s < A.E;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -139,8 +134,6 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   // increasing a (so in token order: a token holds an expert at most once).
   // scan() counts them and puts those of rows [p0, p0 + cap) in alist: a
   // ballot per wave, the waves' counts through LDS, ids read in batches.
-  __shared__ int alist[NTT * kTile];
-  __shared__ int wcnt[kWaves];
   auto scan = [&](int p0, int cap) __attribute__((always_inline)) {
     constexpr int kBatch = 4;
     int total = 0;
@@ -371,6 +364,29 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   }
 }
 
+// One launch covers all segments: tiles_s blocks of the shared expert, then
+// tiles_r blocks per routed expert (blocks of untouched experts exit at
+// once). The routed experts' blocks take NTT_R token tiles per pass (their
+// segments are short: B * k / E tokens on average), the shared expert's
+// blocks NTT_S (its segment holds all B tokens).
+template <bool GATEUP, int NTT_R, int DEPTH_R, int NTT_S, int DEPTH_S>
+__global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
+  constexpr int kNT = NTT_R > NTT_S ? NTT_R : NTT_S;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * kNT * kTile * kBRow];
+  __shared__ int alist[kNT * kTile];
+  __shared__ int wcnt[kWaves];
+  // the shared expert's blocks first: its segment is the longest (every
+  // token), so it starts before the routed blocks fill the device
+  const int bx = blockIdx.x;
+  const bool sh = bx < A.tiles_s;
+  const int s = sh ? A.E : (bx - A.tiles_s) / A.tiles_r;
+  const int tile = sh ? bx : (bx - A.tiles_s) % A.tiles_r;
+  if (s < A.E)
+    mfma_body<GATEUP, NTT_R, DEPTH_R>(A, s, tile, lds_b, alist, wcnt);
+  else
+    mfma_body<GATEUP, NTT_S, DEPTH_S>(A, s, tile, lds_b, alist, wcnt);
+}
+
 // y[t] = (x'[t] if residual) + out_s[t] + sum_j w[t][j] * out_r[t*k + j]
 __global__ void k_bcombine(const float* __restrict__ out_s, const float* __restrict__ out_r,
                            const float* __restrict__ w,
@@ -394,14 +410,21 @@ size_t mfma_scale_lds(int K) { return static_cast<size_t>(kWaves) * kMR * kTile 
 int tiles_per_pass(int B) { return B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4); }
 constexpr size_t kMaxBlockLds = 65536;
 
+// ntt_r: tiles per pass of the routed experts' blocks, ntt_s: of the shared
+// expert's; the launch's static LDS is that of the larger.
 template <bool GATEUP>
-hipError_t launch_mfma(const MArgs& A, int ntt, hipStream_t s) {
+hipError_t launch_mfma(const MArgs& A, int ntt_r, int ntt_s, hipStream_t s) {
   const dim3 grid(A.E * A.tiles_r + A.tiles_s);
   const size_t lds = mfma_scale_lds(GATEUP ? A.H : (A.I > A.Is ? A.I : A.Is));
-  if (mfma_static_lds(ntt) + lds > kMaxBlockLds) return hipErrorInvalidValue;
-  if (ntt <= 1) hipLaunchKernelGGL((k_mfma<GATEUP, 1, 4>), grid, dim3(kThreads), lds, s, A);
-  else if (ntt == 2) hipLaunchKernelGGL((k_mfma<GATEUP, 2, 4>), grid, dim3(kThreads), lds, s, A);
-  else hipLaunchKernelGGL((k_mfma<GATEUP, 4, 3>), grid, dim3(kThreads), lds, s, A);
+  if (mfma_static_lds(ntt_r > ntt_s ? ntt_r : ntt_s) + lds > kMaxBlockLds) return hipErrorInvalidValue;
+#define MOE_MF(R_, DR_, S_, DS_) hipLaunchKernelGGL((k_mfma<GATEUP, R_, DR_, S_, DS_>), grid, dim3(kThreads), lds, s, A)
+  if (ntt_r <= 1 && ntt_s <= 1) MOE_MF(1, 4, 1, 4);
+  else if (ntt_r <= 1 && ntt_s == 2) MOE_MF(1, 4, 2, 4);
+  else if (ntt_r <= 1) MOE_MF(1, 4, 4, 3);
+  else if (ntt_r == 2 && ntt_s <= 2) MOE_MF(2, 4, 2, 4);
+  else if (ntt_r == 2) MOE_MF(2, 4, 4, 3);
+  else MOE_MF(4, 3, 4, 3);
+#undef MOE_MF
   return hipGetLastError();
 }
 
@@ -418,17 +441,23 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
                           const float* x, const uint16_t* add_in, bool residual, float* y, hipStream_t s) {
   MArgs A{experts, shared, blob_e, H, I, Is, E, k, B, ids, B * k, u16, tsc,
           bb.act_r, bb.act_s, bb.out_r, bb.out_s, 0, 0};
-  // tokens per pass over a segment's weights: up to 64; a larger shared or
-  // expert segment takes several passes
-  const int ntt = tiles_per_pass(B);
+  // tokens per pass over a segment's weights: up to 64; a longer segment
+  // takes more passes (the later ones read the weights from cache). An
+  // expert's segment holds about B * k / E tokens, so its blocks are sized
+  // for twice that; the shared expert's holds all B, and its blocks (issued
+  // first, so their extra passes overlap the routed blocks) for B / 4, at
+  // most 4 passes. Smaller tiles keep the registers, and so the waves per
+  // SIMD, of the common case.
+  const int ntt_s = tiles_per_pass((B + 3) / 4);
+  const int ntt_r = tiles_per_pass(2 * ((B * k + E - 1) / E));
   // gate/up: 64 row pairs per block
   A.tiles_r = (I + kWaves * kTile - 1) / (kWaves * kTile);
   A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile);
-  hipError_t e = launch_mfma<true>(A, ntt, s);
+  hipError_t e = launch_mfma<true>(A, ntt_r, ntt_s, s);
   if (e != hipSuccess) return e;
   // down: 128 output rows per block
   A.tiles_r = A.tiles_s = (H + kWaves * kMR * kTile - 1) / (kWaves * kMR * kTile);
-  if ((e = launch_mfma<false>(A, ntt, s)) != hipSuccess) return e;
+  if ((e = launch_mfma<false>(A, ntt_r, ntt_s, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bcombine, dim3((H + 255) / 256, B), dim3(256), 0, s, bb.out_s, bb.out_r, w,
                      x, add_in, residual ? 1 : 0, H, k, y);
   return hipGetLastError();
