@@ -171,16 +171,22 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
 // Its stages, for prefill through the slot pool: routing and the stable sort
 // of the assignments (seg / tiles / perm / pos_of in the layout); the routed
 // GEMMs (group == nullptr: every expert, experts + id * blob_e; else only the
-// group's experts, experts + slot * blob_e); the shared expert and the
-// combine into y.
+// group's experts, experts + slot * blob_e; with_shared: the shared expert's
+// gate/up runs in the same launch as the routed one); the shared expert (its
+// gate/up unless gateup_done) and the combine into y.
+struct SharedGateup {
+  const uint8_t* shared;
+  int T, Is;
+};
 hipError_t launch_prefill_route(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
                                 const float* logits_in, const uint16_t* router, const float* bias, int T,
                                 int E, int k, int H, int32_t* ids_out, float* w_out, hipStream_t s);
 hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int k, int H,
                                  int I, const uint8_t* experts, size_t blob_e, const SlotGroup* group,
-                                 hipStream_t s);
+                                 hipStream_t s, const SharedGateup* with_shared = nullptr);
 hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
-                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s);
+                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s,
+                                 bool gateup_done = false);
 
 // ---------------------------------------------------------------- batched decode
 // Stable sort of A assignments (token*k + rank, expert ids[a]) by expert:

@@ -245,14 +245,15 @@ struct GemmArgs {
   SlotGroup group;
 };
 
+// One block's tile (block index bid of its job); lds_b: two activation slice
+// buffers of kTM * kBRow bytes.
 template <bool GATEUP, bool ROUTED>
-__global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+__device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*lds_b)[kTM * kBRow]) {
   constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
   const int nrows = GATEUP ? G.inter : G.H;
   const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
-  const int mt = blockIdx.x / n_tiles_n;
-  const int nt = blockIdx.x % n_tiles_n;
+  const int mt = bid / n_tiles_n;
+  const int nt = bid % n_tiles_n;
   int r0, r_end;
   const uint8_t* blob;
   if (ROUTED) {
@@ -429,6 +430,25 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
   }
 }
 
+template <bool GATEUP, bool ROUTED>
+__global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+  gemm_tile<GATEUP, ROUTED>(G, blockIdx.x, lds_b);
+}
+
+// The shared expert's gate/up (dense over the tokens, its n_shared blocks
+// first) and the routed experts' gate/up in one launch: the two are
+// independent, and the shared blocks, few and long, would otherwise form a
+// launch of their own with a tail of one block per CU.
+__global__ __launch_bounds__(kThreadsGemm) void k_gemm_gateup2(GemmArgs R, GemmArgs Sh, int n_shared) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+  const int bid = blockIdx.x;
+  if (bid < n_shared)
+    gemm_tile<true, false>(Sh, bid, lds_b);
+  else
+    gemm_tile<true, true>(R, bid - n_shared, lds_b);
+}
+
 // Blocks along the weight rows of one GEMM (gate/up: row pairs; down: rows).
 int gemm_row_tiles(bool gateup, int H, int inter) {
   const int rows = gateup ? inter : H;
@@ -536,15 +556,38 @@ GemmArgs routed_args(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16
 }
 }  // namespace
 
+namespace {
+GemmArgs shared_gateup_args(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k, int H,
+                            int Is, const uint8_t* shared) {
+  GemmArgs gs{};
+  gs.H = H;
+  gs.k = k;
+  gs.A = reinterpret_cast<const __bf16*>(x_bf16);
+  gs.lda = H;
+  gs.blob = shared;
+  gs.inter = Is;
+  gs.M_dense = T;
+  gs.act = reinterpret_cast<__bf16*>(ws + L.act_s);
+  return gs;
+}
+}  // namespace
+
 hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int k, int H,
                                  int I, const uint8_t* experts, size_t blob_e, const SlotGroup* group,
-                                 hipStream_t s) {
+                                 hipStream_t s, const SharedGateup* with_shared) {
   GemmArgs g = routed_args(L, ws, x_bf16, k, H, I, experts, blob_e);
   if (group) {
     if (group->n < 1 || group->n > kMaxGroup) return hipErrorInvalidValue;
     g.group = *group;
   }
-  hipLaunchKernelGGL((k_gemm<true, true>), dim3(L.max_tiles * gemm_row_tiles(true, H, I)), dim3(kThreadsGemm), 0, s, g);
+  const int routed_blocks = L.max_tiles * gemm_row_tiles(true, H, I);
+  if (with_shared) {
+    const GemmArgs gs = shared_gateup_args(L, ws, x_bf16, with_shared->T, k, H, with_shared->Is, with_shared->shared);
+    const int n_shared = ((with_shared->T + kTM - 1) / kTM) * gemm_row_tiles(true, H, with_shared->Is);
+    hipLaunchKernelGGL(k_gemm_gateup2, dim3(n_shared + routed_blocks), dim3(kThreadsGemm), 0, s, g, gs, n_shared);
+  } else {
+    hipLaunchKernelGGL((k_gemm<true, true>), dim3(routed_blocks), dim3(kThreadsGemm), 0, s, g);
+  }
   // routed down: rows are the permuted activations, weighted by their routing weight
   GemmArgs d = g;
   d.A = reinterpret_cast<const __bf16*>(ws + L.act_r);
@@ -558,18 +601,11 @@ hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint
 }
 
 hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
-                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s) {
-  GemmArgs gs{};
-  gs.H = H;
-  gs.k = k;
-  gs.A = reinterpret_cast<const __bf16*>(x_bf16);
-  gs.lda = H;
-  gs.blob = shared;
-  gs.inter = Is;
-  gs.M_dense = T;
-  gs.act = reinterpret_cast<__bf16*>(ws + L.act_s);
-  // shared gate/up: dense over tokens
-  hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
+                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s, bool gateup_done) {
+  const GemmArgs gs = shared_gateup_args(L, ws, x_bf16, T, k, H, Is, shared);
+  // shared gate/up: dense over tokens (unless it ran with the routed one)
+  if (!gateup_done)
+    hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
   // shared down + combine into y (each token's routed rows in rank order)
   GemmArgs ds = gs;
   ds.A = reinterpret_cast<const __bf16*>(ws + L.act_s);
@@ -587,8 +623,9 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
                           const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
                           hipStream_t s) {
   hipError_t e = launch_prefill_route(L, ws, x_bf16, logits_in, router, bias, T, E, k, H, ids_out, w_out, s);
-  if (e == hipSuccess) e = launch_prefill_routed(L, ws, x_bf16, k, H, I, experts, blob_e, nullptr, s);
-  if (e == hipSuccess) e = launch_prefill_shared(L, ws, x_bf16, T, k, H, Is, shared, y, s);
+  const SharedGateup sg{shared, T, Is};
+  if (e == hipSuccess) e = launch_prefill_routed(L, ws, x_bf16, k, H, I, experts, blob_e, nullptr, s, &sg);
+  if (e == hipSuccess) e = launch_prefill_shared(L, ws, x_bf16, T, k, H, Is, shared, y, s, true);
   return e;
 }
 
