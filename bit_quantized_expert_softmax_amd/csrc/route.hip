@@ -24,7 +24,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;  // 2 waves (2 experts) per block: 64 blocks at E = 128
 constexpr int kWaves = kThreads / kWave;
 
 struct RouteArgs {
