@@ -82,12 +82,13 @@ __device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, i
   int32_t* lwhere = llast + S;   // [E]
   int32_t* lseen = lwhere + E;   // [E]
   __shared__ int32_t hit[kMaxTopK], nm_sh, victim_sh;
-  for (int i = tid; i < S; i += kThreads) {
+  const int nt = blockDim.x;
+  for (int i = tid; i < S; i += nt) {
     lexp[i] = C.expert[i];
     lfreq[i] = C.freq[i];
     llast[i] = C.last[i];
   }
-  for (int e = tid; e < E; e += kThreads) {
+  for (int e = tid; e < E; e += nt) {
     lwhere[e] = C.where[e];
     lseen[e] = 0;
   }
@@ -166,12 +167,12 @@ __device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, i
     }
     __syncthreads();
   }
-  for (int i = tid; i < S; i += kThreads) {
+  for (int i = tid; i < S; i += nt) {
     C.expert[i] = lexp[i];
     C.freq[i] = lfreq[i];
     C.last[i] = llast[i];
   }
-  for (int e = tid; e < E; e += kThreads) C.where[e] = lwhere[e];
+  for (int e = tid; e < E; e += nt) C.where[e] = lwhere[e];
   if (tid == 0) {
     const int nm = nm_sh;
     C.miss[0] = nm;
@@ -195,7 +196,7 @@ __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* s
   }
   __syncthreads();
   if (!is_last) return;
-  for (int f = threadIdx.x; f < A.E; f += kThreads)
+  for (int f = threadIdx.x; f < A.E; f += blockDim.x)
     zs[f] = __hip_atomic_load(A.z + static_cast<size_t>(tok) * A.E + f, __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -393,8 +394,12 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
 // of k_route_fused, so the logits (and the ids) are the same bits.
 constexpr int kEW = 4;
 
+// 4 waves per block (more blocks per token only add arrivals and input loads)
+constexpr int kTokWaves = 4;
+constexpr int kTokThreads = kTokWaves * kWave;
+
 template <bool HAS_ADD, bool RMS, int STEPS>
-__global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
+__global__ __launch_bounds__(kTokThreads) void k_route_tok(RouteArgs A) {
   extern __shared__ double zs[];  // [E] for the top-k of the last block
   __shared__ double sel_z[kMaxTopK];
   __shared__ int sel_e[kMaxTopK];
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
   const int lane = threadIdx.x & (kWave - 1);
   const int H = A.H, n8 = H / 8;
   const int b = blockIdx.y;
-  const int e0 = (blockIdx.x * kWaves + wave) * kEW;
+  const int e0 = (blockIdx.x * kTokWaves + wave) * kEW;
   const float* xb = A.x + static_cast<size_t>(b) * H;
   const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
 
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void k_route_tok(RouteArgs A) {
 #pragma unroll
     for (int t = 0; t < STEPS; ++t) {
       const int c = lane + kWave * t;
-      if (t % kWaves != wave || c >= n8) continue;
+      if (t % kTokWaves != wave || c >= n8) continue;
       uint32_t hw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -569,13 +574,13 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
   // batched router, a token's input held in registers (H <= 4096)
   const int steps = (H / 8 + kWave - 1) / kWave;
   if (B > 1 && ids && !udig && u16 && tsc && steps <= kMaxSteps) {
-    const dim3 grid((E + kWaves * kEW - 1) / (kWaves * kEW), B);
+    const dim3 grid((E + kTokWaves * kEW - 1) / (kTokWaves * kEW), B);
 #define MOE_ROUTE_TOK(A_, R_)                                                                        \
   do {                                                                                             \
-    if (steps <= 2) hipLaunchKernelGGL((k_route_tok<A_, R_, 2>), grid, dim3(kThreads), lds, s, A); \
-    else if (steps <= 4) hipLaunchKernelGGL((k_route_tok<A_, R_, 4>), grid, dim3(kThreads), lds, s, A); \
-    else if (steps <= 6) hipLaunchKernelGGL((k_route_tok<A_, R_, 6>), grid, dim3(kThreads), lds, s, A); \
-    else hipLaunchKernelGGL((k_route_tok<A_, R_, 8>), grid, dim3(kThreads), lds, s, A);             \
+    if (steps <= 2) hipLaunchKernelGGL((k_route_tok<A_, R_, 2>), grid, dim3(kTokThreads), lds, s, A); \
+    else if (steps <= 4) hipLaunchKernelGGL((k_route_tok<A_, R_, 4>), grid, dim3(kTokThreads), lds, s, A); \
+    else if (steps <= 6) hipLaunchKernelGGL((k_route_tok<A_, R_, 6>), grid, dim3(kTokThreads), lds, s, A); \
+    else hipLaunchKernelGGL((k_route_tok<A_, R_, 8>), grid, dim3(kTokThreads), lds, s, A);             \
   } while (0)
     if (add_in && rmsnorm) MOE_ROUTE_TOK(true, true);
     else if (add_in) MOE_ROUTE_TOK(true, false);
