@@ -99,3 +99,41 @@ def test_same_inputs_same_bits_across_split_counts():
     y1 = st.run(x, 2000)
     y2 = st.run(x, 2000)
     assert np.array_equal(y1, y2)
+
+
+def test_captured_step_replays_equal_eager_calls():
+    """A graph of two layers' attention steps at a fixed position, replayed
+    with new inputs, gives the eager calls' bits (and writes the same cache row)."""
+    a = GEMMA_ATTN
+    pos = 700
+    eager = [Step(a, layer=l, filled=pos) for l in range(2)]
+    graph = [Step(a, layer=l, filled=pos) for l in range(2)]
+    xg = torch.empty((a.hidden,), device=DEV)
+    mid = torch.empty_like(xg)
+    yg = torch.empty_like(xg)
+    cap = torch.cuda.Stream()
+
+    def run(steps, x, m, y, stream=None):
+        api.moe_attn_decode(a, steps[0].w, steps[0].kc, steps[0].vc, pos, x, m, steps[0].ws, stream=stream)
+        api.moe_attn_decode(a, steps[1].w, steps[1].kc, steps[1].vc, pos, m, y, steps[1].ws, stream=stream)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run(graph, xg, mid, yg, stream=cap)
+    torch.cuda.synchronize()
+    for t in range(3):
+        print(f"attn graph replay {t}", flush=True)
+        x = dev(gen.x_fp32(1, a.hidden, 5, sub=50 + t)[0])
+        xg.copy_(x)
+        g.replay()
+        torch.cuda.synchronize()
+        m2, y2 = torch.empty_like(x), torch.empty_like(x)
+        run(eager, x, m2, y2)
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y2), t
+        for se, sg in zip(eager, graph):
+            ke, ve = se.cache()
+            kg, vg = sg.cache()
+            assert np.array_equal(ke[:, pos], kg[:, pos]) and np.array_equal(ve[:, pos], vg[:, pos])
+    del g
