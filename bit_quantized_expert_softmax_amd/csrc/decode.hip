@@ -199,24 +199,18 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
                                                    const uint16_t* __restrict__ add_in,
                                                    int residual, float* __restrict__ y) {
   extern __shared__ uint4 lds_raw[];
-  __shared__ float wsh[kMaxTopK + 1];
-  __shared__ const uint8_t* srcb[kMaxTopK + 1];
   const int gi = S.I / kGroup;
   const int gsh = S.Is / kGroup;
   const int nga = S.k * gi + gsh;  // chunks of the virtual row
   float* part = reinterpret_cast<float*>(lds_raw);  // [kOutPerBlock][nga]
   const int n0 = blockIdx.x * kOutPerBlock;
   const int nout = S.H - n0 < kOutPerBlock ? S.H - n0 : kOutPerBlock;
-  if (threadIdx.x <= static_cast<unsigned>(S.k)) {
-    const int j = threadIdx.x;
-    srcb[j] = source_base(S, j);
-    wsh[j] = j < S.k ? w[j] : 1.0f;
-  }
-  __syncthreads();
   // Lane (o0, c) = (threadIdx / nga, threadIdx % nga) owns chunk c of the
   // virtual row for outputs o0, o0 + R, ... (R = kThreads / nga); it loads
   // that chunk's activation digits once, with the routing weight of the
-  // chunk's source folded into the scale.
+  // chunk's source folded into the scale. Each lane finds its source's
+  // address itself, so no barrier and no routing-weight load stands before
+  // the weight loads (the weight only scales the sum).
   const int R = kThreads / nga;
   const int c = threadIdx.x % nga;
   const int o0 = threadIdx.x / nga;
@@ -232,10 +226,12 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     inter = S.Is;
   }
   const BlobOffsets o = blob_offsets(S.H, inter);
-  const uint8_t* qb = srcb[j] + o.down_q + 16 * static_cast<size_t>(cc);
-  const uint16_t* sb = reinterpret_cast<const uint16_t*>(srcb[j] + o.down_s) + cc;
+  const uint8_t* srcj = source_base(S, j);
+  const uint8_t* qb = srcj + o.down_q + 16 * static_cast<size_t>(cc);
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(srcj + o.down_s) + cc;
   const DigitGroup xd = adig[c];  // first, as in the gate/up kernel
   const float xsa = asc[c];
+  const float wj = j < S.k ? w[j] : 1.0f;
   uint4 wv[NT];
   uint16_t sw[NT];
 #pragma unroll
@@ -247,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     sw[t] = sb[n * (inter / kGroup)];
   }
   __builtin_amdgcn_sched_barrier(0);
-  const float xs = xsa * wsh[j];
+  const float xs = xsa * wj;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int ob = o0 + R * t;
