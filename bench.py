@@ -154,7 +154,7 @@ def main():
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import ctypes as C
