@@ -47,16 +47,38 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
                                                      const DigitGroup* __restrict__ udig,
                                                      const float* __restrict__ usc,
                                                      DigitGroup* __restrict__ adig,
-                                                     float* __restrict__ asc, FillList F) {
+                                                     float* __restrict__ asc, FillList F, TopkPublish P) {
+  extern __shared__ uint4 lds_raw[];
+  __shared__ double sel_z[kMaxTopK];
+  __shared__ int sel_e[kMaxTopK];
+  const int ngu = S.H / kGroup;
+  int bx = blockIdx.x;
+  if (P.z) {
+    // the token's top-k and its publication to the host, ahead of the rest
+    if (bx == 0) {
+      double* zs = reinterpret_cast<double*>(reinterpret_cast<float*>(lds_raw) + 2 * kGroupRows * ngu + 2);
+      for (int f = threadIdx.x; f < P.E; f += kThreads) zs[f] = P.z[f];
+      __syncthreads();
+      topk_block(zs, P.E, P.k, sel_z, sel_e, P.ids, P.w, P.ids2, P.w2);
+      if (threadIdx.x == 0) {
+        // the release store orders the id stores before the sequence number
+        for (int j = 0; j < P.k; ++j)
+          __hip_atomic_store(P.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(P.seq_host, P.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      return;
+    }
+    bx -= 1;
+  }
   // fill blocks first (cache mode, fill-kernel option): block f copies its
   // share of blob f / blocks_per_blob from the pinned host store to the slot,
   // while the compute blocks of the same launch run
   const int nfill = F.n * F.blocks_per_blob;
-  if (static_cast<int>(blockIdx.x) < nfill) {
-    const int m = blockIdx.x / F.blocks_per_blob;
+  if (bx < nfill) {
+    const int m = bx / F.blocks_per_blob;
     const size_t n16 = F.bytes / 16;
     const size_t per = (n16 + F.blocks_per_blob - 1) / F.blocks_per_blob;
-    const size_t lo = (blockIdx.x % F.blocks_per_blob) * per;
+    const size_t lo = (bx % F.blocks_per_blob) * per;
     const size_t hi = lo + per < n16 ? lo + per : n16;
     const uint4* __restrict__ src;
     uint4* __restrict__ dst;
@@ -88,12 +110,8 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
     }
     return;
   }
-  const int bid = blockIdx.x - nfill;
-  extern __shared__ uint4 lds_raw[];
-  __shared__ double sel_z[kMaxTopK];
-  __shared__ int sel_e[kMaxTopK];
+  const int bid = bx - nfill;
   __shared__ float rowsum[2 * kGroupRows];
-  const int ngu = S.H / kGroup;
   float* part = reinterpret_cast<float*>(lds_raw);                          // [64][ngu]
   double* zs = reinterpret_cast<double*>(part + 2 * kGroupRows * ngu + 2);  // [E]
 
@@ -559,25 +577,34 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
 
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
-                             hipStream_t s, hipEvent_t t0, hipEvent_t t1, const FillList* fill) {
+                             hipStream_t s, hipEvent_t t0, hipEvent_t t1, const FillList* fill,
+                             const TopkPublish* topk) {
   FillList F{};
   if (fill && fill->n > 0) {
     if (fill->n > kMaxTopK || fill->blocks_per_blob < 1 || fill->bytes % 16) return hipErrorInvalidValue;
     F = *fill;
   }
+  TopkPublish P{};
+  if (topk) {
+    if (!topk->z || !topk->ids || !topk->w || !topk->ids_host || !topk->seq_host || topk->k < 1 ||
+        topk->k > kMaxTopK || topk->k > topk->E)
+      return hipErrorInvalidValue;
+    P = *topk;
+  }
   const int nr = do_routed ? (src.nsel > 0 ? src.nsel : src.k) * (src.I / kGroupRows) : 0;
   const int shared = src.Is / kGroupRows;
-  const int n = F.n * F.blocks_per_blob + nr + (do_shared ? shared : 0);
+  const int n = (topk ? 1 : 0) + F.n * F.blocks_per_blob + nr + (do_shared ? shared : 0);
   if (n == 0) return hipSuccess;
   const int ngu = src.H / kGroup;
-  const size_t lds = static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 + (src.z ? sizeof(double) * src.E : 0);
+  const int Ez = src.z ? src.E : (topk ? topk->E : 0);
+  const size_t lds = static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 + sizeof(double) * Ez;
   if (ngu > kThreads) return hipErrorInvalidValue;
   const int rows_per_pass = kThreads / ngu;
   const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
 #define MOE_GATEUP(NT)                                                                                   \
   do {                                                                                                   \
-    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F); \
-    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F);               \
+    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F, P); \
+    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F, P);               \
   } while (0)
   if (need <= 1) MOE_GATEUP(1);
   else if (need <= 2) MOE_GATEUP(2);

@@ -132,10 +132,25 @@ size_t dcache_lds_bytes(int n_slots, int E);
 // t0/t1 (optional, both or neither): events stamped by the dispatch itself at
 // the kernel's start and end (kernel time without the cost of separate records).
 // fill (optional): blobs copied by extra blocks of the same launch.
+// topk (optional, one token): an extra first block takes the top-k of the
+// logits z (written by the previous launch), writes ids / w (and the
+// optional copies), then the ids to host-coherent memory and seq to
+// *seq_host with a system-scope release store, while the other blocks run.
+struct TopkPublish {
+  const double* z;
+  int E, k;
+  int32_t* ids;
+  float* w;
+  int32_t* ids2;
+  float* w2;
+  int32_t* ids_host;
+  int32_t* seq_host;
+  int32_t seq;
+};
 hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_shared,
                              const DigitGroup* udig, const float* usc, DigitGroup* adig, float* asc,
                              hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr,
-                             const FillList* fill = nullptr);
+                             const FillList* fill = nullptr, const TopkPublish* topk = nullptr);
 // Down GEMVs of all k+1 sources, weighted combine (w [k], shared weight 1),
 // optional residual x' = x + add_in, y [H].
 hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGroup* adig,

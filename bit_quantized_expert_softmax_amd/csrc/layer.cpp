@@ -11,13 +11,15 @@
 // pinned host memory, and each miss is one host->HBM copy on a side stream.
 // The ids must reach the host before any copy can be issued (the routing of
 // a layer depends on the previous layer's output), so a cache-mode call
-// waits once: the routing kernel's last block writes the ids to
-// host-coherent memory and then a sequence word (system-scope release), and
+// waits once: a block takes the top-k of the router logits and writes the ids
+// to host-coherent memory and then a sequence word (system-scope release), and
 // the host spins on that word (bounded) instead of a device->host copy and an
-// event; the shared-expert gate/up kernel is enqueued before the wait so the
-// GPU is busy meanwhile. A slot overwritten for token t was last read by the
-// previous call's kernels, which precede this call's routing kernel on the
-// same stream and so have finished when the ids are published.
+// event. With copy-engine fills that block is the first of the shared-expert
+// gate/up launch (the router launch then only writes logits, and the shared
+// expert computes while the host waits and the copies run); with fill blocks
+// it is the routing kernel's last block. A slot overwritten for token t was
+// last read by the previous call's kernels, which precede this call's routing
+// kernel on the same stream and so have finished when the ids are published.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -518,16 +520,21 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   // one token, resident: the router only produces logits; each gate/up block
   // takes the top-k itself (no cross-block handshake on the critical path)
   const bool in_kernel_topk = !L->cache_mode && !grouped;
+  // one token, host-stepped cache with copy-engine fills: the router only
+  // produces logits too; an extra first block of the shared-expert gate/up
+  // launch takes the top-k and publishes the ids to the host, so the router
+  // launch ends sooner and the host's wait overlaps the shared expert
+  const bool deferred_topk = L->cache_mode && !L->dcache && !fill_kernel;
+  const bool router_topk = !in_kernel_topk && !deferred_topk;
   uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
   float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
   const int32_t seq = L->cache_mode ? L->seq + 1 : 0;
   HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
                                       grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
-                                      in_kernel_topk ? nullptr : ids,
-                                      in_kernel_topk ? nullptr : w, in_kernel_topk ? nullptr : ids_out,
-                                      in_kernel_topk ? nullptr : w_out,
-                                      L->cache_mode && !L->dcache ? L->ids_host : nullptr,
-                                      L->cache_mode && !L->dcache ? L->seq_host : nullptr, seq, s,
+                                      router_topk ? ids : nullptr, router_topk ? w : nullptr,
+                                      router_topk ? ids_out : nullptr, router_topk ? w_out : nullptr,
+                                      router_topk && L->cache_mode && !L->dcache ? L->ids_host : nullptr,
+                                      router_topk && L->cache_mode && !L->dcache ? L->seq_host : nullptr, seq, s,
                                       L->dcache ? &L->dc : nullptr), fn);
   if (L->cache_mode && !L->dcache) L->seq = seq;
   prof_end(L, 0, pb, s);
@@ -620,8 +627,9 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   if (!fill_kernel) {
     // the shared-expert gate/up runs while the host waits for the ids and
     // while the copy engine fills the misses
+    const moe::TopkPublish P{z, E, k, ids, w, ids_out, w_out, L->ids_host, L->seq_host, seq};
     const ProfPair p1 = prof_pair(L, 1);
-    HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b), fn);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, nullptr, &P), fn);
     prof_add(L, 1, p1);
   }
   if (!wait_routing(L)) return fail(MOE_EHIP, "%s: timed out waiting for the routing kernel", fn);
