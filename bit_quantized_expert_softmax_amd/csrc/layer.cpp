@@ -681,9 +681,20 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       src_d[j] = L->host_dev ? L->host_dev + static_cast<size_t>(ev[j].expert) * L->blob_e : nullptr;
     }
   }
+  for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
+  // the ranks whose experts were resident need not wait for the copies: their
+  // gate/up runs while the misses are copied, the missed ranks' after them
+  const bool split = !fused && n_miss > 0 && n_miss < k;
+  moe::SourceSet S_hit = S, S_miss = S;
+  if (split)
+    for (int j = 0; j < k; ++j) {
+      moe::SourceSet& T = ev[j].hit ? S_hit : S_miss;
+      T.rsel.v[T.nsel++] = j;
+    }
   hipError_t ce = hipSuccess;
   if (fill_kernel) {
     // the misses are copied by fill blocks of the shared-expert gate/up launch
+    // (with the hit ranks' gate/up blocks when split)
     moe::FillList F{};
     F.blocks_per_blob = 16;
     F.bytes = L->blob_e;
@@ -693,8 +704,8 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       F.dst[F.n] = L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e;
       ++F.n;
     }
-    const ProfPair p1 = prof_pair(L, 1);
-    ce = moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
+    const ProfPair p1 = split ? ProfPair{} : prof_pair(L, 1);
+    ce = moe::launch_ffn_gateup(split ? S_hit : S, split, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
     if (ce == hipSuccess) prof_add(L, 1, p1);
     if (ce == hipSuccess && L->d.store && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, s);
@@ -709,6 +720,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     }
     if (ce == hipSuccess && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, cp);
+      if (ce == hipSuccess && split) ce = moe::launch_ffn_gateup(S_hit, true, false, udig, usc, adg, asc, s);
       if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
       L->staging_busy = ce == hipSuccess && L->d.store;
     }
@@ -717,15 +729,15 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     moe::cache_assign(L->cache, L->cache_backup);
     return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
   }
-  for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
   if (fused) {
     const ProfPair p2 = prof_pair(L, 2);
     HIP_OR_FAIL(moe::launch_ffn_fused(S, udig, usc, adg, asc, w, x, add_in, res, y, bar_ctr, bar_err, s, p2.a,
                                       p2.b), fn);
     prof_add(L, 2, p2);
   } else {
-    const ProfPair p2 = prof_pair(L, 2);
-    HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+    // profiled only where the launch covers all k ranks
+    const ProfPair p2 = split ? ProfPair{} : prof_pair(L, 2);
+    HIP_OR_FAIL(moe::launch_ffn_gateup(split ? S_miss : S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
     prof_add(L, 2, p2);
     const ProfPair p3 = prof_pair(L, 3);
     HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
