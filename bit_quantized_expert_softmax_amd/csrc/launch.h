@@ -37,16 +37,20 @@ struct DevCache;  // device-stepped expert-slot cache (below)
 // E/16 blocks, four experts per wave). cnt holds B arrival counters, zero
 // before the launch and after it.
 // Top-k variant (ids != nullptr): the last block of each token's grid row
-// takes that token's top-k. With seq_host (B == 1 only) it also writes the
-// ids to ids_host (host-coherent memory) and then seq to *seq_host
-// (system-scope release), so the host can wait for them without a copy or an
-// event.
+// takes that token's top-k.
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s,
-                              const DevCache* dcache = nullptr);
+                              hipStream_t s);
+// Selection step of a one-token cache-mode call, after a logits-only
+// launch_route_layer: one block takes the top-k of z [E], writes ids / w (and
+// the optional copies), then steps the device-side cache (dcache) or
+// publishes the ids to host memory (ids_host, then seq to *seq_host with a
+// system-scope release store), or both or neither.
+hipError_t launch_route_select(const double* z, int E, int k, int32_t* ids, float* w, int32_t* ids2, float* w2,
+                               int32_t* ids_host, int32_t* seq_host, int32_t seq, const DevCache* dcache,
+                               hipStream_t s);
 // Standalone router: z[b][e] = sum_h u[b][h] * wr[e][h] (+ bias[e]) in fp64.
 hipError_t launch_route_logits(const float* u, int B, int H, const uint16_t* wr, const float* bias,
                                int E, double* z, hipStream_t s);
@@ -97,7 +101,7 @@ struct FillList {
 };
 
 // LFU (or LRU) expert-slot cache of one layer kept in device memory and
-// stepped by the router's last block, with the host cache's rule (lowest
+// stepped by one block after the token's top-k, with the host cache's rule (lowest
 // empty slot, else the smallest (frequency, last use, slot), or (last use,
 // slot) for LRU, among slots holding none of the token's ids; hits first).
 struct DevCache {

@@ -17,7 +17,7 @@
 // event. With copy-engine fills that block is the first of the shared-expert
 // gate/up launch (the router launch then only writes logits, and the shared
 // expert computes while the host waits and the copies run); with fill blocks
-// it is the routing kernel's last block. A slot overwritten for token t was
+// it is a one-block launch after the router. A slot overwritten for token t was
 // last read by the previous call's kernels, which precede this call's routing
 // kernel on the same stream and so have finished when the ids are published.
 #include <hip/hip_runtime.h>
@@ -525,17 +525,24 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   // launch takes the top-k and publishes the ids to the host, so the router
   // launch ends sooner and the host's wait overlaps the shared expert
   const bool deferred_topk = L->cache_mode && !L->dcache && !fill_kernel;
-  const bool router_topk = !in_kernel_topk && !deferred_topk;
+  // one token, cache mode otherwise (device-stepped cache, or fill blocks that
+  // need the misses before their launch): the logits-only router is followed
+  // by a one-block selection launch that takes the top-k and steps the cache
+  // or publishes the ids (shorter than a last-arriving block of the router)
+  const bool select_launch = L->cache_mode && !deferred_topk;
+  const bool router_topk = !in_kernel_topk && !deferred_topk && !select_launch;
   uint16_t* u16 = grouped ? L->at<uint16_t>(L->ws.u16) : nullptr;
   float* tsc = grouped ? L->at<float>(L->ws.tsc) : nullptr;
   const int32_t seq = L->cache_mode ? L->seq + 1 : 0;
   HIP_OR_FAIL(moe::launch_route_layer(x, add_in, B, H, rms, L->d.router, L->d.bias, E, k, u_out,
                                       grouped ? nullptr : udig, usc, u16, tsc, z, cnt,
                                       router_topk ? ids : nullptr, router_topk ? w : nullptr,
-                                      router_topk ? ids_out : nullptr, router_topk ? w_out : nullptr,
-                                      router_topk && L->cache_mode && !L->dcache ? L->ids_host : nullptr,
-                                      router_topk && L->cache_mode && !L->dcache ? L->seq_host : nullptr, seq, s,
-                                      L->dcache ? &L->dc : nullptr), fn);
+                                      router_topk ? ids_out : nullptr, router_topk ? w_out : nullptr, s),
+              fn);
+  if (select_launch)
+    HIP_OR_FAIL(moe::launch_route_select(z, E, k, ids, w, ids_out, w_out, L->dcache ? nullptr : L->ids_host,
+                                         L->dcache ? nullptr : L->seq_host, seq, L->dcache ? &L->dc : nullptr, s),
+                fn);
   if (L->cache_mode && !L->dcache) L->seq = seq;
   prof_end(L, 0, pb, s);
 

@@ -44,13 +44,13 @@ struct RouteArgs {
   int32_t* cnt;       // arrival counter, zero between calls
   int32_t *ids, *ids2;
   float *w, *w2;
-  // optional (top-k variant, B == 1): the ids also go to host-coherent memory,
-  // then seq_host is set to seq with a system-scope release store
+  // optional (selection launch, one token): the ids also go to host-coherent
+  // memory, then seq_host is set to seq with a system-scope release store
   int32_t* ids_host;
   int32_t* seq_host;
   int32_t seq;
-  // optional (top-k variant, B == 1): the layer's expert-slot cache is stepped
-  // on the device by the last block, right after the top-k
+  // optional (selection launch, one token): the layer's expert-slot cache is
+  // stepped right after the top-k
   DevCache dc;
   int use_dc;
 };
@@ -63,9 +63,6 @@ struct RouteArgs {
 // digit planes straight from registers.
 constexpr int kMaxSteps = 8;  // H <= 8 * 64 * 8 = 4096 in one batch
 
-// Top-k variant, after the block's logit stores (agent scope): the block
-// bumps its token's counter; the last of the token's gridDim.x blocks takes
-// the token's top-k (and publishes it to the host, B == 1). All threads call.
 // One step of the layer's expert-slot cache for the token's ids (sel_e, rank
 // order), by the whole block, on an LDS copy of the state: hits first (in
 // parallel, the ids are distinct), then the misses in rank order, each
@@ -182,6 +179,9 @@ __device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, i
   }
 }
 
+// Top-k variant, after the block's logit stores (agent scope): the block
+// bumps its token's counter; the last of the token's gridDim.x blocks takes
+// the token's top-k. All threads call.
 __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
   int& is_last = *is_last_p;
   const int nb = gridDim.x;
@@ -203,14 +203,6 @@ __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* s
   const size_t o = static_cast<size_t>(tok) * A.k;
   topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids + o, A.w + o, A.ids2 ? A.ids2 + o : nullptr,
              A.w2 ? A.w2 + o : nullptr);
-  if (A.use_dc) dcache_step(A.dc, sel_e, A.k, A.E, reinterpret_cast<int32_t*>(zs + A.E));
-  if (A.seq_host && threadIdx.x == 0) {
-    // one thread writes the ids and then publishes them: the release store
-    // orders its own earlier stores before the sequence number
-    for (int j = 0; j < A.k; ++j)
-      __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
 }
 
 template <bool HAS_ADD, bool RMS, bool TOPK>
@@ -555,21 +547,62 @@ __global__ __launch_bounds__(kThreads) void k_route_topk(const double* __restric
   topk_block(zs, E, k, sel_z, sel_e, ids + o, w + o, ids2 ? ids2 + o : nullptr, w2 ? w2 + o : nullptr);
 }
 
+// Selection step of one token (a block of kSelThreads): top-k of the logits,
+// then the device-side cache step and / or the publication of the ids.
+constexpr int kSelThreads = 1024;
+__global__ __launch_bounds__(kSelThreads) void k_route_select(RouteArgs A) {
+  extern __shared__ double zs[];  // [E], then the cache state
+  __shared__ double sel_z[kMaxTopK];
+  __shared__ int sel_e[kMaxTopK];
+  for (int f = threadIdx.x; f < A.E; f += kSelThreads) zs[f] = A.z[f];
+  __syncthreads();
+  topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids, A.w, A.ids2, A.w2);
+  if (A.use_dc) dcache_step(A.dc, sel_e, A.k, A.E, reinterpret_cast<int32_t*>(zs + A.E));
+  if (A.seq_host && threadIdx.x == 0) {
+    // one thread writes the ids and then publishes them: the release store
+    // orders its own earlier stores before the sequence number
+    for (int j = 0; j < A.k; ++j)
+      __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_route_select(const double* z, int E, int k, int32_t* ids, float* w, int32_t* ids2, float* w2,
+                               int32_t* ids_host, int32_t* seq_host, int32_t seq, const DevCache* dcache,
+                               hipStream_t s) {
+  if (!z || !ids || !w || k < 1 || k > kMaxTopK || k > E || (seq_host && !ids_host)) return hipErrorInvalidValue;
+  RouteArgs A{};
+  A.z = const_cast<double*>(z);  // read only by the selection kernel
+  A.E = E;
+  A.k = k;
+  A.ids = ids;
+  A.w = w;
+  A.ids2 = ids2;
+  A.w2 = w2;
+  A.ids_host = ids_host;
+  A.seq_host = seq_host;
+  A.seq = seq;
+  if (dcache) {
+    A.dc = *dcache;
+    A.use_dc = 1;
+  }
+  const size_t lds = sizeof(double) * E + (dcache ? dcache_lds_bytes(dcache->n_slots, E) : 0);
+  hipLaunchKernelGGL(k_route_select, dim3(1), dim3(kSelThreads), lds, s, A);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int H, bool rmsnorm,
                               const uint16_t* wr, const float* bias, int E, int k, float* u_out,
                               DigitGroup* udig, float* usc, uint16_t* u16, float* tsc, double* z,
                               int32_t* cnt, int32_t* ids, float* w, int32_t* ids2, float* w2,
-                              int32_t* ids_host, int32_t* seq_host, int32_t seq, hipStream_t s,
-                              const DevCache* dcache) {
-  if (seq_host && (B != 1 || !ids)) return hipErrorInvalidValue;
-  if (dcache && (B != 1 || !ids || !udig)) return hipErrorInvalidValue;
+                              hipStream_t s) {
   RouteArgs A{x, add_in, B, H, rmsnorm ? 1 : 0, wr, bias, E, k, u_out, udig, usc, u16, tsc, z, cnt,
-              ids, ids2, w, w2, ids_host, seq_host, seq, dcache ? *dcache : DevCache{}, dcache ? 1 : 0};
+              ids, ids2, w, w2, nullptr, nullptr, 0, DevCache{}, 0};
   const int blocks = (E + kWaves - 1) / kWaves;
-  // one token's logits, for the top-k (and the cache state for its step)
-  const size_t lds = sizeof(double) * E + (dcache ? dcache_lds_bytes(dcache->n_slots, E) : 0);
+  // one token's logits, for the top-k
+  const size_t lds = sizeof(double) * E;
   // a batch with its top-k, for the matrix-core path (no digit planes): the
   // batched router, a token's input held in registers (H <= 4096)
   const int steps = (H / 8 + kWave - 1) / kWave;
