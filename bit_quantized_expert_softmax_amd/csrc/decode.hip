@@ -42,7 +42,10 @@ __device__ __forceinline__ const uint8_t* source_base(const SourceSet& S, int j)
 }
 
 // Gate/up of one group of 32 (gate row i, up row i) pairs; NT tasks per lane.
-template <int NT>
+// PUB: block 0 takes the token's top-k and publishes it (P), the other blocks
+// shift down by one (a separate instantiation, so that the code of the
+// launches without it stays as it is).
+template <int NT, bool PUB>
 __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_blocks,
                                                      const DigitGroup* __restrict__ udig,
                                                      const float* __restrict__ usc,
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   __shared__ int sel_e[kMaxTopK];
   const int ngu = S.H / kGroup;
   int bx = blockIdx.x;
-  if (P.z) {
+  if constexpr (PUB) {
     // the token's top-k and its publication to the host, ahead of the rest
     if (bx == 0) {
       double* zs = reinterpret_cast<double*>(reinterpret_cast<float*>(lds_raw) + 2 * kGroupRows * ngu + 2);
@@ -601,10 +604,15 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
   if (ngu > kThreads) return hipErrorInvalidValue;
   const int rows_per_pass = kThreads / ngu;
   const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
-#define MOE_GATEUP(NT)                                                                                   \
+#define MOE_GATEUP_PUB(NT, PUB)                                                                          \
   do {                                                                                                   \
-    if (t0) hipExtLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F, P); \
-    else hipLaunchKernelGGL(k_gateup<NT>, dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F, P);               \
+    if (t0) hipExtLaunchKernelGGL((k_gateup<NT, PUB>), dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F, P); \
+    else hipLaunchKernelGGL((k_gateup<NT, PUB>), dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F, P);               \
+  } while (0)
+#define MOE_GATEUP(NT)                        \
+  do {                                        \
+    if (topk) MOE_GATEUP_PUB(NT, true);       \
+    else MOE_GATEUP_PUB(NT, false);           \
   } while (0)
   if (need <= 1) MOE_GATEUP(1);
   else if (need <= 2) MOE_GATEUP(2);
@@ -615,6 +623,7 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
   else if (need <= 16) MOE_GATEUP(16);
   else return hipErrorInvalidValue;  // H beyond what the LDS budget admits
 #undef MOE_GATEUP
+#undef MOE_GATEUP_PUB
   return hipGetLastError();
 }
 
