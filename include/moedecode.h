@@ -217,8 +217,8 @@ typedef struct moe_layer_desc {
   int32_t store_layer;
   int32_t cache_policy;         /* cache mode: MOE_POLICY_LFU (0) or MOE_POLICY_LRU */
   /* cache mode with experts_host in device-accessible pinned memory: 1 = the
-   * cache lives in device memory (in the workspace) and the routing kernel
-   * steps it, so a decode call waits for nothing on the host and can be
+   * cache lives in device memory (in the workspace) and a kernel after the
+   * router steps it, so a decode call waits for nothing on the host and can be
    * captured in a graph; the misses are then always copied by fill blocks
    * (as with MOE_F_FILL_KERNEL). Same rule, same trace, same bits as the host
    * cache. 0 = the host steps the cache. */
