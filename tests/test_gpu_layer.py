@@ -147,6 +147,32 @@ def test_fill_kernel_matches_copy_engine_bitwise():
 
 
 @pytest.mark.parametrize("flags", [0, api.MOE_F_FILL_KERNEL], ids=["copy_engine", "fill_kernel"])
+def test_cache_mode_matches_resident_bitwise(flags):
+    """Cache mode (top-k in its own block, the hit ranks' gate/up ahead of the
+    copies and the missed ranks' after them) gives the resident path's bits,
+    ids and weights, on tokens with all hits, all misses and a mix."""
+    sh = GEMMA_LAYER
+    d = layer_data(sh, 2)
+    bias = gen.zipf_bias(sh.n_experts, 2, 0)
+    R = Layer(sh, d, bias=bias)
+    C = Layer(sh, d, bias=bias, cache_slots=16)
+    xs = gen.x_fp32(12, sh.hidden, 2, sub=13)
+    kinds = set()
+    for t in range(12):
+        x = dev(xs[t:t + 1])
+        print(f"cache vs resident t={t} flags={flags}", flush=True)
+        yr, idr, wr, _, _ = run_decode(R, x)
+        yc, idc, wc, _, tr = run_decode(C, x, flags=flags, trace_k=sh.top_k)
+        hits = int(sum(e[2] for e in tr.tolist()))
+        kinds.add("all hit" if hits == sh.top_k else "all miss" if hits == 0 else "mixed")
+        assert np.array_equal(idr, idc) and np.array_equal(wr, wc), t
+        assert np.array_equal(yr, yc), t
+    assert {"all miss", "mixed"} <= kinds, kinds
+    R.close()
+    C.close()
+
+
+@pytest.mark.parametrize("flags", [0, api.MOE_F_FILL_KERNEL], ids=["copy_engine", "fill_kernel"])
 def test_file_store_matches_host_memory_bitwise(tmp_path, flags):
     """Misses read from an expert file (parallel pread into pinned staging,
     layer 1 of a 2-layer file) leave the same slots and give the same bits as
