@@ -704,6 +704,24 @@ def main():
         us_1 = api.moe_debug_read_floor(src, one, 176, fout, region_stride=stride, regions=nreg,
                                         reps=10 * nreg, timed=True)
         floor["one_load_per_lane_176x1024_us"] = us_1
+        # the same read-only stream at 2-16x the bytes per launch (8 loads per
+        # lane, as many 1024-thread blocks as that takes), rotating over 1 GiB:
+        # how much of the HBM peak one launch reaches as its size grows
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=devn)
+        bout = torch.zeros(4096 * 16, dtype=torch.int32, device=devn)  # 16 words per block, <= 4096 blocks
+        by_size = {}
+        for m in (1, 2, 4, 8, 16):
+            nb_m = fb * m
+            st_m = (nb_m + 255) // 256 * 256
+            reg_m = big.numel() // st_m
+            blk_m = (nb_m // 16 + 8 * 1024 - 1) // (8 * 1024)
+            assert blk_m <= 4096
+            api.moe_debug_read_floor(big, nb_m, blk_m, bout, region_stride=st_m, regions=reg_m, reps=reg_m)
+            us_m = api.moe_debug_read_floor(big, nb_m, blk_m, bout, region_stride=st_m, regions=reg_m,
+                                            reps=max(4 * reg_m, 20), timed=True)
+            by_size[f"{nb_m / 1e6:.1f}MB"] = {"blocks": blk_m, "us": us_m, "frac": nb_m / (us_m * 1e-6) / 8e12}
+        floor["by_launch_size"] = by_size
+        del big, bout
         detail["launch_floor"] = floor
         print(f"[bench] launch floor: {floor}", file=sys.stderr, flush=True)
 
