@@ -71,7 +71,8 @@ struct MArgs {
   uint16_t* act_s;       // [B][Is]   shared activations by token
   float* out_r;          // [B*k][H]
   float* out_s;          // [B][H]
-  int tiles_r, tiles_s;  // blocks per routed / shared segment
+  int tiles_r, tiles_s;  // blocks per routed / shared segment (row tiles x token groups)
+  int s_groups;          // the shared segment's token passes, split over this many blocks per row tile
 };
 
 // 8 signed nibbles (k = 0..7 in bits 4k..4k+3) times scale s, as fp16 in the
@@ -122,9 +123,10 @@ __device__ __forceinline__ void for_slots(std::integer_sequence<int, D...>, F&& 
 // 16 gate rows and the 16 matching up rows; else 32 consecutive down rows.
 // lds_slices: the two activation slice buffers, NTT * kTile * kBRow bytes
 // each; alist: NTT * kTile ints.
+// Passes p0 = first, first + stride, ... (in tokens) of the segment.
 template <bool GATEUP, int NTT, int DEPTH>
-__device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, uint8_t* lds_slices, int* alist,
-                                          int* wcnt) {
+__device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int first, int stride,
+                                          uint8_t* lds_slices, int* alist, int* wcnt) {
   static_assert(DEPTH >= 2 && DEPTH <= 8, "ring of 2..8 load units");
   uint8_t* const lds_b[2] = {lds_slices, lds_slices + NTT * kTile * kBRow};
   const bool routed = s < A.E;
@@ -166,7 +168,7 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, uint8
     return total;
   };
   const int m = routed ? scan(0, NTT * kTile) : A.B;
-  if (m == 0) return;  // uniform over the block
+  if (m <= first) return;  // uniform over the block
   const uint8_t* blob = routed ? A.experts + static_cast<size_t>(s) * A.blob_e : A.shared;
   const int inter = routed ? A.I : A.Is;
   const int K = GATEUP ? A.H : inter;
@@ -203,7 +205,7 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, uint8
     for (int c = lane; c < 2 * ngk; c += kWave) dst[c] = src[c < cmax ? c : cmax];
   }
 
-  for (int p0 = 0; p0 < m; p0 += NTT * kTile) {
+  for (int p0 = first; p0 < m; p0 += stride) {
     const int mt = m - p0 < NTT * kTile ? m - p0 : NTT * kTile;
     if (routed && p0 > 0) scan(p0, NTT * kTile);  // this pass's assignments
     // this thread's 16-byte chunks of a step slice (token = c / 16)
@@ -380,11 +382,14 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
   const int bx = blockIdx.x;
   const bool sh = bx < A.tiles_s;
   const int s = sh ? A.E : (bx - A.tiles_s) / A.tiles_r;
-  const int tile = sh ? bx : (bx - A.tiles_s) % A.tiles_r;
-  if (s < A.E)
-    mfma_body<GATEUP, NTT_R, DEPTH_R>(A, s, tile, lds_b, alist, wcnt);
-  else
-    mfma_body<GATEUP, NTT_S, DEPTH_S>(A, s, tile, lds_b, alist, wcnt);
+  if (s < A.E) {
+    mfma_body<GATEUP, NTT_R, DEPTH_R>(A, s, (bx - A.tiles_s) % A.tiles_r, 0, NTT_R * kTile, lds_b, alist, wcnt);
+  } else {
+    // row tile bx % rows, token group bx / rows of the shared segment
+    const int rows = A.tiles_s / A.s_groups;
+    mfma_body<GATEUP, NTT_S, DEPTH_S>(A, s, bx % rows, (bx / rows) * NTT_S * kTile,
+                                      A.s_groups * NTT_S * kTile, lds_b, alist, wcnt);
+  }
 }
 
 // y[t] = (x'[t] if residual) + out_s[t] + sum_j w[t][j] * out_r[t*k + j]
@@ -409,6 +414,7 @@ size_t mfma_static_lds(int ntt) { return 2 * static_cast<size_t>(ntt) * kTile * 
 size_t mfma_scale_lds(int K) { return static_cast<size_t>(kWaves) * kMR * kTile * (K / kGroup) * 2; }
 int tiles_per_pass(int B) { return B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4); }
 constexpr size_t kMaxBlockLds = 65536;
+constexpr bool kSharedSplit = true;
 
 // ntt_r: tiles per pass of the routed experts' blocks, ntt_s: of the shared
 // expert's; the launch's static LDS is that of the larger.
@@ -450,13 +456,16 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
   // SIMD, of the common case.
   const int ntt_s = tiles_per_pass((B + 3) / 4);
   const int ntt_r = tiles_per_pass(2 * ((B * k + E - 1) / E));
+  // the shared segment's passes, each in blocks of its own
+  A.s_groups = kSharedSplit ? (B + ntt_s * kTile - 1) / (ntt_s * kTile) : 1;
   // gate/up: 64 row pairs per block
   A.tiles_r = (I + kWaves * kTile - 1) / (kWaves * kTile);
-  A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile);
+  A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile) * A.s_groups;
   hipError_t e = launch_mfma<true>(A, ntt_r, ntt_s, s);
   if (e != hipSuccess) return e;
   // down: 128 output rows per block
-  A.tiles_r = A.tiles_s = (H + kWaves * kMR * kTile - 1) / (kWaves * kMR * kTile);
+  A.tiles_r = (H + kWaves * kMR * kTile - 1) / (kWaves * kMR * kTile);
+  A.tiles_s = A.tiles_r * A.s_groups;
   if ((e = launch_mfma<false>(A, ntt_r, ntt_s, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_bcombine, dim3((H + 255) / 256, B), dim3(256), 0, s, bb.out_s, bb.out_r, w,
                      x, add_in, residual ? 1 : 0, H, k, y);
