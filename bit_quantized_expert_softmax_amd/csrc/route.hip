@@ -404,6 +404,22 @@ __global__ __launch_bounds__(kTokThreads) void k_route_tok(RouteArgs A) {
   const float* xb = A.x + static_cast<size_t>(b) * H;
   const uint16_t* ab = HAS_ADD ? A.add_in + static_cast<size_t>(b) * H : nullptr;
 
+  // the rows of the wave's kEW experts first, all in one batch of loads with
+  // the token's input below (issued per expert next to its products, the
+  // compiler serialised the later experts' loads, one round trip each)
+  uint4 wv[kEW][STEPS];
+#pragma unroll
+  for (int j = 0; j < kEW; ++j) {
+    const int e = e0 + j < A.E ? e0 + j : A.E - 1;
+    const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      int c = lane + kWave * t;
+      c = c < n8 ? c : n8 - 1;
+      wv[j][t] = *reinterpret_cast<const uint4*>(row + 8 * c);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   float u[STEPS][8];
   float ss = 0.f;
 #pragma unroll
@@ -471,15 +487,11 @@ __global__ __launch_bounds__(kTokThreads) void k_route_tok(RouteArgs A) {
 #pragma unroll
   for (int j = 0; j < kEW; ++j) {
     const int e = e0 + j < A.E ? e0 + j : A.E - 1;
-    const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
     double acc = 0.0;
 #pragma unroll
     for (int t = 0; t < STEPS; ++t) {
-      int c = lane + kWave * t;
-      const bool valid = c < n8;
-      c = valid ? c : n8 - 1;
-      const uint4 wv = *reinterpret_cast<const uint4*>(row + 8 * c);
-      const uint32_t wp[4] = {wv.x, wv.y, wv.z, wv.w};
+      const bool valid = lane + kWave * t < n8;
+      const uint32_t wp[4] = {wv[j][t].x, wv[j][t].y, wv[j][t].z, wv[j][t].w};
       double part = 0.0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
