@@ -371,8 +371,13 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int f
 // once). The routed experts' blocks take NTT_R token tiles per pass (their
 // segments are short: B * k / E tokens on average), the shared expert's
 // blocks NTT_S (its segment holds all B tokens).
+// Waves per SIMD the compiler must leave room for: 4 (at most 128 registers)
+// for the one-tile kernels of B <= 64, whose gate/up otherwise takes 132
+// registers and 3 waves; no constraint for the larger tiles.
+template <int NTT_R, int NTT_S>
+constexpr int kMfmaWaves = NTT_R == 1 && NTT_S == 1 ? 4 : 1;
 template <bool GATEUP, int NTT_R, int DEPTH_R, int NTT_S, int DEPTH_S>
-__global__ __launch_bounds__(kThreads) void k_mfma(MArgs A) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMfmaWaves<NTT_R, NTT_S>))) void k_mfma(MArgs A) {
   constexpr int kNT = NTT_R > NTT_S ? NTT_R : NTT_S;
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2 * kNT * kTile * kBRow];
   __shared__ int alist[kNT * kTile];
