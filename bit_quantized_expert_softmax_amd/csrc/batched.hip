@@ -57,6 +57,9 @@ constexpr int kTile = 16;               // MFMA tile edge: rows and tokens
 constexpr int kStepK = 4 * kGroup;      // K per step: one group per 16-lane row
 constexpr int kBRow = kStepK * 2 + 16;  // LDS bytes per token of a step slice (padded)
 constexpr int kMR = 2;                  // 16-row weight tiles per wave
+// 16-byte scale chunks per lane and tile: a tile's 32 * K/32 scale bytes over
+// a wave, K <= kScaleIters * 64 * 16 = 4096
+constexpr int kScaleIters = 4;
 
 struct MArgs {
   const uint8_t* experts;
@@ -73,6 +76,7 @@ struct MArgs {
   float* out_s;          // [B][H]
   int tiles_r, tiles_s;  // blocks per routed / shared segment (row tiles x token groups)
   int s_groups;          // the shared segment's token passes, split over this many blocks per row tile
+  int early_scales;      // issue the scale loads before the scan of the ids (nearly every expert touched)
 };
 
 // 8 signed nibbles (k = 0..7 in bits 4k..4k+3) times scale s, as fp16 in the
@@ -167,8 +171,6 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int f
     }
     return total;
   };
-  const int m = routed ? scan(0, NTT * kTile) : A.B;
-  if (m <= first) return;  // uniform over the block
   const uint8_t* blob = routed ? A.experts + static_cast<size_t>(s) * A.blob_e : A.shared;
   const int inter = routed ? A.I : A.Is;
   const int K = GATEUP ? A.H : inter;
@@ -187,8 +189,15 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int f
   // cache lines per instruction for 128 bytes). Chunks are clamped to the
   // matrix's scale array; rows past it (and idle waves, which take the first
   // tile) get finite scales of other rows, whose results are not stored.
+  // With early_scales the scale loads are issued before the scan of the ids,
+  // so that their round trip and the scan's overlap; a block of an untouched
+  // expert then reads its scales for nothing, so small batches (many
+  // untouched experts) scan first.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_scales[];
   uint16_t* ssc = reinterpret_cast<uint16_t*>(lds_scales) + static_cast<size_t>(wave) * kMR * kTile * ngk;
+  u32x4 sv[kMR][kScaleIters];
+  const u32x4* ssrc[kMR];
+  int scmax[kMR];
 #pragma unroll
   for (int mr = 0; mr < kMR; ++mr) {
     const int t0r = GATEUP ? rbase : rbase + kTile * mr;  // first row of the tile
@@ -199,10 +208,32 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int f
     const size_t so = GATEUP ? (mr == 0 ? o.gate_s : o.up_s) : o.down_s;
     qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
     const u32x4* src = reinterpret_cast<const u32x4*>(blob + so + static_cast<size_t>(t0) * ngk * 2);
-    u32x4* dst = reinterpret_cast<u32x4*>(ssc + mr * kTile * ngk);
     const int t_rows = nrows - t0 < kTile ? nrows - t0 : kTile;  // 16: nrows, t0 multiples of 16
     const int cmax = t_rows * ngk / 8 - 1;                       // last chunk inside the scale array
-    for (int c = lane; c < 2 * ngk; c += kWave) dst[c] = src[c < cmax ? c : cmax];
+    ssrc[mr] = src;
+    scmax[mr] = cmax;
+  }
+  auto load_scales = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int mr = 0; mr < kMR; ++mr)
+#pragma unroll
+      for (int i = 0; i < kScaleIters; ++i) {
+        const int c = lane + kWave * i;
+        sv[mr][i] = ssrc[mr][c < scmax[mr] ? c : scmax[mr]];
+      }
+  };
+  if (A.early_scales) load_scales();
+  const int m = routed ? scan(0, NTT * kTile) : A.B;
+  if (m <= first) return;  // uniform over the block
+  if (!A.early_scales) load_scales();
+#pragma unroll
+  for (int mr = 0; mr < kMR; ++mr) {
+    u32x4* dst = reinterpret_cast<u32x4*>(ssc + mr * kTile * ngk);
+#pragma unroll
+    for (int i = 0; i < kScaleIters; ++i) {
+      const int c = lane + kWave * i;
+      if (c < 2 * ngk) dst[c] = sv[mr][i];
+    }
   }
 
   for (int p0 = first; p0 < m; p0 += stride) {
@@ -442,6 +473,9 @@ hipError_t launch_mfma(const MArgs& A, int ntt_r, int ntt_s, hipStream_t s) {
 }  // namespace
 
 bool batched_lds_fits(int H, int I, int Is, int max_B) {
+  // every K of the products within what a wave stages in kScaleIters chunks per lane
+  const int kmax = kScaleIters * kWave / 2 * kGroup;  // 2 * K/32 chunks <= kScaleIters * 64: K <= 4096
+  if (H > kmax || I > kmax || Is > kmax) return false;
   const size_t st = mfma_static_lds(tiles_per_pass(max_B));
   return st + mfma_scale_lds(H) <= kMaxBlockLds && st + mfma_scale_lds(I > Is ? I : Is) <= kMaxBlockLds;
 }
@@ -450,6 +484,7 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
                           size_t blob_e, int H, int I, int Is, int E, int k, int B,
                           const uint16_t* u16, const float* tsc, const int32_t* ids, const float* w,
                           const float* x, const uint16_t* add_in, bool residual, float* y, hipStream_t s) {
+  if (!batched_lds_fits(H, I, Is, B)) return hipErrorInvalidValue;
   MArgs A{experts, shared, blob_e, H, I, Is, E, k, B, ids, B * k, u16, tsc,
           bb.act_r, bb.act_s, bb.out_r, bb.out_s, 0, 0};
   // tokens per pass over a segment's weights: up to 64; a longer segment
@@ -463,6 +498,9 @@ hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, cons
   const int ntt_r = tiles_per_pass(2 * ((B * k + E - 1) / E));
   // the shared segment's passes, each in blocks of its own
   A.s_groups = kSharedSplit ? (B + ntt_s * kTile - 1) / (ntt_s * kTile) : 1;
+  // B*k assignments over E experts: at B*k >= 4E about 1 in 50 experts is
+  // untouched (B = 64: 3 of 128), at B*k = E about 1 in 3 (B = 16: 46)
+  A.early_scales = B * k >= 4 * E;
   // gate/up: 64 row pairs per block
   A.tiles_r = (I + kWaves * kTile - 1) / (kWaves * kTile);
   A.tiles_s = (Is + kWaves * kTile - 1) / (kWaves * kTile) * A.s_groups;
