@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--no-attn", action="store_true", help="skip the attention-step measurements")
     ap.add_argument("--no-device-cache", action="store_true",
                     help="skip the stack with the slot caches stepped on the device")
-    ap.add_argument("--probe", choices=["gateup", "copy"], default=None,
+    ap.add_argument("--probe", choices=["gateup", "copy", "batched"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
                          "tokens (the measured kernel included), 'copy' copies 1 GiB once")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("GU_FETCH", "GU_WRITE", "CP_FETCH", "CP_WRITE"),
@@ -176,6 +176,28 @@ def main():
         return
     sh = C2.shape
     H, E, k, I, Is = sh.hidden, sh.n_experts, sh.top_k, sh.inter, sh.shared_inter
+    if args.probe == "batched":
+        # batched decode at B = 64 over 4 resident layers in turn (1.7 GB of
+        # experts, so no step finds its weights in the last-level cache), for
+        # counter runs of the matrix-core kernels
+        devb, Bp = "cuda:0", 64
+        hb, keep = [], []
+        wsb = torch.zeros(api.moe_layer_workspace_bytes(sh, Bp, 0), dtype=torch.uint8, device=devb)
+        for l in range(4):
+            ex = torch.from_numpy(gen.expert_blobs(sh, C2.config_id, l)).to(devb)
+            rt = torch.from_numpy(gen.router(sh, C2.config_id, l).view(np.int16)).to(devb)
+            shb = torch.from_numpy(gen.shared_blob(sh, C2.config_id, l)).to(devb)
+            keep += [ex, rt, shb]
+            hb.append(api.moe_layer_create(sh, router=rt, shared_blob=shb, workspace=wsb, experts_dev=ex, max_B=Bp))
+        xb = torch.from_numpy(gen.x_fp32(Bp, H, 3, sub=Bp)).to(devb)
+        yb = torch.empty((Bp, H), device=devb)
+        for i in range(4 * args.warmup):
+            api.moe_layer_decode(hb[i % 4], xb, None, Bp, 0, yb)
+        torch.cuda.synchronize()
+        for h in hb:
+            api.moe_layer_destroy(h)
+        print(f"[bench] probe: {4 * args.warmup} batched steps at B = {Bp}", file=sys.stderr, flush=True)
+        return
     Lyr, T, S = args.layers, args.tokens, args.slots
     cid = C2.config_id
     devn = "cuda:0"

@@ -82,13 +82,18 @@ struct MArgs {
 // 8 signed nibbles (k = 0..7 in bits 4k..4k+3) times scale s, as fp16 in the
 // order (0,4,1,5,2,6,3,7).
 __device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
-  const uint32_t x = w ^ 0x88888888u;  // nibble n -> n + 8 (unsigned)
   const f16x2 bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
   const f16x2 sc = {s, s};
-  const f16x2 h0 = (__builtin_bit_cast(f16x2, (x & 0x000F000Fu) | 0x64006400u) - bias) * sc;
-  const f16x2 h1 = (__builtin_bit_cast(f16x2, ((x >> 4) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
-  const f16x2 h2 = (__builtin_bit_cast(f16x2, ((x >> 8) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
-  const f16x2 h3 = (__builtin_bit_cast(f16x2, ((x >> 12) & 0x000F000Fu) | 0x64006400u) - bias) * sc;
+  // the two nibbles at bits 4i and 16 + 4i: (b & 0xF) ^ 8 is n + 8 for the
+  // two's complement nibble n, and the same xor sets the exponent bits of
+  // 1024 (0x6400), so one and-xor (v_bitop3) gives fp16(1024 + n + 8)
+  auto pair = [&](uint32_t v) __attribute__((always_inline)) {
+    return (__builtin_bit_cast(f16x2, (v & 0x000F000Fu) ^ 0x64086408u) - bias) * sc;
+  };
+  const f16x2 h0 = pair(w);
+  const f16x2 h1 = pair(w >> 4);
+  const f16x2 h2 = pair(w >> 8);
+  const f16x2 h3 = pair(w >> 12);
   return f16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
