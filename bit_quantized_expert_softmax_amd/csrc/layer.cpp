@@ -133,6 +133,12 @@ struct moe_layer {
   int32_t seq = 0;              // sequence number of the last routing published
   const uint8_t* host_dev = nullptr;  // device address of experts_host (fill-kernel option)
   hipEvent_t ev_fill = nullptr;
+  // a second copy stream of the handle's own: misses alternate between the
+  // caller's copy stream and this one, so two copy engines overlap each
+  // copy's fixed cost (ev_fill2: its copies of the last call)
+  hipStream_t copy2 = nullptr;
+  hipEvent_t ev_fill2 = nullptr;
+  bool fill2_pending = false;
   // file store (cache mode): the misses are read into pinned staging first
   uint8_t* staging = nullptr;            // [kMaxTopK][stride]
   const uint8_t* staging_dev = nullptr;  // its device address (fill-kernel option)
@@ -359,6 +365,8 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
       (void)hipGetLastError();  // a failed query leaves the option unavailable, not an error
     }
     e = hipEventCreateWithFlags(&L->ev_fill, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_fill2, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&L->copy2, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_pool, hipEventDisableTiming);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
     if (max_T > 0) {
@@ -402,6 +410,8 @@ void moe_layer_destroy(moe_layer* L) {
   if (L->seg_host) (void)hipHostFree(L->seg_host);
   if (L->ev_pool) (void)hipEventDestroy(L->ev_pool);
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
+  if (L->ev_fill2) (void)hipEventDestroy(L->ev_fill2);
+  if (L->copy2) (void)hipStreamDestroy(L->copy2);
   for (auto& v : L->rec)
     for (auto& p : v) {
       (void)hipEventDestroy(p.first);
@@ -655,12 +665,14 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   if (L->d.store && n_miss > 0) {
     // the staging's previous copies (this handle's last call) must be done
     if (L->staging_busy) {
-      const hipError_t se = hipEventSynchronize(L->ev_fill);
+      hipError_t se = hipEventSynchronize(L->ev_fill);
+      if (se == hipSuccess && L->fill2_pending) se = hipEventSynchronize(L->ev_fill2);
       if (se != hipSuccess) {
         moe::cache_assign(L->cache, L->cache_backup);
         return fail(MOE_EHIP, "%s: waiting for the staging: %s", fn, hipGetErrorString(se));
       }
       L->staging_busy = false;
+      L->fill2_pending = false;
     }
     int32_t mexp[moe::kMaxTopK];
     void* mdst[moe::kMaxTopK];
@@ -720,16 +732,22 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     }
   } else {
     hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
-    for (int j = 0; j < k && ce == hipSuccess; ++j) {
+    bool used2 = false;
+    for (int j = 0, m = 0; j < k && ce == hipSuccess; ++j) {
       if (ev[j].hit) continue;
+      const bool second = (m++ & 1) != 0;  // every other miss on the second copy stream
+      used2 = used2 || second;
       ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src_h[j], L->blob_e,
-                          hipMemcpyHostToDevice, cp);
+                          hipMemcpyHostToDevice, second ? L->copy2 : cp);
     }
     if (ce == hipSuccess && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, cp);
+      if (ce == hipSuccess && used2) ce = hipEventRecord(L->ev_fill2, L->copy2);
       if (ce == hipSuccess && split) ce = moe::launch_ffn_gateup(S_hit, true, false, udig, usc, adg, asc, s);
       if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
+      if (ce == hipSuccess && used2) ce = hipStreamWaitEvent(s, L->ev_fill2, 0);
       L->staging_busy = ce == hipSuccess && L->d.store;
+      L->fill2_pending = L->staging_busy && used2;
     }
   }
   if (ce != hipSuccess) {
@@ -814,7 +832,9 @@ moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logit
         if (ce == hipSuccess && L->d.store) {
           if (L->staging_busy) {
             ce = hipEventSynchronize(L->ev_fill);
+            if (ce == hipSuccess && L->fill2_pending) ce = hipEventSynchronize(L->ev_fill2);
             L->staging_busy = false;
+            L->fill2_pending = false;
           }
           int32_t mexp[moe::kMaxGroup];
           void* mdst[moe::kMaxGroup];

@@ -207,7 +207,9 @@ typedef struct moe_layer_desc {
   const uint8_t* experts_host;  /* cache mode: pinned host [E][blob]; else NULL  */
   uint8_t* slot_pool;           /* cache mode: dev [n_slots][blob]; else NULL    */
   int32_t n_slots;              /* cache mode: k <= n_slots <= E                 */
-  void* copy_stream;            /* cache mode: hipStream_t for the miss copies   */
+  void* copy_stream;            /* cache mode: hipStream_t for the miss copies
+                                   (decode alternates the misses between it and a
+                                   second copy stream the handle creates)        */
   void* workspace;              /* dev, moe_layer_workspace_bytes bytes          */
   size_t workspace_bytes;
   /* cache mode, instead of experts_host: the misses are read from this store
@@ -298,7 +300,8 @@ moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, i
  * same tolerance, and its ids are the same. Cache mode requires B == 1 and
  * blocks the calling thread once, until the token's ids are on the host; it
  * returns with the miss copies and the expert kernels enqueued (the copies on
- * copy_stream, ordered before the expert kernels by an event; with
+ * copy_stream and the handle's second copy stream, every other miss on each,
+ * ordered before the expert kernels by events; with
  * MOE_F_FILL_KERNEL the copies are fill blocks of the shared-expert launch on
  * stream). */
 moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in, int32_t B,
