@@ -177,6 +177,13 @@ def test_gpu_entry_points_reject_bad_arguments_before_enqueue(tmp_path):
     assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 64, 0, C.byref(h)) == -2
     assert "LDS" in api.moe_last_error()
     assert lib.moe_layer_create(C.byref(wide), C.byref(d2), 1, 0, C.byref(h)) == -1
+    # batched decode stages at most 4 chunks of scales per lane and tile: a
+    # product with K above 4096 (here the shared expert's down) is refused too
+    deep = api.make_shape(SMALL_LAYER)
+    deep.shared_inter = 4352
+    assert lib.moe_layer_create(C.byref(deep), C.byref(d2), 16, 0, C.byref(h)) == -2
+    assert "4096" in api.moe_last_error()
+    assert lib.moe_layer_create(C.byref(deep), C.byref(d2), 1, 0, C.byref(h)) == -1
     assert lib.moe_layer_decode(None, 16, None, 1, 0, 32, None, None, None, None, None, None) == -1
     # attention step: shapes, positions, alignment and workspace size are
     # checked before anything is enqueued
