@@ -138,6 +138,81 @@ def summarize_pmc(dirs):
                     "algorithmic bytes per launch 17,875,968"}
 
 
+# ---------------------------------------------------------------- CPU baseline workers
+# The oracle timed on the host: each spawned worker (no GPU use) builds one
+# layer of the stack from the seeded generators, then runs random teacher-
+# forced (token, layer) units of it for a fixed wall time with one BLAS
+# thread; the units are independent, so the workers together use the cores.
+_CPU = {}
+
+
+def _cpu_init(counter, layers, tokens, cid):
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from synth import gen
+    from synth.configs import C2
+    with counter.get_lock():
+        idx = counter.value
+        counter.value += 1
+    sh = C2.shape
+    l = idx % layers
+    _CPU["lim"] = threadpool_limits(1)
+    _CPU["sh"] = sh
+    _CPU["lay"] = {"router": gen.router(sh, cid, l), "bias": gen.zipf_bias(sh.n_experts, cid, l),
+                   "shared": gen.shared_blob(sh, cid, l), "experts": gen.expert_blobs(sh, cid, l)}
+    _CPU["x"] = gen.x_fp32(tokens, sh.hidden, cid)
+    _CPU["eps"] = np.ascontiguousarray(gen.eps_fp16(layers, tokens, sh.hidden, cid)[l])
+    _CPU["idx"] = idx
+
+
+def _cpu_run(args):
+    import numpy as np
+
+    from oracle import moe as omoe
+    seconds, seed = args
+    rng = np.random.default_rng(seed)
+    t0 = time.time()
+    units = 0
+    while time.time() - t0 < seconds:
+        t = int(rng.integers(0, _CPU["x"].shape[0]))
+        omoe.stack_layer_step(_CPU["x"][t], _CPU["eps"][t], _CPU["sh"], _CPU["lay"])
+        units += 1
+    return t0, time.time(), units
+
+
+def cpu_baseline(layers, tokens, cid, seconds):
+    """fp64 oracle rate in tokens/s on a pool of host cores (at most 16)."""
+    import multiprocessing as mp
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(16, avail))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    ctx = mp.get_context("spawn")
+    counter = ctx.Value("i", 0)
+    with ctx.Pool(workers, initializer=_cpu_init, initargs=(counter, layers, tokens, cid)) as pool:
+        # one untimed unit per worker first, so every worker has built its layer
+        pool.map(_cpu_run, [(0.0, i) for i in range(workers)], chunksize=1)
+        res = pool.map(_cpu_run, [(seconds, 100 + i) for i in range(workers)], chunksize=1)
+    units = sum(r[2] for r in res)
+    wall = max(r[1] for r in res) - min(r[0] for r in res)
+    return {"value": units / wall / layers, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{units} random teacher-forced (token, layer) units of the {layers}-layer stack at full "
+                      f"shape, fp64 numpy, on {workers} worker processes with one BLAS thread each "
+                      f"({avail} cores available, os.cpu_count() = {os.cpu_count()}, CPU: {model}), "
+                      f"{wall:.1f}s wall; tokens/s = units/s / {layers}",
+            "cpu_model": model}
+
+
 def load_traffic():
     """The committed counter summary if it was taken on the current kernel source."""
     try:
@@ -326,6 +401,70 @@ def main():
         },
         "down_combine_GBps": down_bytes / (us_dn * 1e-6) / 1e9 if us_dn > 0 else None,
     }
+
+    # ---------------------------------------------------------------- stage times
+    # A few more tokens with MOE_F_STAGE_TIMES (each call then waits for its
+    # own work, so this pass is slower than the headline): per layer call the
+    # routing latency until the ids are on the host, the misses' copy time,
+    # the compute stream's wait for the copies and the call's GPU time.
+    st_t = api.moe_decode_stats()
+    acc = {"route": 0.0, "fill": 0.0, "wait": 0.0, "total": 0.0, "calls": 0, "miss_calls": 0, "misses": 0}
+    t_base = args.warmup + args.steps + 16
+    for t in range(t_base, t_base + 8):
+        tt = t % T
+        src = xp0 + tt * H * 4
+        for l in range(Lyr):
+            dst = hp[l & 1]
+            m0 = st_t.misses
+            rc = decode(handles[l], src, ep0 + (l * T + tt) * H * 2, 1, flags | api.MOE_F_STAGE_TIMES, dst, None,
+                        None, None, None, C.byref(st_t), sp)
+            if rc:
+                raise api.MoeError(rc, "moe_layer_decode", api.moe_last_error())
+            src = dst
+            nm = st_t.misses - m0
+            acc["route"] += st_t.ms_route
+            acc["wait"] += st_t.ms_wait_fill
+            acc["total"] += st_t.ms_total
+            acc["calls"] += 1
+            if nm:
+                acc["fill"] += st_t.ms_fill
+                acc["miss_calls"] += 1
+                acc["misses"] += nm
+    torch.cuda.synchronize()
+    detail["stage_times_ms"] = {
+        "route_to_host_per_layer": acc["route"] / acc["calls"],
+        "fill_per_layer_with_misses": acc["fill"] / max(acc["miss_calls"], 1),
+        "fill_per_missed_expert": acc["fill"] / max(acc["misses"], 1),
+        "wait_fill_per_layer": acc["wait"] / acc["calls"],
+        "gpu_per_layer": acc["total"] / acc["calls"],
+        "layer_calls": acc["calls"], "misses": acc["misses"],
+        "note": "MOE_F_STAGE_TIMES pass of 8 tokens after the timed region (each call synchronises)"}
+
+    # ---------------------------------------------------------------- link-bound ceiling
+    # The copy engines alone: 8 expert blobs from pinned host memory to HBM,
+    # alternating over two streams as the decode does, repeated; the stack
+    # cannot beat H2D bytes per token / this rate.
+    cp_dst = torch.empty((8, blob), dtype=torch.uint8, device=devn)
+    cp_s2 = torch.cuda.Stream()
+    hsrc = layers[0]["host"]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_rep = 12
+    for r in range(n_rep):
+        for j in range(8):
+            st_ = copy_stream if j % 2 == 0 else cp_s2
+            with torch.cuda.stream(st_):
+                cp_dst[j].copy_(hsrc[(8 * r + j) % E], non_blocking=True)
+    torch.cuda.synchronize()
+    el_cp = time.perf_counter() - t0
+    copy_gbps = n_rep * 8 * blob / el_cp / 1e9
+    del cp_dst
+    h2d_tok = h2d / args.steps
+    ceil_tok = copy_gbps * 1e9 / h2d_tok if h2d_tok > 0 else None
+    detail["link_bound"] = {"h2d_GBps_copy_engines": copy_gbps, "h2d_MB_per_token": h2d_tok / 1e6,
+                            "ceiling_tokens_per_s": ceil_tok,
+                            "frac_of_ceiling": tok_s / ceil_tok if ceil_tok else None,
+                            "note": "ceiling = H2D bytes per token / rate of 8-blob copies on two streams alone"}
 
     # ---------------------------------------------------------------- other fill variant
     # Same stack, caches emptied, misses filled the other way (fill blocks of
@@ -851,25 +990,8 @@ def main():
     # ---------------------------------------------------------------- oracle on host cores
     cpu = None
     if not args.no_cpu:
-        from threadpoolctl import threadpool_info
-
-        from oracle import moe as omoe
-        units = 0
-        t0 = time.perf_counter()
-        rng = np.random.default_rng(0)
-        while time.perf_counter() - t0 < args.cpu_seconds:
-            t = int(rng.integers(0, T))
-            l = int(rng.integers(0, Lyr))
-            d = layers[l]
-            lay = {"router": d["router_np"], "bias": d["bias_np"], "shared": d["shared_np"],
-                   "experts": d["host"].numpy()}
-            omoe.stack_layer_step(x_np[t], eps_np[l, t], sh, lay)
-            units += 1
-        el_c = time.perf_counter() - t0
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        cpu = {"value": units / el_c / Lyr, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"{units} random (token, layer) units of the 30-layer stack at full shape, "
-                         f"fp64 numpy, {el_c:.1f}s; tokens/s = units/s / {Lyr}"}
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(Lyr, T, cid, args.cpu_seconds)
 
     traffic = load_traffic()
     if traffic:

@@ -49,7 +49,9 @@ class moe_layer_desc(C.Structure):
 
 
 class moe_decode_stats(C.Structure):
-    _fields_ = [("hits", C.c_int64), ("misses", C.c_int64), ("h2d_bytes", C.c_int64), ("calls", C.c_int64)]
+    _fields_ = [("hits", C.c_int64), ("misses", C.c_int64), ("h2d_bytes", C.c_int64), ("calls", C.c_int64),
+                ("ms_route", C.c_float), ("ms_fill", C.c_float), ("ms_wait_fill", C.c_float),
+                ("ms_total", C.c_float)]
 
 
 class moe_kernel_time(C.Structure):
@@ -83,12 +85,11 @@ SIGNATURES = {
                                     P(moe_cache_event), P(moe_decode_stats), vp]),
     "moe_layer_prefill": (c_status, [vp, vp, vp, C.c_int32, vp, vp, vp, vp]),
     "moe_layer_prefill_chunk": (c_status, [vp, C.c_int32]),
+    "moe_debug_fail_copy": (c_status, [vp, C.c_int32]),
     "moe_layer_profile": (c_status, [vp, C.c_int32]),
     "moe_layer_profile_kinds": (c_status, [vp, C.c_uint32, C.c_int32, C.c_int32]),
     "moe_layer_profile_read": (c_status, [vp, C.c_int32, P(moe_kernel_time)]),
     "moe_debug_unpack_q4": (c_status, [P(moe_q4), C.c_int32, C.c_int32, vp, vp]),
-    "moe_layer_fused": (C.c_int32, [vp]),
-    "moe_layer_check": (c_status, [vp, vp]),
     "moe_layer_cache_state": (c_status, [vp, vp, vp, vp, C.c_int32, vp, vp, vp, vp]),
     "moe_attn_workspace_bytes": (c_status, [P(moe_attn_shape), P(C.c_size_t)]),
     "moe_attn_decode": (c_status, [P(moe_attn_shape), P(moe_attn_weights), vp, vp, C.c_int32, vp, vp, vp,

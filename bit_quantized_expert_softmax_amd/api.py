@@ -16,7 +16,7 @@ from . import _lib as L
 MOE_F_RMSNORM_IN = 1
 MOE_F_RESIDUAL = 2
 MOE_F_FILL_KERNEL = 4
-MOE_F_FUSED = 8
+MOE_F_STAGE_TIMES = 16
 MOE_POLICY_LFU = 0
 MOE_POLICY_LRU = 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_ESHAPE", -3: "MOE_EALIGN", -4: "MOE_EHIP",
@@ -228,14 +228,6 @@ def moe_layer_cache(h):
     return lib().moe_layer_cache(h)
 
 
-def moe_layer_fused(h) -> bool:
-    return bool(lib().moe_layer_fused(h))
-
-
-def moe_layer_check(h, stream=None) -> None:
-    _check(lib().moe_layer_check(h, _stream(stream)), "moe_layer_check")
-
-
 def moe_layer_cache_state(h, n_slots, stream=None):
     """(expert, freq, last, hits, misses, steps) of the handle's slot cache."""
     ex = np.zeros(n_slots, np.int32)
@@ -261,6 +253,10 @@ def moe_layer_decode(h, x, add_in, B, flags, y, ids_out=None, w_out=None, u_out=
 
 def moe_layer_prefill_chunk(h, tokens: int) -> None:
     _check(lib().moe_layer_prefill_chunk(h, tokens), "moe_layer_prefill_chunk")
+
+
+def moe_debug_fail_copy(h, nth: int) -> None:
+    _check(lib().moe_debug_fail_copy(h, nth), "moe_debug_fail_copy")
 
 
 def moe_layer_prefill(h, x_bf16, logits_in, T, y, ids_out=None, w_out=None, stream=None):

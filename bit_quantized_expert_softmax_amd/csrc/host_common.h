@@ -26,6 +26,9 @@ inline moe_status fail(moe_status code, const char* fmt, ...) {
 
 // Copies the whole state of one cache into another of the same size.
 void cache_assign(moe_cache* dst, const moe_cache* src);
+// Empties one slot (expert -1, frequency 0, never used), as if it had never
+// been filled; the counters and the step are unchanged.
+void cache_clear_slot(moe_cache* c, int32_t slot);
 
 inline void clear_error() { last_error_text().clear(); }
 

@@ -115,18 +115,6 @@ struct DevCache {
   int32_t* ev;        // [k][4]: expert, slot, hit, evicted
   int n_slots, policy;
 };
-// Routed gate/up and down + combine in one launch with a grid barrier (cache
-// mode, one token; the shared expert's gate/up already ran). Only where every
-// block of the grid is resident at once: ffn_fused_fits (on the current
-// device). ctr: a 64-bit ticket counter in device memory, zero at creation
-// and never reset; err: set to 1 if a barrier wait gives up (about 1 s).
-int ffn_fused_grid(int H, int k, int I);
-bool ffn_fused_fits(int H, int k, int I, int Is);
-hipError_t launch_ffn_fused(const SourceSet& S, const DigitGroup* udig, const float* usc, DigitGroup* adig,
-                            float* asc, const float* w, const float* x, const uint16_t* add_in, bool residual,
-                            float* y, unsigned long long* ctr, int* err, hipStream_t s, hipEvent_t t0 = nullptr,
-                            hipEvent_t t1 = nullptr);
-
 // LDS bytes the step needs beyond the router's own.
 size_t dcache_lds_bytes(int n_slots, int E);
 

@@ -42,8 +42,6 @@ struct WsLayout {
   // device-stepped slot cache: counters, per-slot and per-expert arrays, the
   // call's slot per rank, miss list and events
   size_t dc;
-  // fused expert FFN: grid-barrier ticket counter (8 bytes) and error flag
-  size_t bar;
   // batched decode (max_B > 1): fp16 inputs and per-assignment outputs
   size_t out_r, out_s, u16, tsc, act;
   size_t total;
@@ -93,7 +91,6 @@ WsLayout ws_layout(const moe_shape& sh, int maxB, int maxT) {
   L.asc = take(B * npos * 4);
   L.cnt = take(B * 4);  // router arrival counters, one per token
   L.dc = take(dcache_region_bytes(static_cast<int>(E)));
-  L.bar = take(16);
   L.pre = take(maxT > 0 ? prefill_layout(maxT, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                          sh.shared_inter).total
                         : 0);
@@ -121,7 +118,6 @@ struct moe_layer {
   bool cache_mode = false;
   bool dcache = false;     // the slot cache is stepped on the device
   moe::DevCache dc{};
-  bool fused = false;      // MOE_F_FUSED can take effect (cache mode, B = 1)
   int max_B = 0, max_T = 0;
   moe_cache* cache = nullptr;
   moe_cache* cache_backup = nullptr;
@@ -148,6 +144,13 @@ struct moe_layer {
   int32_t* seg_host = nullptr;    // pinned, the chunk's expert offsets [E+1]
   int32_t prefill_chunk = 128;    // tokens per chunk (the pages' value), at most max_T
   hipEvent_t ev_pool = nullptr;   // the pool's readers (kernels on the call's stream) are done
+  // test support: the fail_copy_in-th miss copy from now on fails before it
+  // is issued, as if the runtime had refused it (0 = off)
+  int32_t fail_copy_in = 0;
+  // stage times (MOE_F_STAGE_TIMES): start of the call on the stream, the two
+  // copy streams' first and last copy, the stream's wait for them, the end
+  hipEvent_t st_t0 = nullptr, st_c0 = nullptr, st_c1 = nullptr, st_d0 = nullptr, st_d1 = nullptr;
+  hipEvent_t st_w0 = nullptr, st_w1 = nullptr, st_end = nullptr;
   // profiling
   bool prof = false;
   uint32_t prof_mask = 0;  // kinds recorded while profiling (bit i = kind i)
@@ -247,6 +250,47 @@ moe::SourceSet make_sources(const moe_layer* L) {
   return S;
 }
 
+// One miss copy host -> slot on copy stream cs, unless the test hook says
+// that this one fails first.
+hipError_t enqueue_miss_copy(moe_layer* L, uint8_t* dst, const uint8_t* src, hipStream_t cs, bool* injected) {
+  if (L->fail_copy_in > 0 && --L->fail_copy_in == 0) {
+    *injected = true;
+    return hipErrorUnknown;
+  }
+  return hipMemcpyAsync(dst, src, L->blob_e, hipMemcpyHostToDevice, cs);
+}
+
+// A step of the miss fill failed after n_enq copies (or fill blocks) into
+// the slots enq_slot[] had been enqueued. Those copies still run: wait for
+// them (so that none writes a slot after this returns and no later copy into
+// the same slot can race with it), restore the cache's state from before the
+// call's step, and mark each of those slots empty, since its bytes are no
+// longer its old expert's and may not yet be the new one's. A later call
+// then refills them like any other miss.
+moe_status undo_fill(moe_layer* L, const int32_t* enq_slot, int n_enq, bool kernel_fill, hipStream_t s,
+                     const char* fn, const char* what, hipError_t cause, bool injected) {
+  if (n_enq > 0) {
+    if (kernel_fill) (void)hipStreamSynchronize(s);
+    if (L->d.copy_stream) (void)hipStreamSynchronize(static_cast<hipStream_t>(L->d.copy_stream));
+    if (L->copy2) (void)hipStreamSynchronize(L->copy2);
+    (void)hipGetLastError();
+  }
+  moe::cache_assign(L->cache, L->cache_backup);
+  for (int i = 0; i < n_enq; ++i) moe::cache_clear_slot(L->cache, enq_slot[i]);
+  if (n_enq > 0) {
+    L->staging_busy = false;
+    L->fill2_pending = false;
+  }
+  return fail(MOE_EHIP, "%s: %s: %s", fn, what,
+              injected ? "failure injected by moe_debug_fail_copy" : hipGetErrorString(cause));
+}
+
+float elapsed_ms(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return -1.f;
+  return ms;
+}
+
 }  // namespace
 
 #define HIP_OR_FAIL(expr, fn)                                                        \
@@ -334,7 +378,6 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     return fail(code, "%s: %s: %s", fn, what, hipGetErrorString(e));
   };
   hipError_t e = hipMemset(L->wsb + ws.cnt, 0, static_cast<size_t>(max_B) * 4);
-  if (e == hipSuccess) e = hipMemset(L->wsb + ws.bar, 0, 16);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return cleanup(MOE_EHIP, "clearing the workspace counters", e);
   if (cache_mode) {
@@ -368,6 +411,8 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
     if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_fill2, hipEventDisableTiming);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&L->copy2, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&L->ev_pool, hipEventDisableTiming);
+    for (hipEvent_t* t : {&L->st_t0, &L->st_c0, &L->st_c1, &L->st_d0, &L->st_d1, &L->st_w0, &L->st_w1, &L->st_end})
+      if (e == hipSuccess) e = hipEventCreate(t);
     if (e != hipSuccess) return cleanup(MOE_EHIP, "events", e);
     if (max_T > 0) {
       e = hipHostMalloc(reinterpret_cast<void**>(&L->seg_host), sizeof(int32_t) * (sh->n_experts + 1),
@@ -389,9 +434,6 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
       L->dcache = true;
       L->dc = moe::dcache_at(L->wsb + ws.dc, E, d->n_slots, d->cache_policy);
     }
-    // the one-launch option (MOE_F_FUSED) only where the device holds the
-    // whole grid at once (its grid barrier needs that)
-    L->fused = moe::ffn_fused_fits(sh->hidden, sh->top_k, sh->inter, sh->shared_inter);
     moe_status cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache);
     if (!cs) cs = moe_cache_create_policy(d->n_slots, sh->n_experts, d->cache_policy, &L->cache_backup);
     if (cs) {
@@ -412,6 +454,8 @@ void moe_layer_destroy(moe_layer* L) {
   if (L->ev_fill) (void)hipEventDestroy(L->ev_fill);
   if (L->ev_fill2) (void)hipEventDestroy(L->ev_fill2);
   if (L->copy2) (void)hipStreamDestroy(L->copy2);
+  for (hipEvent_t t : {L->st_t0, L->st_c0, L->st_c1, L->st_d0, L->st_d1, L->st_w0, L->st_w1, L->st_end})
+    if (t) (void)hipEventDestroy(t);
   for (auto& v : L->rec)
     for (auto& p : v) {
       (void)hipEventDestroy(p.first);
@@ -433,20 +477,6 @@ moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev) {
 }
 
 moe_cache* moe_layer_cache(moe_layer* L) { return L && !L->dcache ? L->cache : nullptr; }
-
-int32_t moe_layer_fused(const moe_layer* L) { return L && L->fused ? 1 : 0; }
-
-moe_status moe_layer_check(moe_layer* L, void* stream) {
-  moe::clear_error();
-  const char* fn = "moe_layer_check";
-  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
-  int32_t err = 0;
-  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-  if (e == hipSuccess) e = hipMemcpy(&err, L->wsb + L->ws.bar + 8, sizeof(err), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
-  if (err) return fail(MOE_EHIP, "%s: a grid-barrier wait of the fused expert kernel gave up", fn);
-  return MOE_OK;
-}
 
 moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, int64_t* last, int32_t n,
                                  int64_t* hits, int64_t* misses, int64_t* steps, void* stream) {
@@ -487,11 +517,11 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   moe::clear_error();
   const char* fn = "moe_layer_decode";
   if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
-  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL | MOE_F_FILL_KERNEL | MOE_F_FUSED))
+  if (flags & ~(MOE_F_RMSNORM_IN | MOE_F_RESIDUAL | MOE_F_FILL_KERNEL | MOE_F_STAGE_TIMES))
     return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
-  const bool fused = L->fused && (flags & MOE_F_FUSED);
-  auto* bar_ctr = reinterpret_cast<unsigned long long*>(L->wsb + L->ws.bar);
-  auto* bar_err = reinterpret_cast<int*>(L->wsb + L->ws.bar + 8);
+  const bool timed = flags & MOE_F_STAGE_TIMES;
+  if (timed && (!L->cache_mode || L->dcache || !stats))
+    return fail(MOE_EINVAL, "%s: MOE_F_STAGE_TIMES needs a host-stepped cache-mode handle and stats", fn);
   const bool fill_kernel = flags & MOE_F_FILL_KERNEL;
   if (fill_kernel && !L->cache_mode) return fail(MOE_EINVAL, "%s: MOE_F_FILL_KERNEL needs a cache-mode handle", fn);
   if (fill_kernel && !(L->d.store ? L->staging_dev : L->host_dev))
@@ -521,6 +551,9 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   const bool rms = flags & MOE_F_RMSNORM_IN;
   const bool res = flags & MOE_F_RESIDUAL;
 
+  const auto t_host0 = std::chrono::steady_clock::now();
+  float ms_route = 0.f;
+  if (timed) HIP_OR_FAIL(hipEventRecord(L->st_t0, s), fn);
   hipEvent_t pb = prof_begin(L, 0, s);
   // grouped path (B > 1, all experts resident): every touched expert is read
   // once per call by the matrix-core kernels, which take fp16 inputs and
@@ -618,12 +651,7 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     HIP_OR_FAIL(moe::launch_ffn_gateup(S, false, true, udig, usc, adg, asc, s, p1.a, p1.b, &F), fn);
     prof_add(L, 1, p1);
     S.ids = L->dc.slot_of_rank;
-    if (fused) {
-      const ProfPair p2 = prof_pair(L, 2);
-      HIP_OR_FAIL(moe::launch_ffn_fused(S, udig, usc, adg, asc, w, x, add_in, res, y, bar_ctr, bar_err, s, p2.a,
-                                        p2.b), fn);
-      prof_add(L, 2, p2);
-    } else {
+    {
       const ProfPair p2 = prof_pair(L, 2);
       HIP_OR_FAIL(moe::launch_ffn_gateup(S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
       prof_add(L, 2, p2);
@@ -650,9 +678,9 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     prof_add(L, 1, p1);
   }
   if (!wait_routing(L)) return fail(MOE_EHIP, "%s: timed out waiting for the routing kernel", fn);
+  if (timed) ms_route = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t_host0).count();
 
-  // LFU step; the pre-step state is kept so that a failed copy enqueue leaves
-  // the cache unchanged (no slot is marked resident with stale bytes)
+  // LFU step; the pre-step state is kept so that a failed fill can restore it
   moe_cache_event ev[moe::kMaxTopK];
   int32_t n_miss = 0;
   moe::cache_assign(L->cache_backup, L->cache);
@@ -662,6 +690,8 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   // store, or the staging that the file store reads them into
   const uint8_t* src_h[moe::kMaxTopK];
   const uint8_t* src_d[moe::kMaxTopK];
+  std::chrono::steady_clock::time_point t_read0;
+  float ms_read = 0.f;
   if (L->d.store && n_miss > 0) {
     // the staging's previous copies (this handle's last call) must be done
     if (L->staging_busy) {
@@ -683,11 +713,13 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
         mdst[nm] = L->staging + static_cast<size_t>(nm) * L->stride;
         ++nm;
       }
+    if (timed) t_read0 = std::chrono::steady_clock::now();
     const moe_status rs = moe_store_read(L->d.store, L->d.store_layer, mexp, nm, mdst);
     if (rs) {
       moe::cache_assign(L->cache, L->cache_backup);
       return rs;
     }
+    if (timed) ms_read = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t_read0).count();
   }
   for (int j = 0, m = 0; j < k; ++j) {
     if (ev[j].hit) continue;
@@ -703,14 +735,19 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
   for (int j = 0; j < k; ++j) S.slot.v[j] = ev[j].slot;
   // the ranks whose experts were resident need not wait for the copies: their
   // gate/up runs while the misses are copied, the missed ranks' after them
-  const bool split = !fused && n_miss > 0 && n_miss < k;
+  const bool split = n_miss > 0 && n_miss < k;
   moe::SourceSet S_hit = S, S_miss = S;
   if (split)
     for (int j = 0; j < k; ++j) {
       moe::SourceSet& T = ev[j].hit ? S_hit : S_miss;
       T.rsel.v[T.nsel++] = j;
     }
+  // slots that enqueued work writes (for undo_fill if a later step fails)
+  int32_t enq_slot[moe::kMaxTopK];
+  int n_enq = 0;
+  bool injected = false;
   hipError_t ce = hipSuccess;
+  bool used2 = false;
   if (fill_kernel) {
     // the misses are copied by fill blocks of the shared-expert gate/up launch
     // (with the hit ranks' gate/up blocks when split)
@@ -723,49 +760,60 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
       F.dst[F.n] = L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e;
       ++F.n;
     }
+    if (timed) ce = hipEventRecord(L->st_c0, s);
     const ProfPair p1 = split ? ProfPair{} : prof_pair(L, 1);
-    ce = moe::launch_ffn_gateup(split ? S_hit : S, split, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
-    if (ce == hipSuccess) prof_add(L, 1, p1);
+    if (ce == hipSuccess)
+      ce = moe::launch_ffn_gateup(split ? S_hit : S, split, true, udig, usc, adg, asc, s, p1.a, p1.b, &F);
+    if (ce == hipSuccess) {
+      prof_add(L, 1, p1);
+      for (int j = 0; j < k; ++j)
+        if (!ev[j].hit) enq_slot[n_enq++] = ev[j].slot;
+    }
+    if (ce == hipSuccess && timed) ce = hipEventRecord(L->st_c1, s);
     if (ce == hipSuccess && L->d.store && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, s);
       L->staging_busy = ce == hipSuccess;
     }
   } else {
     hipStream_t cp = static_cast<hipStream_t>(L->d.copy_stream);
-    bool used2 = false;
+    if (timed && n_miss > 0) {
+      ce = hipEventRecord(L->st_c0, cp);
+      if (ce == hipSuccess && n_miss > 1) ce = hipEventRecord(L->st_d0, L->copy2);
+    }
     for (int j = 0, m = 0; j < k && ce == hipSuccess; ++j) {
       if (ev[j].hit) continue;
       const bool second = (m++ & 1) != 0;  // every other miss on the second copy stream
-      used2 = used2 || second;
-      ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src_h[j], L->blob_e,
-                          hipMemcpyHostToDevice, second ? L->copy2 : cp);
+      ce = enqueue_miss_copy(L, L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src_h[j],
+                             second ? L->copy2 : cp, &injected);
+      if (ce == hipSuccess) {
+        used2 = used2 || second;
+        enq_slot[n_enq++] = ev[j].slot;
+      }
     }
     if (ce == hipSuccess && n_miss > 0) {
       ce = hipEventRecord(L->ev_fill, cp);
       if (ce == hipSuccess && used2) ce = hipEventRecord(L->ev_fill2, L->copy2);
+      if (ce == hipSuccess && timed) ce = hipEventRecord(L->st_c1, cp);
+      if (ce == hipSuccess && timed && used2) ce = hipEventRecord(L->st_d1, L->copy2);
       if (ce == hipSuccess && split) ce = moe::launch_ffn_gateup(S_hit, true, false, udig, usc, adg, asc, s);
+      if (ce == hipSuccess && timed) ce = hipEventRecord(L->st_w0, s);
       if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
       if (ce == hipSuccess && used2) ce = hipStreamWaitEvent(s, L->ev_fill2, 0);
+      if (ce == hipSuccess && timed) ce = hipEventRecord(L->st_w1, s);
       L->staging_busy = ce == hipSuccess && L->d.store;
       L->fill2_pending = L->staging_busy && used2;
     }
   }
-  if (ce != hipSuccess) {
-    moe::cache_assign(L->cache, L->cache_backup);
-    return fail(MOE_EHIP, "%s: miss copy: %s", fn, hipGetErrorString(ce));
-  }
-  if (fused) {
-    const ProfPair p2 = prof_pair(L, 2);
-    HIP_OR_FAIL(moe::launch_ffn_fused(S, udig, usc, adg, asc, w, x, add_in, res, y, bar_ctr, bar_err, s, p2.a,
-                                      p2.b), fn);
-    prof_add(L, 2, p2);
-  } else {
+  if (ce != hipSuccess) return undo_fill(L, enq_slot, n_enq, fill_kernel, s, fn, "miss fill", ce, injected);
+  {
     // profiled only where the launch covers all k ranks
     const ProfPair p2 = split ? ProfPair{} : prof_pair(L, 2);
-    HIP_OR_FAIL(moe::launch_ffn_gateup(split ? S_miss : S, true, false, udig, usc, adg, asc, s, p2.a, p2.b), fn);
+    ce = moe::launch_ffn_gateup(split ? S_miss : S, true, false, udig, usc, adg, asc, s, p2.a, p2.b);
+    if (ce != hipSuccess) return undo_fill(L, enq_slot, n_enq, fill_kernel, s, fn, "expert gate/up", ce, false);
     prof_add(L, 2, p2);
     const ProfPair p3 = prof_pair(L, 3);
-    HIP_OR_FAIL(moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b), fn);
+    ce = moe::launch_ffn_down(S, w, adg, asc, x, add_in, res, y, s, p3.a, p3.b);
+    if (ce != hipSuccess) return undo_fill(L, enq_slot, n_enq, fill_kernel, s, fn, "expert down", ce, false);
     prof_add(L, 3, p3);
   }
   if (trace) memcpy(trace, ev, sizeof(moe_cache_event) * k);
@@ -774,6 +822,26 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
     stats->misses += n_miss;
     stats->h2d_bytes += static_cast<int64_t>(n_miss) * static_cast<int64_t>(L->blob_e);
     stats->calls += 1;
+  }
+  if (timed) {
+    // wait for this call's work and read its stage times
+    HIP_OR_FAIL(hipEventRecord(L->st_end, s), fn);
+    HIP_OR_FAIL(hipEventSynchronize(L->st_end), fn);
+    float ms_fill = 0.f, ms_wait = 0.f;
+    if (n_miss > 0) {
+      HIP_OR_FAIL(hipEventSynchronize(L->st_c1), fn);
+      ms_fill = elapsed_ms(L->st_c0, L->st_c1);
+      if (used2) {
+        HIP_OR_FAIL(hipEventSynchronize(L->st_d1), fn);
+        const float m2 = elapsed_ms(L->st_d0, L->st_d1);
+        ms_fill = m2 > ms_fill ? m2 : ms_fill;
+      }
+      if (!fill_kernel) ms_wait = elapsed_ms(L->st_w0, L->st_w1);
+    }
+    stats->ms_route = ms_route;
+    stats->ms_fill = ms_read + ms_fill;
+    stats->ms_wait_fill = ms_wait;
+    stats->ms_total = elapsed_ms(L->st_t0, L->st_end);
   }
   return MOE_OK;
 }
@@ -820,10 +888,9 @@ moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logit
       moe::cache_assign(L->cache_backup, L->cache);
       moe_status cs = moe_cache_step(L->cache, experts + g0, n, ev, &n_miss);
       if (cs) return cs;
-      auto undo = [&](moe_status code, const char* what, const char* detail) {
-        moe::cache_assign(L->cache, L->cache_backup);
-        return fail(code, "%s: %s: %s", fn, what, detail);
-      };
+      int32_t enq_slot[moe::kMaxGroup];
+      int n_enq = 0;
+      bool injected = false;
       if (n_miss > 0) {
         // a miss may evict a slot that earlier kernels on s still read
         hipError_t ce = hipEventRecord(L->ev_pool, s);
@@ -858,12 +925,14 @@ moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logit
             if (!ev[j].hit) src[j] = L->d.experts_host + static_cast<size_t>(ev[j].expert) * L->blob_e;
         }
         for (int j = 0; j < n && ce == hipSuccess; ++j)
-          if (!ev[j].hit)
-            ce = hipMemcpyAsync(L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src[j], L->blob_e,
-                                hipMemcpyHostToDevice, cp);
+          if (!ev[j].hit) {
+            ce = enqueue_miss_copy(L, L->d.slot_pool + static_cast<size_t>(ev[j].slot) * L->blob_e, src[j], cp,
+                                   &injected);
+            if (ce == hipSuccess) enq_slot[n_enq++] = ev[j].slot;
+          }
         if (ce == hipSuccess) ce = hipEventRecord(L->ev_fill, cp);
         if (ce == hipSuccess) ce = hipStreamWaitEvent(s, L->ev_fill, 0);
-        if (ce != hipSuccess) return undo(MOE_EHIP, "miss copy", hipGetErrorString(ce));
+        if (ce != hipSuccess) return undo_fill(L, enq_slot, n_enq, false, s, fn, "miss copy", ce, injected);
         L->staging_busy = L->d.store != nullptr;
       }
       moe::SlotGroup grp{};
@@ -872,7 +941,8 @@ moe_status prefill_pool(moe_layer* L, const uint16_t* x_bf16, const float* logit
         grp.expert[j] = ev[j].expert;
         grp.slot[j] = ev[j].slot;
       }
-      HIP_OR_FAIL(moe::launch_prefill_routed(P, pw, xc, k, H, sh.inter, L->d.slot_pool, L->blob_e, &grp, s), fn);
+      const hipError_t ge = moe::launch_prefill_routed(P, pw, xc, k, H, sh.inter, L->d.slot_pool, L->blob_e, &grp, s);
+      if (ge != hipSuccess) return undo_fill(L, enq_slot, n_enq, false, s, fn, "routed GEMMs", ge, false);
     }
     HIP_OR_FAIL(moe::launch_prefill_shared(P, pw, xc, Tc, k, H, sh.shared_inter, L->d.shared_blob,
                                            y + static_cast<size_t>(c0) * H, s), fn);
@@ -921,6 +991,16 @@ moe_status moe_layer_prefill_chunk(moe_layer* L, int32_t tokens) {
   if (tokens < 1 || tokens > L->max_T)
     return fail(MOE_ESHAPE, "%s: %d tokens outside [1, max_T=%d]", fn, tokens, L->max_T);
   L->prefill_chunk = tokens;
+  return MOE_OK;
+}
+
+moe_status moe_debug_fail_copy(moe_layer* L, int32_t nth) {
+  moe::clear_error();
+  const char* fn = "moe_debug_fail_copy";
+  if (!L) return fail(MOE_EINVAL, "%s: NULL handle", fn);
+  if (!L->cache_mode || L->dcache) return fail(MOE_ESTATE, "%s: needs a host-stepped cache-mode handle", fn);
+  if (nth < 0) return fail(MOE_EINVAL, "%s: nth = %d is negative", fn, nth);
+  L->fail_copy_in = nth;
   return MOE_OK;
 }
 

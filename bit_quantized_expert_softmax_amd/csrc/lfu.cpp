@@ -38,6 +38,14 @@ std::string& last_error_text() {
   return s;
 }
 void cache_assign(moe_cache* dst, const moe_cache* src) { *dst = *src; }
+void cache_clear_slot(moe_cache* c, int32_t slot) {
+  if (slot < 0 || slot >= c->n_slots) return;
+  const int32_t e = c->expert[slot];
+  if (e >= 0) c->where[e] = -1;
+  c->expert[slot] = -1;
+  c->freq[slot] = 0;
+  c->last[slot] = -1;
+}
 }  // namespace moe
 
 using moe::fail;

@@ -185,12 +185,14 @@ __device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, i
 __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
   int& is_last = *is_last_p;
   const int nb = gridDim.x;
-  // every logit store of this block has completed before the block arrives
+  // every logit store of this block has completed before the block arrives;
+  // the arrival releases them and, for the last block, acquires the others'
+  // (agent scope: the blocks of a token run on different XCDs)
   const int tok = blockIdx.y;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     is_last = old == nb - 1;
     if (is_last) __hip_atomic_store(A.cnt + tok, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

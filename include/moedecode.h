@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 #define MOE_OK 0
@@ -227,9 +227,29 @@ typedef struct moe_layer_desc {
   int32_t cache_on_device;
 } moe_layer_desc;
 
+/* Counters of decode calls (accumulated over the calls given the struct) and
+ * the stage times of the last call made with MOE_F_STAGE_TIMES (left
+ * unchanged by other calls), in milliseconds:
+ *   ms_route      host clock, from the call's entry until the token's ids were
+ *                 on the host (routing kernel, top-k and its publication)
+ *   ms_fill       the misses' fill: with copy-engine fills the GPU time of the
+ *                 longer of the two copy streams' runs of copies (first copy
+ *                 start to last copy end), plus the host time of the expert
+ *                 file reads when a store is the source; with fill blocks the
+ *                 GPU time of the launch that holds them; 0 without misses.
+ *                 Divided by the miss count it is the time per missed expert
+ *                 ("Show HN: mecanismo de código aberto executando Gemma 4 26B
+ *                 em 2 GB de RAM", section "Abordagem técnica": about 3 ms per
+ *                 3.36 MB expert read from an SSD)
+ *   ms_wait_fill  GPU time the call's stream waited for the copies after it
+ *                 had run everything before them (copy-engine fills; 0 with
+ *                 fill blocks, which the stream runs in order)
+ *   ms_total      GPU time from the start of the call's first kernel to the
+ *                 end of its last */
 typedef struct moe_decode_stats {
   int64_t hits, misses, h2d_bytes; /* cache mode; accumulated over calls       */
   int64_t calls;
+  float ms_route, ms_fill, ms_wait_fill, ms_total;
 } moe_decode_stats;
 
 #define MOE_F_RMSNORM_IN 1u /* u = x' / sqrt(mean(x'^2) + 1e-6) feeds router and FFN */
@@ -240,14 +260,10 @@ typedef struct moe_decode_stats {
  * cross-stream event). experts_host must then be device-accessible pinned
  * memory (hipHostMalloc); copy_stream is unused. Same cache trace, same bits. */
 #define MOE_F_FILL_KERNEL 4u
-/* Cache mode, one token: run the routed gate/up and the down projections with
- * the combine as one launch whose blocks meet at a grid barrier between the
- * two phases (only where the device holds the whole grid at once, see
- * moe_layer_fused; otherwise the flag is ignored). Same bits as the default
- * two launches, but slower on MI355X: the barrier's round trips through
- * memory across the XCDs and the re-read of the activations cost more than
- * the kernel boundary they replace. */
-#define MOE_F_FUSED 8u
+/* Host-stepped cache mode with stats != NULL: record events around the call's
+ * stages, wait for the call's work before returning and write its stage times
+ * into stats (a measurement mode: the events and the wait cost time). */
+#define MOE_F_STAGE_TIMES 16u
 
 /* Workspace for up to max_B decode tokens per call and max_T prefill tokens. */
 moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
@@ -265,13 +281,6 @@ void moe_layer_destroy(moe_layer* L);
 moe_status moe_layer_set_experts(moe_layer* L, const uint8_t* experts_dev);
 /* The handle's LFU cache (cache mode, host-stepped), or NULL. Owned by the handle. */
 moe_cache* moe_layer_cache(moe_layer* L);
-/* 1 if MOE_F_FUSED can take effect on this handle (cache mode, and the device
- * holds the fused launch's whole grid at once), else 0. */
-int32_t moe_layer_fused(const moe_layer* L);
-/* Synchronises stream and reports MOE_EHIP if a grid-barrier wait of the fused
- * launch ever gave up (about a second without all blocks arriving: the grid
- * was not resident at once, e.g. the device was shared), else MOE_OK. */
-moe_status moe_layer_check(moe_layer* L, void* stream);
 /* State of the handle's expert-slot cache, host- or device-stepped: per slot
  * the expert (-1 empty), frequency and last use (n = n_slots), and the
  * counters. A device-stepped cache is read after synchronising stream (the
@@ -284,7 +293,7 @@ moe_status moe_layer_cache_state(moe_layer* L, int32_t* expert, int32_t* freq, i
  *   x       dev fp32 [B][H] layer input
  *   add_in  dev fp16 [B][H] added first, x' = x + add_in, or NULL (x' = x)
  *   flags   MOE_F_RMSNORM_IN | MOE_F_RESIDUAL (u = x' without RMSNORM_IN),
- *           MOE_F_FILL_KERNEL (cache mode only)
+ *           MOE_F_FILL_KERNEL, MOE_F_STAGE_TIMES (cache mode only)
  *   y       dev fp32 [B][H] output; must not alias x
  *   ids_out dev int32 [B][k], w_out dev fp32 [B][k], u_out dev fp32 [B][H]:
  *           optional copies of the routing and of u (NULL to skip)
@@ -326,6 +335,17 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
  * chunk's expert list) and for store reads. Same bits as resident mode. */
 moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* logits_in,
                              int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
+/* Test support for the failure path of the miss fill (host-stepped cache
+ * mode): the nth host->slot miss copy enqueued from now on, counted over this
+ * handle's following decode and prefill calls, fails before it is issued, as
+ * if the runtime had refused it (0 disarms; it fires once). The call then
+ * returns MOE_EHIP after waiting for the copies it had already enqueued; its
+ * cache step is undone, except that each slot one of those copies wrote is
+ * left empty (expert -1, frequency 0, last use -1), since its bytes are no
+ * longer those of the expert it held. Later calls refill such slots like any
+ * other miss. */
+moe_status moe_debug_fail_copy(moe_layer* L, int32_t nth);
+
 /* Cache-mode prefill: tokens per chunk through the slot pool, 1..max_T
  * (default 128, the pages' value; a longer chunk loads each expert once for
  * more rows). MOE_ESHAPE outside that range. */

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported_and_bound():
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
     assert set(_lib.SIGNATURES) == set(names)
-    assert api.moe_abi_version() == 2
+    assert api.moe_abi_version() == 3
 
 
 def test_blob_layout_closed_form():

@@ -79,6 +79,35 @@ def test_gemv_q4_special_inputs():
     assert_close(g[3], x[3].astype(np.float64) @ W.T, "large")
 
 
+def mixed_groups(M, K, seed):
+    """Rows whose groups of 32 mix magnitudes: one entry of +-1e4 next to
+    entries of +-1e-3 in the same group, some groups small only, some zero."""
+    rng = np.random.default_rng(seed)
+    x = (rng.choice([-1.0, 1.0], (M, K)) * rng.uniform(0.5, 1.5, (M, K)) * 1e-3).astype(np.float32)
+    g = K // 32
+    for m in range(M):
+        for j in range(g):
+            kind = (m + j) % 4
+            if kind == 0 or kind == 1:                       # one large entry among small ones
+                x[m, 32 * j + rng.integers(0, 32)] = rng.choice([-1.0, 1.0]) * 1e4
+            elif kind == 2:                                  # two large of opposite sign
+                i0, i1 = rng.choice(32, 2, replace=False)
+                x[m, 32 * j + i0], x[m, 32 * j + i1] = 1e4, -7.5e3
+            # kind 3: the group stays at 1e-3
+        x[m, :32] = 0.0                                      # one all-zero group
+    return x
+
+
+@pytest.mark.parametrize("N,K,M", [(704, 2816, 1), (2816, 704, 1), (96, 256, 4)])
+def test_gemv_q4_mixed_magnitudes_in_a_group(N, K, M):
+    q, s = _q4(N, K, N + K)
+    x = mixed_groups(M, K, N)
+    y = poisoned((M, N))
+    api.moe_expert_gemv_q4(dev(q), dev_u16(s), N, K, dev(x), M, y)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), x.astype(np.float64) @ q4.dequant(q, s).T, f"mixed N={N} K={K}")
+
+
 def test_gemv_q4_deterministic():
     N, K = 2816, 2112
     q, s = _q4(N, K, 9)

@@ -48,6 +48,23 @@ def test_resident_decode_b1(shape, cid, tokens):
     L.close()
 
 
+@pytest.mark.parametrize("cache", [False, True], ids=["resident", "cache_mode"])
+def test_decode_mixed_magnitudes_in_a_group(cache):
+    """u's groups of 32 mix 1e4 with 1e-3 (so do the GeGLU activations that follow)."""
+    from tests.test_gpu_kernels import mixed_groups
+    shape = GEMMA_LAYER
+    d = layer_data(shape, 1)
+    L = Layer(shape, d, cache_slots=16 if cache else 0)
+    xs = mixed_groups(3, shape.hidden, 5)
+    for t in range(3):
+        y, ids, w, u, _ = run_decode(L, dev(xs[t:t + 1]), trace_k=shape.top_k if cache else 0)
+        r = moe.layer_decode(xs[t].astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+        assert np.array_equal(ids, r["ids"]), t
+        assert_close(w, r["w"], f"w t={t}")
+        assert_close(y, r["y"], f"y t={t}")
+    L.close()
+
+
 def test_resident_decode_batched_call():
     shape = GEMMA_LAYER
     d = layer_data(shape, 1)

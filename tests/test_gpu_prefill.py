@@ -109,6 +109,12 @@ def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, s
         api.moe_layer_prefill_chunk(Cm.h, 0)
     api.moe_layer_prefill_chunk(Cm.h, chunk)
     y_c, ids_c, w_c = run_prefill(Cm, xb, logits, T)
+    # the oracle on the same inputs, then bitwise equality with the resident path
+    ref = moe.prefill(gen.bf16_bits_to_f32(xb).astype(np.float64), sh, d["shared"], d["experts"],
+                      logits_in=logits)
+    assert np.array_equal(ids_c, ref["ids"])
+    assert_close(w_c, ref["w"], "w slot pool")
+    assert_close(y_c, ref["y"], f"y slot pool T={T} chunk={chunk}")
     assert np.array_equal(ids_c, ids_r) and np.array_equal(w_c, w_r)
     assert np.array_equal(y_c, y_r)
     sim = lfu.LFUCache(slots, sh.n_experts)

@@ -124,3 +124,26 @@ def test_bytes_against_the_pages():
     hi = 30 * p["experts_per_token"] * (1 - p["hit_rate_lo"]) * blob / 1e6
     assert abs(lo - p["read_per_token_lo_mb"]) / p["read_per_token_lo_mb"] < 0.05
     assert abs(hi - p["read_per_token_hi_mb"]) / p["read_per_token_hi_mb"] < 0.05
+
+
+def test_layer_bytes_closed_form_and_generated_arrays():
+    """The algorithmic bytes of one B=1 token-layer: k expert blobs, the shared
+    blob and the fp16 router, checked against the closed form and against the
+    sizes of the arrays the generator actually builds."""
+    from oracle import moe
+    lb = moe.layer_bytes(GEMMA_LAYER)
+    assert lb == {"expert_blob": 3_345_408, "routed": 8 * 3_345_408, "shared": 10_036_224, "router": 720_896}
+    assert lb["routed"] + lb["shared"] + lb["router"] == 37_520_384
+    # thirty such layers per token with every expert resident
+    assert 30 * (lb["routed"] + lb["shared"] + lb["router"]) == 1_125_611_520
+    for sh in (SMALL_LAYER, GEMMA_LAYER):
+        d = gen.layer_inputs(sh, 0) if sh is SMALL_LAYER else None
+        lb = moe.layer_bytes(sh)
+        if d is not None:
+            assert d["experts"][0].nbytes == lb["expert_blob"]
+            assert d["shared"].nbytes == lb["shared"]
+            assert d["router"].nbytes == lb["router"]
+            assert lb["routed"] == sh.top_k * d["experts"][0].nbytes
+        # a blob is its six arrays: gate and up [I][H/2] + down [H][I/2] nibbles, one fp16 per 32
+        H, I = sh.hidden, sh.inter
+        assert lb["expert_blob"] == 3 * H * I // 2 + 3 * H * I // 32 * 2
