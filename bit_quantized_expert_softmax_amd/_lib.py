@@ -68,6 +68,7 @@ SIGNATURES = {
     "moe_blob_layout_of": (c_status, [C.c_int32, C.c_int32, P(moe_blob_layout)]),
     "moe_route_workspace_bytes": (C.c_size_t, [P(moe_shape), C.c_int32]),
     "moe_route": (c_status, [P(moe_shape), vp, vp, vp, vp, C.c_int32, vp, vp, vp, C.c_size_t, vp]),
+    "moe_route_noalloc": (c_status, [P(moe_shape), vp, vp, vp, vp, C.c_int32, vp, vp, vp]),
     "moe_cache_create": (c_status, [C.c_int32, C.c_int32, P(vp)]),
     "moe_cache_create_policy": (c_status, [C.c_int32, C.c_int32, C.c_int32, P(vp)]),
     "moe_cache_destroy": (None, [vp]),

@@ -97,6 +97,15 @@ def moe_route(sh, x, wr, bias, logits_in, B, ids, w, workspace=None, stream=None
                            _p(workspace), ws_bytes, _stream(stream)), "moe_route")
 
 
+MOE_ROUTE_NOALLOC_MAX = 131072
+
+
+def moe_route_noalloc(sh, x, wr, bias, logits_in, B, ids, w, stream=None):
+    s = make_shape(sh)
+    _check(lib().moe_route_noalloc(C.byref(s), _p(x), _p(wr), _p(bias), _p(logits_in), B, _p(ids), _p(w),
+                                   _stream(stream)), "moe_route_noalloc")
+
+
 # ------------------------------------------------------------------ LFU cache
 def moe_cache_create(n_slots: int, n_experts: int, policy: int = 0) -> int:
     h = C.c_void_p()

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libmoedecode.so")
 # plain C++ (no HIP headers)
 HOST_SOURCES = ["lfu.cpp", "store.cpp"]
 # compiled as HIP: kernels, and host code that calls the HIP runtime
-HIP_SOURCES = ["abi.cpp", "layer.cpp", "route.hip", "decode.hip", "gemv.hip", "prefill.hip", "batched.hip", "attn.hip"]
+HIP_SOURCES = ["abi.cpp", "layer.cpp", "route.hip", "decode.hip", "gemv.hip", "prefill.hip", "batched.hip", "attn.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -117,6 +117,19 @@ moe_status moe_route(const moe_shape* sh, const float* x, const uint16_t* wr, co
                      const float* logits_in, int32_t B, int32_t* ids, float* w, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_route
+ * without the workspace argument. The fp64 logits live in a device array of
+ * the library's own (MOE_ROUTE_NOALLOC_MAX doubles = 1 MiB per GPU, held
+ * until the process ends); the call allocates nothing. Same kernels, same
+ * results as moe_route. MOE_ESHAPE when B * n_experts exceeds
+ * MOE_ROUTE_NOALLOC_MAX (only without logits_in, which needs no scratch).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams or threads) race. Asynchronous on stream. */
+#define MOE_ROUTE_NOALLOC_MAX 131072
+moe_status moe_route_noalloc(const moe_shape* sh, const float* x, const uint16_t* wr, const float* bias,
+                             const float* logits_in, int32_t B, int32_t* ids, float* w, void* stream);
+
 /* ---------------------------------------------------------------- 2. LFU cache
  * Host-only, synchronous, deterministic. One cache per layer, n_slots slots.
  * moe_cache_step looks up one token's k ids (host, rank order, distinct):
