@@ -56,12 +56,15 @@ def parse():
     ap.add_argument("--no-attn", action="store_true", help="skip the attention-step measurements")
     ap.add_argument("--no-device-cache", action="store_true",
                     help="skip the stack with the slot caches stepped on the device")
-    ap.add_argument("--probe", choices=["gateup", "copy", "batched"], default=None,
+    ap.add_argument("--probe", choices=["gateup", "copy", "batched", "prefill"], default=None,
                     help="short run for hardware counters: 'gateup' decodes a few cache-mode "
                          "tokens (the measured kernel included), 'copy' copies 1 GiB once")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("GU_FETCH", "GU_WRITE", "CP_FETCH", "CP_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of a "
                          "'--probe gateup' and a '--probe copy' run) into the traffic summary (JSON)")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE run of "
+                         "'--probe prefill' into a per-kernel MFMA-busy table (markdown)")
     return ap.parse_args()
 
 
@@ -213,6 +216,35 @@ def cpu_baseline(layers, tokens, cid, seconds):
             "cpu_model": model}
 
 
+def summarize_mfma(d):
+    """MFMA-busy share per prefill kernel: SQ_VALU_MFMA_BUSY_CYCLES summed over
+    the SIMDs / (GPU-busy cycles of one XCD x 1024 SIMDs), the MfmaUtil formula
+    of rocprofv3's derived counters (GRBM_GUI_ACTIVE is summed over the 8 XCDs,
+    so its per-XCD value is the sum / 8)."""
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+            key = (name, int(r["Grid_Size"]) // int(r["Workgroup_Size"]), int(r["Workgroup_Size"]),
+                   r.get("VGPR_Count", ""), r.get("Accum_VGPR_Count", ""))
+            acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = ["| kernel | blocks x threads | VGPR (arch + acc) | dispatches | GPU-busy us (one XCD at 2.4 GHz) | MFMA busy |",
+             "|---|---|---|---|---|---|"]
+    for (name, blocks, wg, vg, ag), c in sorted(acc.items(), key=lambda kv: -sum(kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", [0]))):
+        mf = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        gr = c.get("GRBM_GUI_ACTIVE")
+        if not mf or not gr or sum(mf) == 0:
+            continue
+        n = len(mf)
+        per_xcd = sum(gr) / len(gr) / 8
+        util = (sum(mf) / n) / (per_xcd * 1024)
+        lines.append(f"| `{name}` | {blocks} x {wg} | {vg} + {ag} | {n} | {per_xcd / 2400:.1f} | {util:.3f} |")
+    return "\n".join(lines)
+
+
 def load_traffic():
     """The committed counter summary if it was taken on the current kernel source."""
     try:
@@ -227,6 +259,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -272,6 +307,28 @@ def main():
         for h in hb:
             api.moe_layer_destroy(h)
         print(f"[bench] probe: {4 * args.warmup} batched steps at B = {Bp}", file=sys.stderr, flush=True)
+        return
+    if args.probe == "prefill":
+        # 2048-token prefills over 3 resident layers in turn, for counter runs
+        # of the matrix-core GEMMs
+        devp, Tp = "cuda:0", 2048
+        wsp = torch.zeros(api.moe_layer_workspace_bytes(sh, 1, Tp), dtype=torch.uint8, device=devp)
+        hp_, keep = [], []
+        for l in range(3):
+            ex = torch.from_numpy(gen.expert_blobs(sh, C2.config_id, l)).to(devp)
+            rt = torch.from_numpy(gen.router(sh, C2.config_id, l).view(np.int16)).to(devp)
+            shb = torch.from_numpy(gen.shared_blob(sh, C2.config_id, l)).to(devp)
+            keep += [ex, rt, shb]
+            hp_.append(api.moe_layer_create(sh, router=rt, shared_blob=shb, workspace=wsp, experts_dev=ex, max_T=Tp))
+        xq = torch.from_numpy(gen.x_bf16(Tp, H, 4).view(np.int16)).to(devp)
+        lq = torch.from_numpy(gen.logits_uniform(Tp, E, 4)).to(devp)
+        yq = torch.empty((Tp, H), device=devp)
+        for i in range(args.warmup):
+            api.moe_layer_prefill(hp_[i % 3], xq, lq, Tp, yq)
+        torch.cuda.synchronize()
+        for h in hp_:
+            api.moe_layer_destroy(h)
+        print(f"[bench] probe: {args.warmup} prefills of {Tp} tokens", file=sys.stderr, flush=True)
         return
     Lyr, T, S = args.layers, args.tokens, args.slots
     cid = C2.config_id

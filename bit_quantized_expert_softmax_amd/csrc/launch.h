@@ -195,14 +195,16 @@ hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint
                                  int H, int Is, const uint8_t* shared, float* y, hipStream_t s,
                                  bool gateup_done = false);
 
-// ---------------------------------------------------------------- batched decode
 // Stable sort of A assignments (token*k + rank, expert ids[a]) by expert:
 // seg [E+1] segment starts, perm [A] sorted position -> assignment, pos_of [A]
-// assignment -> sorted position, tiles/n_tiles the 64-row tile table.
+// assignment -> sorted position, tiles/n_tiles the GEMM tile table
+// (expert, first row, rows; at most 128 rows per tile).
 hipError_t launch_permute(const int32_t* ids, int A, int E, int chunks, int32_t* hist, int32_t* lrank,
-                          int32_t* base, int32_t* seg, int2* tiles, int32_t* n_tiles, int32_t* perm,
+                          int32_t* base, int32_t* seg, int4* tiles, int32_t* n_tiles, int32_t* perm,
                           int32_t* pos_of, hipStream_t s);
 int permute_chunks(int A);
+
+// ---------------------------------------------------------------- batched decode
 
 struct BatchedBuffers {
   uint16_t* act_r;  // [B*k][I] fp16 GeGLU activations by assignment token*k + rank

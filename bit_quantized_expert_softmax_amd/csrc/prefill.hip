@@ -13,8 +13,8 @@
 // expert's down GEMM adds the k routed rows of every token in rank order.
 //
 // Stages (one launch each): count per 256-assignment chunk, scan (expert
-// offsets and the GEMM tile table), stable scatter, routed gate/up, shared
-// gate/up, routed down, shared down + combine.
+// offsets and the GEMM tile table), stable scatter, routed + shared gate/up,
+// routed down, shared down, combine.
 #include <type_traits>
 
 #include "launch.h"
@@ -52,13 +52,16 @@ __global__ __launch_bounds__(kChunk) void k_perm_count(const int32_t* __restrict
 }
 
 // Single block: expert offsets (seg [E+1]), per-(chunk, expert) bases, and the
-// routed tile table (expert, first row) with its length in *n_tiles. P
+// routed tile table (expert, first row, rows) with its length in *n_tiles:
+// an expert's n rows form ceil(n / 128) tiles of equal size rounded up to 16
+// rows (the last one shorter), so no tile carries a mostly empty 128-row
+// remainder (with 2048 tokens the mean expert has exactly 128 rows). P
 // threads per expert (P = 1024 / E) each take a contiguous range of chunks;
 // their partial counts meet in LDS, and the expert offsets and tile starts
 // come from one block-wide scan (wave scans, then the waves' totals).
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ hist, int C, int E,
                                                     int32_t* __restrict__ base, int32_t* __restrict__ seg,
-                                                    int2* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+                                                    int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
   constexpr int kT = 1024;
   __shared__ int part[kT];
   __shared__ int tot[MOE_MAX_EXPERTS + 1];
@@ -123,7 +126,12 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
       r += hist[static_cast<size_t>(c) * E + e];
     }
     const int rows = tot[e + 1] - tot[e];
-    for (int m = p * kTM; m < rows; m += P * kTM) tiles[tst[e] + m / kTM] = make_int2(e, tot[e] + m);
+    const int ntl = (rows + kTM - 1) / kTM;
+    const int size = ntl > 0 ? ((rows + ntl - 1) / ntl + 15) / 16 * 16 : 0;
+    for (int m = p; m < ntl; m += P) {
+      const int r0 = m * size;
+      tiles[tst[e] + m] = make_int4(e, tot[e] + r0, rows - r0 < size ? rows - r0 : size, 0);
+    }
   }
 }
 
@@ -141,30 +149,64 @@ __global__ __launch_bounds__(kChunk) void k_perm_scatter(const int32_t* __restri
 
 // ---------------------------------------------------------------- grouped GEMM
 // Weight rows stream from HBM into registers and are dequantised there; the
-// block's 128 activation rows are staged in LDS per K step (double buffered)
+// block's token rows are loaded per K step straight into LDS (global_load_lds,
+// 16 bytes per lane, no registers on the way) into a ring of kBufs slices
 // and shared by its 8 waves. A wave owns two 16-row weight tiles (GATEUP: 16
 // gate rows and the matching 16 up rows; else 32 consecutive down rows) and
-// all 8 16-row token tiles, so each dequantised weight feeds 8 MFMAs. (Four
-// tiles per wave halve the LDS reads per flop but need one wave per SIMD;
-// measured slower, 1.04 vs 0.83 ms, as dequant, LDS reads and MFMAs of one
-// wave then overlap too little.)
+// all of the block's 16-token tiles, so each dequantised weight feeds up to
+// 8 MFMAs (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 //
 // K step = 4 quant groups (128 values). The lane of 16-lane row q loads group
 // 4*st + q of its weight row (16 bytes) and that group's scale; MFMA j of the
 // step takes dword j (8 nibbles) of every lane's group, so one MFMA's K = 32
 // spans the step's 4 groups, 8 values of each, and the activations are read
-// at the same positions. Loads are issued kDepth steps ahead (activation
-// slice first, then weights) into a register ring whose slots are
-// compile-time indices, so every wait is for the oldest unit only.
-constexpr int kTok = kTM / 16;            // 16-token tiles per block
+// at the same positions (16-byte chunk 4q + j of the token's 256-byte row).
+//
+// Pipeline: the loads of step s + kDepth (activation slice and weights) are
+// issued at the start of step s, into the slice the previous step read; the
+// weights of step s + 1 are dequantised while the MFMAs of step s run, so a
+// wave's dequantisation overlaps its own matrix work; one barrier per step
+// both frees the slice just read and publishes the next one (each wave has
+// waited for its own loads of it). The slice rows are unpadded 256-byte rows
+// whose 16 chunks are stored XOR-swizzled by the row (position = chunk ^
+// (row & 15)); the direct loads choose each lane's source chunk so that the
+// stored image has this layout, and the MFMA reads of 16 consecutive token
+// rows at one chunk then fall on 16 different bank groups.
+constexpr int kTok = kTM / 16;            // 16-token tiles per block (at most)
 constexpr int kWavesG = 8;               // waves per GEMM block
 constexpr int kThreadsGemm = kWavesG * kWave;
-constexpr int kStage = kTM * 16 / kThreadsGemm;  // 16-byte activation chunks per thread and step
 constexpr int kStepK = 4 * kGroup;       // 128
-constexpr int kBRow = kStepK * 2 + 16;   // LDS bytes per activation row of a step (padded)
-constexpr int kDepth = 4;
+constexpr int kRowB = kStepK * 2;        // LDS bytes per token row of a slice
+constexpr int kSlice = kTM * kRowB;      // 32 KB
+constexpr int kDepth = 3;                // steps loaded ahead of the one computed
+constexpr int kBufs = kDepth + 1;        // slices in LDS (128 KB)
 constexpr int kMR = 2;                   // 16-row weight tiles per wave (GATEUP: half gate, half up)
 constexpr int kHalf = kMR / 2;
+constexpr int kXcds = 8;                 // accelerator complex dies of an MI355X, each with its own L2
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Barrier of the GEMM blocks. __syncthreads() orders memory with a fence
+// whose lowering waits for every outstanding vector load, the loads of the
+// later steps included, which would drain the pipeline every step. Here each
+// wave has already waited for its own loads whose LDS data the others read
+// next (wait_vmcnt), waits for its own LDS reads (lgkmcnt 0), then meets the
+// others; the empty asm statements keep the compiler from moving memory
+// accesses across, sched_barrier keeps the scheduler from moving instructions.
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only (vmcnt 63, expcnt 7: no wait)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Byte B of x as a float (v_cvt_f32_ubyteB; written out because the compiler
 // folds the surrounding masks and then loses the byte-select forms).
@@ -226,67 +268,43 @@ struct GemmArgs {
   const uint8_t* experts;
   size_t blob_e;
   int H, inter;
-  // routed tiles from the table (tiles/n_tiles/seg), or a dense job of M_dense rows
-  const int2* tiles;
+  // routed tiles from the table (tiles/n_tiles), or a dense job of M_dense rows
+  const int4* tiles;
   const int32_t* n_tiles;
-  const int32_t* seg;
   int M_dense;
   // outputs
   __bf16* act;        // gate/up: activations [rows][inter] bf16
   float* out;         // down: [rows][H] fp32 (routed, weighted) or y [T][H] (shared)
   const float* wrow;  // routed down: routing weight per assignment (by perm[row])
   const int32_t* perm;
-  // shared down: y[t] = o_shared[t] + sum_j out_r[pos_of[t*k + j]]
-  const float* out_r;
-  const int32_t* pos_of;
   int k;
   // routed, slot pool: only the tiles of these experts run, each expert's
   // weights at experts + slot * blob_e (n_group == 0: every expert, at its id)
   SlotGroup group;
 };
 
-// One block's tile (block index bid of its job); lds_b: two activation slice
-// buffers of kTM * kBRow bytes.
-template <bool GATEUP, bool ROUTED>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*lds_b)[kTM * kBRow]) {
+// The GEMM of one block: token rows [r0, r_end) (at most NTT 16-row tiles)
+// against row tile nt of the weights in blob; lds: kBufs activation slices.
+template <bool GATEUP, bool ROUTED, int NTT>
+__device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int r_end, const uint8_t* blob,
+                                          uint8_t* lds) {
+  constexpr int kTok = NTT;
+  constexpr int kRows = NTT * 16;                                     // slice rows
+  constexpr int kStage = (kRows + 4 * kWavesG - 1) / (4 * kWavesG);   // 4 rows per wave load
+  constexpr int kLoads = kStage + 2 * kMR;                            // vector loads per step
   constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
   const int nrows = GATEUP ? G.inter : G.H;
-  const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
-  const int mt = bid / n_tiles_n;
-  const int nt = bid % n_tiles_n;
-  int r0, r_end;
-  const uint8_t* blob;
-  if (ROUTED) {
-    if (mt >= *G.n_tiles) return;
-    const int2 td = G.tiles[mt];
-    int where = td.x;  // expert id (resident) or its slot (slot pool)
-    if (G.group.n > 0) {
-      where = -1;
-      for (int i = 0; i < G.group.n; ++i)
-        if (G.group.expert[i] == td.x) where = G.group.slot[i];
-      if (where < 0) return;  // uniform over the block: not this group's expert
-    }
-    r0 = td.y;
-    const int e_end = G.seg[td.x + 1];
-    r_end = r0 + kTM < e_end ? r0 + kTM : e_end;
-    blob = G.experts + static_cast<size_t>(where) * G.blob_e;
-  } else {
-    r0 = mt * kTM;
-    if (r0 >= G.M_dense) return;
-    r_end = r0 + kTM < G.M_dense ? r0 + kTM : G.M_dense;
-    blob = G.blob;
-  }
   const int mtok = r_end - r0;
   const BlobOffsets o = blob_offsets(G.H, G.inter);
   const int K = GATEUP ? G.H : G.inter;
   const int ngk = K / kGroup;
   const int nsteps = (ngk + 3) / 4;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar registers
   const int lane = threadIdx.x & (kWave - 1);
   const int q = lane >> 4;
   const int l16 = lane & 15;
   const int rbase = nt * rows_per_block + wave * (GATEUP ? kHalf * 16 : kMR * 16);
-  const bool live = rbase < nrows;  // waves past the last row only stage and sync
+  const bool live = rbase < nrows;  // waves past the last row only load and sync
   const uint8_t* qrow[kMR];
   const uint16_t* srow[kMR];
 #pragma unroll
@@ -299,18 +317,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*
     qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
     srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
   }
-  // this thread's 16-byte chunks of an activation slice (row = c / 16)
-  const __bf16* brow[kStage];
-  int boff[kStage], loff[kStage];
+  // This lane's part of the slice loads: load u of the wave fills slice rows
+  // 4 (wave + 8u) .. + 3 (modulo the slice, so small slices are filled more
+  // than once with the same bytes); lane i takes row + i / 16 at position
+  // i % 16, i.e. the token's chunk (i % 16) ^ (row & 15). Rows past the tile
+  // repeat its last token (their outputs are dropped).
+  const __bf16* arow[kStage];
+  int achunk[kStage];
+  uint32_t alds[kStage];  // wave-uniform LDS offset of the load's first row
 #pragma unroll
-  for (int r = 0; r < kStage; ++r) {
-    int c = threadIdx.x + kThreadsGemm * r;
-    c = c < mtok * 16 ? c : mtok * 16 - 1;
-    const int row = r0 + (c >> 4);
+  for (int u = 0; u < kStage; ++u) {
+    const int rr = (4 * (wave + kWavesG * u)) % kRows;
+    alds[u] = static_cast<uint32_t>(rr * kRowB);
+    const int r = rr + (lane >> 4);
+    achunk[u] = (lane & 15) ^ (r & 15);
+    const int row = r0 + (r < mtok ? r : mtok - 1);
     const int idx = G.rmap ? G.rmap[row] / G.rdiv : row;
-    brow[r] = G.A + static_cast<size_t>(idx) * G.lda;
-    boff[r] = 8 * (c & 15);
-    loff[r] = (c >> 4) * kBRow + 16 * (c & 15);
+    arow[u] = G.A + static_cast<size_t>(idx) * G.lda;
   }
 
   f32x4 acc[kMR][kTok];
@@ -319,78 +342,86 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*
 #pragma unroll
     for (int tt = 0; tt < kTok; ++tt) acc[mr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  WStep w[kDepth];
-  u32x4 bs[kDepth][kStage];
-  // st past the last step re-reads the last step: every step issues the same
-  // loads, so the wait counts are the same on every path
-  auto issue = [&](int st, WStep& wd, u32x4* bd) __attribute__((always_inline)) {
+  WStep w[kBufs];
+  // dequantised weights: slice j holds the current step's until its MFMAs
+  // are issued, then the next step's
+  bf16x8 a[kMR][4];
+  // the loads of step st into slot sl (st past the last step re-loads the
+  // last one: every step issues the same loads, so the wait counts hold on
+  // every path)
+  auto issue = [&](int st, int sl, WStep& wd) __attribute__((always_inline)) {
     st = st < nsteps ? st : nsteps - 1;
 #pragma unroll
-    for (int r = 0; r < kStage; ++r) {
-      int kk = st * kStepK + boff[r];
+    for (int u = 0; u < kStage; ++u) {
+      int kk = st * kStepK + 8 * achunk[u];
       kk = kk < K ? kk : K - 8;  // past the end: any finite values (their weights are 0)
-      bd[r] = *reinterpret_cast<const u32x4*>(brow[r] + kk);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[u] + kk),
+                                       (__attribute__((address_space(3))) void*)(lds + sl * kSlice + alds[u]),
+                                       16, 0, 0);
     }
     load_step(wd, qrow, srow, ngk, st, q);
   };
-  auto stage_store = [&](int bi, const u32x4* bd) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < kStage; ++r) *reinterpret_cast<u32x4*>(lds_b[bi] + loff[r]) = bd[r];
-  };
-  auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
-    constexpr int D = decltype(slot)::value;
-    const int st = s0 + D;
-    if (tail && st >= nsteps) return;  // uniform over the block
-    stage_store((st + 1) & 1, bs[(D + 1) % kDepth]);  // past the end: unused
-    const uint8_t* lb = lds_b[st & 1];
+  // slice j (dword j of each weight tile's group) of step st, into a[.][j]
+  auto dequant = [&](int st, const WStep& wd, int j) __attribute__((always_inline)) {
     const bool gv = 4 * st + q < ngk;  // groups past K weigh 0
-    bf16x8 a[kMR][4];
 #pragma unroll
     for (int mr = 0; mr < kMR; ++mr) {
-      const float sc = gv ? h2f(static_cast<uint16_t>(w[D].s[mr])) : 0.0f;
-      a[mr][0] = dequant8_bf16(w[D].q[mr].x, sc);
-      a[mr][1] = dequant8_bf16(w[D].q[mr].y, sc);
-      a[mr][2] = dequant8_bf16(w[D].q[mr].z, sc);
-      a[mr][3] = dequant8_bf16(w[D].q[mr].w, sc);
+      const float sc = gv ? h2f(static_cast<uint16_t>(wd.s[mr])) : 0.0f;
+      const uint32_t wj = j == 0 ? wd.q[mr].x : (j == 1 ? wd.q[mr].y : (j == 2 ? wd.q[mr].z : wd.q[mr].w));
+      a[mr][j] = dequant8_bf16(wj, sc);
     }
+  };
+  auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
+    constexpr int D = decltype(slot)::value;  // slot of this step (step % kBufs)
+    const int st = s0 + D;
+    if (tail && st >= nsteps) return;  // uniform over the block
+    __builtin_amdgcn_sched_barrier(0);
+    issue(st + kDepth, (D + kDepth) % kBufs, w[(D + kDepth) % kBufs]);
+    // this wave's loads of step st + 1 are in (those of st + 2, st + 3 may not be)
+    wait_vmcnt<(kDepth - 1) * kLoads>();
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* lb = lds + D * kSlice;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // every token tile, also past mtok: an output column depends on its
       // own activation row only, and the columns of absent rows are dropped
 #pragma unroll
       for (int tt = 0; tt < kTok; ++tt) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + (tt * 16 + l16) * kBRow + 64 * q + 16 * j);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + (tt * 16 + l16) * kRowB + 16 * ((4 * q + j) ^ l16));
 #pragma unroll
         for (int mr = 0; mr < kMR; ++mr)
           acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mr][j], bv, acc[mr][tt], 0, 0, 0);
       }
+      // slice j of the next step, while the matrix cores work through this one
+      dequant(st + 1, w[(D + 1) % kBufs], j);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    issue(st + kDepth, w[D], bs[D]);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    // every wave is done with slot D (the next step's loads may refill it),
+    // and every wave's loads of step st + 1 have landed
+    block_sync();
   };
-  static_assert(kDepth == 3 || kDepth == 4, "the step sequence below is written out for 3 or 4 slots");
-  constexpr int kD3 = kDepth > 3 ? 3 : 0;
-  issue(0, w[0], bs[0]);
-  issue(1, w[1], bs[1]);
-  issue(2, w[2], bs[2]);
-  if constexpr (kDepth > 3) issue(3, w[kD3], bs[kD3]);
-  stage_store(0, bs[0]);
-  __syncthreads();
+  static_assert(kBufs == 4, "the step sequence below is written out for 4 slots");
+  issue(0, 0, w[0]);
+  issue(1, 1, w[1]);
+  issue(2, 2, w[2]);
+  wait_vmcnt<(kDepth - 1) * kLoads>();
+  block_sync();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dequant(0, w[0], j);
   int s0 = 0;
-  for (; s0 + kDepth <= nsteps; s0 += kDepth) {
+  for (; s0 + kBufs <= nsteps; s0 += kBufs) {
     step(std::integral_constant<int, 0>{}, s0, false);
     step(std::integral_constant<int, 1>{}, s0, false);
     step(std::integral_constant<int, 2>{}, s0, false);
-    if constexpr (kDepth > 3) step(std::integral_constant<int, kD3>{}, s0, false);
+    step(std::integral_constant<int, 3>{}, s0, false);
   }
-  if (s0 < nsteps) {  // the last 1..kDepth-1 steps
+  if (s0 < nsteps) {  // the last 1..3 steps
     step(std::integral_constant<int, 0>{}, s0, true);
     step(std::integral_constant<int, 1>{}, s0, true);
-    if constexpr (kDepth > 3) step(std::integral_constant<int, 2>{}, s0, true);
+    step(std::integral_constant<int, 2>{}, s0, true);
   }
+  // the loads still in flight (past the last step) complete before the
+  // block ends: LDS is released with the block
+  wait_vmcnt<0>();
 
   // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token row
   // l16 of each token tile
@@ -416,13 +447,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*
         if (ROUTED) {
           const float wr = G.wrow[G.perm[m]];
           v = make_float4(v.x * wr, v.y * wr, v.z * wr, v.w * wr);
-        } else {
-          // shared expert output plus the token's routed rows in rank order
-          for (int jj = 0; jj < G.k; ++jj) {
-            const float4 r = *reinterpret_cast<const float4*>(
-                G.out_r + static_cast<size_t>(G.pos_of[m * G.k + jj]) * G.H + n);
-            v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
-          }
         }
         *reinterpret_cast<float4*>(G.out + static_cast<size_t>(m) * G.H + n) = v;
       }
@@ -430,9 +454,91 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t (*
   }
 }
 
+// One block's tile (block index bid of its job): the token rows of its tile
+// and its weight row tile, then the GEMM for the tile's number of 16-row
+// token tiles (block-uniform, so each count runs its own unrolled code).
+template <bool GATEUP, bool ROUTED>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t* lds_b) {
+  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
+  const int nrows = GATEUP ? G.inter : G.H;
+  const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
+  // XCD-aware order: blocks are dealt to the 8 XCDs in turn (block b to XCD
+  // b % 8), so all row tiles of token tile mt get block ids congruent to mt
+  // mod 8: they run on one XCD, and the token rows that the first of them
+  // brings into that XCD's L2 serve the others
+  const int xcd = bid % kXcds, jx = bid / kXcds;
+  const int mt = xcd + kXcds * (jx / n_tiles_n);
+  const int nt = jx % n_tiles_n;
+  int r0, r_end;
+  const uint8_t* blob;
+  if (ROUTED) {
+    if (mt >= *G.n_tiles) return;
+    const int4 td = G.tiles[mt];
+    int where = td.x;  // expert id (resident) or its slot (slot pool)
+    if (G.group.n > 0) {
+      where = -1;
+      for (int i = 0; i < G.group.n; ++i)
+        if (G.group.expert[i] == td.x) where = G.group.slot[i];
+      if (where < 0) return;  // uniform over the block: not this group's expert
+    }
+    r0 = td.y;
+    r_end = r0 + td.z;
+    blob = G.experts + static_cast<size_t>(where) * G.blob_e;
+  } else {
+    r0 = mt * kTM;
+    if (r0 >= G.M_dense) return;
+    r_end = r0 + kTM < G.M_dense ? r0 + kTM : G.M_dense;
+    blob = G.blob;
+  }
+  if (r_end <= r0) return;
+  switch ((r_end - r0 + 15) / 16) {
+    case 1: gemm_core<GATEUP, ROUTED, 1>(G, nt, r0, r_end, blob, lds_b); break;
+    case 2: gemm_core<GATEUP, ROUTED, 2>(G, nt, r0, r_end, blob, lds_b); break;
+    case 3: gemm_core<GATEUP, ROUTED, 3>(G, nt, r0, r_end, blob, lds_b); break;
+    case 4: gemm_core<GATEUP, ROUTED, 4>(G, nt, r0, r_end, blob, lds_b); break;
+    case 5: gemm_core<GATEUP, ROUTED, 5>(G, nt, r0, r_end, blob, lds_b); break;
+    case 6: gemm_core<GATEUP, ROUTED, 6>(G, nt, r0, r_end, blob, lds_b); break;
+    case 7: gemm_core<GATEUP, ROUTED, 7>(G, nt, r0, r_end, blob, lds_b); break;
+    default: gemm_core<GATEUP, ROUTED, 8>(G, nt, r0, r_end, blob, lds_b); break;
+  }
+}
+
+// y[t] += sum over j of the routed rows out_r[pos_of[t*k + j]], in rank
+// order, after the shared expert's output o_shared[t] that y holds: the same
+// additions in the same order as a combine inside the shared down GEMM, as a
+// streaming pass over all blocks of the GPU (each token's k rows are read
+// once, 16 bytes per lane). KMAX >= k: every lane issues KMAX loads (past k
+// they repeat the last row) before the first add, and adds the first k.
+template <int KMAX>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ out_r,
+                                                 const int32_t* __restrict__ pos_of, int k, int H,
+                                                 float* __restrict__ y) {
+  const int t = blockIdx.y;
+  int n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  const bool on = n < H;
+  n = on ? n : H - 4;
+  float4 r[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int p = pos_of[static_cast<size_t>(t) * k + (j < k ? j : k - 1)];
+    r[j] = *reinterpret_cast<const float4*>(out_r + static_cast<size_t>(p) * H + n);
+  }
+  const float4 y0 = *reinterpret_cast<const float4*>(y + static_cast<size_t>(t) * H + n);
+  float vx = y0.x, vy = y0.y, vz = y0.z, vw = y0.w;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool add = j < k;  // per-component selects (a select of a float4 goes through memory)
+    vx = add ? vx + r[j].x : vx;
+    vy = add ? vy + r[j].y : vy;
+    vz = add ? vz + r[j].z : vz;
+    vw = add ? vw + r[j].w : vw;
+  }
+  if (on) *reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H + n) = make_float4(vx, vy, vz, vw);
+}
+
 template <bool GATEUP, bool ROUTED>
 __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBufs * kSlice];
   gemm_tile<GATEUP, ROUTED>(G, blockIdx.x, lds_b);
 }
 
@@ -441,7 +547,7 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
 // independent, and the shared blocks, few and long, would otherwise form a
 // launch of their own with a tail of one block per CU.
 __global__ __launch_bounds__(kThreadsGemm) void k_gemm_gateup2(GemmArgs R, GemmArgs Sh, int n_shared) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kTM * kBRow];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBufs * kSlice];
   const int bid = blockIdx.x;
   if (bid < n_shared)
     gemm_tile<true, false>(Sh, bid, lds_b);
@@ -456,6 +562,12 @@ int gemm_row_tiles(bool gateup, int H, int inter) {
   return (rows + per - 1) / per;
 }
 
+// Grid of a GEMM of m_tiles token tiles (rounded up to whole XCD rounds, see
+// gemm_tile; the blocks past the last tile exit).
+int gemm_blocks(int m_tiles, bool gateup, int H, int inter) {
+  return (m_tiles + kXcds - 1) / kXcds * kXcds * gemm_row_tiles(gateup, H, inter);
+}
+
 __global__ void k_bf16_to_f32(const uint16_t* __restrict__ x, size_t n, float* __restrict__ y) {
   for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -467,7 +579,7 @@ __global__ void k_bf16_to_f32(const uint16_t* __restrict__ x, size_t n, float* _
 int permute_chunks(int A) { return (A + kChunk - 1) / kChunk; }
 
 hipError_t launch_permute(const int32_t* ids, int A, int E, int chunks, int32_t* hist, int32_t* lrank,
-                          int32_t* base, int32_t* seg, int2* tiles, int32_t* n_tiles, int32_t* perm,
+                          int32_t* base, int32_t* seg, int4* tiles, int32_t* n_tiles, int32_t* perm,
                           int32_t* pos_of, hipStream_t s) {
   hipLaunchKernelGGL(k_perm_count, dim3(chunks), dim3(kChunk), 0, s, ids, A, E, hist, lrank);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, hist, chunks, E, base, seg, tiles, n_tiles);
@@ -493,7 +605,7 @@ PrefillLayout prefill_layout(int T, int E, int k, int H, int I, int Is) {
   L.base = take(C * E * 4);
   L.local_rank = take(A * 4);
   L.seg = take((E + 1) * 4);
-  L.tiles = take(static_cast<size_t>(L.max_tiles) * 8);
+  L.tiles = take(static_cast<size_t>(L.max_tiles) * 16);
   L.n_tiles = take(4);
   L.perm = take(A * 4);
   L.pos_of = take(A * 4);
@@ -528,7 +640,7 @@ hipError_t launch_prefill_route(const PrefillLayout& L, uint8_t* ws, const uint1
   if (e != hipSuccess) return e;
   return launch_permute(ids, T * k, E, L.chunks, reinterpret_cast<int32_t*>(at(L.hist)),
                         reinterpret_cast<int32_t*>(at(L.local_rank)), reinterpret_cast<int32_t*>(at(L.base)),
-                        reinterpret_cast<int32_t*>(at(L.seg)), reinterpret_cast<int2*>(at(L.tiles)),
+                        reinterpret_cast<int32_t*>(at(L.seg)), reinterpret_cast<int4*>(at(L.tiles)),
                         reinterpret_cast<int32_t*>(at(L.n_tiles)), reinterpret_cast<int32_t*>(at(L.perm)),
                         reinterpret_cast<int32_t*>(at(L.pos_of)), s);
 }
@@ -548,9 +660,8 @@ GemmArgs routed_args(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16
   g.experts = experts;
   g.blob_e = blob_e;
   g.inter = I;
-  g.tiles = reinterpret_cast<const int2*>(at(L.tiles));
+  g.tiles = reinterpret_cast<const int4*>(at(L.tiles));
   g.n_tiles = reinterpret_cast<const int32_t*>(at(L.n_tiles));
-  g.seg = reinterpret_cast<const int32_t*>(at(L.seg));
   g.act = reinterpret_cast<__bf16*>(at(L.act_r));
   return g;
 }
@@ -580,10 +691,10 @@ hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint
     if (group->n < 1 || group->n > kMaxGroup) return hipErrorInvalidValue;
     g.group = *group;
   }
-  const int routed_blocks = L.max_tiles * gemm_row_tiles(true, H, I);
+  const int routed_blocks = gemm_blocks(L.max_tiles, true, H, I);
   if (with_shared) {
     const GemmArgs gs = shared_gateup_args(L, ws, x_bf16, with_shared->T, k, H, with_shared->Is, with_shared->shared);
-    const int n_shared = ((with_shared->T + kTM - 1) / kTM) * gemm_row_tiles(true, H, with_shared->Is);
+    const int n_shared = gemm_blocks((with_shared->T + kTM - 1) / kTM, true, H, with_shared->Is);
     hipLaunchKernelGGL(k_gemm_gateup2, dim3(n_shared + routed_blocks), dim3(kThreadsGemm), 0, s, g, gs, n_shared);
   } else {
     hipLaunchKernelGGL((k_gemm<true, true>), dim3(routed_blocks), dim3(kThreadsGemm), 0, s, g);
@@ -596,7 +707,7 @@ hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint
   d.out = reinterpret_cast<float*>(ws + L.out_r);
   d.wrow = reinterpret_cast<const float*>(ws + L.w);
   d.perm = reinterpret_cast<const int32_t*>(ws + L.perm);
-  hipLaunchKernelGGL((k_gemm<false, true>), dim3(L.max_tiles * gemm_row_tiles(false, H, I)), dim3(kThreadsGemm), 0, s, d);
+  hipLaunchKernelGGL((k_gemm<false, true>), dim3(gemm_blocks(L.max_tiles, false, H, I)), dim3(kThreadsGemm), 0, s, d);
   return hipGetLastError();
 }
 
@@ -605,15 +716,18 @@ hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint
   const GemmArgs gs = shared_gateup_args(L, ws, x_bf16, T, k, H, Is, shared);
   // shared gate/up: dense over tokens (unless it ran with the routed one)
   if (!gateup_done)
-    hipLaunchKernelGGL((k_gemm<true, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
-  // shared down + combine into y (each token's routed rows in rank order)
+    hipLaunchKernelGGL((k_gemm<true, false>), dim3(gemm_blocks((T + kTM - 1) / kTM, true, H, Is)), dim3(kThreadsGemm), 0, s, gs);
+  // shared down into y, then the combine (each token's routed rows in rank order)
   GemmArgs ds = gs;
   ds.A = reinterpret_cast<const __bf16*>(ws + L.act_s);
   ds.lda = Is;
   ds.out = y;
-  ds.out_r = reinterpret_cast<const float*>(ws + L.out_r);
-  ds.pos_of = reinterpret_cast<const int32_t*>(ws + L.pos_of);
-  hipLaunchKernelGGL((k_gemm<false, false>), dim3(((T + kTM - 1) / kTM) * gemm_row_tiles(false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
+  hipLaunchKernelGGL((k_gemm<false, false>), dim3(gemm_blocks((T + kTM - 1) / kTM, false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
+  const dim3 cg((H / 4 + 255) / 256, T);
+  const float* out_r = reinterpret_cast<const float*>(ws + L.out_r);
+  const int32_t* pos_of = reinterpret_cast<const int32_t*>(ws + L.pos_of);
+  if (k <= 8) hipLaunchKernelGGL(k_combine<8>, cg, dim3(256), 0, s, out_r, pos_of, k, H, y);
+  else hipLaunchKernelGGL(k_combine<kMaxTopK>, cg, dim3(256), 0, s, out_r, pos_of, k, H, y);
   return hipGetLastError();
 }
 

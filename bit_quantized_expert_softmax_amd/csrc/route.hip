@@ -185,14 +185,18 @@ __device__ void dcache_step(const DevCache& C, const int* sel_e, int k, int E, i
 __device__ void route_tail(const RouteArgs& A, double* zs, double* sel_z, int* sel_e, int* is_last_p) {
   int& is_last = *is_last_p;
   const int nb = gridDim.x;
-  // every logit store of this block has completed before the block arrives;
-  // the arrival releases them and, for the last block, acquires the others'
-  // (agent scope: the blocks of a token run on different XCDs)
+  // Every logit store of this block has completed before the block arrives:
+  // the stores are agent-scope atomics (written through to the device-coherent
+  // level, not held in this XCD's L2), s_waitcnt(0) waits for their
+  // completion, and the last block reads the logits with agent-scope atomic
+  // loads. A release/acquire arrival would add an L2 write-back (buffer_wbl2)
+  // per block for data that is already coherent: measured 15.1 -> 23.6 us for
+  // the batched router at B = 64 (512 blocks), so the arrival stays relaxed.
   const int tok = blockIdx.y;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(A.cnt + tok, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = old == nb - 1;
     if (is_last) __hip_atomic_store(A.cnt + tok, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
