@@ -62,6 +62,12 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("GU_FETCH", "GU_WRITE", "CP_FETCH", "CP_WRITE"),
                     help="turn four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of a "
                          "'--probe gateup' and a '--probe copy' run) into the traffic summary (JSON)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace run of this benchmark into the routed gate/up's "
+                         "kernel-trace summary (JSON, written to profiles/)")
+    ap.add_argument("--summarize-kernels", metavar="TRACE_DIR",
+                    help="per-kernel table (markdown) of a rocprofv3 --kernel-trace run: calls, mean and "
+                         "median duration and share of the GPU time, by kernel and launch size")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="turn a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE run of "
                          "'--probe prefill' into a per-kernel MFMA-busy table (markdown)")
@@ -69,6 +75,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gateup_routed_gemma_layer.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "trace_k_gateup_routed_gemma_layer.json")
 # sources that define the measured kernel: the summary is void once one changes
 KERNEL_SOURCES = ["bit_quantized_expert_softmax_amd/csrc/decode.hip",
                   "bit_quantized_expert_softmax_amd/csrc/device_common.h",
@@ -216,6 +223,26 @@ def cpu_baseline(layers, tokens, cid, seconds):
             "cpu_model": model}
 
 
+def summarize_kernels(d, top=60):
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("void ", "").replace("moe::(anonymous namespace)::", "").split("(")[0]
+            wg = int(r.get("Workgroup_Size_X", 0) or 0)
+            blocks = int(r.get("Grid_Size_X", 0) or 0) // max(wg, 1)
+            acc[(name, blocks, wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in acc.values())
+    lines = ["| kernel | blocks x threads | calls | mean µs | median µs | share |", "|---|---|---|---|---|---|"]
+    for (name, blocks, wg), v in sorted(acc.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        v = sorted(v)
+        lines.append(f"| `{name}` | {blocks} x {wg} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} | "
+                     f"{100 * sum(v) / total:.1f}% |")
+    return "\n".join(lines)
+
+
 def summarize_mfma(d):
     """MFMA-busy share per prefill kernel: SQ_VALU_MFMA_BUSY_CYCLES summed over
     the SIMDs / (GPU-busy cycles of one XCD x 1024 SIMDs), the MfmaUtil formula
@@ -245,6 +272,39 @@ def summarize_mfma(d):
     return "\n".join(lines)
 
 
+def summarize_trace(d):
+    """Mean and median duration (kernel trace: dispatch begin to end) of the
+    routed gate/up launches that cover all 8 routed experts (176 x 1024)."""
+    import csv
+    import glob
+
+    from synth.configs import C2
+    grid = routed_gateup_grid(C2.shape)
+    durs = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "k_gateup" in r["Kernel_Name"] and "false" in r["Kernel_Name"] and \
+                    int(r.get("Grid_Size_X", r.get("Grid_Size", 0))) == grid:
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    durs.sort()
+    return {"kernel": "k_gateup (routed experts, cache mode)", "grid": grid, "launches": len(durs),
+            "mean_us": sum(durs) / len(durs), "median_us": durs[len(durs) // 2],
+            "source_hash": kernel_source_hash(),
+            "command": "rocprofv3 --kernel-trace --stats --output-format csv -d " + d +
+                       " -o run -- python -u bench.py --steps 24 --warmup 8 --no-cpu --no-file-store",
+            "note": "kernel-trace durations of the launches of the benchmark's measured kernel"}
+
+
+def load_trace():
+    """The committed kernel-trace summary if it was taken on the current kernel source."""
+    try:
+        with open(TRACE_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("source_hash") == kernel_source_hash() else None
+
+
 def load_traffic():
     """The committed counter summary if it was taken on the current kernel source."""
     try:
@@ -259,6 +319,15 @@ def main():
     args = parse()
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return
+    if args.summarize_trace:
+        t = summarize_trace(args.summarize_trace)
+        with open(TRACE_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t, indent=1))
+        return
+    if args.summarize_kernels:
+        print(summarize_kernels(args.summarize_kernels))
         return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma))
@@ -1053,6 +1122,15 @@ def main():
     traffic = load_traffic()
     if traffic:
         detail["traffic_vs_algorithmic"] = traffic["traffic_bytes"] / gu_bytes
+    trace = load_trace()
+    # all expert weight bytes of a cache-mode layer step (the routed experts'
+    # gate/up and down, the shared expert's down) over the routed gate/up and
+    # the down kernels' event-timed durations
+    exp_bytes = k * 3 * I * (H // 2 + 2 * (H // 32)) + H * (Is // 2 + 2 * (Is // 32))
+    detail["expert_GBps_gateup_plus_down"] = exp_bytes / ((us_gu + us_dn) * 1e-6) / 1e9 if us_dn > 0 else None
+    fl = detail.get("launch_floor", {}).get("grid_176x1024")
+    if fl:
+        detail["routed_gateup_frac_of_read_floor"] = fl["us"] / us_gu
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -1076,7 +1154,9 @@ def main():
                      "frac": gbps_gu / HBM_PEAK_GBPS,
                      "traffic": traffic["traffic_bytes"] if traffic else None,
                      "kernel": "k_gateup (routed experts, cache mode)", "bytes_per_launch": gu_bytes,
-                     "mean_us": us_gu, "launches": n_gu},
+                     "mean_us": us_gu, "launches": n_gu,
+                     "trace_mean_us": trace["mean_us"] if trace else None,
+                     "trace_frac": gu_bytes / (trace["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS if trace else None},
         "cpu_baseline": cpu,
         "detail": detail,
     }
