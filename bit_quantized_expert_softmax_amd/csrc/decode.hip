@@ -33,32 +33,95 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kGroupRows = 32;  // activations per gate/up block
 
+// Entry i of a kernel-argument list, by selects over its constant-offset
+// words: scalar loads from the argument segment (indexing it at run time
+// reads it through the vector memory path, one more round trip). The empty
+// asm statements keep the compiler from folding the selects back into an
+// indexed load.
+__device__ __forceinline__ int list_at(const SlotList& L, int i) {
+  int v = L.v[0];
+  asm("" : "+s"(v));
+#pragma unroll
+  for (int t = 1; t < kMaxTopK; ++t) {
+    int c = L.v[t];
+    asm("" : "+s"(c));
+    v = i == t ? c : v;
+  }
+  return v;
+}
+
 __device__ __forceinline__ const uint8_t* source_base(const SourceSet& S, int j) {
   if (j >= S.k) return S.shared;
-  const int e = S.ids ? S.ids[j] : S.slot.v[j];
+  const int e = S.ids ? S.ids[j] : list_at(S.slot, j);
   return S.experts + static_cast<size_t>(e) * S.blob_e;
 }
 
-// Gate/up of one group of 32 (gate row i, up row i) pairs; NT tasks per lane.
-// PUB: block 0 takes the token's top-k and publishes it (P), the other blocks
-// shift down by one (a separate instantiation, so that the code of the
-// launches without it stays as it is).
-template <int NT, bool PUB>
-__global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_blocks,
+// Touches, in one batch of scalar loads with one wait, every kernel argument
+// the compute blocks of the B = 1 FFN kernels read before their first weight
+// load: the arguments span several scalar-cache lines, and a chain of first
+// touches, each issued behind the last one's wait, costs a memory round trip
+// apiece while the other blocks' loads already queue at the memory.
+__device__ __forceinline__ void touch_args(const SourceSet& S) {
+  asm volatile("" ::"s"(S.experts), "s"(S.ids), "s"(S.slot.v[0]), "s"(S.slot.v[kMaxTopK - 1]),
+               "s"(S.rsel.v[0]), "s"(S.rsel.v[kMaxTopK - 1]), "s"(S.nsel), "s"(S.shared),
+               "s"(S.blob_e), "s"(S.H), "s"(S.I), "s"(S.Is), "s"(S.k), "s"(S.z), "s"(S.E));
+}
+
+// LDS of a gate/up block (byte offsets): the logits for an in-kernel top-k
+// [E] fp64, the token's activation digits [4][ngu] uint4 (plane-major, so
+// that adjacent lanes read adjacent words) and their scales [ngu], the weight
+// scales of each 16-lane segment's rows (rps rows of ngu fp16, from the
+// 16-byte boundary at or below their first byte: seg_sc bytes a segment),
+// the block's 32 GeGLU values.
+struct GuLds {
+  size_t zs, dig, dsc, wsc, seg_sc, act, total;
+};
+__host__ __device__ inline GuLds gateup_lds(int ngu, int E, int rps) {
+  GuLds L;
+  L.zs = 0;
+  L.dig = (sizeof(double) * E + 15) & ~static_cast<size_t>(15);
+  L.dsc = L.dig + static_cast<size_t>(ngu) * sizeof(DigitGroup);
+  L.wsc = (L.dsc + 4 * static_cast<size_t>(ngu) + 15) & ~static_cast<size_t>(15);
+  L.seg_sc = (14 + 2 * static_cast<size_t>(rps) * ngu + 15) & ~static_cast<size_t>(15);
+  L.act = L.wsc + (2 * kGroupRows / rps) * L.seg_sc;
+  L.total = L.act + 4 * kGroupRows;
+  return L;
+}
+
+// Gate/up rows per 16-lane segment for nc chunk columns per lane and row: 4
+// (a block of 4 waves) while the weight chunks fit in registers, else 1
+// (1024 lanes); launches whose blocks also take a top-k keep 1024 lanes too,
+// since the block top-k's compares are spread over all the block's lanes.
+__host__ __device__ constexpr int gu_rows_per_seg(int nc, bool topk) { return topk || nc > 8 ? 1 : 4; }
+__host__ __device__ constexpr int gu_threads(int rps) { return kWave * (kGroupRows / 2) / rps; }
+
+// Gate/up of one group of 32 (gate row i, up row i) pairs; NC chunk columns
+// per lane and row, RPS rows per 16-lane segment (a block of 16/RPS waves).
+// PUB: block 0 takes the token's top-k and publishes it (P), the other
+// blocks shift down by one (a separate instantiation, so that the code of
+// the launches without it stays as it is).
+template <int NC, int RPS, bool PUB>
+__global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_routed_blocks,
                                                      const DigitGroup* __restrict__ udig,
                                                      const float* __restrict__ usc,
                                                      DigitGroup* __restrict__ adig,
                                                      float* __restrict__ asc, FillList F, TopkPublish P) {
+  constexpr int BT = kWave * 16 / RPS;  // threads of the block
   extern __shared__ uint4 lds_raw[];
   __shared__ double sel_z[kMaxTopK];
   __shared__ int sel_e[kMaxTopK];
+  touch_args(S);
+  asm volatile("" ::"s"(n_routed_blocks), "s"(udig), "s"(usc), "s"(adig), "s"(asc), "s"(F.n),
+               "s"(F.blocks_per_blob));
   const int ngu = S.H / kGroup;
+  const GuLds lay = gateup_lds(ngu, S.z ? S.E : (PUB ? P.E : 0), RPS);
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_raw);
   int bx = blockIdx.x;
   if constexpr (PUB) {
     // the token's top-k and its publication to the host, ahead of the rest
     if (bx == 0) {
-      double* zs = reinterpret_cast<double*>(reinterpret_cast<float*>(lds_raw) + 2 * kGroupRows * ngu + 2);
-      for (int f = threadIdx.x; f < P.E; f += kThreads) zs[f] = P.z[f];
+      double* zs = reinterpret_cast<double*>(lds + lay.zs);
+      for (int f = threadIdx.x; f < P.E; f += BT) zs[f] = P.z[f];
       __syncthreads();
       topk_block(zs, P.E, P.k, sel_z, sel_e, P.ids, P.w, P.ids2, P.w2);
       if (threadIdx.x == 0) {
@@ -93,11 +156,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
       dst = reinterpret_cast<uint4*>(F.dst[m]);
     }
     constexpr int U = 4;
-    for (size_t i0 = lo; i0 < hi; i0 += static_cast<size_t>(kThreads) * U) {
+    for (size_t i0 = lo; i0 < hi; i0 += static_cast<size_t>(BT) * U) {
       uint4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const size_t i = i0 + threadIdx.x + static_cast<size_t>(kThreads) * u;
+        const size_t i = i0 + threadIdx.x + static_cast<size_t>(BT) * u;
         v[u] = src[i < hi ? i : hi - 1];
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -105,16 +168,14 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
       // kernels, so it need not stay in (and be written back from) the L2
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const size_t i = i0 + threadIdx.x + static_cast<size_t>(kThreads) * u;
+        const size_t i = i0 + threadIdx.x + static_cast<size_t>(BT) * u;
         if (i < hi) store_nt16(dst + i, v[u]);
       }
     }
     return;
   }
   const int bid = bx - nfill;
-  __shared__ float rowsum[2 * kGroupRows];
-  float* part = reinterpret_cast<float*>(lds_raw);                          // [64][ngu]
-  double* zs = reinterpret_cast<double*>(part + 2 * kGroupRows * ngu + 2);  // [E]
+  double* zs = reinterpret_cast<double*>(lds + lay.zs);  // [E]
 
   // blocks [0, n_routed_blocks): groups of the routed ranks (all k, or the
   // selected ones); the rest: groups of the shared expert
@@ -123,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   int grp;  // group of 32 activations in [0, (k*I + I_s)/32)
   if (bid < n_routed_blocks) {
     const int ls = bid / gpr;
-    grp = (S.nsel > 0 ? S.rsel.v[ls] : ls) * gpr + bid % gpr;
+    grp = (S.nsel > 0 ? list_at(S.rsel, ls) : ls) * gpr + bid % gpr;
   } else {
     grp = routed_groups + (bid - n_routed_blocks);
   }
@@ -141,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   // from the logits; the first block publishes ids and weights for the down kernel
   const uint8_t* base;
   if (src < S.k && S.z) {
-    for (int f = threadIdx.x; f < S.E; f += kThreads) zs[f] = S.z[f];
+    for (int f = threadIdx.x; f < S.E; f += BT) zs[f] = S.z[f];
     __syncthreads();
     const bool first = grp == 0;
     topk_block(zs, S.E, S.k, sel_z, sel_e, first ? S.ids_g : nullptr, first ? S.w_g : nullptr,
@@ -152,57 +213,117 @@ __global__ __launch_bounds__(kThreads) void k_gateup(SourceSet S, int n_routed_b
   }
   const BlobOffsets o = blob_offsets(S.H, inter);
   const size_t rowb = static_cast<size_t>(S.H) / 2;
-  // Lane (r0, c) = (threadIdx / ngu, threadIdx % ngu) owns chunk column c of
-  // rows r0, r0 + R, ... (R = kThreads / ngu; rows 0..31 gate, 32..63 up).
-  // It loads that chunk's activation digits once into registers, next to its
-  // weights, so no staging pass and no per-chunk LDS reads are needed;
-  // consecutive lanes read consecutive 16-byte chunks of a row.
-  const int R = kThreads / ngu;
-  const int c = threadIdx.x % ngu;
-  const int r0 = threadIdx.x / ngu;
-  const uint8_t* gq = base + o.gate_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(c);
-  const uint8_t* uq = base + o.up_q + static_cast<size_t>(i0) * rowb + 16 * static_cast<size_t>(c);
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(base + o.gate_s) + static_cast<size_t>(i0) * ngu + c;
-  const uint16_t* us = reinterpret_cast<const uint16_t*>(base + o.up_s) + static_cast<size_t>(i0) * ngu + c;
-  // the activation digits first: loads retire in order, so chunk t can be
-  // consumed as soon as its own bytes are in while later chunks still stream
-  const DigitGroup xd = udig[c];
-  const float xs = usc[c];
-  uint4 wv[NT];
-  uint16_t sw[NT];
+  // Wave w owns RPS gate rows and RPS up rows per pair of 16-lane segments:
+  // segments 0 and 1 gate rows 2 RPS w + [0, RPS) and + [RPS, 2 RPS),
+  // segments 2 and 3 the same up rows. Lane j of a segment takes chunk
+  // columns j, j + 16, ... (NC of them; past ngu masked) of each of its rows,
+  // so a row's sum stays in its segment's registers (DPP) and the GeGLU pairs
+  // meet in one wave: no partial sums in LDS. The token's activation digits
+  // and their scales (L2-resident: every block reads them) and the segment's
+  // rows' weight scales are staged in LDS; the weight chunks go to registers.
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int seg = lane >> 4;
+  const int j = lane & 15;
+  const bool upr = seg >= 2;
+  const int rb = 2 * RPS * wave + RPS * (seg & 1);  // first row of the segment, in its half
+  const uint8_t* qrow = base + (upr ? o.up_q : o.gate_q) + static_cast<size_t>(i0 + rb) * rowb;
+  // the segment's rows' weight scales, from the 16-byte boundary at or below
+  // them (the blob and its scale arrays start on one, and the bytes after the
+  // up scales are the down scales, so the vectors stay inside the blob)
+  const uint8_t* sbeg = base + (upr ? o.up_s : o.gate_s) + static_cast<size_t>(i0 + rb) * ngu * 2;
+  const int lead = static_cast<int>(reinterpret_cast<uintptr_t>(sbeg) & 15);
+  const u32x4* svec = reinterpret_cast<const u32x4*>(sbeg - lead);
+  uint4* sdig = reinterpret_cast<uint4*>(lds + lay.dig);    // [4][ngu]
+  float* sdsc = reinterpret_cast<float*>(lds + lay.dsc);    // [ngu]
+  uint8_t* sseg = lds + lay.wsc + (4 * wave + seg) * lay.seg_sc;
+  const uint16_t* swsc = reinterpret_cast<const uint16_t*>(sseg + lead);  // [RPS][ngu]
+  float* sact = reinterpret_cast<float*>(lds + lay.act);    // [32]
+  // staging loads, issued first (loads return in order): digit items
+  // i = 4 c + q, digit scales and the segment's scale vectors, clamped (the
+  // same bytes to the same place where repeated)
+  constexpr int DI = (4 * 16 * NC + BT - 1) / BT;                    // digit items per lane
+  constexpr int SI = (16 * NC + BT - 1) / BT;                        // digit scales per lane
+  constexpr int WV = ((14 + 2 * RPS * 16 * NC + 15) / 16 + 15) / 16;  // scale vectors per lane
+  const int nd = 4 * ngu;
+  const int nv = (lead + 2 * RPS * ngu + 15) / 16;  // the segment's scale vectors
+  // (16-byte values as vector types: arrays of them stay in registers)
+  u32x4 dv[DI];
+  float sv[SI];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int r = r0 + R * t;
-    r = r < 2 * kGroupRows ? r : 2 * kGroupRows - 1;  // clamped: loaded, not stored
-    const bool up = r >= kGroupRows;
-    const int rr = up ? r - kGroupRows : r;
-    wv[t] = load_w16((up ? uq : gq) + static_cast<size_t>(rr) * rowb);
-    sw[t] = (up ? us : gs)[static_cast<size_t>(rr) * ngu];
+  for (int u = 0; u < DI; ++u) {
+    const int di = static_cast<int>(threadIdx.x) + BT * u;
+    dv[u] = reinterpret_cast<const u32x4*>(udig)[di < nd ? di : nd - 1];
+  }
+#pragma unroll
+  for (int u = 0; u < SI; ++u) {
+    const int si = static_cast<int>(threadIdx.x) + BT * u;
+    sv[u] = usc[si < ngu ? si : ngu - 1];
+  }
+  u32x4 wsv[WV];
+#pragma unroll
+  for (int u = 0; u < WV; ++u) {
+    const int vi = j + 16 * u;
+    wsv[u] = svec[vi < nv ? vi : nv - 1];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 wv[RPS][NC];
+#pragma unroll
+  for (int r = 0; r < RPS; ++r) {
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+      int cc = j + 16 * m;
+      cc = cc < ngu ? cc : ngu - 1;  // clamped: loaded, not summed
+      wv[r][m] = load_w16(qrow + static_cast<size_t>(r) * rowb + 16 * static_cast<size_t>(cc));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int r = r0 + R * t;
-    const float p = static_cast<float>(chunk_dot(wv[t], xd)) * (h2f(sw[t]) * xs);
-    if (r < 2 * kGroupRows) part[r * ngu + c] = p;
+  for (int u = 0; u < DI; ++u) {
+    int di = static_cast<int>(threadIdx.x) + BT * u;
+    di = di < nd ? di : nd - 1;
+    reinterpret_cast<u32x4*>(sdig)[(di & 3) * ngu + (di >> 2)] = dv[u];
   }
-  __syncthreads();
-  // 64 row sums: 16 lanes per row, 4 rows per wave, fixed order
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  {
-    const int r = 4 * wave + (lane >> 4);
-    const int l = lane & 15;
-    float acc = 0.f;
-    for (int c = l; c < ngu; c += 16) acc += part[r * ngu + c];
-    acc = dpp_sum<16>(acc);
-    if (l == 0) rowsum[r] = acc;
+#pragma unroll
+  for (int u = 0; u < SI; ++u) {
+    const int si = static_cast<int>(threadIdx.x) + BT * u;
+    sdsc[si < ngu ? si : ngu - 1] = sv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < WV; ++u) {
+    const int vi = j + 16 * u;
+    reinterpret_cast<u32x4*>(sseg)[vi < nv ? vi : nv - 1] = wsv[u];
+  }
+  block_sync();  // the weight loads stay in flight
+  float acc[RPS];
+#pragma unroll
+  for (int r = 0; r < RPS; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int m = 0; m < NC; ++m) {
+    const int cc = j + 16 * m;
+    const int cl = cc < ngu ? cc : ngu - 1;
+    DigitGroup xd;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xd.p[q] = sdig[q * ngu + cl];
+    const float xs = sdsc[cl];
+#pragma unroll
+    for (int r = 0; r < RPS; ++r) {
+      const float p = static_cast<float>(chunk_dot(wv[r][m], xd)) * (h2f(swsc[r * ngu + cl]) * xs);
+      acc[r] += cc < ngu ? p : 0.f;
+    }
+  }
+  // row sums over the 16 lanes (the order: each lane's columns j, j + 16, ...
+  // in turn, then the DPP tree); the gate lanes take the matching up sums
+#pragma unroll
+  for (int r = 0; r < RPS; ++r) {
+    const float g = dpp_sum<16>(acc[r]);
+    const float upv = __shfl_xor(g, 32, kWave);
+    if (seg < 2 && j == 0) sact[rb + r] = gelu_tanh(g) * upv;
   }
   __syncthreads();
   if (wave == 0) {
-    // GeGLU of the 32 activations of this group, then their digit planes
-    float a = 0.f;
-    if (lane < kGroupRows) a = gelu_tanh(rowsum[lane]) * rowsum[kGroupRows + lane];
+    // the group's 32 GeGLU values as digit planes
+    const float a = lane < kGroupRows ? sact[lane] : 0.f;
     quant_pair_of_groups(a, grp, grp + 1, adig, asc);
   }
 }
@@ -218,6 +339,8 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
                                                    const uint16_t* __restrict__ add_in,
                                                    int residual, float* __restrict__ y) {
   extern __shared__ uint4 lds_raw[];
+  touch_args(S);
+  asm volatile("" ::"s"(w), "s"(adig), "s"(asc), "s"(x), "s"(add_in), "s"(residual), "s"(y));
   const int gi = S.I / kGroup;
   const int gsh = S.Is / kGroup;
   const int nga = S.k * gi + gsh;  // chunks of the virtual row
@@ -295,7 +418,13 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
 
 size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
   const size_t ngu = H / kGroup, nga = (static_cast<size_t>(k) * I + Is) / kGroup;
-  const size_t gu = (2 * kGroupRows * ngu + 2) * 4 + sizeof(double) * E;
+  // the largest over the row splits a launch may take (the staged scales'
+  // padding grows as rows per segment shrink)
+  size_t gu = 0;
+  for (int rps : {1, 4}) {
+    const size_t b = gateup_lds(static_cast<int>(ngu), E, rps).total;
+    gu = b > gu ? b : gu;
+  }
   const size_t dn = static_cast<size_t>(kOutPerBlock) * nga * 4;
   return gu > dn ? gu : dn;
 }
@@ -316,36 +445,43 @@ hipError_t launch_ffn_gateup(const SourceSet& src, bool do_routed, bool do_share
       return hipErrorInvalidValue;
     P = *topk;
   }
+  const int ngu = src.H / kGroup;
+  const int need = (ngu + 15) / 16;  // chunk columns per lane and row
+  if (need > 16) return hipErrorInvalidValue;
+  const int nc = need <= 4 ? need : (need <= 6 ? 6 : (need <= 8 ? 8 : (need <= 12 ? 12 : 16)));
+  const bool with_topk = topk != nullptr || (do_routed && src.z != nullptr);
+  const int rps = gu_rows_per_seg(nc, with_topk);
+  F.blocks_per_blob *= kThreads / gu_threads(rps);  // the same lanes per blob
   const int nr = do_routed ? (src.nsel > 0 ? src.nsel : src.k) * (src.I / kGroupRows) : 0;
   const int shared = src.Is / kGroupRows;
   const int n = (topk ? 1 : 0) + F.n * F.blocks_per_blob + nr + (do_shared ? shared : 0);
   if (n == 0) return hipSuccess;
-  const int ngu = src.H / kGroup;
   const int Ez = src.z ? src.E : (topk ? topk->E : 0);
-  const size_t lds = static_cast<size_t>(2 * kGroupRows * ngu + 2) * 4 + sizeof(double) * Ez;
-  if (ngu > kThreads) return hipErrorInvalidValue;
-  const int rows_per_pass = kThreads / ngu;
-  const int need = (2 * kGroupRows + rows_per_pass - 1) / rows_per_pass;
-#define MOE_GATEUP_PUB(NT, PUB)                                                                          \
+  const size_t lds = gateup_lds(ngu, Ez, rps).total;
+#define MOE_GATEUP_RPS(NT, RPS, PUB)                                                                     \
   do {                                                                                                   \
-    if (t0) hipExtLaunchKernelGGL((k_gateup<NT, PUB>), dim3(n), dim3(kThreads), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F, P); \
-    else hipLaunchKernelGGL((k_gateup<NT, PUB>), dim3(n), dim3(kThreads), lds, s, src, nr, udig, usc, adig, asc, F, P);               \
+    constexpr int BT_ = gu_threads(RPS);                                                                 \
+    if (t0) hipExtLaunchKernelGGL((k_gateup<NT, RPS, PUB>), dim3(n), dim3(BT_), lds, s, t0, t1, 0, src, nr, udig, usc, adig, asc, F, P); \
+    else hipLaunchKernelGGL((k_gateup<NT, RPS, PUB>), dim3(n), dim3(BT_), lds, s, src, nr, udig, usc, adig, asc, F, P);               \
   } while (0)
-#define MOE_GATEUP(NT)                        \
-  do {                                        \
-    if (topk) MOE_GATEUP_PUB(NT, true);       \
-    else MOE_GATEUP_PUB(NT, false);           \
+#define MOE_GATEUP(NT)                                               \
+  do {                                                               \
+    if (topk) MOE_GATEUP_RPS(NT, 1, true);                           \
+    else if (with_topk) MOE_GATEUP_RPS(NT, 1, false);                \
+    else MOE_GATEUP_RPS(NT, gu_rows_per_seg(NT, false), false);      \
   } while (0)
-  if (need <= 1) MOE_GATEUP(1);
-  else if (need <= 2) MOE_GATEUP(2);
-  else if (need <= 4) MOE_GATEUP(4);
-  else if (need <= 6) MOE_GATEUP(6);
-  else if (need <= 8) MOE_GATEUP(8);
-  else if (need <= 12) MOE_GATEUP(12);
-  else if (need <= 16) MOE_GATEUP(16);
-  else return hipErrorInvalidValue;  // H beyond what the LDS budget admits
+  switch (nc) {
+    case 1: MOE_GATEUP(1); break;
+    case 2: MOE_GATEUP(2); break;
+    case 3: MOE_GATEUP(3); break;
+    case 4: MOE_GATEUP(4); break;
+    case 6: MOE_GATEUP(6); break;
+    case 8: MOE_GATEUP(8); break;
+    case 12: MOE_GATEUP(12); break;
+    default: MOE_GATEUP(16); break;
+  }
 #undef MOE_GATEUP
-#undef MOE_GATEUP_PUB
+#undef MOE_GATEUP_RPS
   return hipGetLastError();
 }
 

@@ -214,4 +214,21 @@ __device__ __forceinline__ void store_nt16(uint4* p, uint4 v) {
   __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
 
+// Barrier of a block that keeps its vector loads in flight. __syncthreads()
+// orders memory with a fence whose lowering waits for every outstanding
+// vector load, loads meant for later work included, which would drain a
+// prefetch. Here each wave has already waited (by data dependence or an
+// explicit s_waitcnt) for its own loads whose LDS data the others read next,
+// waits for its own LDS accesses (lgkmcnt 0), then meets the others; the empty
+// asm statements keep the compiler from moving memory accesses across,
+// sched_barrier keeps the scheduler from moving instructions.
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only (vmcnt 63, expcnt 7: no wait)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace moe

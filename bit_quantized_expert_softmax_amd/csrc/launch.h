@@ -93,7 +93,7 @@ struct FillList {
   const uint8_t* src[kMaxTopK];  // device-accessible pinned host blobs
   uint8_t* dst[kMaxTopK];        // slots in HBM
   int n;                         // number of blobs
-  int blocks_per_blob;
+  int blocks_per_blob;           // in units of 1024 lanes (the launch may split them)
   size_t bytes;                  // blob size, a multiple of 16
   const int32_t* dlist;
   const uint8_t* src_base;

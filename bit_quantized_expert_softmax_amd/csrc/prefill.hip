@@ -192,22 +192,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Barrier of the GEMM blocks. __syncthreads() orders memory with a fence
-// whose lowering waits for every outstanding vector load, the loads of the
-// later steps included, which would drain the pipeline every step. Here each
-// wave has already waited for its own loads whose LDS data the others read
-// next (wait_vmcnt), waits for its own LDS reads (lgkmcnt 0), then meets the
-// others; the empty asm statements keep the compiler from moving memory
-// accesses across, sched_barrier keeps the scheduler from moving instructions.
-__device__ __forceinline__ void block_sync() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only (vmcnt 63, expcnt 7: no wait)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Byte B of x as a float (v_cvt_f32_ubyteB; written out because the compiler
 // folds the surrounding masks and then loses the byte-select forms).
 template <int B>
