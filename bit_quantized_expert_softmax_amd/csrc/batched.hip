@@ -82,18 +82,23 @@ struct MArgs {
 // 8 signed nibbles (k = 0..7 in bits 4k..4k+3) times scale s, as fp16 in the
 // order (0,4,1,5,2,6,3,7).
 __device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
-  const f16x2 bias = {static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
   const f16x2 sc = {s, s};
-  // the two nibbles at bits 4i and 16 + 4i: (b & 0xF) ^ 8 is n + 8 for the
-  // two's complement nibble n, and the same xor sets the exponent bits of
-  // 1024 (0x6400), so one and-xor (v_bitop3) gives fp16(1024 + n + 8)
-  auto pair = [&](uint32_t v) __attribute__((always_inline)) {
-    return (__builtin_bit_cast(f16x2, (v & 0x000F000Fu) ^ 0x64086408u) - bias) * sc;
+  // The nibbles at bits 4i and 16 + 4i for i = 0, 1 sit in the fp16
+  // mantissa in place; w >> 8 brings i = 2, 3 to the same places. (b & 0xF)
+  // ^ 8 is n + 8 for the two's complement nibble n, and the same xor sets
+  // the exponent: at bits 0-3 it gives fp16(1024 + n + 8) (exponent 0x6400),
+  // at bits 4-7 the mantissa is 16 (n + 8), so exponent 0x5400 gives
+  // fp16(64 + n + 8). One and-xor (v_bitop3) per pair, one shift per 8
+  // nibbles; n itself is exact, so the one rounding is that of n * s.
+  auto pair = [&](uint32_t v, uint32_t mask, uint32_t bits, float bias) __attribute__((always_inline)) {
+    const f16x2 bb = {static_cast<_Float16>(bias), static_cast<_Float16>(bias)};
+    return (__builtin_bit_cast(f16x2, (v & mask) ^ bits) - bb) * sc;
   };
-  const f16x2 h0 = pair(w);
-  const f16x2 h1 = pair(w >> 4);
-  const f16x2 h2 = pair(w >> 8);
-  const f16x2 h3 = pair(w >> 12);
+  const uint32_t w8 = w >> 8;
+  const f16x2 h0 = pair(w, 0x000F000Fu, 0x64086408u, 1032.0f);
+  const f16x2 h1 = pair(w, 0x00F000F0u, 0x54805480u, 72.0f);
+  const f16x2 h2 = pair(w8, 0x000F000Fu, 0x64086408u, 1032.0f);
+  const f16x2 h3 = pair(w8, 0x00F000F0u, 0x54805480u, 72.0f);
   return f16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
