@@ -35,6 +35,10 @@ using moe::fail;
 namespace moe {
 moe_status check_shape(const moe_shape* sh, const char* fn);
 
+// Widest hidden size of the one-token gate/up: a lane takes at most 16
+// chunks (quantisation groups) of a row, 16 lanes a row.
+constexpr int kMaxDecodeHidden = 16 * 16 * kGroup;
+
 namespace {
 
 struct WsLayout {
@@ -321,6 +325,9 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
   if (!d || !out) return fail(MOE_EINVAL, "%s: NULL argument", fn);
   if (max_B < 1 || max_B > 4096 || max_T < 0 || max_T > 65536)
     return fail(MOE_ESHAPE, "%s: max_B %d / max_T %d out of range", fn, max_B, max_T);
+  if (sh->hidden > moe::kMaxDecodeHidden)
+    return fail(MOE_ESHAPE, "%s: hidden %d above %d (the one-token gate/up takes at most 16 chunks of a row per lane)",
+                fn, sh->hidden, moe::kMaxDecodeHidden);
   const int nga = (sh->top_k * sh->inter + sh->shared_inter) / moe::kGroup;
   if (nga > 512)
     return fail(MOE_ESHAPE, "%s: (top_k*inter + shared_inter)/32 = %d exceeds 512", fn, nga);

@@ -282,6 +282,7 @@ typedef struct moe_decode_stats {
 moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t max_T,
                                      size_t* out);
 /* Validates, clears the workspace counters (synchronously) and returns a handle.
+ * The one-token kernels take hidden up to 8192 (MOE_ESHAPE above).
  * max_B > 1 (batched decode, resident mode) also needs the batched kernels'
  * per-block LDS (the staged group scales of 128 weight rows of length H, and
  * the activation slices of up to 64 tokens) to fit 64 KiB: MOE_ESHAPE if not
