@@ -8,20 +8,21 @@
 // and the layer output is o_shared + sum_j w_j o_j.
 //
 // The work is HBM-bound (~3.5 flop per weight byte) and short (tens of MB per
-// token), so both kernels are shaped for latency: 1024-thread blocks (16 waves
-// per CU); every lane owns one 16-byte chunk column and a few rows of it,
-// loads that chunk's activation digits once into registers and issues all of
-// its loads before any is consumed; per-chunk partial products are reduced in
-// LDS in a fixed order; the two kernels do not synchronise across blocks.
+// token), so both kernels are shaped for latency: every lane issues all of its
+// loads before any is consumed, each block reads its kernel arguments in one
+// batch, row sums are fixed-order DPP trees, and the two kernels do not
+// synchronise across blocks.
 //
-// gate/up kernel: one block per group of 32 activations of one source: the 32
-//   gate rows and 32 up rows (contiguous in the blob) are streamed as one
-//   span; after the row sums, the GeGLU values of the group are quantised to
-//   digit planes for the down projection.
-// down kernel: one block per 11 outputs; an output gathers the down rows of
-//   all k+1 sources as one virtual row of (k*I + I_s)/32 chunks, the routing
-//   weight folded into each group's scale; the row sum is the weighted
-//   combine, in a fixed order, without atomics.
+// gate/up kernel: one block per group of 32 activations of one source (its 32
+//   gate rows and 32 up rows); a 16-lane segment owns whole rows, so the row
+//   sums stay in registers; the token's activation digits are staged in LDS;
+//   after the row sums, the GeGLU values of the group are quantised to digit
+//   planes for the down projection.
+// down kernel: 1024-thread blocks, one per 11 outputs; an output gathers the
+//   down rows of all k+1 sources as one virtual row of (k*I + I_s)/32 chunks,
+//   the routing weight folded into each group's scale; a lane owns one chunk
+//   column (its activation digits in registers) and a few outputs; the row
+//   sum is the weighted combine, in a fixed order, without atomics.
 #include <hip/hip_ext.h>
 
 #include "launch.h"
@@ -30,7 +31,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 1024;  // lanes of a down block (and the unit of fill-block lanes)
 constexpr int kGroupRows = 32;  // activations per gate/up block
 
 // Entry i of a kernel-argument list, by selects over its constant-offset
