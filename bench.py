@@ -93,9 +93,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-# lanes per block of the routed gate/up launch (4 waves; launches that carry a
+# lanes per block of the routed gate/up launch (8 waves; launches that carry a
 # top-k use 1024)
-GU_ROUTED_THREADS = 256
+GU_ROUTED_THREADS = 512
 
 
 def routed_gateup_grid(sh):
@@ -148,7 +148,7 @@ def summarize_pmc(dirs):
                 "rocprofv3 --pmc WRITE_SIZE --output-format csv -d " + dirs[3] + " -o run -- "
                 "python -u bench.py --probe copy",
                 "python bench.py --summarize-pmc " + " ".join(dirs)],
-            "note": "FETCH_SIZE / WRITE_SIZE (KiB units) of the routed gate/up launches (176 x 256), each "
+            "note": "FETCH_SIZE / WRITE_SIZE (KiB units) of the routed gate/up launches (176 x 512), each "
                     "scaled by the bytes per unit the same counter reads for a plain 1 GiB device copy; "
                     "algorithmic bytes per launch 17,875,968"}
 
@@ -279,7 +279,7 @@ def summarize_mfma(d):
 
 def summarize_trace(d):
     """Mean and median duration (kernel trace: dispatch begin to end) of the
-    routed gate/up launches that cover all 8 routed experts (176 x 256)."""
+    routed gate/up launches that cover all 8 routed experts (176 x 512)."""
     import csv
     import glob
 

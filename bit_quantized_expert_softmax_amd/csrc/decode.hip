@@ -73,7 +73,7 @@ __device__ __forceinline__ void touch_args(const SourceSet& S) {
 // that adjacent lanes read adjacent words) and their scales [ngu], the weight
 // scales of each 16-lane segment's rows (rps rows of ngu fp16, from the
 // 16-byte boundary at or below their first byte: seg_sc bytes a segment),
-// the block's 32 GeGLU values.
+// the block's 64 row sums.
 struct GuLds {
   size_t zs, dig, dsc, wsc, seg_sc, act, total;
 };
@@ -85,15 +85,18 @@ __host__ __device__ inline GuLds gateup_lds(int ngu, int E, int rps) {
   L.wsc = (L.dsc + 4 * static_cast<size_t>(ngu) + 15) & ~static_cast<size_t>(15);
   L.seg_sc = (14 + 2 * static_cast<size_t>(rps) * ngu + 15) & ~static_cast<size_t>(15);
   L.act = L.wsc + (2 * kGroupRows / rps) * L.seg_sc;
-  L.total = L.act + 4 * kGroupRows;
+  L.total = L.act + 4 * 2 * kGroupRows;
   return L;
 }
 
-// Gate/up rows per 16-lane segment for nc chunk columns per lane and row: 4
-// (a block of 4 waves) while the weight chunks fit in registers, else 1
-// (1024 lanes); launches whose blocks also take a top-k keep 1024 lanes too,
-// since the block top-k's compares are spread over all the block's lanes.
-__host__ __device__ constexpr int gu_rows_per_seg(int nc, bool topk) { return topk || nc > 8 ? 1 : 4; }
+// Gate/up rows per 16-lane segment: 2 (a block of 8 waves, 2 per SIMD);
+// launches whose blocks also take a top-k keep 1024 lanes (1 row a segment),
+// since the block top-k's compares are spread over all the block's lanes, and
+// so do rows of more than 8 x 16 chunks, whose weights would not fit in
+// registers. Fewer waves issue the dot products too slowly (one wave per SIMD
+// issues a VALU instruction every 12 cycles, four every 3); more read the
+// staged digits from LDS too often (once per column and lane, for RPS rows).
+__host__ __device__ constexpr int gu_rows_per_seg(int nc, bool topk) { return topk || nc > 8 ? 1 : 2; }
 __host__ __device__ constexpr int gu_threads(int rps) { return kWave * (kGroupRows / 2) / rps; }
 
 // Gate/up of one group of 32 (gate row i, up row i) pairs; NC chunk columns
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
   float* sdsc = reinterpret_cast<float*>(lds + lay.dsc);    // [ngu]
   uint8_t* sseg = lds + lay.wsc + (4 * wave + seg) * lay.seg_sc;
   const uint16_t* swsc = reinterpret_cast<const uint16_t*>(sseg + lead);  // [RPS][ngu]
-  float* sact = reinterpret_cast<float*>(lds + lay.act);    // [32]
+  float* sact = reinterpret_cast<float*>(lds + lay.act);    // [64]: gate, then up row sums
   // staging loads, issued first (loads return in order): digit items
   // i = 4 c + q, digit scales and the segment's scale vectors, clamped (the
   // same bytes to the same place where repeated)
@@ -268,11 +271,12 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
     wsv[u] = svec[vi < nv ? vi : nv - 1];
   }
   __builtin_amdgcn_sched_barrier(0);
+  // issued in the order of use (column by column, the rows of a column together)
   uint4 wv[RPS][NC];
 #pragma unroll
-  for (int r = 0; r < RPS; ++r) {
+  for (int m = 0; m < NC; ++m) {
 #pragma unroll
-    for (int m = 0; m < NC; ++m) {
+    for (int r = 0; r < RPS; ++r) {
       int cc = j + 16 * m;
       cc = cc < ngu ? cc : ngu - 1;  // clamped: loaded, not summed
       wv[r][m] = load_w16(qrow + static_cast<size_t>(r) * rowb + 16 * static_cast<size_t>(cc));
@@ -314,17 +318,16 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
     }
   }
   // row sums over the 16 lanes (the order: each lane's columns j, j + 16, ...
-  // in turn, then the DPP tree); the gate lanes take the matching up sums
+  // in turn, then the DPP tree), gate rows then up rows in LDS; wave 0 takes
+  // the GeGLU of the 32 pairs and writes their digit planes
 #pragma unroll
   for (int r = 0; r < RPS; ++r) {
-    const float g = dpp_sum<16>(acc[r]);
-    const float upv = __shfl_xor(g, 32, kWave);
-    if (seg < 2 && j == 0) sact[rb + r] = gelu_tanh(g) * upv;
+    const float rs = dpp_sum<16>(acc[r]);
+    if (j == 0) sact[(upr ? kGroupRows : 0) + rb + r] = rs;
   }
   __syncthreads();
   if (wave == 0) {
-    // the group's 32 GeGLU values as digit planes
-    const float a = lane < kGroupRows ? sact[lane] : 0.f;
+    const float a = lane < kGroupRows ? gelu_tanh(sact[lane]) * sact[kGroupRows + lane] : 0.f;
     quant_pair_of_groups(a, grp, grp + 1, adig, asc);
   }
 }
@@ -422,7 +425,7 @@ size_t decode_lds_bytes(int H, int E, int k, int I, int Is) {
   // the largest over the row splits a launch may take (the staged scales'
   // padding grows as rows per segment shrink)
   size_t gu = 0;
-  for (int rps : {1, 4}) {
+  for (int rps : {1, 2}) {
     const size_t b = gateup_lds(static_cast<int>(ngu), E, rps).total;
     gu = b > gu ? b : gu;
   }
