@@ -12,6 +12,10 @@
 // handful of scalar ops, with no nibble unpacking at all. The weight side is
 // exact; the activation side is rounded to 16 bits relative to its group's
 // largest magnitude (error <= max|x_g| / (2 kQmax) per element).
+//
+// The digits need no digit-by-digit loop: for |q| <= 0x7777 every nibble of
+// q + 0x8888 is d_i + 8 (no borrow leaves a nibble), so the two's complement
+// digit nibbles d_i & 15 are the nibbles of (q + 0x8888) ^ 0x8888.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -21,8 +25,14 @@
 namespace moe {
 
 constexpr int kGroup = 32;
-// Largest |q| whose balanced base-16 expansion has d3 in -8..7 on both signs.
+// Largest |q| whose balanced base-16 expansion has d3 in -8..7 on both signs
+// (0x7777).
 constexpr int kQmax = 30583;
+
+// The 4 digit nibbles of q (|q| <= kQmax), digit d in bits 4d..4d+3.
+__device__ __forceinline__ uint32_t digit_nibbles(int q) {
+  return (static_cast<uint32_t>(q + 0x8888) ^ 0x8888u) & 0xFFFFu;
+}
 constexpr int kWave = 64;
 
 // Digit planes of one group: 4 positions x uint4 (digit words 0..3).
@@ -134,17 +144,12 @@ __device__ __forceinline__ void quant_pair_of_groups(float v, int g0, int ng, Di
   const float inv = m > 0.f ? static_cast<float>(kQmax) / m : 0.f;
   int q = static_cast<int>(rintf(v * inv));
   q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
-  const int d0 = ((q + 8) & 15) - 8;
-  q = (q - d0) / 16;
-  const int d1 = ((q + 8) & 15) - 8;
-  q = (q - d1) / 16;
-  const int d2 = ((q + 8) & 15) - 8;
-  const int d3 = (q - d2) / 16;
+  const uint32_t nb = digit_nibbles(q);
   const int sh = 4 * (i & 7);
-  uint32_t w0 = static_cast<uint32_t>(d0 & 15) << sh;
-  uint32_t w1 = static_cast<uint32_t>(d1 & 15) << sh;
-  uint32_t w2 = static_cast<uint32_t>(d2 & 15) << sh;
-  uint32_t w3 = static_cast<uint32_t>(d3 & 15) << sh;
+  uint32_t w0 = (nb & 15u) << sh;
+  uint32_t w1 = ((nb >> 4) & 15u) << sh;
+  uint32_t w2 = ((nb >> 8) & 15u) << sh;
+  uint32_t w3 = (nb >> 12) << sh;
   // OR over each aligned 8 lanes: quads, then the mirrored quad
   w0 |= dpp<0xB1>(w0);
   w1 |= dpp<0xB1>(w1);

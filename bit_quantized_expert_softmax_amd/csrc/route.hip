@@ -220,9 +220,15 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int H = A.H, ngu = H / kGroup, n8 = H / 8;
-  const int nb = gridDim.x;
   const int gw = blockIdx.x * kWaves + wave;        // global wave index
   const int e = gw < A.E ? gw : A.E - 1;            // expert row of this wave
+  // blocks past the logit blocks quantise: wave qw takes steps qw, qw + nqw,
+  // ... of the token (64 x 8 inputs each, 16 groups, every lane); the logit
+  // waves skip the quantisation, the quantising waves the dot products
+  const int nlog = (A.E + kWaves - 1) / kWaves;
+  const bool qblk = static_cast<int>(blockIdx.x) >= nlog;
+  const int qw = (static_cast<int>(blockIdx.x) - nlog) * kWaves + wave;
+  const int nqw = (static_cast<int>(gridDim.x) - nlog) * kWaves;
   const uint16_t* row = A.wr + static_cast<size_t>(e) * H;
 
   {
@@ -304,27 +310,26 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
       for (int t = 0; t < kMaxSteps; ++t) {
         const int c = c0 + lane + kWave * t;
         const uint32_t wp[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
-        double part = 0.0;
+        if (RMS) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (RMS) {
-            u[t][2 * i] *= r;
-            u[t][2 * i + 1] *= r;
-          }
-          part = fma(static_cast<double>(u[t][2 * i]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu))), part);
-          part = fma(static_cast<double>(u[t][2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), part);
+          for (int i = 0; i < 8; ++i) u[t][i] *= r;
         }
-        acc += c < n8 ? part : 0.0;
-        // quantise group g = c / 4 if this wave owns it: 4 lanes hold its
-        // 4 positions of 8 values. A wave owns groups gw, gw + nb*4, ...; the
-        // test below is uniform across the wave, so the shuffles run only on
-        // the steps that hold an owned group.
+        if (!qblk) {
+          double part = 0.0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            part = fma(static_cast<double>(u[t][2 * i]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] & 0xFFFFu))), part);
+            part = fma(static_cast<double>(u[t][2 * i + 1]), static_cast<double>(h2f(static_cast<uint16_t>(wp[i] >> 16))), part);
+          }
+          acc += c < n8 ? part : 0.0;
+          continue;
+        }
+        // a quantising wave's step: group g = c / 4, its 4 positions of 8
+        // values in an aligned lane quad (uniform test: whole steps)
         const int g = c / 4;
-        const int g_lo = (c0 + kWave * t) / 4;  // first group of this step
-        const int period = nb * kWaves;
-        const int first_owned = g_lo + ((gw - g_lo) % period + period) % period;
-        if (first_owned >= g_lo + kWave / 4 || first_owned >= ngu) continue;
-        const bool own = c < n8 && (g % period) == gw;
+        const int st = c0 / kWave + t;
+        if (st % nqw != qw || c0 + kWave * t >= n8) continue;
+        const bool own = c < n8;
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(u[t][i]));
@@ -337,12 +342,9 @@ __global__ __launch_bounds__(kThreads) void k_route_fused(RouteArgs A) {
           for (int i = 0; i < 8; ++i) {
             int q = static_cast<int>(rintf(u[t][i] * inv));
             q = q > kQmax ? kQmax : (q < -kQmax ? -kQmax : q);
+            const uint32_t nb = digit_nibbles(q);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const int dg = d < 3 ? ((q + 8) & 15) - 8 : q;
-              wd[d] |= static_cast<uint32_t>(dg & 15) << (4 * i);
-              q = (q - dg) / 16;
-            }
+            for (int d = 0; d < 4; ++d) wd[d] |= ((nb >> (4 * d)) & 15u) << (4 * i);
           }
           if (A.udig) {
             DigitGroup* dg = A.udig + static_cast<size_t>(b) * ngu + g;
@@ -641,7 +643,9 @@ hipError_t launch_route_layer(const float* x, const uint16_t* add_in, int B, int
     return hipGetLastError();
   }
   const bool topk = ids != nullptr;
-#define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks, B), dim3(kThreads), lds, s, A)
+  // blocks that quantise u (one wave per 64 x 8 inputs), after the logit blocks
+  const int qblocks = (udig || u16 || u_out) ? (steps + kWaves - 1) / kWaves : 0;
+#define MOE_ROUTE(A_, R_, T_) hipLaunchKernelGGL((k_route_fused<A_, R_, T_>), dim3(blocks + qblocks, B), dim3(kThreads), lds, s, A)
   if (topk) {
     if (add_in && rmsnorm) MOE_ROUTE(true, true, true);
     else if (add_in) MOE_ROUTE(true, false, true);
