@@ -127,13 +127,15 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
       double* zs = reinterpret_cast<double*>(lds + lay.zs);
       for (int f = threadIdx.x; f < P.E; f += BT) zs[f] = P.z[f];
       __syncthreads();
-      topk_block(zs, P.E, P.k, sel_z, sel_e, P.ids, P.w, P.ids2, P.w2);
+      topk_select(zs, P.E, P.k, sel_z, sel_e);
       if (threadIdx.x == 0) {
         // the release store orders the id stores before the sequence number
         for (int j = 0; j < P.k; ++j)
           __hip_atomic_store(P.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         __hip_atomic_store(P.seq_host, P.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
+      // the weights (for the down kernel, a later launch) after the ids are out
+      topk_weights(sel_z, sel_e, P.k, P.ids, P.w, P.ids2, P.w2);
       return;
     }
     bx -= 1;
@@ -208,9 +210,7 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
   if (src < S.k && S.z) {
     for (int f = threadIdx.x; f < S.E; f += BT) zs[f] = S.z[f];
     __syncthreads();
-    const bool first = grp == 0;
-    topk_block(zs, S.E, S.k, sel_z, sel_e, first ? S.ids_g : nullptr, first ? S.w_g : nullptr,
-               first ? S.ids2 : nullptr, first ? S.w2 : nullptr);
+    topk_select(zs, S.E, S.k, sel_z, sel_e);
     base = S.experts + static_cast<size_t>(sel_e[src]) * S.blob_e;
   } else {
     base = source_base(S, src);
@@ -330,6 +330,9 @@ __global__ __launch_bounds__(kWave * 16 / RPS) void k_gateup(SourceSet S, int n_
     const float a = lane < kGroupRows ? gelu_tanh(sact[lane]) * sact[kGroupRows + lane] : 0.f;
     quant_pair_of_groups(a, grp, grp + 1, adig, asc);
   }
+  // in-kernel routing: the first routed block writes the token's ids and
+  // weights for the down kernel, off the path to its weight loads
+  if (src < S.k && S.z && grp == 0) topk_weights(sel_z, sel_e, S.k, S.ids_g, S.w_g, S.ids2, S.w2);
 }
 
 constexpr int kOutPerBlock = 11;

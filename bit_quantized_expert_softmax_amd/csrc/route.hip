@@ -576,15 +576,17 @@ __global__ __launch_bounds__(kSelThreads) void k_route_select(RouteArgs A) {
   __shared__ int sel_e[kMaxTopK];
   for (int f = threadIdx.x; f < A.E; f += kSelThreads) zs[f] = A.z[f];
   __syncthreads();
-  topk_block(zs, A.E, A.k, sel_z, sel_e, A.ids, A.w, A.ids2, A.w2);
-  if (A.use_dc) dcache_step(A.dc, sel_e, A.k, A.E, reinterpret_cast<int32_t*>(zs + A.E));
+  topk_select(zs, A.E, A.k, sel_z, sel_e);
   if (A.seq_host && threadIdx.x == 0) {
-    // one thread writes the ids and then publishes them: the release store
-    // orders its own earlier stores before the sequence number
+    // one thread writes the ids and then publishes them (the host waits for
+    // them, so before the weights): the release store orders its own earlier
+    // stores before the sequence number
     for (int j = 0; j < A.k; ++j)
       __hip_atomic_store(A.ids_host + j, sel_e[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_store(A.seq_host, A.seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
+  topk_weights(sel_z, sel_e, A.k, A.ids, A.w, A.ids2, A.w2);
+  if (A.use_dc) dcache_step(A.dc, sel_e, A.k, A.E, reinterpret_cast<int32_t*>(zs + A.E));
 }
 
 }  // namespace

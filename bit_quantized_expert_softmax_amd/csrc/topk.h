@@ -5,6 +5,8 @@
 
 #include "launch.h"
 
+static_assert(moe::kMaxTopK <= 16, "the weights' sum runs over one 16-lane DPP row");
+
 namespace moe {
 
 // Order-preserving 64-bit key of an fp64 logit: the unsigned order of the
@@ -31,11 +33,10 @@ __device__ __forceinline__ bool key_better(uint2 kf, int f, uint2 ke, int e) {
 }
 
 // Top-k of E logits held in LDS (zs), by rank: an expert's rank is the number
-// of experts ranking before it; ranks below k are the selection in rank order.
-// zs is overwritten with the logits' keys. Writes ids / w (and the optional
-// copies). All block threads call.
-__device__ inline void topk_block(double* zs, int E, int k, double* sel_z, int* sel_e,
-                                  int32_t* ids, float* w, int32_t* ids2, float* w2) {
+// of experts ranking before it; ranks below k are the selection in rank order
+// (sel_z, sel_e), visible to the whole block on return. zs is overwritten with
+// the logits' keys. All block threads call.
+__device__ inline void topk_select(double* zs, int E, int k, double* sel_z, int* sel_e) {
   // every rank slot starts with a valid id, so non-finite logits cannot
   // produce an out-of-range expert index downstream
   if (threadIdx.x < static_cast<unsigned>(k)) {
@@ -81,16 +82,35 @@ __device__ inline void topk_block(double* zs, int E, int k, double* sel_z, int* 
     }
   }
   __syncthreads();
-  if (threadIdx.x < static_cast<unsigned>(k)) {
+}
+
+// The selection's softmax weights w_j = exp(z_j - z_0) / sum_i exp(z_i - z_0)
+// (one exp per lane, the sum over the k lanes by DPP in a fixed order) and
+// the writes of ids / w and the optional copies, by the first 16 lanes of the
+// block (k <= 16); nothing to write, nothing done. All block threads call;
+// no barrier.
+__device__ inline void topk_weights(const double* sel_z, const int* sel_e, int k, int32_t* ids, float* w,
+                                    int32_t* ids2, float* w2) {
+  if (!ids && !w && !ids2 && !w2) return;
+  if (threadIdx.x < 16u) {
     const int j = threadIdx.x;
-    float tot = 0.f;
-    for (int i = 0; i < k; ++i) tot += expf(static_cast<float>(sel_z[i] - sel_z[0]));
-    const float wj = expf(static_cast<float>(sel_z[j] - sel_z[0])) / tot;
-    if (ids) ids[j] = sel_e[j];
-    if (w) w[j] = wj;
-    if (ids2) ids2[j] = sel_e[j];
-    if (w2) w2[j] = wj;
+    const float ej = j < k ? expf(static_cast<float>(sel_z[j] - sel_z[0])) : 0.f;
+    const float tot = dpp_sum<16>(ej);
+    if (j < k) {
+      const float wj = ej / tot;
+      if (ids) ids[j] = sel_e[j];
+      if (w) w[j] = wj;
+      if (ids2) ids2[j] = sel_e[j];
+      if (w2) w2[j] = wj;
+    }
   }
+}
+
+// Both, with a barrier after the writes.
+__device__ inline void topk_block(double* zs, int E, int k, double* sel_z, int* sel_e,
+                                  int32_t* ids, float* w, int32_t* ids2, float* w2) {
+  topk_select(zs, E, k, sel_z, sel_e);
+  topk_weights(sel_z, sel_e, k, ids, w, ids2, w2);
   __syncthreads();
 }
 
