@@ -391,6 +391,14 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     wv[t] = load_w16(qb + n * (inter / 2));
     sw[t] = sb[n * (inter / kGroup)];
   }
+  // the residual input of the output this wave sums at the end (wave w <
+  // nout owns output n0 + w), loaded now, behind the weights, so that no
+  // round trip follows the sums; branch-free (a wave-uniform address, add_in
+  // replaced by x when absent and its value dropped)
+  const int wv_out = static_cast<int>(threadIdx.x) / kWave;
+  const int nres = n0 + (wv_out < nout ? wv_out : nout - 1);
+  const float xres = x[nres];
+  const uint16_t ares = (add_in ? add_in : reinterpret_cast<const uint16_t*>(x))[nres];
   __builtin_amdgcn_sched_barrier(0);
   const float xs = xsa * wj;
 #pragma unroll
@@ -415,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void k_down(SourceSet S, const float* __r
     if (lane == 0) {
       const int n = n0 + wave;
       float r = 0.f;
-      if (residual) r = x[n] + (add_in ? h2f(add_in[n]) : 0.f);
+      if (residual) r = xres + (add_in ? h2f(ares) : 0.f);
       y[n] = r + acc;
     }
   }
@@ -497,7 +505,7 @@ hipError_t launch_ffn_down(const SourceSet& src, const float* w, const DigitGrou
                            hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
   const int nga = src.k * (src.I / kGroup) + src.Is / kGroup;
   const size_t lds = static_cast<size_t>(kOutPerBlock) * nga * 4;
-  if (nga > kThreads) return hipErrorInvalidValue;
+  if (nga > kThreads || !x) return hipErrorInvalidValue;  // x: read for every output (residual or not)
   const int blocks = (src.H + kOutPerBlock - 1) / kOutPerBlock;
   const int outs_per_pass = kThreads / nga;
   const int need = (kOutPerBlock + outs_per_pass - 1) / outs_per_pass;
