@@ -192,35 +192,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Byte B of x as a float (v_cvt_f32_ubyteB; written out because the compiler
-// folds the surrounding masks and then loses the byte-select forms).
-template <int B>
-__device__ __forceinline__ float ubyte_f32(uint32_t x) {
-  float r;
-  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
-  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
-  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
-  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
 // bf16(n * s) for the 8 signed nibbles of w (k = 0..7 in bits 4k..4k+3), in
-// k order: the product (n + 8) * s - 8 * s is exact in fp32 (at most 15
-// significant bits), so the single rounding is the one to bf16.
-__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s) {
-  const uint32_t x = w ^ 0x88888888u;          // nibble n -> n + 8
-  const uint32_t lo = x & 0x0F0F0F0Fu;         // byte b: k = 2b
-  const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // byte b: k = 2b + 1
-  const float m8 = -8.0f * s;
+// k order. One and-xor (v_bitop3) per pair of nibbles at bits 4i and 16 + 4i
+// puts them in fp16 mantissas with the offset n + 8: at bits 0-3 under the
+// exponent of 1024 (fp16 1032 + n), at bits 4-7 under that of 64 (the
+// mantissa is then 16 (n + 8): fp16 72 + n); w >> 8 brings i = 2, 3 to the
+// same places. Each weight is then one mixed-precision fma (fp16 operand, fp32
+// arithmetic): (1032 + n) s - 1032 s, with 1032 s and 72 s exact in fp32 (two
+// set bits times an 11-bit scale), so the fma returns n s exactly (15
+// significant bits at most) and the single rounding is the one to bf16.
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float s, float c_lo, float c_hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t w8 = w >> 8;
+  const h2 p0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) ^ 0x64086408u);   // k = 0, 4
+  const h2 p1 = __builtin_bit_cast(h2, (w & 0x00F000F0u) ^ 0x54805480u);   // k = 1, 5
+  const h2 p2 = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) ^ 0x64086408u);  // k = 2, 6
+  const h2 p3 = __builtin_bit_cast(h2, (w8 & 0x00F000F0u) ^ 0x54805480u);  // k = 3, 7
   bf16x8 r;
-  r[0] = static_cast<__bf16>(fmaf(ubyte_f32<0>(lo), s, m8));
-  r[1] = static_cast<__bf16>(fmaf(ubyte_f32<0>(hi), s, m8));
-  r[2] = static_cast<__bf16>(fmaf(ubyte_f32<1>(lo), s, m8));
-  r[3] = static_cast<__bf16>(fmaf(ubyte_f32<1>(hi), s, m8));
-  r[4] = static_cast<__bf16>(fmaf(ubyte_f32<2>(lo), s, m8));
-  r[5] = static_cast<__bf16>(fmaf(ubyte_f32<2>(hi), s, m8));
-  r[6] = static_cast<__bf16>(fmaf(ubyte_f32<3>(lo), s, m8));
-  r[7] = static_cast<__bf16>(fmaf(ubyte_f32<3>(hi), s, m8));
+  r[0] = static_cast<__bf16>(fmaf(static_cast<float>(p0.x), s, c_lo));
+  r[1] = static_cast<__bf16>(fmaf(static_cast<float>(p1.x), s, c_hi));
+  r[2] = static_cast<__bf16>(fmaf(static_cast<float>(p2.x), s, c_lo));
+  r[3] = static_cast<__bf16>(fmaf(static_cast<float>(p3.x), s, c_hi));
+  r[4] = static_cast<__bf16>(fmaf(static_cast<float>(p0.y), s, c_lo));
+  r[5] = static_cast<__bf16>(fmaf(static_cast<float>(p1.y), s, c_hi));
+  r[6] = static_cast<__bf16>(fmaf(static_cast<float>(p2.y), s, c_lo));
+  r[7] = static_cast<__bf16>(fmaf(static_cast<float>(p3.y), s, c_hi));
   return r;
 }
 
@@ -352,7 +348,7 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
     for (int mr = 0; mr < kMR; ++mr) {
       const float sc = gv ? h2f(static_cast<uint16_t>(wd.s[mr])) : 0.0f;
       const uint32_t wj = j == 0 ? wd.q[mr].x : (j == 1 ? wd.q[mr].y : (j == 2 ? wd.q[mr].z : wd.q[mr].w));
-      a[mr][j] = dequant8_bf16(wj, sc);
+      a[mr][j] = dequant8_bf16(wj, sc, -1032.0f * sc, -72.0f * sc);
     }
   };
   auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
