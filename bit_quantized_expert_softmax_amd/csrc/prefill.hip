@@ -151,38 +151,41 @@ __global__ __launch_bounds__(kChunk) void k_perm_scatter(const int32_t* __restri
 // Weight rows stream from HBM into registers and are dequantised there; the
 // block's token rows are loaded per K step straight into LDS (global_load_lds,
 // 16 bytes per lane, no registers on the way) into a ring of kBufs slices
-// and shared by its 8 waves. A wave owns two 16-row weight tiles (GATEUP: 16
-// gate rows and the matching 16 up rows; else 32 consecutive down rows) and
-// all of the block's 16-token tiles, so each dequantised weight feeds up to
-// 8 MFMAs (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+// shared by its 4 waves. A wave owns two 32-row weight tiles (GATEUP: 32 gate
+// rows and the matching 32 up rows; else 64 consecutive down rows) and all of
+// the block's 32-token tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+// each dequantised weight feeds up to 4 MFMAs and each activation operand
+// read from LDS feeds 2, half the LDS bytes per flop of 16-row tiles.
 //
-// K step = 4 quant groups (128 values). The lane of 16-lane row q loads group
-// 4*st + q of its weight row (16 bytes) and that group's scale; MFMA j of the
-// step takes dword j (8 nibbles) of every lane's group, so one MFMA's K = 32
-// spans the step's 4 groups, 8 values of each, and the activations are read
-// at the same positions (16-byte chunk 4q + j of the token's 256-byte row).
+// K step = 2 quant groups (64 values). The lane of 32-lane half h loads
+// group 2*st + h of its weight row (16 bytes) and that group's scale; MFMA i
+// of the step takes dword i (8 nibbles) of every lane's group, so one MFMA's
+// K = 16 spans the step's 2 groups, 8 values of each, and the activations
+// are read at the same positions (16-byte chunk 4h + i of the token's
+// 128-byte step row).
 //
 // Pipeline: the loads of step s + kDepth (activation slice and weights) are
-// issued at the start of step s, into the slice the previous step read; the
-// weights of step s + 1 are dequantised while the MFMAs of step s run, so a
-// wave's dequantisation overlaps its own matrix work; one barrier per step
-// both frees the slice just read and publishes the next one (each wave has
-// waited for its own loads of it). The slice rows are unpadded 256-byte rows
-// whose 16 chunks are stored XOR-swizzled by the row (position = chunk ^
-// (row & 15)); the direct loads choose each lane's source chunk so that the
-// stored image has this layout, and the MFMA reads of 16 consecutive token
-// rows at one chunk then fall on 16 different bank groups.
-constexpr int kTok = kTM / 16;            // 16-token tiles per block (at most)
-constexpr int kWavesG = 8;               // waves per GEMM block
+// issued at the start of step s, into the slice the previous step read; one
+// barrier per step both frees the slice just read and publishes the next one
+// (each wave has waited for its own loads of it). Within a step the weights
+// of MFMA i + 1 are dequantised while the MFMAs of i run. The slice rows are
+// 128-byte rows whose 8 chunks are stored XOR-swizzled (chunk c of token row
+// t at position c ^ swz(t), swz(t) = (t & 7) ^ ((t >> 3) & 1)): the operand
+// reads of 16 consecutive token rows at one chunk then fall on 16 different
+// 16-byte bank groups over a 256-byte bank cycle, and on 8 over a 128-byte
+// one.
+constexpr int kWavesG = 4;               // waves per GEMM block
 constexpr int kThreadsGemm = kWavesG * kWave;
-constexpr int kStepK = 4 * kGroup;       // 128
+constexpr int kStepK = 2 * kGroup;       // 64
 constexpr int kRowB = kStepK * 2;        // LDS bytes per token row of a slice
-constexpr int kSlice = kTM * kRowB;      // 32 KB
+constexpr int kSlice = kTM * kRowB;      // 16 KB
 constexpr int kDepth = 3;                // steps loaded ahead of the one computed
-constexpr int kBufs = kDepth + 1;        // slices in LDS (128 KB)
-constexpr int kMR = 2;                   // 16-row weight tiles per wave (GATEUP: half gate, half up)
+constexpr int kBufs = kDepth + 1;        // slices in LDS (64 KB: two blocks per CU)
+constexpr int kMR = 2;                   // 32-row weight tiles per wave (GATEUP: half gate, half up)
 constexpr int kHalf = kMR / 2;
 constexpr int kXcds = 8;                 // accelerator complex dies of an MI355X, each with its own L2
+
+__device__ __forceinline__ int slice_swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
@@ -226,8 +229,8 @@ struct WStep {
 };
 
 __device__ __forceinline__ void load_step(WStep& b, const uint8_t* const* qrow,
-                                          const uint16_t* const* srow, int ngk, int st, int q) {
-  int g = 4 * st + q;
+                                          const uint16_t* const* srow, int ngk, int st, int h) {
+  int g = 2 * st + h;
   g = g < ngk ? g : ngk - 1;
 #pragma unroll
   for (int m = 0; m < kMR; ++m) {
@@ -263,69 +266,66 @@ struct GemmArgs {
   SlotGroup group;
 };
 
-// The GEMM of one block: token rows [r0, r_end) (at most NTT 16-row tiles)
+// The GEMM of one block: token rows [r0, r_end) (at most NTT 32-row tiles)
 // against row tile nt of the weights in blob; lds: kBufs activation slices.
 template <bool GATEUP, bool ROUTED, int NTT>
 __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int r_end, const uint8_t* blob,
                                           uint8_t* lds) {
-  constexpr int kTok = NTT;
-  constexpr int kRows = NTT * 16;                                     // slice rows
-  constexpr int kStage = (kRows + 4 * kWavesG - 1) / (4 * kWavesG);   // 4 rows per wave load
-  constexpr int kLoads = kStage + 2 * kMR;                            // vector loads per step
-  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int kRows = NTT * 32;                         // slice rows
+  constexpr int kStage = kRows * (kRowB / 16) / kThreadsGemm;  // slice loads per thread and step
+  static_assert(kStage * kThreadsGemm == kRows * (kRowB / 16), "whole slice loads per thread");
+  constexpr int kLoads = kStage + 2 * kMR;                // vector loads per step
+  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 32 : kWavesG * kMR * 32;
   const int nrows = GATEUP ? G.inter : G.H;
   const int mtok = r_end - r0;
   const BlobOffsets o = blob_offsets(G.H, G.inter);
   const int K = GATEUP ? G.H : G.inter;
   const int ngk = K / kGroup;
-  const int nsteps = (ngk + 3) / 4;
+  const int nsteps = (ngk + 1) / 2;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar registers
   const int lane = threadIdx.x & (kWave - 1);
-  const int q = lane >> 4;
-  const int l16 = lane & 15;
-  const int rbase = nt * rows_per_block + wave * (GATEUP ? kHalf * 16 : kMR * 16);
+  const int h = lane >> 5;     // K half of the MFMA operands
+  const int l32 = lane & 31;   // weight row / token of the tiles
+  const int rbase = nt * rows_per_block + wave * (GATEUP ? kHalf * 32 : kMR * 32);
   const bool live = rbase < nrows;  // waves past the last row only load and sync
   const uint8_t* qrow[kMR];
   const uint16_t* srow[kMR];
 #pragma unroll
   for (int mr = 0; mr < kMR; ++mr) {
-    int row = (GATEUP ? rbase + 16 * (mr % kHalf) : rbase + 16 * mr) + l16;
-    row = live && row < nrows ? row : l16;
+    int row = (GATEUP ? rbase + 32 * (mr % kHalf) : rbase + 32 * mr) + l32;
+    row = live && row < nrows ? row : l32;
     const bool up = mr >= kHalf;
     const size_t qo = GATEUP ? (up ? o.up_q : o.gate_q) : o.down_q;
     const size_t so = GATEUP ? (up ? o.up_s : o.gate_s) : o.down_s;
     qrow[mr] = blob + qo + static_cast<size_t>(row) * (K / 2);
     srow[mr] = reinterpret_cast<const uint16_t*>(blob + so) + static_cast<size_t>(row) * ngk;
   }
-  // This lane's part of the slice loads: load u of the wave fills slice rows
-  // 4 (wave + 8u) .. + 3 (modulo the slice, so small slices are filled more
-  // than once with the same bytes); lane i takes row + i / 16 at position
-  // i % 16, i.e. the token's chunk (i % 16) ^ (row & 15). Rows past the tile
-  // repeat its last token (their outputs are dropped).
+  // This lane's part of the slice loads: load u of the wave writes slice
+  // positions P = 64 (wave + 4u) + lane (16 bytes each), i.e. row P / 8 at
+  // position P % 8, which holds the token's chunk (P % 8) ^ swz(row). Rows
+  // past the tile repeat its last token (their outputs are dropped).
   const __bf16* arow[kStage];
   int achunk[kStage];
-  uint32_t alds[kStage];  // wave-uniform LDS offset of the load's first row
 #pragma unroll
   for (int u = 0; u < kStage; ++u) {
-    const int rr = (4 * (wave + kWavesG * u)) % kRows;
-    alds[u] = static_cast<uint32_t>(rr * kRowB);
-    const int r = rr + (lane >> 4);
-    achunk[u] = (lane & 15) ^ (r & 15);
+    const int P = kWave * (wave + kWavesG * u) + lane;
+    const int r = P >> 3;
+    achunk[u] = (P & 7) ^ slice_swz(r);
     const int row = r0 + (r < mtok ? r : mtok - 1);
     const int idx = G.rmap ? G.rmap[row] / G.rdiv : row;
     arow[u] = G.A + static_cast<size_t>(idx) * G.lda;
   }
 
-  f32x4 acc[kMR][kTok];
+  f32x16 acc[kMR][NTT];
 #pragma unroll
   for (int mr = 0; mr < kMR; ++mr)
 #pragma unroll
-    for (int tt = 0; tt < kTok; ++tt) acc[mr][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mr][tt][v] = 0.f;
 
   WStep w[kBufs];
-  // dequantised weights: slice j holds the current step's until its MFMAs
-  // are issued, then the next step's
-  bf16x8 a[kMR][4];
   // the loads of step st into slot sl (st past the last step re-loads the
   // last one: every step issues the same loads, so the wait counts hold on
   // every path)
@@ -336,21 +336,23 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
       int kk = st * kStepK + 8 * achunk[u];
       kk = kk < K ? kk : K - 8;  // past the end: any finite values (their weights are 0)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[u] + kk),
-                                       (__attribute__((address_space(3))) void*)(lds + sl * kSlice + alds[u]),
+                                       (__attribute__((address_space(3))) void*)(lds + sl * kSlice +
+                                                                                 kWave * 16 * (wave + kWavesG * u)),
                                        16, 0, 0);
     }
-    load_step(wd, qrow, srow, ngk, st, q);
+    load_step(wd, qrow, srow, ngk, st, h);
   };
-  // slice j (dword j of each weight tile's group) of step st, into a[.][j]
-  auto dequant = [&](int st, const WStep& wd, int j) __attribute__((always_inline)) {
-    const bool gv = 4 * st + q < ngk;  // groups past K weigh 0
+  // MFMA operand i (dword i of each weight tile's group) of step st
+  auto dequant = [&](int st, const WStep& wd, int i, bf16x8* a) __attribute__((always_inline)) {
+    const bool gv = 2 * st + h < ngk;  // groups past K weigh 0
 #pragma unroll
     for (int mr = 0; mr < kMR; ++mr) {
       const float sc = gv ? h2f(static_cast<uint16_t>(wd.s[mr])) : 0.0f;
-      const uint32_t wj = j == 0 ? wd.q[mr].x : (j == 1 ? wd.q[mr].y : (j == 2 ? wd.q[mr].z : wd.q[mr].w));
-      a[mr][j] = dequant8_bf16(wj, sc, -1032.0f * sc, -72.0f * sc);
+      const uint32_t wi = i == 0 ? wd.q[mr].x : (i == 1 ? wd.q[mr].y : (i == 2 ? wd.q[mr].z : wd.q[mr].w));
+      a[mr] = dequant8_bf16(wi, sc, -1032.0f * sc, -72.0f * sc);
     }
   };
+  bf16x8 acur[kMR];
   auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
     constexpr int D = decltype(slot)::value;  // slot of this step (step % kBufs)
     const int st = s0 + D;
@@ -362,18 +364,24 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* lb = lds + D * kSlice;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int i = 0; i < 4; ++i) {
+      // operand i + 1 of this step, or 0 of the next, while the matrix cores
+      // work through operand i
+      bf16x8 anext[kMR];
+      if (i < 3) dequant(st, w[D], i + 1, anext);
+      else dequant(st + 1, w[(D + 1) % kBufs], 0, anext);
       // every token tile, also past mtok: an output column depends on its
       // own activation row only, and the columns of absent rows are dropped
 #pragma unroll
-      for (int tt = 0; tt < kTok; ++tt) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + (tt * 16 + l16) * kRowB + 16 * ((4 * q + j) ^ l16));
+      for (int tt = 0; tt < NTT; ++tt) {
+        const int t = tt * 32 + l32;
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + t * kRowB + 16 * ((4 * h + i) ^ slice_swz(t)));
 #pragma unroll
         for (int mr = 0; mr < kMR; ++mr)
-          acc[mr][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mr][j], bv, acc[mr][tt], 0, 0, 0);
+          acc[mr][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mr], bv, acc[mr][tt], 0, 0, 0);
       }
-      // slice j of the next step, while the matrix cores work through this one
-      dequant(st + 1, w[(D + 1) % kBufs], j);
+#pragma unroll
+      for (int mr = 0; mr < kMR; ++mr) acur[mr] = anext[mr];
     }
     // every wave is done with slot D (the next step's loads may refill it),
     // and every wave's loads of step st + 1 have landed
@@ -385,8 +393,7 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
   issue(2, 2, w[2]);
   wait_vmcnt<(kDepth - 1) * kLoads>();
   block_sync();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) dequant(0, w[0], j);
+  dequant(0, w[0], 0, acur);
   int s0 = 0;
   for (; s0 + kBufs <= nsteps; s0 += kBufs) {
     step(std::integral_constant<int, 0>{}, s0, false);
@@ -403,32 +410,35 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
   // block ends: LDS is released with the block
   wait_vmcnt<0>();
 
-  // epilogue: a lane holds rows 4q..4q+3 of each weight tile for token row
-  // l16 of each token tile
+  // epilogue: for token column l32 of each token tile, a lane holds rows
+  // 8a + 4h + b (a, b = 0..3) of each 32-row weight tile in element 4a + b
 #pragma unroll
-  for (int tt = 0; tt < kTok; ++tt) {
-    const int m = r0 + tt * 16 + l16;
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int m = r0 + tt * 32 + l32;
     if (m >= r_end || !live) continue;
     if (GATEUP) {
 #pragma unroll
-      for (int mr = 0; mr < kHalf; ++mr) {
+      for (int a = 0; a < 4; ++a) {
         __attribute__((aligned(8))) __bf16 av[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          av[i] = static_cast<__bf16>(gelu_tanh(acc[mr][tt][i]) * acc[mr + kHalf][tt][i]);
-        *reinterpret_cast<uint2*>(G.act + static_cast<size_t>(m) * G.inter + rbase + 16 * mr + 4 * q) =
+        for (int b = 0; b < 4; ++b)
+          av[b] = static_cast<__bf16>(gelu_tanh(acc[0][tt][4 * a + b]) * acc[1][tt][4 * a + b]);
+        *reinterpret_cast<uint2*>(G.act + static_cast<size_t>(m) * G.inter + rbase + 8 * a + 4 * h) =
             *reinterpret_cast<const uint2*>(av);
       }
     } else {
+      const float wr = ROUTED ? G.wrow[G.perm[m]] : 1.0f;
 #pragma unroll
       for (int mr = 0; mr < kMR; ++mr) {
-        const int n = rbase + 16 * mr + 4 * q;
-        float4 v = make_float4(acc[mr][tt][0], acc[mr][tt][1], acc[mr][tt][2], acc[mr][tt][3]);
-        if (ROUTED) {
-          const float wr = G.wrow[G.perm[m]];
-          v = make_float4(v.x * wr, v.y * wr, v.z * wr, v.w * wr);
+        if (rbase + 32 * mr >= nrows) continue;  // H a multiple of 32, not of 64: the wave's second tile is past it
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int n = rbase + 32 * mr + 8 * a + 4 * h;
+          float4 v = make_float4(acc[mr][tt][4 * a], acc[mr][tt][4 * a + 1], acc[mr][tt][4 * a + 2],
+                                 acc[mr][tt][4 * a + 3]);
+          if (ROUTED) v = make_float4(v.x * wr, v.y * wr, v.z * wr, v.w * wr);
+          *reinterpret_cast<float4*>(G.out + static_cast<size_t>(m) * G.H + n) = v;
         }
-        *reinterpret_cast<float4*>(G.out + static_cast<size_t>(m) * G.H + n) = v;
       }
     }
   }
@@ -439,7 +449,7 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
 // token tiles (block-uniform, so each count runs its own unrolled code).
 template <bool GATEUP, bool ROUTED>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t* lds_b) {
-  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
+  constexpr int rows_per_block = GATEUP ? kWavesG * kHalf * 32 : kWavesG * kMR * 32;
   const int nrows = GATEUP ? G.inter : G.H;
   const int n_tiles_n = (nrows + rows_per_block - 1) / rows_per_block;
   // XCD-aware order: blocks are dealt to the 8 XCDs in turn (block b to XCD
@@ -471,15 +481,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t* l
     blob = G.blob;
   }
   if (r_end <= r0) return;
-  switch ((r_end - r0 + 15) / 16) {
+  switch ((r_end - r0 + 31) / 32) {
     case 1: gemm_core<GATEUP, ROUTED, 1>(G, nt, r0, r_end, blob, lds_b); break;
     case 2: gemm_core<GATEUP, ROUTED, 2>(G, nt, r0, r_end, blob, lds_b); break;
     case 3: gemm_core<GATEUP, ROUTED, 3>(G, nt, r0, r_end, blob, lds_b); break;
-    case 4: gemm_core<GATEUP, ROUTED, 4>(G, nt, r0, r_end, blob, lds_b); break;
-    case 5: gemm_core<GATEUP, ROUTED, 5>(G, nt, r0, r_end, blob, lds_b); break;
-    case 6: gemm_core<GATEUP, ROUTED, 6>(G, nt, r0, r_end, blob, lds_b); break;
-    case 7: gemm_core<GATEUP, ROUTED, 7>(G, nt, r0, r_end, blob, lds_b); break;
-    default: gemm_core<GATEUP, ROUTED, 8>(G, nt, r0, r_end, blob, lds_b); break;
+    default: gemm_core<GATEUP, ROUTED, 4>(G, nt, r0, r_end, blob, lds_b); break;
   }
 }
 
@@ -516,8 +522,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ out_r
   if (on) *reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H + n) = make_float4(vx, vy, vz, vw);
 }
 
+// Two waves per SIMD: the accumulation registers (128) and the rest within 256.
 template <bool GATEUP, bool ROUTED>
-__global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
+__global__ __launch_bounds__(kThreadsGemm) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(GemmArgs G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBufs * kSlice];
   gemm_tile<GATEUP, ROUTED>(G, blockIdx.x, lds_b);
 }
@@ -526,7 +533,7 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm(GemmArgs G) {
 // first) and the routed experts' gate/up in one launch: the two are
 // independent, and the shared blocks, few and long, would otherwise form a
 // launch of their own with a tail of one block per CU.
-__global__ __launch_bounds__(kThreadsGemm) void k_gemm_gateup2(GemmArgs R, GemmArgs Sh, int n_shared) {
+__global__ __launch_bounds__(kThreadsGemm) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_gateup2(GemmArgs R, GemmArgs Sh, int n_shared) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBufs * kSlice];
   const int bid = blockIdx.x;
   if (bid < n_shared)
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(kThreadsGemm) void k_gemm_gateup2(GemmArgs R, GemmA
 // Blocks along the weight rows of one GEMM (gate/up: row pairs; down: rows).
 int gemm_row_tiles(bool gateup, int H, int inter) {
   const int rows = gateup ? inter : H;
-  const int per = gateup ? kWavesG * kHalf * 16 : kWavesG * kMR * 16;
+  const int per = gateup ? kWavesG * kHalf * 32 : kWavesG * kMR * 32;
   return (rows + per - 1) / per;
 }
 

@@ -66,6 +66,26 @@ def test_batched_decode_matches_per_token_oracle(shape, cid, B):
     L1.close()
 
 
+# Every token is one input row times a power of two: the logits scale with it,
+# so every token picks the same k experts (the weights differ), and each of
+# them serves all B tokens, more than one 16-token pass of its blocks (small
+# layer B = 32: two passes; Gemma layer B = 64: four).
+@pytest.mark.parametrize("shape,cid,B", [(SMALL_LAYER, 0, 32), (GEMMA_LAYER, 3, 64)])
+def test_batched_all_tokens_on_the_same_experts(shape, cid, B):
+    d = layer_data(shape, cid)
+    L = Layer(shape, d, max_B=B)
+    row = gen.x_fp32(1, shape.hidden, cid, sub=5)[0]
+    x = np.stack([row * np.float32(2.0 ** (t % 7 - 3)) for t in range(B)]).astype(np.float32)
+    y, ids, w, _ = decode(L, x)
+    r = moe.layer_decode(x.astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+    assert np.array_equal(ids, r["ids"])
+    assert all(np.array_equal(ids[t], ids[0]) for t in range(B))
+    assert_close(w, r["w"], "w")
+    for t in range(B):  # each row at its own scale
+        assert_close(y[t], r["y"][t], f"y B={B} token {t}")
+    L.close()
+
+
 def test_batched_norm_residual_perturbation():
     sh = GEMMA_LAYER
     d = layer_data(sh, 3)
