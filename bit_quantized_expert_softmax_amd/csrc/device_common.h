@@ -116,11 +116,16 @@ __device__ __forceinline__ double wave_sum(double v) {
   return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
-// GELU, tanh form: z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+// GELU, tanh form: z/2 * (1 + tanh(u)), u = sqrt(2/pi) * (z + 0.044715 z^3),
+// evaluated as z / (1 + exp(-2u)) (the same function: (1 + tanh u) / 2 is the
+// logistic function of 2u) with the hardware exp2 and reciprocal, a few
+// units in the last place from the exact value; large |z| give z or -0.
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
-  return 0.5f * z * (1.0f + tanhf(k0 * (z + k1 * z * z * z)));
+  const float u = k0 * (z + k1 * z * z * z);
+  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);  // exp(-2u) = 2^(-2u log2 e)
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Quantise two groups of 32 values to digit planes; called by a whole wave.

@@ -353,35 +353,55 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
     }
   };
   bf16x8 acur[kMR];
+  // the activation operands of MFMA i of the slice in slot D (every token
+  // tile, also past mtok: an output column depends on its own activation row
+  // only, and the columns of absent rows are dropped)
+  auto read_b = [&](int D, int i, bf16x8* b) __attribute__((always_inline)) {
+    const uint8_t* lb = lds + D * kSlice;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int t = tt * 32 + l32;
+      b[tt] = *reinterpret_cast<const bf16x8*>(lb + t * kRowB + 16 * ((4 * h + i) ^ slice_swz(t)));
+    }
+  };
   auto step = [&](auto slot, int s0, bool tail) __attribute__((always_inline)) {
     constexpr int D = decltype(slot)::value;  // slot of this step (step % kBufs)
     const int st = s0 + D;
     if (tail && st >= nsteps) return;  // uniform over the block
+    // the first operands' LDS reads ahead of this step's loads (step st + 3)
+    bf16x8 bcur[NTT];
+    read_b(D, 0, bcur);
     __builtin_amdgcn_sched_barrier(0);
     issue(st + kDepth, (D + kDepth) % kBufs, w[(D + kDepth) % kBufs]);
-    // this wave's loads of step st + 1 are in (those of st + 2, st + 3 may not be)
-    wait_vmcnt<(kDepth - 1) * kLoads>();
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* lb = lds + D * kSlice;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // operand i + 1 of this step, or 0 of the next, while the matrix cores
-      // work through operand i
+      // the next operands' LDS reads, and the weights of MFMA i + 1 of this
+      // step (or 0 of the next), while the matrix cores work through i
+      bf16x8 bnext[NTT];
+      if (i < 3) read_b(D, i + 1, bnext);
       bf16x8 anext[kMR];
-      if (i < 3) dequant(st, w[D], i + 1, anext);
-      else dequant(st + 1, w[(D + 1) % kBufs], 0, anext);
-      // every token tile, also past mtok: an output column depends on its
-      // own activation row only, and the columns of absent rows are dropped
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        const int t = tt * 32 + l32;
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(lb + t * kRowB + 16 * ((4 * h + i) ^ slice_swz(t)));
-#pragma unroll
-        for (int mr = 0; mr < kMR; ++mr)
-          acc[mr][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mr], bv, acc[mr][tt], 0, 0, 0);
+      if (i < 3) {
+        dequant(st, w[D], i + 1, anext);
+      } else {
+        // this wave's loads of step st + 1 are in (those of st + 2, st + 3
+        // may not be): its weights for the dequantisation below, its part of
+        // the slice that the barrier publishes
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(kDepth - 1) * kLoads>();
+        __builtin_amdgcn_sched_barrier(0);
+        dequant(st + 1, w[(D + 1) % kBufs], 0, anext);
       }
 #pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int mr = 0; mr < kMR; ++mr)
+          acc[mr][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mr], bcur[tt], acc[mr][tt], 0, 0, 0);
+#pragma unroll
       for (int mr = 0; mr < kMR; ++mr) acur[mr] = anext[mr];
+      if (i < 3)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) bcur[tt] = bnext[tt];
     }
     // every wave is done with slot D (the next step's loads may refill it),
     // and every wave's loads of step st + 1 have landed
