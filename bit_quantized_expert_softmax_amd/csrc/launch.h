@@ -179,11 +179,14 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
 // of the assignments (seg / tiles / perm / pos_of in the layout); the routed
 // GEMMs (group == nullptr: every expert, experts + id * blob_e; else only the
 // group's experts, experts + slot * blob_e; with_shared: the shared expert's
-// gate/up runs in the same launch as the routed one); the shared expert (its
-// gate/up unless gateup_done) and the combine into y.
+// gate/up runs in the same launch as the routed one, and with y its down
+// projection into y in the same launch as the routed down); the shared expert
+// (its gate/up unless gateup_done, its down unless down_done) and the combine
+// into y.
 struct SharedGateup {
   const uint8_t* shared;
   int T, Is;
+  float* y;  // nullable
 };
 hipError_t launch_prefill_route(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16,
                                 const float* logits_in, const uint16_t* router, const float* bias, int T,
@@ -193,7 +196,7 @@ hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint
                                  hipStream_t s, const SharedGateup* with_shared = nullptr);
 hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
                                  int H, int Is, const uint8_t* shared, float* y, hipStream_t s,
-                                 bool gateup_done = false);
+                                 bool gateup_done = false, bool down_done = false);
 
 // Stable sort of A assignments (token*k + rank, expert ids[a]) by expert:
 // seg [E+1] segment starts, perm [A] sorted position -> assignment, pos_of [A]

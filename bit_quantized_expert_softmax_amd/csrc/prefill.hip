@@ -562,6 +562,18 @@ __global__ __launch_bounds__(kThreadsGemm) __attribute__((amdgpu_waves_per_eu(2)
     gemm_tile<true, true>(R, bid - n_shared, lds_b);
 }
 
+// The shared expert's down projection (its n_shared blocks first) and the
+// routed experts' in one launch, for the same reason: alone, the shared
+// expert's 176 blocks fill a third of the device's block slots.
+__global__ __launch_bounds__(kThreadsGemm) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_down2(GemmArgs R, GemmArgs Sh, int n_shared) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[kBufs * kSlice];
+  const int bid = blockIdx.x;
+  if (bid < n_shared)
+    gemm_tile<false, false>(Sh, bid, lds_b);
+  else
+    gemm_tile<false, true>(R, bid - n_shared, lds_b);
+}
+
 // Blocks along the weight rows of one GEMM (gate/up: row pairs; down: rows).
 int gemm_row_tiles(bool gateup, int H, int inter) {
   const int rows = gateup ? inter : H;
@@ -714,12 +726,25 @@ hipError_t launch_prefill_routed(const PrefillLayout& L, uint8_t* ws, const uint
   d.out = reinterpret_cast<float*>(ws + L.out_r);
   d.wrow = reinterpret_cast<const float*>(ws + L.w);
   d.perm = reinterpret_cast<const int32_t*>(ws + L.perm);
-  hipLaunchKernelGGL((k_gemm<false, true>), dim3(gemm_blocks(L.max_tiles, false, H, I)), dim3(kThreadsGemm), 0, s, d);
+  const int down_blocks = gemm_blocks(L.max_tiles, false, H, I);
+  if (with_shared && with_shared->y) {
+    // the shared expert's down into y in the same launch (its blocks first; a
+    // multiple of 8 blocks, so the routed blocks keep their XCDs)
+    GemmArgs ds = shared_gateup_args(L, ws, x_bf16, with_shared->T, k, H, with_shared->Is, with_shared->shared);
+    ds.A = reinterpret_cast<const __bf16*>(ws + L.act_s);
+    ds.lda = with_shared->Is;
+    ds.out = with_shared->y;
+    const int n_shared = gemm_blocks((with_shared->T + kTM - 1) / kTM, false, H, with_shared->Is);
+    hipLaunchKernelGGL(k_gemm_down2, dim3(n_shared + down_blocks), dim3(kThreadsGemm), 0, s, d, ds, n_shared);
+  } else {
+    hipLaunchKernelGGL((k_gemm<false, true>), dim3(down_blocks), dim3(kThreadsGemm), 0, s, d);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint16_t* x_bf16, int T, int k,
-                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s, bool gateup_done) {
+                                 int H, int Is, const uint8_t* shared, float* y, hipStream_t s, bool gateup_done,
+                                 bool down_done) {
   const GemmArgs gs = shared_gateup_args(L, ws, x_bf16, T, k, H, Is, shared);
   // shared gate/up: dense over tokens (unless it ran with the routed one)
   if (!gateup_done)
@@ -729,7 +754,8 @@ hipError_t launch_prefill_shared(const PrefillLayout& L, uint8_t* ws, const uint
   ds.A = reinterpret_cast<const __bf16*>(ws + L.act_s);
   ds.lda = Is;
   ds.out = y;
-  hipLaunchKernelGGL((k_gemm<false, false>), dim3(gemm_blocks((T + kTM - 1) / kTM, false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
+  if (!down_done)
+    hipLaunchKernelGGL((k_gemm<false, false>), dim3(gemm_blocks((T + kTM - 1) / kTM, false, H, Is)), dim3(kThreadsGemm), 0, s, ds);
   const dim3 cg((H / 4 + 255) / 256, T);
   const float* out_r = reinterpret_cast<const float*>(ws + L.out_r);
   const int32_t* pos_of = reinterpret_cast<const int32_t*>(ws + L.pos_of);
@@ -744,9 +770,9 @@ hipError_t launch_prefill(const PrefillLayout& L, uint8_t* ws, const uint16_t* x
                           const uint8_t* shared, float* y, int32_t* ids_out, float* w_out,
                           hipStream_t s) {
   hipError_t e = launch_prefill_route(L, ws, x_bf16, logits_in, router, bias, T, E, k, H, ids_out, w_out, s);
-  const SharedGateup sg{shared, T, Is};
+  const SharedGateup sg{shared, T, Is, y};
   if (e == hipSuccess) e = launch_prefill_routed(L, ws, x_bf16, k, H, I, experts, blob_e, nullptr, s, &sg);
-  if (e == hipSuccess) e = launch_prefill_shared(L, ws, x_bf16, T, k, H, Is, shared, y, s, true);
+  if (e == hipSuccess) e = launch_prefill_shared(L, ws, x_bf16, T, k, H, Is, shared, y, s, true, true);
   return e;
 }
 
