@@ -971,8 +971,10 @@ moe_status moe_layer_prefill(moe_layer* L, const uint16_t* x_bf16, const float* 
   L->prof_now = L->prof && (L->prof_calls++ % L->prof_every) == 0;
   if (!moe::aligned16(x_bf16)) return fail(MOE_EALIGN, "%s: x_bf16 must be 16-byte aligned", fn);
   const moe_shape& sh = L->sh;
-  if (sh.inter % 64 || sh.shared_inter % 64 || sh.hidden % 128)
-    return fail(MOE_ESHAPE, "%s: needs inter and shared_inter multiples of 64 and hidden a multiple of 128", fn);
+  // the GEMMs take any K and row count in whole groups (32-row tiles; groups
+  // past K of a step weigh 0, a wave's second 32-row tile past H is not stored)
+  if (sh.inter % moe::kGroup || sh.shared_inter % moe::kGroup || sh.hidden % moe::kGroup)
+    return fail(MOE_ESHAPE, "%s: needs hidden, inter and shared_inter multiples of %d", fn, moe::kGroup);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const moe::PrefillLayout P = moe::prefill_layout(L->max_T, sh.n_experts, sh.top_k, sh.hidden, sh.inter,
                                                    sh.shared_inter);

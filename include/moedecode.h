@@ -336,7 +336,8 @@ moe_status moe_layer_decode(moe_layer* L, const float* x, const uint16_t* add_in
  * by expert; expert weights are dequantised to bf16 (one rounding of the
  * exact product) and multiplied on the matrix cores with fp32 accumulation; the GeGLU activation is rounded
  * to bf16 before the down projection. y dev fp32 [T][H]. ids_out / w_out
- * optional as in decode.
+ * optional as in decode. Any shape the handle holds (hidden, inter and
+ * shared_inter multiples of 32).
  * Resident mode: asynchronous on stream.
  * Cache mode (source: "Como executar um modelo de 26 bilhões de parâmetros em
  * dois gigabytes de memória em um Mac comum", section "Desempenho no mundo

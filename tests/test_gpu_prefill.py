@@ -6,7 +6,7 @@ import torch
 from bit_quantized_expert_softmax_amd import api
 from oracle import lfu, moe
 from synth import gen
-from synth.configs import GEMMA_LAYER, SMALL_LAYER
+from synth.configs import GEMMA_LAYER, SMALL_LAYER, Shape
 from tests.gpu_util import DEV, Layer, assert_close, dev, dev_u16, poisoned
 
 pytestmark = pytest.mark.gpu
@@ -43,6 +43,28 @@ def test_prefill_small_layer_given_logits(T):
     assert np.array_equal(ids, ref["ids"])
     assert_close(w, ref["w"], "w")
     assert_close(y, ref["y"], f"y T={T}")
+    L.close()
+
+
+# Odd shapes for the GEMM tiles (32-row weight tiles, 64 rows per wave): a
+# hidden size of 3 groups (96: the down projection's last wave holds one
+# 32-row tile inside H and one past it; the gate/up's K is 3 groups, an odd
+# number, so its last step holds one), routed rows of 3 and 5 groups, and
+# token counts that leave ragged 32-token tiles.
+@pytest.mark.parametrize("shape,T", [
+    (Shape(hidden=96, n_experts=8, top_k=2, inter=96, shared_inter=160), 77),
+    (Shape(hidden=160, n_experts=4, top_k=2, inter=160, shared_inter=96), 130),
+])
+def test_prefill_odd_shapes(shape, T):
+    d = gen.layer_inputs(shape, 11)
+    L = Layer(shape, d, max_T=T)
+    xb = gen.x_bf16(T, shape.hidden, 50 + T)
+    logits = gen.logits_uniform(T, shape.n_experts, 50 + T)
+    y, ids, w = run_prefill(L, xb, logits, T)
+    x = gen.bf16_bits_to_f32(xb).astype(np.float64)
+    ref = moe.prefill(x, shape, d["shared"], d["experts"], logits_in=logits)
+    assert np.array_equal(ids, ref["ids"])
+    assert_close(y, ref["y"], f"y H={shape.hidden} T={T}")
     L.close()
 
 
