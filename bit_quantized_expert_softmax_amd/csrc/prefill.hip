@@ -465,7 +465,7 @@ __device__ __forceinline__ void gemm_core(const GemmArgs& G, int nt, int r0, int
 }
 
 // One block's tile (block index bid of its job): the token rows of its tile
-// and its weight row tile, then the GEMM for the tile's number of 16-row
+// and its weight row tile, then the GEMM for the tile's number of 32-row
 // token tiles (block-uniform, so each count runs its own unrolled code).
 template <bool GATEUP, bool ROUTED>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& G, int bid, uint8_t* lds_b) {
