@@ -1032,15 +1032,18 @@ def main():
 
             def bstep(i):
                 api.moe_layer_decode(hbs[i % Lyr], xb[(i % 8) * B:(i % 8 + 1) * B], None, B, 0, yb, idsb)
-            for i in range(5):
+            # steady state: 4 untimed rotations over the layers first (the
+            # first touches each layer's pages; the clocks settle over about
+            # 100 ms of sustained work), then 8 timed rotations
+            n_warm, n_it = 4 * Lyr, 8 * Lyr
+            for i in range(n_warm):
                 bstep(i)
             torch.cuda.synchronize()
-            n_it = 60
             ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             ev0.record()
             touched = 0
             for i in range(n_it):
-                bstep(i)
+                bstep(n_warm + i)
             ev1.record()
             torch.cuda.synchronize()
             ms = ev0.elapsed_time(ev1) / n_it
@@ -1061,14 +1064,16 @@ def main():
         xp = torch.from_numpy(gen.x_bf16(Tp, H, 4).view(np.int16)).to(devn)
         lp = torch.from_numpy(gen.logits_uniform(Tp, E, 4)).to(devn)
         yp = torch.empty((Tp, H), device=devn)
-        for i in range(3):
+        # steady state, as for batched decode: 3 untimed rotations over the
+        # layers, then 2 timed ones
+        n_warm, n_it = 3 * Lyr, 2 * Lyr
+        for i in range(n_warm):
             api.moe_layer_prefill(hps[i % Lyr], xp, lp, Tp, yp)
         torch.cuda.synchronize()
-        n_it = 20
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         for i in range(n_it):
-            api.moe_layer_prefill(hps[i % Lyr], xp, lp, Tp, yp)
+            api.moe_layer_prefill(hps[(n_warm + i) % Lyr], xp, lp, Tp, yp)
         ev1.record()
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / n_it
