@@ -57,8 +57,9 @@ constexpr int kTile = 16;               // MFMA tile edge: rows and tokens
 constexpr int kStepK = 4 * kGroup;      // K per step: one group per 16-lane row
 constexpr int kBRow = kStepK * 2 + 16;  // LDS bytes per token of a step slice (padded)
 constexpr int kMR = 2;                  // 16-row weight tiles per wave
-// 16-byte scale chunks per lane and tile: a tile's 32 * K/32 scale bytes over
-// a wave, K <= kScaleIters * 64 * 16 = 4096
+// 16-byte scale chunks per lane and tile staged in registers in one batch: a
+// tile's 32 * K/32 scale bytes over a wave, up to K = kScaleIters * 64 * 16 =
+// 4096; the chunks past that (K above 4096) follow one per lane at a time
 constexpr int kScaleIters = 4;
 
 struct MArgs {
@@ -244,6 +245,8 @@ __device__ __forceinline__ void mfma_body(const MArgs& A, int s, int tile, int f
       const int c = lane + kWave * i;
       if (c < 2 * ngk) dst[c] = sv[mr][i];
     }
+    // K above 4096 (wave-uniform; no iteration at smaller K)
+    for (int c = lane + kWave * kScaleIters; c < 2 * ngk; c += kWave) dst[c] = ssrc[mr][c < scmax[mr] ? c : scmax[mr]];
   }
 
   for (int p0 = first; p0 < m; p0 += stride) {
@@ -459,8 +462,23 @@ __global__ void k_bcombine(const float* __restrict__ out_s, const float* __restr
 size_t mfma_static_lds(int ntt) { return 2 * static_cast<size_t>(ntt) * kTile * kBRow; }
 size_t mfma_scale_lds(int K) { return static_cast<size_t>(kWaves) * kMR * kTile * (K / kGroup) * 2; }
 int tiles_per_pass(int B) { return B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4); }
-constexpr size_t kMaxBlockLds = 65536;
 constexpr bool kSharedSplit = true;
+
+// LDS one block may use on the current device (160 KiB on gfx950), looked up
+// once per device; 64 KiB if the query fails.
+size_t block_lds_limit() {
+  constexpr int kDevs = 64;
+  static size_t cached[kDevs] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 65536;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+      v = 65536;
+    cached[dev] = static_cast<size_t>(v);
+  }
+  return cached[dev];
+}
 
 // ntt_r: tiles per pass of the routed experts' blocks, ntt_s: of the shared
 // expert's; the launch's static LDS is that of the larger.
@@ -468,7 +486,7 @@ template <bool GATEUP>
 hipError_t launch_mfma(const MArgs& A, int ntt_r, int ntt_s, hipStream_t s) {
   const dim3 grid(A.E * A.tiles_r + A.tiles_s);
   const size_t lds = mfma_scale_lds(GATEUP ? A.H : (A.I > A.Is ? A.I : A.Is));
-  if (mfma_static_lds(ntt_r > ntt_s ? ntt_r : ntt_s) + lds > kMaxBlockLds) return hipErrorInvalidValue;
+  if (mfma_static_lds(ntt_r > ntt_s ? ntt_r : ntt_s) + lds > block_lds_limit()) return hipErrorInvalidValue;
 #define MOE_MF(R_, DR_, S_, DS_) hipLaunchKernelGGL((k_mfma<GATEUP, R_, DR_, S_, DS_>), grid, dim3(kThreads), lds, s, A)
   if (ntt_r <= 1 && ntt_s <= 1) MOE_MF(1, 4, 1, 4);
   else if (ntt_r <= 1 && ntt_s == 2) MOE_MF(1, 4, 2, 4);
@@ -483,11 +501,9 @@ hipError_t launch_mfma(const MArgs& A, int ntt_r, int ntt_s, hipStream_t s) {
 }  // namespace
 
 bool batched_lds_fits(int H, int I, int Is, int max_B) {
-  // every K of the products within what a wave stages in kScaleIters chunks per lane
-  const int kmax = kScaleIters * kWave / 2 * kGroup;  // 2 * K/32 chunks <= kScaleIters * 64: K <= 4096
-  if (H > kmax || I > kmax || Is > kmax) return false;
   const size_t st = mfma_static_lds(tiles_per_pass(max_B));
-  return st + mfma_scale_lds(H) <= kMaxBlockLds && st + mfma_scale_lds(I > Is ? I : Is) <= kMaxBlockLds;
+  const size_t lim = block_lds_limit();
+  return st + mfma_scale_lds(H) <= lim && st + mfma_scale_lds(I > Is ? I : Is) <= lim;
 }
 
 hipError_t launch_batched(const BatchedBuffers& bb, const uint8_t* experts, const uint8_t* shared,

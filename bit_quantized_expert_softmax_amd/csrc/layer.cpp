@@ -335,7 +335,7 @@ moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_
   if (lds > 65536)
     return fail(MOE_ESHAPE, "%s: shape needs %zu bytes of LDS per decode block (limit 65536)", fn, lds);
   if (max_B > 1 && !moe::batched_lds_fits(sh->hidden, sh->inter, sh->shared_inter, max_B))
-    return fail(MOE_ESHAPE, "%s: batched decode of this shape needs more than 64 KiB of LDS per block or a K above 4096", fn);
+    return fail(MOE_ESHAPE, "%s: batched decode of this shape needs more LDS per block than the device has", fn);
   if (!d->router || !d->shared_blob || !d->workspace)
     return fail(MOE_EINVAL, "%s: router, shared_blob and workspace are required", fn);
   const bool cache_mode = d->experts_dev == nullptr;

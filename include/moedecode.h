@@ -284,9 +284,11 @@ moe_status moe_layer_workspace_bytes(const moe_shape* sh, int32_t max_B, int32_t
 /* Validates, clears the workspace counters (synchronously) and returns a handle.
  * The one-token kernels take hidden up to 8192 (MOE_ESHAPE above).
  * max_B > 1 (batched decode, resident mode) also needs the batched kernels'
- * per-block LDS (the staged group scales of 128 weight rows of length H, and
- * the activation slices of up to 64 tokens) to fit 64 KiB: MOE_ESHAPE if not
- * (max_B <= 16: H up to 7104; max_B > 32: H up to 3840). */
+ * per-block LDS (the staged group scales of 128 weight rows of length K, i.e.
+ * 8 K bytes for K = H and for K = max(inter, shared_inter), plus the
+ * activation slices of up to 64 tokens, 8.5 / 17 / 34 KiB for max_B up to
+ * 16 / 32 / above) to fit the device's LDS per block (160 KiB on gfx950:
+ * every hidden up to 8192 at any max_B): MOE_ESHAPE if not. */
 moe_status moe_layer_create(const moe_shape* sh, const moe_layer_desc* d, int32_t max_B,
                             int32_t max_T, moe_layer** out);
 void moe_layer_destroy(moe_layer* L);

@@ -7,7 +7,7 @@ import torch
 from bit_quantized_expert_softmax_amd import api
 from oracle import moe
 from synth import gen
-from synth.configs import GEMMA_LAYER, SMALL_LAYER, TINY_LAYER
+from synth.configs import GEMMA_LAYER, SMALL_LAYER, TINY_LAYER, Shape
 from tests.gpu_util import Layer, assert_close, dev, dev_u16, poisoned
 
 pytestmark = pytest.mark.gpu
@@ -127,4 +127,27 @@ def test_batched_input_scale(scale):
     r = moe.layer_decode(x.astype(np.float64), sh, d["router"], d["shared"], d["experts"])
     assert np.array_equal(ids, r["ids"])
     assert_close(y, r["y"], f"y scale={scale}")
+    L.close()
+
+
+# K above 4096 (the scales of a block's rows staged in more than one batch,
+# above 64 KiB of LDS per block): hidden 8192 (gate/up K = 8192, 128 KiB of
+# staged scales at 34 KiB of slices for B above 32) and a down projection of
+# K = 4608 (inter) and 4160 (shared_inter), with ragged and full token tiles.
+LARGE_K = [Shape(hidden=8192, n_experts=8, top_k=2, inter=64, shared_inter=96),
+           Shape(hidden=256, n_experts=8, top_k=2, inter=4608, shared_inter=4160)]
+
+
+@pytest.mark.parametrize("shape,B", [(LARGE_K[0], 5), (LARGE_K[0], 40), (LARGE_K[1], 7), (LARGE_K[1], 33)],
+                         ids=["H8192-B5", "H8192-B40", "I4608-B7", "I4608-B33"])
+def test_batched_decode_large_k(shape, B):
+    d = layer_data(shape, 11)
+    print(f"batched large K: H={shape.hidden} I={shape.inter} Is={shape.shared_inter} B={B}", flush=True)
+    L = Layer(shape, d, max_B=B)
+    x = gen.x_fp32(B, shape.hidden, 11, sub=B)
+    y, ids, w, _ = decode(L, x)
+    r = moe.layer_decode(x.astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+    assert np.array_equal(ids, r["ids"])
+    assert_close(w, r["w"], "w")
+    assert_close(y, r["y"], f"y B={B}")
     L.close()
