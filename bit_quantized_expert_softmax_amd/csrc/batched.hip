@@ -38,6 +38,7 @@
 // 1/tsc^2). down: a wave owns 32 output rows and writes one fp32 row per
 // assignment; the combine adds, per token and in rank order, w_j times its
 // routed rows to the shared expert's row (and the residual).
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -465,19 +466,22 @@ int tiles_per_pass(int B) { return B <= kTile ? 1 : (B <= 2 * kTile ? 2 : 4); }
 constexpr bool kSharedSplit = true;
 
 // LDS one block may use on the current device (160 KiB on gfx950), looked up
-// once per device; 64 KiB if the query fails.
+// once per device (threads that race on the first lookup store the same
+// value); 64 KiB if the query fails.
 size_t block_lds_limit() {
   constexpr int kDevs = 64;
-  static size_t cached[kDevs] = {};
+  static std::atomic<size_t> cached[kDevs];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 65536;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
-      v = 65536;
-    cached[dev] = static_cast<size_t>(v);
+  size_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int a = 0;
+    v = hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && a > 0
+            ? static_cast<size_t>(a)
+            : 65536;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 // ntt_r: tiles per pass of the routed experts' blocks, ntt_s: of the shared
