@@ -151,3 +151,20 @@ def test_batched_decode_large_k(shape, B):
     assert_close(w, r["w"], "w")
     assert_close(y, r["y"], f"y B={B}")
     L.close()
+
+
+# The largest batch a handle takes (max_B = 4096): 32768 assignments, 1024
+# tokens per routed expert on average (16 passes of 64 over each block's
+# rows) and a shared segment of 4096 tokens.
+def test_batched_decode_max_batch():
+    shape, B = SMALL_LAYER, 4096
+    d = layer_data(shape, 0)
+    L = Layer(shape, d, max_B=B)
+    x = gen.x_fp32(B, shape.hidden, 0, sub=B)
+    y, ids, w, u = decode(L, x)
+    r = moe.layer_decode(x.astype(np.float64), shape, d["router"], d["shared"], d["experts"])
+    assert np.array_equal(ids, r["ids"])
+    assert_close(w, r["w"], "w")
+    assert_close(y, r["y"], f"y B={B}")
+    assert np.array_equal(u, x)
+    L.close()

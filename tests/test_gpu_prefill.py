@@ -54,6 +54,7 @@ def test_prefill_small_layer_given_logits(T):
 @pytest.mark.parametrize("shape,T", [
     (Shape(hidden=96, n_experts=8, top_k=2, inter=96, shared_inter=160), 77),
     (Shape(hidden=160, n_experts=4, top_k=2, inter=160, shared_inter=96), 130),
+    (Shape(hidden=8192, n_experts=8, top_k=2, inter=64, shared_inter=96), 100),  # the largest hidden size
 ])
 def test_prefill_odd_shapes(shape, T):
     d = gen.layer_inputs(shape, 11)
@@ -164,6 +165,22 @@ def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, s
     Cm.close()
     if store is not None:
         api.moe_store_close(store)
+
+
+# The largest prefill a handle takes (max_T = 65536 tokens, 524288
+# assignments, 16384 rows per expert on average) on the small layer.
+def test_prefill_maximum_tokens():
+    sh, T = SMALL_LAYER, 65536
+    d = layer_data(sh, 0)
+    L = Layer(sh, d, max_T=T)
+    xb = gen.x_bf16(T, sh.hidden, 91)
+    logits = gen.logits_uniform(T, sh.n_experts, 91)
+    y, ids, w = run_prefill(L, xb, logits, T)
+    L.close()
+    ref = moe.prefill(gen.bf16_bits_to_f32(xb).astype(np.float64), sh, d["shared"], d["experts"], logits_in=logits)
+    assert np.array_equal(ids, ref["ids"])
+    assert_close(w, ref["w"], "w")
+    assert_close(y, ref["y"], f"y T={T}")
 
 
 def test_prefill_needs_max_T_and_empty_is_noop():
