@@ -78,6 +78,16 @@ def test_gemma_shape_splits(pos):
     check(st, pos, pos)
 
 
+# The longest context the Gemma-shaped step takes (max_ctx = 128 splits of
+# 128 positions at d = 256): half of it and its last position.
+@pytest.mark.parametrize("pos", [8192, 16383])
+def test_gemma_shape_longest_context(pos):
+    a = AttnShape(hidden=GEMMA_ATTN.hidden, n_heads=GEMMA_ATTN.n_heads, n_kv_heads=GEMMA_ATTN.n_kv_heads,
+                  head_dim=GEMMA_ATTN.head_dim, max_ctx=16384)
+    st = Step(a, filled=pos)
+    check(st, pos, pos)
+
+
 @pytest.mark.parametrize("a,pos", [(WIDE_GROUP, 300), (WIDE_GROUP, 1023), (MHA, 1500), (MHA, 3),
                                    (ONE_HEAD, 1099), (ONE_HEAD, 600)])
 def test_group_sizes_and_widths(a, pos):
