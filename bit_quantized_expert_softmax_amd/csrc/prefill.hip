@@ -9,12 +9,14 @@
 // rounding of the exact product); bf16 MFMA with fp32 accumulation computes
 // gate/up against activation tiles staged in LDS, the GeGLU activation is
 // rounded to bf16,
-// the down GEMM weights each row by its routing weight, and the shared
-// expert's down GEMM adds the k routed rows of every token in rank order.
+// the routed down GEMM weights each row by its routing weight, the shared
+// expert's down GEMM writes y, and a combine adds the k routed rows of every
+// token to it in rank order.
 //
 // Stages (one launch each): count per 256-assignment chunk, scan (expert
-// offsets and the GEMM tile table), stable scatter, routed + shared gate/up,
-// routed down, shared down, combine.
+// offsets and the GEMM tile table), stable scatter, shared + routed gate/up,
+// shared + routed down, combine (through the slot pool the routed GEMMs run
+// per group of resident experts, and the shared expert's on their own).
 #include <type_traits>
 
 #include "launch.h"
