@@ -7,13 +7,18 @@
 // the lower expert id, the weights are a softmax over the selected logits.
 //
 // Layer path (k_route_fused): one launch per call. Every block recomputes the
-// (cheap) RMSNorm of the token, quantises its share of the input groups to
-// digit planes for the expert GEMVs, and computes the logits of 4 experts in
-// fp64. The logits are written with agent-scope (L2-bypassing) stores; after
-// its stores have completed each block bumps its token's counter, and the
-// block that arrives last takes that token's top-k. No block waits for
-// another and no cache writeback is needed, so the launch costs little more
-// than its loads.
+// (cheap) RMSNorm of the token; the logit blocks compute the logits of 2
+// experts each (one per wave) in fp64, and blocks of their own after them
+// quantise the normalised input to digit planes for the expert GEMVs. Where
+// the launch also takes the top-k, the logits are written with agent-scope
+// (L2-bypassing) stores; after its stores have completed each block bumps its
+// token's counter, and the block that arrives last takes that token's top-k.
+// No block waits for another and no cache writeback is needed. Otherwise (one
+// token) the logits cross the kernel boundary and the top-k runs in a later
+// launch: in every routed gate/up block (resident), in the first block of the
+// shared-expert launch (cache mode, copy engine) or in a one-block selection
+// launch (cache mode with fill blocks or a device-stepped cache). The batched
+// router (k_route_tok) is described below.
 #include <float.h>
 #include <math.h>
 
