@@ -97,3 +97,30 @@ def test_widest_routing_prefill():
     assert_close(w.cpu().numpy(), ref["w"], "w")
     assert_close(y.cpu().numpy(), ref["y"], f"y T={T}")
     L.close()
+
+
+# The cache stepped on the device at the limits: 1024 experts, 16 ranks, the
+# fewest slots a token needs (16) and more (64), both policies; the trace is
+# the simulator's, the outputs the oracle's.
+@pytest.mark.parametrize("policy,slots", [("lfu", 16), ("lru", 16), ("lfu", 64)])
+def test_widest_routing_device_stepped_cache(policy, slots):
+    d = layer_data()
+    pol = api.MOE_POLICY_LRU if policy == "lru" else api.MOE_POLICY_LFU
+    L = Layer(WIDE, d, cache_slots=slots, cache_policy=pol, cache_on_device=True)
+    sim = lfu.LFUCache(slots, WIDE.n_experts, policy=policy)
+    xs = gen.x_fp32(8, WIDE.hidden, 23, sub=slots)
+    for t in range(xs.shape[0]):
+        print(f"limits: device-stepped cache {policy} slots={slots} token {t}", flush=True)
+        y, ids, w, tr = decode(L, xs[t:t + 1], trace_k=WIDE.top_k)
+        r = moe.layer_decode(xs[t].astype(np.float64), WIDE, d["router"], d["shared"], d["experts"])
+        assert np.array_equal(ids, r["ids"]), t
+        assert [tuple(e) for e in tr.tolist()] == [tuple(e) for e in sim.step(ids[0])], t
+        assert_close(y, r["y"], f"y t={t}")
+    ex, fr, la, hits, misses, steps = api.moe_layer_cache_state(L.h, slots)
+    assert list(ex) == list(sim.expert) and list(fr) == list(sim.freq) and list(la) == list(sim.last)
+    assert (hits, misses, steps) == (sim.hits, sim.misses, xs.shape[0])
+    pool = L.pool.cpu().numpy()
+    for s_, e in enumerate(sim.expert):
+        if e >= 0:
+            assert np.array_equal(pool[s_], d["experts"][e]), (s_, e)
+    L.close()
