@@ -110,7 +110,10 @@ def test_prefill_full_2048_tokens():
 @pytest.mark.parametrize("shape,slots,T,source,chunk", [(SMALL_LAYER, 8, 300, "host", 128),
                                                          (SMALL_LAYER, 8, 300, "store", 128),
                                                          (GEMMA_LAYER, 16, 260, "host", 128),
-                                                         (SMALL_LAYER, 8, 300, "host", 300)])
+                                                         (SMALL_LAYER, 8, 300, "host", 300),
+                                                         # the routing limits: 1024 experts, top 16 (55 groups of 16 per chunk)
+                                                         (Shape(hidden=256, n_experts=1024, top_k=16, inter=32, shared_inter=64),
+                                                          16, 300, "host", 128)])
 def test_prefill_through_slot_pool_matches_resident(tmp_path, shape, slots, T, source, chunk):
     """Chunks of 128 tokens (or one chunk) through the LFU slot pool (ragged last chunk) give
     the resident prefill's bits, ids and weights; the cache ends in the
