@@ -20,6 +20,9 @@ WIDE_GROUP = AttnShape(hidden=1024, n_heads=8, n_kv_heads=2, head_dim=128, max_c
 MHA = AttnShape(hidden=256, n_heads=2, n_kv_heads=2, head_dim=64, max_ctx=2048)
 # one query head of width 64: a combine grid of one partly used block
 ONE_HEAD = AttnShape(hidden=128, n_heads=1, n_kv_heads=1, head_dim=64, max_ctx=1100)
+# the widest step the library takes: hidden 4096, 32 query heads of 256 over 8
+# key/value heads (n_heads * d = 8192)
+WIDEST = AttnShape(hidden=4096, n_heads=32, n_kv_heads=8, head_dim=256, max_ctx=640)
 
 
 class Step:
@@ -89,7 +92,7 @@ def test_gemma_shape_longest_context(pos):
 
 
 @pytest.mark.parametrize("a,pos", [(WIDE_GROUP, 300), (WIDE_GROUP, 1023), (MHA, 1500), (MHA, 3),
-                                   (ONE_HEAD, 1099), (ONE_HEAD, 600)])
+                                   (ONE_HEAD, 1099), (ONE_HEAD, 600), (WIDEST, 639), (WIDEST, 64)])
 def test_group_sizes_and_widths(a, pos):
     st = Step(a, filled=pos)
     check(st, pos, pos)
