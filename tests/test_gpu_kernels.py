@@ -160,3 +160,40 @@ def test_route_given_logits_and_ties():
     assert ids[2].tolist() == [3, 7, 12, 0, 1, 2, 4, 5]
     assert ids[3].tolist() == [40, 0, 1, 2, 3, 4, 5, 6]
     assert_close(w.cpu().numpy(), r_w, "w")
+
+
+def _order_with_nonfinite(z, k):
+    """Rank order of one token's logits as the library takes it for non-finite
+    values: +inf above every number, NaN below every number (-inf included),
+    -0 equal to +0, ties to the lower id. The oracle is not defined on
+    non-finite logits; this is the property the ids must have."""
+    def key(e):
+        v = z[e]
+        if np.isnan(v):
+            return (0, 0.0, e)
+        return (1, -float(v) if v != 0 else 0.0, e)
+    order = sorted(range(len(z)), key=lambda e: (-key(e)[0], key(e)[1], e))
+    return order[:k]
+
+
+def test_route_nonfinite_logits_give_valid_ids():
+    sh = GEMMA_LAYER
+    T = 6
+    logits = gen.logits_uniform(T, sh.n_experts, 8)
+    logits[0] = np.nan                                  # all NaN: ids 0..7
+    logits[1, 3] = np.inf                               # +inf first, NaNs never chosen
+    logits[1, 0:3] = np.nan
+    logits[2, ::2] = np.nan                             # half NaN: the top 8 odd experts
+    logits[3, 10] = -np.inf                             # -inf below every finite value
+    logits[3, :] = np.where(np.arange(sh.n_experts) == 10, -np.inf, -1e30)
+    logits[4, 50] = np.inf                              # two +inf: the lower id first
+    logits[4, 20] = np.inf
+    logits[5] = -np.inf                                 # all -inf: ids 0..7
+    ids = poisoned((T, sh.top_k), torch.int32)
+    w = poisoned((T, sh.top_k))
+    api.moe_route(sh, None, None, None, dev(logits), T, ids, w, None)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    for t in range(T):
+        assert got[t].tolist() == _order_with_nonfinite(logits[t], sh.top_k), t
+        assert len(set(got[t].tolist())) == sh.top_k and got[t].min() >= 0 and got[t].max() < sh.n_experts

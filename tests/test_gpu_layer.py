@@ -278,3 +278,33 @@ def test_empty_call_and_errors():
     with pytest.raises(api.MoeError):
         api.moe_layer_decode(L.h, x, None, 1, 0, x)     # y aliases x
     L.close()
+
+
+@pytest.mark.parametrize("mode", ["resident", "copy_engine", "batched"])
+def test_nonfinite_input_gives_valid_ids_and_the_handle_recovers(mode):
+    """A token whose input holds a NaN: every logit is NaN, so the ids are the
+    lowest k (NaN ranks below every number, ties to the lower id), the output
+    is not finite, nothing faults, and the next finite tokens decode as the
+    oracle says (in cache mode the NaN token's ids step the cache like any
+    other). The oracle is not defined on NaN inputs; this is a property."""
+    sh = SMALL_LAYER
+    d = layer_data(sh, 0)
+    cache = mode == "copy_engine"
+    B = 4 if mode == "batched" else 1
+    L = Layer(sh, d, cache_slots=sh.top_k if cache else 0, max_B=B)
+    sim = lfu.LFUCache(sh.top_k, sh.n_experts)
+    xs = gen.x_fp32(3 * B, sh.hidden, 0, sub=13)
+    xs[0:B, 5] = np.nan
+    for t in range(3):
+        x = xs[t * B:(t + 1) * B]
+        y, ids, w, u, tr = run_decode(L, dev(x), trace_k=sh.top_k if cache else 0)
+        if t == 0:
+            assert all(ids[b].tolist() == list(range(sh.top_k)) for b in range(B))
+            assert not np.isfinite(y).all()
+        else:
+            r = moe.layer_decode(x.astype(np.float64), sh, d["router"], d["shared"], d["experts"])
+            assert np.array_equal(ids, r["ids"]), t
+            assert_close(y, r["y"], f"y t={t}")
+        if cache:
+            assert [tuple(e) for e in tr.tolist()] == [tuple(e) for e in sim.step(ids[0])], t
+    L.close()
