@@ -50,7 +50,9 @@ def test_read_floor_reads_every_word(n16, blocks):
 
 @pytest.mark.parametrize("N,K,M", [(128, 512, 1), (256, 512, 3), (37, 32, 2), (704, 2816, 1),
                                    (2816, 704, 1), (2816, 2112, 1), (300, 2816, 8), (64, 1024, 17),
-                                   (5, 16384, 1)])
+                                   (5, 16384, 1),
+                                   # the limits: N and K up to 16384, M up to 64 token rows
+                                   (16384, 512, 64), (333, 16384, 64), (16384, 16384, 2)])
 def test_gemv_q4_against_oracle(N, K, M):
     q, s = _q4(N, K, N * 7 + K)
     x = gen.x_fp32(M, K, 50, sub=N)
